@@ -1,0 +1,129 @@
+"""Named workloads and seeded synthetic inputs for the selective scan.
+
+This module only draws random numbers and lays them out; it holds none of the
+scan's arithmetic, so both the HIP path and the fp64 oracle can be fed from it.
+
+Recipe (the same for every workload):
+  * numpy ``Generator(PCG64(seed))``; draws are float64, rounded to float32
+    (round-to-nearest-even) and, for bf16 I/O, further rounded to bf16 (RNE).
+  * Fixed draw order: x, delta_raw, z, B, C, D_skip, u (for dt_bias), h0/state, dy.
+  * x, delta_raw, z, B, C, dy ~ N(0, 1).  B and C are [batch, seqlen, dstate],
+    i.e. shared by every channel of a (batch, time) position.
+  * A_log[d, n] = log(n + 1), so A = -(n + 1) for every channel.
+  * "bias" distributions:
+      - "zero":  dt_bias = 0 and D_skip ~ N(0, 1)        (small fp32 case)
+      - "mamba": dt_bias[d] = log(expm1(u_d)), u_d ~ U[1e-3, 1e-1] (so that
+                 softplus(dt_bias) = u_d), and D_skip = 1.
+  * A decode state (step workloads) ~ N(0, sd = 0.1).  Scans start from h0 = 0
+    unless a test asks for a random h0 (also N(0, 0.1)).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str        # "fwd", "step" or "fwdbwd"
+    batch: int
+    seqlen: int
+    dim: int         # d_inner, the channel count
+    dstate: int      # N
+    io: str          # "f32" or "bf16": dtype of x, delta_raw, z, B, C, y (state and params stay fp32)
+    gated: bool
+    bias: str        # "zero" or "mamba"
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+    @property
+    def state_updates(self) -> int:
+        return self.elements * self.dstate
+
+
+# The five workloads the build is measured and checked on.
+WORKLOADS = {
+    "fwd_small": Workload("fwd_small", "fwd", 1, 64, 16, 4, "f32", False, "zero", 1001),
+    "fwd_b8_l2048_d1536": Workload("fwd_b8_l2048_d1536", "fwd", 8, 2048, 1536, 16, "f32", True, "mamba", 1002),
+    "fwd_bf16_b4_l4096_d4096": Workload("fwd_bf16_b4_l4096_d4096", "fwd", 4, 4096, 4096, 16, "bf16", True, "mamba", 1003),
+    "step_b256_d5120": Workload("step_b256_d5120", "step", 256, 1, 5120, 16, "f32", True, "mamba", 1004),
+    "fwdbwd_b4_l2048_d2048": Workload("fwdbwd_b4_l2048_d2048", "fwdbwd", 4, 2048, 2048, 16, "f32", True, "mamba", 1005),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest-even) and return the raw uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_io(a: np.ndarray, io: str) -> np.ndarray:
+    """float64 -> float32 (RNE) -> optionally bf16 (RNE); returned as float32 values."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    if io == "bf16":
+        f = bf16_bits_to_f32(f32_to_bf16_bits(f))
+    return f
+
+
+def make_inputs(w: Workload, *, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                dim: Optional[int] = None, dstate: Optional[int] = None,
+                gated: Optional[bool] = None, random_h0: bool = False,
+                seed: Optional[int] = None, with_dy: Optional[bool] = None) -> dict:
+    """Seeded inputs of workload ``w`` (optionally at other sizes, same distributions).
+
+    Returns float32 numpy arrays (bf16-representable where ``w.io == "bf16"``):
+      scan workloads: x, delta_raw, z|None, B, C, A_log, D, dt_bias, h0|None, dy|None
+      step workloads: state, x, delta_raw, z|None, B, C, A_log, D, dt_bias
+    plus "io" and the dims.
+    """
+    b = w.batch if batch is None else batch
+    l = w.seqlen if seqlen is None else seqlen
+    d = w.dim if dim is None else dim
+    n = w.dstate if dstate is None else dstate
+    g = w.gated if gated is None else gated
+    want_dy = (w.kind == "fwdbwd") if with_dy is None else with_dy
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    io = w.io
+    step = w.kind == "step"
+    act = (b, d) if step else (b, l, d)
+    bc = (b, n) if step else (b, l, n)
+
+    x = round_to_io(rng.standard_normal(act), io)
+    delta_raw = round_to_io(rng.standard_normal(act), io)
+    z = round_to_io(rng.standard_normal(act), io) if g else None
+    B = round_to_io(rng.standard_normal(bc), io)
+    C = round_to_io(rng.standard_normal(bc), io)
+    if w.bias == "zero":
+        D = rng.standard_normal(d).astype(np.float32)
+        dt_bias = np.zeros(d, np.float32)
+    elif w.bias == "mamba":
+        D = np.ones(d, np.float32)
+        u = rng.uniform(1e-3, 1e-1, size=d)
+        dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    else:
+        raise ValueError("unknown bias distribution %r" % w.bias)
+    A_log = np.broadcast_to(np.log(np.arange(1, n + 1, dtype=np.float64)), (d, n)).astype(np.float32)
+    A_log = np.ascontiguousarray(A_log)
+    out = {"io": io, "batch": b, "seqlen": 1 if step else l, "dim": d, "dstate": n,
+           "x": x, "delta_raw": delta_raw, "z": z, "B": B, "C": C,
+           "A_log": A_log, "D": D, "dt_bias": dt_bias}
+    if step:
+        out["state"] = (0.1 * rng.standard_normal((b, d, n))).astype(np.float32)
+    else:
+        out["h0"] = (0.1 * rng.standard_normal((b, d, n))).astype(np.float32) if random_h0 else None
+        out["dy"] = rng.standard_normal((b, l, d)).astype(np.float32) if want_dy else None
+    return out
