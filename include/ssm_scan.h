@@ -1,0 +1,134 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the gfx950 (MI355X) selective-scan library.
+ *
+ * The operation (Mamba selective scan, names as on the pages):
+ *   Delta[b,t,d] = softplus(delta_raw[b,t,d] + dt_bias[d])      discretisation
+ *   A[d,n]       = -exp(A_log[d,n])
+ *   h_t[b,d,n]   = exp(Delta_t A[d,n]) h_{t-1}[b,d,n] + Delta_t B[b,t,n] x[b,t,d]
+ *   s_t[b,d]     = sum_n C[b,t,n] h_t[b,d,n] + D[d] x[b,t,d]    readout from the updated state
+ *   y[b,t,d]     = s_t silu(z[b,t,d])   (y = s_t when z is NULL)  optional SiLU gate
+ * Passages that define it: the selective_scan_kernel and its softplus device
+ * function in the POPCORNBENCH transcript "FW-GLM-5-1 l2_p30" (recurrence order,
+ * readout after the update, skip term D*x); mamba-rs kernels.rs, MambaKernels
+ * (ssm_step_fwd "single-step SSM forward (T=1 inference)", exp_negate,
+ * softplus_fwd, split_gate_silu and gating_backward "y = ssm_out * gate_silu",
+ * and the gradient shapes of ssm_reduce_d_B/_C/_D/_a_log).
+ *
+ * Conventions shared by every entry point
+ *   Layout: contiguous row-major, last index fastest.
+ *     x, delta_raw, z, y, dy, dx, ddelta_raw, dz : [batch, seqlen, d_inner]
+ *     B, C                                      : [batch, seqlen, d_state]  (shared by all channels)
+ *     dB, dC                                    : [batch, seqlen, d_state]  fp32
+ *     A_log, dA_log                             : [d_inner, d_state]        fp32
+ *     D_skip, dt_bias, dD, d_dt_bias            : [d_inner]                 fp32
+ *     h0, h_final, state                        : [batch, d_inner, d_state] fp32
+ *   io_dtype (ssm_dtype) is the element type of x, delta_raw, z, B, C, y (and of
+ *   dy, dx, ddelta_raw, dz in the backward).  Parameters, states and all
+ *   arithmetic are fp32.  bf16 results are rounded to nearest even.
+ *   Pointers are device pointers (hipMalloc / torch CUDA tensors), naturally
+ *   aligned for their element type.  Outputs must not overlap inputs, except
+ *   `state` of ssm_scan_step, which is read and written in place.
+ *   Ownership: the caller allocates and frees every buffer, including any
+ *   workspace; the library allocates no device memory and keeps no pointer
+ *   after a call returns.
+ *   Asynchrony: work is enqueued on `stream` (NULL = the default stream) and the
+ *   call returns without waiting.  Faults inside a kernel surface at the
+ *   caller's next synchronisation.
+ *   Errors: every call returns an ssm_status.  Arguments are validated before
+ *   anything is enqueued, so a call that returns a validation error has launched
+ *   nothing.  A launch failure returns SSM_ERR_HIP.  No C++ exception crosses
+ *   this boundary.  ssm_status_string() names a status.
+ *   Determinism: for fixed sizes every output is bit-identical from run to run;
+ *   sums over channels, batch and time are taken in a fixed order, with no
+ *   atomics.
+ *   Supported sizes: batch, seqlen, d_inner >= 1; 1 <= d_state <= 16.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  SSM_ERR_DIM = 2,         /* a size is out of range                              */
+  SSM_ERR_UNSUPPORTED = 3, /* valid request this build does not handle            */
+  SSM_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size        */
+  SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
+  SSM_ERR_ALIAS = 6,       /* an output overlaps an input                         */
+  SSM_ERR_HIP = 7          /* the HIP runtime reported an error at launch         */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ssm_status_string(int status);
+
+/* Forward scan over a whole sequence.
+ *   Inputs : x, delta_raw, B, C (io_dtype); A_log (fp32) required.
+ *            z (io_dtype) optional: NULL means no gate.
+ *            D_skip, dt_bias (fp32) optional: NULL means zero.
+ *            h0 (fp32) optional: NULL means a zero initial state.
+ *   Outputs: y (io_dtype) required; h_final (fp32) optional (NULL: not written),
+ *            the state after the last step.
+ *   workspace: optional scratch for the time-split path that long sequences of
+ *            few channels use; ssm_scan_fwd_workspace_bytes() gives the size that
+ *            enables it (0 when it is never used).  NULL or a smaller buffer is
+ *            not an error: the scan then runs unsplit.
+ *   io_dtype: SSM_F32 or SSM_BF16. */
+size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                    int64_t d_state, int io_dtype);
+int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void* B,
+                 const void* C, const float* A_log, const float* D_skip, const float* dt_bias,
+                 const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int io_dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Single-step decode update (the scan at seqlen = 1), state updated in place.
+ *   state [batch, d_inner, d_state] fp32, read and written.
+ *   x, delta_raw, z (z optional) : [batch, d_inner] io_dtype.
+ *   B, C                         : [batch, d_state] io_dtype.
+ *   y                            : [batch, d_inner] io_dtype, written. */
+int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void* z,
+                  const void* B, const void* C, const float* A_log, const float* D_skip,
+                  const float* dt_bias, void* y, int64_t batch, int64_t d_inner,
+                  int64_t d_state, int io_dtype, hipStream_t stream);
+
+/* Backward of ssm_scan_fwd for the loss gradient dy = dLoss/dy.
+ *   Inputs : the forward's inputs (same meaning, h0 optional) and dy (io_dtype).
+ *   Outputs (overwritten, never accumulated):
+ *     dx, ddelta_raw (io_dtype, required), dz (io_dtype, required iff z != NULL),
+ *     dB, dC (fp32, required), dA_log, dD, d_dt_bias (fp32, optional: NULL means
+ *     not written).  dD and d_dt_bias are the gradients as if D_skip / dt_bias
+ *     were present (they are when NULL, with value zero).
+ *   The gradient flowing into h_final is taken as zero and no gradient of h0 is
+ *   produced.
+ *   workspace: required, at least ssm_scan_bwd_workspace_bytes() bytes, 256-byte
+ *   aligned; its contents on entry are ignored.
+ *   Reductions: dB and dC (sums over channels), dA_log, dD and d_dt_bias (sums
+ *   over batch and time) are fixed-order fp32 sums of per-tile partials, without
+ *   atomics, following the single-writer ordered-reduction policy of
+ *   deterministic_backward.py (ordered_cumsum: partials added in lexical
+ *   (batch, chunk) order) and the deterministic row partial of
+ *   mamba3_preprocess_backward.slang (dt_bias_partial).
+ *   This build supports io_dtype = SSM_F32 only (SSM_ERR_UNSUPPORTED otherwise). */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                    int64_t d_state, int io_dtype);
+int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void* B,
+                 const void* C, const float* A_log, const float* D_skip, const float* dt_bias,
+                 const float* h0, const void* dy, void* dx, void* ddelta_raw, void* dz,
+                 float* dB, float* dC, float* dA_log, float* dD, float* d_dt_bias,
+                 void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,174 @@
+// ssm_api.hip -- the extern "C" entry points declared in include/ssm_scan.h.
+// Every argument is validated before anything is enqueued; launch errors are mapped
+// to SSM_ERR_HIP.  No exception crosses the boundary.
+#include <stdint.h>
+
+#include <new>
+
+#include "../../include/ssm_scan.h"
+#include "ssm_internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool dims_ok(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state < 1 || d_state > 16) return false;
+  // element counts must fit comfortably in int64 byte offsets and grid sizes
+  const int64_t lim = (int64_t)1 << 40;
+  if (batch > lim / seqlen) return false;
+  if (batch * seqlen > lim / d_inner) return false;
+  if ((d_inner + 63) / 64 * batch > ((int64_t)1 << 31) - 1) return false;
+  return true;
+}
+
+size_t esize(int io_dtype) { return io_dtype == SSM_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
+    case SSM_ERR_DIM: return "SSM_ERR_DIM: a size is out of range";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: request not handled by this build";
+    case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: a pointer is not aligned to its element size";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown ssm_status";
+  }
+}
+
+size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                    int io_dtype) {
+  (void)batch; (void)seqlen; (void)d_inner; (void)d_state; (void)io_dtype;
+  return 0;  // this build always runs the scan unsplit
+}
+
+int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void* B, const void* C,
+                 const float* A_log, const float* D_skip, const float* dt_bias, const float* h0, void* y,
+                 float* h_final, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int io_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (!x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
+  const size_t es = esize(io_dtype);
+  const void* io_in[] = {x, delta_raw, z, B, C};
+  for (const void* p : io_in)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_in[] = {A_log, D_skip, dt_bias, h0, h_final};
+  for (const void* p : f_in)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  if (!aligned(y, es)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
+  const size_t H = (size_t)batch * d_inner * d_state;
+  const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
+                       rng(C, S * es), rng(A_log, (size_t)d_inner * d_state * 4),
+                       rng(D_skip, D_skip ? d_inner * 4 : 0), rng(dt_bias, dt_bias ? d_inner * 4 : 0),
+                       rng(h0, h0 ? H * 4 : 0)};
+  const Range outs[] = {rng(y, E * es), rng(h_final, h_final ? H * 4 : 0)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return SSM_ERR_ALIAS;
+  if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+
+  ssm::FwdArgs a;
+  a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log; a.D_skip = D_skip;
+  a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
+  a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
+  a.bf16 = io_dtype == SSM_BF16;
+  return ssm::launch_fwd(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void* z, const void* B,
+                  const void* C, const float* A_log, const float* D_skip, const float* dt_bias, void* y,
+                  int64_t batch, int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream) {
+  if (!state || !x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!dims_ok(batch, 1, d_inner, d_state)) return SSM_ERR_DIM;
+  if (batch * d_inner * 4 >= ((int64_t)1 << 31) * 256) return SSM_ERR_DIM;  // grid limit
+  const size_t es = esize(io_dtype);
+  const void* io_in[] = {x, delta_raw, z, B, C, y};
+  for (const void* p : io_in)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_in[] = {state, A_log, D_skip, dt_bias};
+  for (const void* p : f_in)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * d_inner, S = (size_t)batch * d_state, H = E * d_state;
+  const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
+                       rng(C, S * es), rng(A_log, (size_t)d_inner * d_state * 4),
+                       rng(D_skip, D_skip ? d_inner * 4 : 0), rng(dt_bias, dt_bias ? d_inner * 4 : 0)};
+  const Range outs[] = {rng(state, H * 4), rng(y, E * es)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return SSM_ERR_ALIAS;
+  if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+
+  ssm::StepArgs a;
+  a.state = state; a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log;
+  a.D_skip = D_skip; a.dt_bias = dt_bias; a.y = y;
+  a.batch = batch; a.dim = d_inner; a.dstate = (int)d_state; a.bf16 = io_dtype == SSM_BF16;
+  return ssm::launch_step(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                    int io_dtype) {
+  (void)io_dtype;
+  if (!dims_ok(batch, seqlen, d_inner, d_state)) return 0;
+  return ssm::bwd_layout(batch, seqlen, d_inner, (int)d_state).total;
+}
+
+int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void* B, const void* C,
+                 const float* A_log, const float* D_skip, const float* dt_bias, const float* h0,
+                 const void* dy, void* dx, void* ddelta_raw, void* dz, float* dB, float* dC, float* dA_log,
+                 float* dD, float* d_dt_bias, void* workspace, size_t workspace_bytes, int64_t batch,
+                 int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream) {
+  if (!x || !delta_raw || !B || !C || !A_log || !dy || !dx || !ddelta_raw || !dB || !dC) return SSM_ERR_NULL;
+  if (z && !dz) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
+  if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
+  if (!workspace) return SSM_ERR_WORKSPACE;
+  const ssm::BwdLayout l = ssm::bwd_layout(batch, seqlen, d_inner, (int)d_state);
+  if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
+  const void* all[] = {x, delta_raw, z, B, C, A_log, D_skip, dt_bias, h0, dy,
+                       dx, ddelta_raw, dz, dB, dC, dA_log, dD, d_dt_bias};
+  for (const void* p : all)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
+  const size_t H = (size_t)batch * d_inner * d_state, P = (size_t)d_inner * d_state;
+  const Range ins[] = {rng(x, E * 4), rng(delta_raw, E * 4), rng(z, z ? E * 4 : 0), rng(B, S * 4),
+                       rng(C, S * 4), rng(A_log, P * 4), rng(D_skip, D_skip ? d_inner * 4 : 0),
+                       rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * 4)};
+  const Range outs[] = {rng(dx, E * 4), rng(ddelta_raw, E * 4), rng(dz, dz && z ? E * 4 : 0),
+                        rng(dB, S * 4), rng(dC, S * 4), rng(dA_log, dA_log ? P * 4 : 0),
+                        rng(dD, dD ? d_inner * 4 : 0), rng(d_dt_bias, d_dt_bias ? d_inner * 4 : 0),
+                        rng(workspace, l.total)};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+
+  ssm::BwdArgs a;
+  a.x = (const float*)x; a.delta_raw = (const float*)delta_raw; a.z = (const float*)z;
+  a.B = (const float*)B; a.C = (const float*)C; a.A_log = A_log; a.D_skip = D_skip; a.dt_bias = dt_bias;
+  a.h0 = h0; a.dy = (const float*)dy; a.dx = (float*)dx; a.ddelta_raw = (float*)ddelta_raw;
+  a.dz = z ? (float*)dz : nullptr; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
+  a.d_dt_bias = d_dt_bias; a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
+  return ssm::launch_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

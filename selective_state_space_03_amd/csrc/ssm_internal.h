@@ -1,0 +1,80 @@
+// ssm_internal.h -- launch interface between the C ABI (ssm_api.hip) and the kernels.
+// Host-side only declarations; arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct FwdArgs {
+  const void* x;
+  const void* delta_raw;
+  const void* z;  // nullable
+  const void* B;
+  const void* C;
+  const float* A_log;
+  const float* D_skip;   // nullable
+  const float* dt_bias;  // nullable
+  const float* h0;       // nullable
+  void* y;
+  float* h_final;  // nullable
+  int64_t batch, seqlen, dim;
+  int dstate;
+  int bf16;  // io dtype is bf16
+};
+
+struct StepArgs {
+  float* state;
+  const void* x;
+  const void* delta_raw;
+  const void* z;  // nullable
+  const void* B;
+  const void* C;
+  const float* A_log;
+  const float* D_skip;   // nullable
+  const float* dt_bias;  // nullable
+  void* y;
+  int64_t batch, dim;
+  int dstate;
+  int bf16;
+};
+
+struct BwdArgs {
+  const float* x;
+  const float* delta_raw;
+  const float* z;  // nullable
+  const float* B;
+  const float* C;
+  const float* A_log;
+  const float* D_skip;   // nullable
+  const float* dt_bias;  // nullable
+  const float* h0;       // nullable
+  const float* dy;
+  float* dx;
+  float* ddelta_raw;
+  float* dz;  // non-null iff z
+  float* dB;
+  float* dC;
+  float* dA_log;     // nullable
+  float* dD;         // nullable
+  float* d_dt_bias;  // nullable
+  int64_t batch, seqlen, dim;
+  int dstate;
+};
+
+// Workspace layout of the backward (byte offsets into one caller buffer).
+struct BwdLayout {
+  int chunk;         // time steps per chunk
+  int64_t nchunks;   // ceil(seqlen / chunk)
+  int64_t ngroups;   // ceil(dim / 64) channel groups
+  size_t off_hloc, off_sumdelta, off_hstart, off_dbc, off_dparam, total;
+};
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,161 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/ssm_scan.h declares, and rejects invalid arguments with the documented
+status codes *before* enqueueing anything.  Every call here fails validation, so
+no HIP call is made and no GPU is needed (pointer values are fake addresses that
+are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from selective_state_space_03_amd import ops
+
+# Every call below is built to fail validation.  As a second line of defence, the
+# fake-pointer calls never run where a GPU is visible: a call that passed
+# validation by mistake would launch a kernel on addresses that do not exist.
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                 reason="fake-pointer validation checks run only where no GPU is visible")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+OK, NULL, DIM, UNSUP, ALIGN, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTS), names
+    L = ops.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = ops.lib()
+    for code, name in ops.STATUS.items():
+        assert L.ssm_status_string(code).decode().startswith(name)
+    assert b"unknown" in L.ssm_status_string(99)
+
+
+# fake, well-aligned, non-overlapping device addresses (never dereferenced)
+BASE = 1 << 40
+STRIDE = 1 << 32
+
+
+def addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * STRIDE + off)
+
+
+def fwd_args(**over):
+    a = dict(x=addr(0), delta_raw=addr(1), z=addr(2), B=addr(3), C=addr(4), A_log=addr(5), D=addr(6),
+             dt_bias=addr(7), h0=None, y=addr(8), h_final=addr(9), b=2, l=16, d=64, n=16,
+             io=ops.SSM_F32, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return a
+
+
+def call_fwd(a):
+    return ops.lib().ssm_scan_fwd(a["x"], a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"], a["D"],
+                                  a["dt_bias"], a["h0"], a["y"], a["h_final"], a["b"], a["l"], a["d"],
+                                  a["n"], a["io"], a["ws"], a["wsb"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field", ["x", "delta_raw", "B", "C", "A_log", "y"])
+def test_fwd_null_required_pointer(field):
+    assert call_fwd(fwd_args(**{field: None})) == NULL
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over", [dict(n=0), dict(n=17), dict(b=0), dict(l=0), dict(d=0), dict(l=-5),
+                                  dict(b=1 << 40, l=1 << 20)])
+def test_fwd_bad_dims(over):
+    assert call_fwd(fwd_args(**over)) == DIM
+
+
+@no_gpu_only
+def test_fwd_bad_dtype():
+    assert call_fwd(fwd_args(io=7)) == UNSUP
+
+
+@no_gpu_only
+def test_fwd_misaligned():
+    assert call_fwd(fwd_args(x=addr(0, 2))) == ALIGN            # fp32 needs 4 B
+    assert call_fwd(fwd_args(y=addr(8, 1), io=ops.SSM_BF16)) == ALIGN
+    assert call_fwd(fwd_args(A_log=addr(5, 2))) == ALIGN
+
+
+@no_gpu_only
+def test_fwd_aliasing():
+    assert call_fwd(fwd_args(y=addr(0))) == ALIAS               # y == x
+    assert call_fwd(fwd_args(h_final=addr(5))) == ALIAS         # h_final == A_log
+    assert call_fwd(fwd_args(h_final=addr(8, 64))) == ALIAS     # inside y
+
+
+def test_workspace_sizes():
+    L = ops.lib()
+    assert L.ssm_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 0) == 0
+    wb = L.ssm_scan_bwd_workspace_bytes(4, 2048, 2048, 16, 0)
+    assert wb > 0 and wb % 256 == 0
+    assert L.ssm_scan_bwd_workspace_bytes(4, 2048, 2048, 17, 0) == 0   # invalid sizes
+    # grows with every size
+    assert L.ssm_scan_bwd_workspace_bytes(4, 4096, 2048, 16, 0) > wb
+    assert L.ssm_scan_bwd_workspace_bytes(8, 2048, 2048, 16, 0) > wb
+
+
+def step_call(**over):
+    a = dict(state=addr(0), x=addr(1), delta_raw=addr(2), z=addr(3), B=addr(4), C=addr(5), A_log=addr(6),
+             D=addr(7), dt_bias=addr(8), y=addr(9), b=4, d=64, n=16, io=ops.SSM_F32, stream=None)
+    a.update(over)
+    return ops.lib().ssm_scan_step(a["state"], a["x"], a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"],
+                                   a["D"], a["dt_bias"], a["y"], a["b"], a["d"], a["n"], a["io"], a["stream"])
+
+
+@no_gpu_only
+def test_step_validation():
+    assert step_call(state=None) == NULL
+    assert step_call(y=None) == NULL
+    assert step_call(n=0) == DIM
+    assert step_call(n=20) == DIM
+    assert step_call(io=2) == UNSUP
+    assert step_call(state=addr(0, 2)) == ALIGN
+    assert step_call(y=addr(1)) == ALIAS      # y == x
+    assert step_call(state=addr(6)) == ALIAS  # state == A_log
+
+
+def bwd_call(**over):
+    a = dict(x=addr(0), delta_raw=addr(1), z=addr(2), B=addr(3), C=addr(4), A_log=addr(5), D=addr(6),
+             dt_bias=addr(7), h0=None, dy=addr(8), dx=addr(9), ddelta_raw=addr(10), dz=addr(11), dB=addr(12),
+             dC=addr(13), dA_log=addr(14), dD=addr(15), d_dt_bias=addr(16), ws=addr(17), wsb=None,
+             b=2, l=64, d=128, n=16, io=ops.SSM_F32, stream=None)
+    a.update(over)
+    if a["wsb"] is None:
+        a["wsb"] = ops.lib().ssm_scan_bwd_workspace_bytes(a["b"], a["l"], a["d"], min(max(a["n"], 1), 16), 0)
+    return ops.lib().ssm_scan_bwd(a["x"], a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"], a["D"],
+                                  a["dt_bias"], a["h0"], a["dy"], a["dx"], a["ddelta_raw"], a["dz"], a["dB"],
+                                  a["dC"], a["dA_log"], a["dD"], a["d_dt_bias"], a["ws"], a["wsb"], a["b"],
+                                  a["l"], a["d"], a["n"], a["io"], a["stream"])
+
+
+@no_gpu_only
+def test_bwd_validation():
+    assert bwd_call(dy=None) == NULL
+    assert bwd_call(dz=None) == NULL                 # z given, dz missing
+    assert bwd_call(dB=None) == NULL
+    assert bwd_call(n=0) == DIM
+    assert bwd_call(io=ops.SSM_BF16) == UNSUP
+    assert bwd_call(ws=None) == WS
+    assert bwd_call(wsb=1024) == WS
+    assert bwd_call(ws=addr(17, 64)) == WS           # workspace must be 256 B aligned
+    assert bwd_call(dx=addr(0)) == ALIAS             # dx == x
+    assert bwd_call(ws=addr(9)) == ALIAS             # workspace == dx
+    assert bwd_call(dB=addr(13)) == ALIAS            # dB == dC
+    assert bwd_call(dA_log=addr(14, 2)) == ALIGN

@@ -1,0 +1,109 @@
+"""GPU parity of the backward pass against the fp64 oracle, and its determinism.
+
+All eight gradients (dx, ddelta_raw, dz, dB, dC, dA_log, dD, d_dt_bias) are
+compared element by element at max relative error (RMS floor) <= 1e-4, on small
+cases that span several channel tiles, time chunks and ragged tails, and on the
+full fwd+bwd workload (B=4, L=2048, d_inner=2048, N=16, gated).  Repeated runs
+must be bit-identical (no atomics, fixed reduction order).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import host, rel_err, say, to_dev32
+from selective_state_space_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+GRADS = ("dx", "ddelta_raw", "dz", "dB", "dC", "dA_log", "dD", "d_dt_bias")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from selective_state_space_03_amd import ops
+    ops.lib()
+
+
+def gpu_bwd(inp, optional=True):
+    from selective_state_space_03_amd import ops
+    b, l, d, n = inp["batch"], inp["seqlen"], inp["dim"], inp["dstate"]
+    dev = "cuda"
+    out = None
+    if not optional:
+        f = torch.float32
+        out = {"dx": torch.empty((b, l, d), dtype=f, device=dev),
+               "ddelta_raw": torch.empty((b, l, d), dtype=f, device=dev),
+               "dz": torch.empty((b, l, d), dtype=f, device=dev) if inp["z"] is not None else None,
+               "dB": torch.empty((b, l, n), dtype=f, device=dev), "dC": torch.empty((b, l, n), dtype=f, device=dev)}
+    g = ops.ssm_scan_bwd(to_dev32(inp["x"]), to_dev32(inp["delta_raw"]), to_dev32(inp["B"]), to_dev32(inp["C"]),
+                         to_dev32(inp["A_log"]), to_dev32(inp["dy"]), D_skip=to_dev32(inp["D"]),
+                         dt_bias=to_dev32(inp["dt_bias"]), z=to_dev32(inp["z"]), h0=to_dev32(inp.get("h0")),
+                         out=out)
+    torch.cuda.synchronize()
+    return {k: (host(v) if v is not None else None) for k, v in g.items()}
+
+
+def oracle_bwd(inp):
+    return oracle.bwd(inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"], inp["dy"], D=inp["D"],
+                      dt_bias=inp["dt_bias"], z=inp["z"], h0=inp.get("h0"))
+
+
+def check(g, r, bound=1e-4):
+    bad = {}
+    for k in GRADS:
+        if r.get(k) is None or g.get(k) is None:
+            continue
+        e = rel_err(g[k], r[k])
+        if not e <= bound:
+            bad[k] = e
+    assert not bad, bad
+
+
+BWD_CASES = [
+    ("small_fp32_shape_with_dy", "fwd_small", dict(with_dy=True)),
+    ("ragged_gated_h0", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=37, dim=100, random_h0=True)),
+    ("chunks_tiles_tail", "fwdbwd_b4_l2048_d2048", dict(batch=3, seqlen=300, dim=130)),
+    ("n8", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=75, dim=64, dstate=8)),
+    ("n5_masked_states", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=129, dim=70, dstate=5, random_h0=True)),
+    ("n1", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=40, dim=3, dstate=1)),
+    ("seqlen_one", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=1, dim=65, random_h0=True)),
+    ("ungated", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=90, dim=80, gated=False)),
+    ("long_sequence", "fwdbwd_b4_l2048_d2048", dict(batch=1, seqlen=3000, dim=64)),
+]
+
+
+@pytest.mark.parametrize("name,wl,over", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_parity_small(name, wl, over):
+    inp = W.make_inputs(W.WORKLOADS[wl], **over)
+    say("bwd %s B=%d L=%d D=%d N=%d gated=%s" % (name, inp["batch"], inp["seqlen"], inp["dim"], inp["dstate"],
+                                                  inp["z"] is not None))
+    check(gpu_bwd(inp), oracle_bwd(inp))
+
+
+def test_bwd_optional_outputs_may_be_null():
+    inp = W.make_inputs(W.WORKLOADS["fwdbwd_b4_l2048_d2048"], batch=2, seqlen=50, dim=70)
+    say("bwd without dA_log/dD/d_dt_bias")
+    g = gpu_bwd(inp, optional=False)
+    r = oracle_bwd(inp)
+    assert g.get("dA_log") is None
+    check(g, r)
+
+
+def test_bwd_full_size_workload():
+    inp = W.make_inputs(W.WORKLOADS["fwdbwd_b4_l2048_d2048"])
+    say("bwd full B=4 L=2048 D=2048 N=16")
+    g = gpu_bwd(inp)
+    say("bwd full: oracle")
+    check(g, oracle_bwd(inp))
+
+
+def test_bwd_is_bit_identical_across_runs():
+    inp = W.make_inputs(W.WORKLOADS["fwdbwd_b4_l2048_d2048"], batch=2, seqlen=300, dim=200, random_h0=True)
+    say("bwd determinism")
+    runs = [gpu_bwd(inp) for _ in range(3)]
+    for r in runs[1:]:
+        for k in GRADS:
+            assert np.array_equal(r[k], runs[0][k]), k
