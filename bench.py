@@ -1,0 +1,305 @@
+"""Benchmark of the gfx950 selective-scan hot path on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|bf16|step|fwd5|bwd|copy] [--no-cpu]
+
+Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
+I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
+final state written).  W untimed warmups, then exactly K timed steps between two
+device synchronisations.  Inputs are seeded synthetic tensors (workloads.py),
+resident in HBM before timing; several identical buffer sets are rotated so that
+every step streams from HBM rather than from the 256 MB last-level cache.
+
+Printed: ONE JSON line on stdout (everything else goes to stderr) with the
+headline forward GB/s, its roofline (algorithmic bytes per launch / average launch
+time from HIP events on the launch stream, against 8 TB/s), the fp64 CPU oracle
+timed on the host cores, and secondary lines for the bf16 forward, the decode
+step and the backward.  `traffic` comes from the committed rocprofv3 counter
+summary for the forward kernel when that summary matches the current kernel
+source, else null.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# VALU issue rate of fp32 non-packed instructions: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# minimal issue slots per state update: mul (Delta*A), exp2 (half rate = 2 slots),
+# mul (Delta*x*B), fma (state), fma (readout)
+SLOTS_PER_UPDATE = 6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_bytes(b, l, d, n, es, gated, h_final=True):
+    E, S, H = b * l * d, b * l * n, b * d * n
+    return (E * es * (3 if gated else 2) + E * es + 2 * S * es + (H * 4 if h_final else 0)
+            + d * n * 4 + 2 * d * 4)
+
+
+def step_bytes(b, d, n, es, gated):
+    E, H = b * d, b * d * n
+    return 2 * H * 4 + E * es * (3 if gated else 2) + E * es + 2 * b * n * es + d * n * 4 + 2 * d * 4
+
+
+def bwd_bytes(b, l, d, n, gated):
+    E, S = b * l * d, b * l * n
+    reads = E * 4 * (4 if gated else 3) + 2 * S * 4 + d * n * 4 + 2 * d * 4
+    writes = E * 4 * (3 if gated else 2) + 2 * S * 4 + d * n * 4 + 2 * d * 4
+    return reads + writes
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+FWD_SOURCES = ["selective_state_space_03_amd/csrc/ssm_fwd.hip", "selective_state_space_03_amd/csrc/ssm_device.h"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_b8_l2048_d1536_counters.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward kernel from the committed counter summary,
+    or None if absent or taken on a different kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_digest") != source_digest(FWD_SOURCES):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-launch HIP events on the current (launch) stream plus wall time."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup, nsets):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i % nsets)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            evs[i][0].record()
+            fn(i % nsets)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [a.elapsed_time(b) for a, b in evs]  # ms
+        return wall * 1e3 / steps, sum(per) / len(per), min(per)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "copy"])
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md, sharding); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from selective_state_space_03_amd import ops
+    from selective_state_space_03_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    timer = Timer(torch)
+    K, Wm = args.steps, args.warmup
+    results = {}
+
+    def t32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def tio(a, io):
+        t = t32(a)
+        return t.to(torch.bfloat16) if (t is not None and io == "bf16") else t
+
+    def fwd_case(name, min_bytes_rotation=1.2e9):
+        w = W.WORKLOADS[name]
+        inp = W.make_inputs(w, with_dy=False)
+        io = w.io
+        es = 2 if io == "bf16" else 4
+        nb = fwd_bytes(w.batch, w.seqlen, w.dim, w.dstate, es, w.gated)
+        nsets = max(2, int(np.ceil(min_bytes_rotation / nb)))
+        base = dict(x=tio(inp["x"], io), dr=tio(inp["delta_raw"], io), z=tio(inp["z"], io), B=tio(inp["B"], io),
+                    C=tio(inp["C"], io))
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
+        ys = [torch.empty_like(base["x"]) for _ in range(nsets)]
+        hfs = [torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            ops.ssm_scan_fwd(s["x"], s["dr"], s["B"], s["C"], A_log, D_skip=Dsk, dt_bias=dtb, z=s["z"],
+                             y=ys[i], h_final=hfs[i])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs,
+                    wall_gbs=nb / (wall_ms * 1e-3) / 1e9, inp=inp)
+
+    def step_case(name="step_b256_d5120"):
+        w = W.WORKLOADS[name]
+        inp = W.make_inputs(w)
+        nb = step_bytes(w.batch, w.dim, w.dstate, 4, w.gated)
+        nsets = max(2, int(np.ceil(1.2e9 / nb)))
+        base = dict(st=t32(inp["state"]), x=t32(inp["x"]), dr=t32(inp["delta_raw"]), z=t32(inp["z"]),
+                    B=t32(inp["B"]), C=t32(inp["C"]))
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
+        ys = [torch.empty_like(base["x"]) for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            ops.ssm_scan_step(s["st"], s["x"], s["dr"], s["B"], s["C"], A_log, D_skip=Dsk, dt_bias=dtb, z=s["z"],
+                              y=ys[i])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
+    def bwd_case(name="fwdbwd_b4_l2048_d2048"):
+        w = W.WORKLOADS[name]
+        inp = W.make_inputs(w)
+        b, l, d, n = w.batch, w.seqlen, w.dim, w.dstate
+        nb = bwd_bytes(b, l, d, n, w.gated)
+        nsets = 2
+        base = dict(x=t32(inp["x"]), dr=t32(inp["delta_raw"]), z=t32(inp["z"]), B=t32(inp["B"]), C=t32(inp["C"]),
+                    dy=t32(inp["dy"]))
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
+        f = torch.float32
+        outs = [{"dx": torch.empty((b, l, d), dtype=f, device=dev), "ddelta_raw": torch.empty((b, l, d), dtype=f, device=dev),
+                 "dz": torch.empty((b, l, d), dtype=f, device=dev), "dB": torch.empty((b, l, n), dtype=f, device=dev),
+                 "dC": torch.empty((b, l, n), dtype=f, device=dev), "dA_log": torch.empty((d, n), dtype=f, device=dev),
+                 "dD": torch.empty((d,), dtype=f, device=dev), "d_dt_bias": torch.empty((d,), dtype=f, device=dev)}
+                for _ in range(nsets)]
+        wsb = ops.bwd_workspace_bytes(b, l, d, n)
+        wss = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            ops.ssm_scan_bwd(s["x"], s["dr"], s["B"], s["C"], A_log, s["dy"], D_skip=Dsk, dt_bias=dtb, z=s["z"],
+                             workspace=wss[i], out=outs[i])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  workspace %.1f MB" %
+            ("bwd_b4_l2048_d2048", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, workspace_bytes=wsb)
+
+    if args.only == "copy":
+        # calibration kernel for the HBM byte counters: a plain 1 GiB device-to-device copy
+        nbytes = 1 << 30
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        bb = torch.empty_like(a)
+        wall_ms, ev_ms, _ = timer.run(lambda i: bb.copy_(a), K, Wm, 1)
+        log("copy 1 GiB: %.1f us, %.1f GB/s (read+write)" % (ev_ms * 1e3, 2 * nbytes / (ev_ms * 1e-3) / 1e9))
+        print(json.dumps({"copy_bytes_each_way": nbytes, "ev_ms": ev_ms}))
+        return
+
+    head = None
+    if args.only in ("all", "fwd"):
+        head = fwd_case("fwd_b8_l2048_d1536")
+    if args.only in ("all", "bf16"):
+        results["fwd_bf16_b4_l4096_d4096"] = fwd_case("fwd_bf16_b4_l4096_d4096")
+    if args.only in ("all", "fwd5"):
+        results["fwd_b4_l2048_d2048"] = fwd_case("fwdbwd_b4_l2048_d2048")
+    if args.only in ("all", "step"):
+        results["step_b256_d5120"] = step_case()
+    if args.only in ("all", "bwd"):
+        results["bwd_b4_l2048_d2048"] = bwd_case()
+
+    if head is None:
+        # profiling runs of a single secondary case print a short line
+        print(json.dumps({k: {"gbs": v["gbs"], "us": v["ev_ms"] * 1e3} for k, v in results.items()}))
+        return
+
+    w = head["workload"]
+    updates = w.state_updates
+    valu_tslots = updates * SLOTS_PER_UPDATE / (head["ev_ms"] * 1e-3) / 1e12
+    traffic = measured_traffic()
+    roofline = {"bound": "hbm", "achieved": round(head["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(head["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": head["bytes"],
+                "valu_issue_frac": round(valu_tslots / VALU_PEAK_TSLOTS, 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        inp = head["inp"]
+        nthreads = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.fwd(inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"], D=inp["D"], dt_bias=inp["dt_bias"],
+                   z=inp["z"], nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(head["bytes"] / dt / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+               "sample": "the whole forward workload B=8 L=2048 d_inner=1536 N=16 (one pass, fp64, %.1f s)" % dt,
+               "seconds": round(dt, 3), "gpu_speedup": round(dt / (head["ev_ms"] * 1e-3), 1)}
+        log("cpu oracle: %.2f s on %d threads (%.2f GB/s)" % (dt, nthreads, cpu["value"]))
+
+    secondary = {}
+    for k, v in results.items():
+        secondary[k] = {"gbs": round(v["gbs"], 1), "frac_of_8tbs": round(v["gbs"] / HBM_PEAK_GBS, 4),
+                        "us_per_launch": round(v["ev_ms"] * 1e3, 1), "algorithmic_bytes": v["bytes"],
+                        "elements_per_s": round(v["workload"].elements / (v["ev_ms"] * 1e-3), 1)}
+        if v["workload"].kind != "step":
+            secondary[k]["state_updates_per_s"] = round(v["workload"].state_updates / (v["ev_ms"] * 1e-3), 1)
+
+    out = {
+        "metric": "selective-scan fwd achieved HBM GB/s and % of peak at 1 MI355X; step/bwd GB/s",
+        "value": round(head["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(head["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fwd_b8_l2048_d1536", "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.dim,
+                   "d_state": w.dstate, "io": w.io, "gated": w.gated},
+        "pct_of_hbm_peak": round(100 * head["gbs"] / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(w.elements / (head["ev_ms"] * 1e-3), 1),
+        "state_updates_per_s": round(updates / (head["ev_ms"] * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

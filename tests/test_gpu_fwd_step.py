@@ -207,3 +207,19 @@ def test_step_is_bit_identical_across_runs():
     runs = [gpu_step(inp) for _ in range(3)]
     for y, st in runs[1:]:
         assert np.array_equal(y, runs[0][0]) and np.array_equal(st, runs[0][1])
+
+
+@pytest.mark.parametrize("spw", ["1", "4"])
+def test_fwd_full_size_other_layouts(spw, monkeypatch):
+    """Full-size forward in the 16-wave (one state per wave) and 4-wave layouts: with
+    more waves than rows per time tile, the last full tile's loads must stay inside
+    the tensors (regression: an unguarded row index read past the end of x)."""
+    monkeypatch.setenv("SSM_FWD_STATES_PER_WAVE", spw)
+    w = W.WORKLOADS["fwd_b8_l2048_d1536"]
+    inp = W.make_inputs(w, with_dy=False)
+    say("fwd full fwd_b8_l2048_d1536 states_per_wave=%s" % spw)
+    y, hf = gpu_fwd(inp)
+    chans = [0, 1, 700, 1535]
+    ref = oracle_fwd(inp, chans)
+    assert rel_err(y[..., chans], ref["y"]) <= 1e-4
+    assert rel_err(hf[:, chans], ref["h_final"]) <= 1e-4
