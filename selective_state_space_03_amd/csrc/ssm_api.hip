@@ -62,7 +62,12 @@ int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void
   if (!x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
+  // per-tile buffer offsets of the forward kernel are 32-bit: a 16-row tile of one
+  // batch element must stay below 2^31 bytes
+  if (d_inner > ((int64_t)1 << 24) || seqlen > ((int64_t)1 << 30)) return SSM_ERR_DIM;
   const size_t es = esize(io_dtype);
+  // the forward addresses one batch element's [seqlen, d_inner] slice with 31-bit offsets
+  if ((uint64_t)seqlen * (uint64_t)d_inner * es >= ((uint64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
   const void* io_in[] = {x, delta_raw, z, B, C};
   for (const void* p : io_in)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;

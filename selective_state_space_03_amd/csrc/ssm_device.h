@@ -61,6 +61,21 @@ template <> struct io<bf16_t> {
   __device__ __forceinline__ static void st(bf16_t* __restrict__ p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Wave-uniform read of memory that no kernel of the launch writes (B, C): through the
+// constant address space the load is a scalar (SMEM) load into an SGPR, whatever the
+// compiler can prove about aliasing.
+// (fp32 is read as its bit pattern: a plain float copy from constant memory into a
+// register array can be turned into a memory copy, which keeps the array in scratch.)
+typedef __attribute__((address_space(4))) const uint32_t cu32_t;
+typedef __attribute__((address_space(4))) const uint16_t cbf16_t;
+template <typename T> __device__ __forceinline__ float ld_uniform(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld_uniform<float>(const float* p, int64_t i) {
+  return __uint_as_float(((cu32_t*)p)[i]);
+}
+template <> __device__ __forceinline__ float ld_uniform<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf16_to_f32(((cbf16_t*)p)[i]);
+}
+
 // A[d,n] = -exp(A_log[d,n]) folded with log2(e), so that exp(Delta*A) = exp2(Delta*A2)
 // (mamba-rs exp_negate: out = -exp(a_log)).  Computed once per state per kernel with the
 // accurate library exp.

@@ -21,16 +21,51 @@
 //     phase adds in fixed wave order -- so the result is deterministic.
 // Time is walked in tiles of TT steps with one barrier per tile: between two
 // barriers a wave preps tile k+1, reads out tile k-1 and scans tile k (LDS buffers
-// are double / triple buffered for that).  Global loads of activations run P tiles
-// ahead of the prep and the scalar loads of B/C one tile ahead of the scan, so no step
-// of the scan waits on memory.  The scalar unit is shared by the four SIMDs of a CU,
-// so address arithmetic is kept off it: B/C of a tile are immediate offsets from one
-// base, activations a uniform row base plus a 32-bit lane offset.
+// are double / quadruple buffered for that).  Activation loads run P tiles ahead of
+// the prep through per-tile buffer resources: out-of-range rows and padding channels
+// read 0 and drop their stores in hardware, so the loop has no branch around memory
+// operations and the compiler can wait for exactly the tile it needs.  B/C of the
+// next tile are scalar loads issued at the start of each scan into the other half of
+// a double-buffered SGPR set.  The scalar unit is shared by the four SIMDs of a CU, so
+// address arithmetic is kept off it: B/C of a tile are immediate offsets from one base.
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
 namespace {
+
+// Raw buffer access: a per-tile buffer resource whose range ends at the end of the
+// sequence (or is empty), so loads outside it return 0 and stores outside it are
+// dropped by the hardware.  Lanes of padding channels use an offset >= 2^31, which is
+// always outside.  This keeps every load and store of the loop unconditional.
+constexpr uint32_t kBufWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, word 3
+constexpr uint32_t kOutside = 0x80000000u;
+
+// lane offset + tile offset; either one outside makes the sum outside (no wrap-around)
+__device__ __forceinline__ uint32_t off_add(uint32_t a, uint32_t b) {
+  return ((a | b) & kOutside) ? kOutside : a + b;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t bytes) {
+  const int nr = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kBufWord3);
+}
+template <typename T> __device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ float buf_ld<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));  // bits, not a value cast
+}
+template <> __device__ __forceinline__ float buf_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+template <typename T> __device__ __forceinline__ void buf_st(float v, __amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ void buf_st<float>(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);  // bits, not a value cast
+}
+template <> __device__ __forceinline__ void buf_st<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+}
 
 template <typename T, int S, int G, int TT, int P, bool GATED, bool MASKED>
 __global__ void __launch_bounds__(64 * G)
@@ -41,8 +76,9 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
                 int L, int Dm, int N_rt, int ngroups) {
   static_assert(P == 4, "ring slots and LDS buffer indices are derived from P == 4");
   constexpr int EPL = (TT + G - 1) / G;  // prep/readout elements per lane per tile
-  // Unmasked, d_state == S*G is a compile-time constant, so every B/C load of a tile is
-  // an immediate offset from one scalar base (no per-load scalar address arithmetic).
+  constexpr int ES = (int)sizeof(T);
+  // Unmasked, d_state == S*G is a compile-time constant: B/C loads of a tile are
+  // immediate offsets from one scalar base.
   const int N = MASKED ? N_rt : S * G;
   __shared__ float2 dd[2][TT * 64];       // (Delta, Delta*x) per (t, channel): tile k in k&1
   __shared__ float2 xz[4][TT * 64];       // (D*x, silu(z)) per (t, channel): tile k in k&3
@@ -53,7 +89,6 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   const int b = blockIdx.x / ngroups;
   const int d = (blockIdx.x % ngroups) * 64 + lane;
   const bool dvalid = d < Dm;
-  const int dl = dvalid ? d : Dm - 1;  // clamped channel: loads stay in bounds
   const float bias = (dvalid && dt_bias) ? dt_bias[d] : 0.f;
   const float dsk = (dvalid && D_skip) ? D_skip[d] : 0.f;
 
@@ -72,149 +107,179 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   const int ntiles = (L + TT - 1) / TT;
   const int nfull = L / TT;              // tiles that lie entirely inside the sequence
   const int64_t row0 = (int64_t)b * L;   // row of (b, t) is row0 + t
-  const int64_t tstride = (int64_t)TT * Dm;
-  // per-lane element offsets inside a tile (row wave + G*i of the tile, channel dl)
-  int eoff[EPL];
+  // Rows of one tile handled by this lane in prep (PR) and readout (RO).  With twice as
+  // many waves as tile rows, waves [0, TT) prep and waves [TT, 2TT) read out, so both
+  // phases are spread over every wave; otherwise each wave does both for its rows.
+  constexpr bool SPLIT = (G == 2 * TT);
+  constexpr int EPL2 = SPLIT ? 1 : EPL;
+  const int prow = wave;                        // first prep row (+ G*i)
+  const int rrow = SPLIT ? wave - TT : wave;    // first readout row (+ G*i)
+  // byte offset of (row, channel d) inside a tile; padding lanes and rows beyond the
+  // tile get an offset >= 2^31, outside every resource
+  auto lane_off = [&](int row) __attribute__((always_inline)) {
+    return (dvalid && row >= 0 && row < TT) ? (uint32_t)((row * Dm + d) * ES) : kOutside;
+  };
+  uint32_t poff[EPL2], roff[EPL2];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) eoff[i] = (wave + G * i) * Dm + dl;
+  for (int i = 0; i < EPL2; ++i) {
+    poff[i] = lane_off(prow + G * i);
+    roff[i] = lane_off(rrow + G * i);
+  }
+  // One resource per tensor over this batch element's slice of the sequence (its range
+  // ends at the last row, so rows past the end read 0 / drop stores); the tile offset
+  // j*TT*Dm*ES is added to the lane offset.  The host guarantees L*Dm*ES < 2^31.
+  const int64_t slice = (int64_t)L * Dm * ES;
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rr = tile_rsrc(delta_raw + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rz = tile_rsrc(GATED ? z + row0 * Dm : x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t ry = tile_rsrc(y + row0 * Dm, slice);
+  const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);
+  // offset of tile j (j may be -1 or past the end: then every access is outside)
+  auto toff = [&](int j) __attribute__((always_inline)) {
+    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * tile_bytes;
+  };
 
-  // ---- B/C: a whole tile for this wave's states in SGPRs, next tile loaded while
-  // the current one is scanned
-  float cb[TT][S], cc[TT][S];
-  // whole tile j inside the sequence: constant offsets from one base
-  auto load_bc_full = [&](int j, int t, int s) {
-    const T* __restrict__ Bt = Bm + (row0 + (int64_t)j * TT) * N + n0;
-    const T* __restrict__ Ct = Cm + (row0 + (int64_t)j * TT) * N + n0;
-    if (MASKED) {
-      cb[t][s] = s < nact ? io<T>::ld(Bt, t * N + s) : 0.f;
-      cc[t][s] = s < nact ? io<T>::ld(Ct, t * N + s) : 0.f;
-    } else {
-      cb[t][s] = io<T>::ld(Bt, t * N + s);
-      cc[t][s] = io<T>::ld(Ct, t * N + s);
+  // ---- B/C of a tile for this wave's states: wave-uniform, in SGPRs, double buffered
+  float cb[2][TT][S], cc[2][TT][S];
+  auto load_bc = [&](int j, int buf) __attribute__((always_inline)) {
+    if (j < nfull) {  // whole tile inside the sequence: constant offsets from one base
+      const T* __restrict__ Bt = Bm + (row0 + (int64_t)j * TT) * N + n0;
+      const T* __restrict__ Ct = Cm + (row0 + (int64_t)j * TT) * N + n0;
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          if (MASKED) {
+            cb[buf][t][s] = s < nact ? ld_uniform<T>(Bt, t * N + s) : 0.f;
+            if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Ct, t * N + s) : 0.f;
+          } else {
+            cb[buf][t][s] = ld_uniform<T>(Bt, t * N + s);
+            if (S > 1) cc[buf][t][s] = ld_uniform<T>(Ct, t * N + s);
+          }
+        }
+    } else if (j < ntiles) {  // the partial last tile: rows clamped (padded steps have Delta = 0)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int r = j * TT + t < L ? j * TT + t : L - 1;
+          const int64_t o = (row0 + r) * N + n0 + (s < nact ? s : 0);
+          cb[buf][t][s] = s < nact ? ld_uniform<T>(Bm, o) : 0.f;
+          if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Cm, o) : 0.f;
+        }
     }
   };
-  // partial last tile (or past the end): rows clamped, padded steps have Delta = 0
-  auto load_bc_tail = [&](int j, int t, int s) {
-    int r = j * TT + t;
-    r = r < L ? r : L - 1;
-    const int64_t o = (row0 + r) * N + n0 + (s < nact ? s : 0);
-    cb[t][s] = s < nact ? io<T>::ld(Bm, o) : 0.f;
-    cc[t][s] = s < nact ? io<T>::ld(Cm, o) : 0.f;
-  };
-  auto load_bc = [&](int j, int t, int s) {
-    if (j < nfull) load_bc_full(j, t, s); else load_bc_tail(j, t, s);
-  };
-#pragma unroll
-  for (int t = 0; t < TT; ++t)
-#pragma unroll
-    for (int j = 0; j < S; ++j) load_bc(0, t, j);
 
   // ---- activations of the tiles still to prep, in a ring of P register slots: the
   // loads of tile j are issued P tiles before tile j is prepped (slot j % P)
-  float px[P][EPL], pr[P][EPL], pz[P][EPL];
-  auto load_tile = [&](int j, int slot) {
-    if (j < nfull) {
-      const int64_t base = (row0 + (int64_t)j * TT) * Dm;  // uniform
+  float px[P][EPL2], pr[P][EPL2], pz[P][EPL2];
+  auto load_tile = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint32_t o = toff(j);
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        // with more waves than tile rows (G > TT) the extra waves have no row here
-        if (wave + G * i < TT) {
-          px[slot][i] = io<T>::ld(x + base, eoff[i]);
-          pr[slot][i] = io<T>::ld(delta_raw + base, eoff[i]);
-          pz[slot][i] = GATED ? io<T>::ld(z + base, eoff[i]) : 0.f;
-        } else {
-          px[slot][i] = pr[slot][i] = pz[slot][i] = 0.f;
-        }
-      }
-    } else {  // rows past the end are clamped; prep gives them Delta = 0
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        int r = j * TT + wave + G * i;
-        r = r < L ? r : L - 1;
-        const int64_t base = (row0 + r) * Dm;
-        px[slot][i] = io<T>::ld(x + base, dl);
-        pr[slot][i] = io<T>::ld(delta_raw + base, dl);
-        pz[slot][i] = GATED ? io<T>::ld(z + base, dl) : 0.f;
-      }
+    for (int i = 0; i < EPL2; ++i) {
+      const uint32_t v = off_add(poff[i], o);
+      px[slot][i] = buf_ld<T>(rx, v);
+      pr[slot][i] = buf_ld<T>(rr, v);
+      pz[slot][i] = GATED ? buf_ld<T>(rz, v) : 0.f;
     }
   };
   // prep of tile k: Delta and Delta*x for the scan, D*x and silu(z) for the readout.
   // Padded steps and channels get Delta = 0, which leaves the state as it is.
-  auto prep = [&](int k, int slot, int dbuf, int xbuf) {
-    const bool full = k < nfull;
+  auto prep = [&](int k, int slot, int dbuf, int xbuf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int t = wave + G * i;
-      if (t < TT) {
-        const bool v = dvalid && (full || k * TT + t < L);
+    for (int i = 0; i < EPL2; ++i) {
+      const int t = prow + G * i;
+      if (t >= 0 && t < TT) {
+        const bool v = dvalid && k * TT + t < L;
         const float delta = softplus_f(pr[slot][i] + bias);
         dd[dbuf][t * 64 + lane] = v ? make_float2(delta, delta * px[slot][i]) : make_float2(0.f, 0.f);
         xz[xbuf][t * 64 + lane] = make_float2(dsk * px[slot][i], GATED ? silu_f(pz[slot][i]) : 1.f);
       }
     }
   };
-  // readout of tile k: wave partials added in fixed order, plus skip, times gate
-  auto readout = [&](int k, int pbuf, int xbuf) {
-    const bool full = k < nfull;
-    const int64_t base = (row0 + (int64_t)k * TT) * Dm;
+  // readout of tile k: wave partials added in fixed order, plus skip, times gate; rows
+  // outside the sequence (and k < 0) fall outside the store resource
+  auto readout = [&](int k, int pbuf, int xbuf) __attribute__((always_inline)) {
+    const uint32_t o = toff(k);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int t = wave + G * i;
-      if (t < TT && dvalid && (full || k * TT + t < L)) {
+    for (int i = 0; i < EPL2; ++i) {
+      const int t = rrow + G * i;
+      float out = 0.f;
+      if (t >= 0 && t < TT) {
+        // all partial reads first, one wait, then the fixed-order sum
         const float2 q = xz[xbuf][t * 64 + lane];
-        float s = q.x;
+        float pv[G];
 #pragma unroll
-        for (int w = 0; w < G; ++w) s += yp[pbuf][(t * G + w) * 64 + lane];
-        io<T>::st(y + base, eoff[i], s * q.y);
+        for (int w = 0; w < G; ++w) pv[w] = yp[pbuf][(t * G + w) * 64 + lane];
+        float cw[G];
+        if (S == 1) {  // one state per wave: the partials are the states, weights C[t][n]
+          const int r = min(max(k * TT + t, 0), L - 1);  // row clamped into the sequence (value unused outside)
+#pragma unroll
+          for (int w = 0; w < G; ++w) cw[w] = w < N ? ld_uniform<T>(Cm, (row0 + r) * N + w) : 0.f;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
+        float s = q.x;
+        if (S == 1) {
+#pragma unroll
+          for (int w = 0; w < G; ++w) s = fmaf(cw[w], pv[w], s);
+        } else {
+#pragma unroll
+          for (int w = 0; w < G; ++w) s += pv[w];
+        }
+        out = s * q.y;
       }
+      // the store is issued on every path (rows outside the tile have an outside offset),
+      // so every iteration has the same memory operations
+      buf_st<T>(out, ry, off_add(roff[i], o));
     }
   };
-  // Scan of tile k over this wave's states.  Scalar (B/C) and LDS loads share one
-  // wait counter and scalar loads complete out of order, so the tile's LDS reads are
-  // issued and waited for first; inside the unrolled loop the only memory operations
-  // are the partial stores and the B/C loads of tile k+1.
-  auto scan = [&](int k, int dbuf, int pbuf, auto&& load_next) {
+  // scan of tile k (B/C in buffer cbuf).  Scalar and LDS loads share one wait counter
+  // and scalar loads complete out of order, so the tile's LDS reads are waited for
+  // first; then the B/C of tile k+1 go out (into the other buffer) and have the whole
+  // scan to arrive before the closing barrier waits for them.
+  auto scan = [&](int k, int dbuf, int pbuf, int cbuf) __attribute__((always_inline)) {
     float2 v[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) v[t] = dd[dbuf][t * 64 + lane];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
+    load_bc(k + 1, cbuf ^ 1);
     float* __restrict__ ypw = yp[pbuf] + wave * 64 + lane;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      float acc = 0.f;
+      if (S == 1) {  // store the state; the readout applies C
+        const float a = exp2_hw(v[t].x * A2[0]);
+        h[0] = fmaf(a, h[0], v[t].y * cb[cbuf][t][0]);
+        ypw[t * G * 64] = h[0];
+      } else {
+        float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < S; ++j) {
-        const float a = exp2_hw(v[t].x * A2[j]);
-        h[j] = fmaf(a, h[j], v[t].y * cb[t][j]);
-        acc = fmaf(cc[t][j], h[j], acc);
-        load_next(k + 1, t, j);
+        for (int j = 0; j < S; ++j) {
+          const float a = exp2_hw(v[t].x * A2[j]);
+          h[j] = fmaf(a, h[j], v[t].y * cb[cbuf][t][j]);
+          acc = fmaf(cc[cbuf][t][j], h[j], acc);
+        }
+        ypw[t * G * 64] = acc;
       }
-      ypw[t * G * 64] = acc;
     }
   };
 
-  // prologue: tiles 0..P-1 in flight, tile 0 prepped, then tile P takes slot 0
+  // prologue: tiles 0..P-1 in flight, B/C of tile 0, tile 0 prepped, tile P into slot 0
+  load_bc(0, 0);
 #pragma unroll
-  for (int u = 0; u < P; ++u)
-    if (u < ntiles) load_tile(u, u);
+  for (int u = 0; u < P; ++u) load_tile(u, u);
   prep(0, 0, 0, 0);
-  if (P < ntiles) load_tile(P, 0);
+  load_tile(P, 0);
   __syncthreads();
-  // main loop, unrolled by P = 4 so that ring slots and buffer indices are constants
+  // main loop, unrolled by P = 4 so that every ring slot and buffer index is a constant
   for (int kk = 0; kk < ntiles; kk += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       const int k = kk + u;
       if (k >= ntiles) break;
-      if (k + 1 < ntiles) {
-        prep(k + 1, (u + 1) % P, (u + 1) & 1, (u + 1) & 3);
-        if (k + 1 + P < ntiles) load_tile(k + 1 + P, (u + 1) % P);
-      }
-      if (k >= 1) readout(k - 1, (u + 1) & 1, (u + 3) & 3);
-      if (k + 1 < nfull)
-        scan(k, u & 1, u & 1, load_bc_full);  // tile k+1 lies inside the sequence
-      else
-        scan(k, u & 1, u & 1, load_bc_tail);  // tile k+1 is partial or past the end
+      prep(k + 1, (u + 1) % P, (u + 1) & 1, (u + 1) & 3);
+      load_tile(k + 1 + P, (u + 1) % P);
+      readout(k - 1, (u + 1) & 1, (u + 3) & 3);
+      scan(k, u & 1, u & 1, u & 1);
       __syncthreads();
     }
   }
