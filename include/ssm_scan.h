@@ -26,7 +26,8 @@
  *   dy, dx, ddelta_raw, dz in the backward).  Parameters, states and all
  *   arithmetic are fp32.  bf16 results are rounded to nearest even.
  *   Pointers are device pointers (hipMalloc / torch CUDA tensors), naturally
- *   aligned for their element type.  Outputs must not overlap inputs, except
+ *   aligned for their element type; B and C of ssm_scan_fwd are also 4-byte
+ *   aligned in bf16 (SSM_ERR_ALIGN otherwise).  Outputs must not overlap inputs, except
  *   `state` of ssm_scan_step, which is read and written in place.
  *   Ownership: the caller allocates and frees every buffer, including any
  *   workspace; the library allocates no device memory and keeps no pointer

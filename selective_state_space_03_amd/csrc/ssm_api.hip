@@ -71,6 +71,8 @@ int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void
   const void* io_in[] = {x, delta_raw, z, B, C};
   for (const void* p : io_in)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  // B and C are read by the scalar unit in whole dwords (bf16 included)
+  if (!aligned(B, 4) || !aligned(C, 4)) return SSM_ERR_ALIGN;
   const void* f_in[] = {A_log, D_skip, dt_bias, h0, h_final};
   for (const void* p : f_in)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;

@@ -67,22 +67,21 @@ template <> __device__ __forceinline__ void buf_st<bf16_t>(float v, __amdgpu_buf
   __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
 }
 
-template <typename T, int S, int G, int TT, int P, bool GATED, bool MASKED>
+template <typename T, int S, int G, int TT, int R, bool GATED, bool MASKED>
 __global__ void __launch_bounds__(64 * G)
 fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
                 const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
                 const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
                 const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_final,
                 int L, int Dm, int N_rt, int ngroups) {
-  static_assert(P == 4, "ring slots and LDS buffer indices are derived from P == 4");
-  constexpr int EPL = (TT + G - 1) / G;  // prep/readout elements per lane per tile
+  static_assert(R == 8, "ring slots are tile mod 8; the main loop is unrolled by 8");
+  constexpr int EPL = (TT + G - 1) / G;  // prep/readout rows per lane per tile
   constexpr int ES = (int)sizeof(T);
   // Unmasked, d_state == S*G is a compile-time constant: B/C loads of a tile are
   // immediate offsets from one scalar base.
   const int N = MASKED ? N_rt : S * G;
-  __shared__ float2 dd[2][TT * 64];       // (Delta, Delta*x) per (t, channel): tile k in k&1
-  __shared__ float2 xz[4][TT * 64];       // (D*x, silu(z)) per (t, channel): tile k in k&3
-  __shared__ float yp[2][TT * G * 64];    // per-wave partial readout per (t, wave, channel)
+  __shared__ float2 dd[2][TT * 64];     // (Delta, Delta*x) per (t, channel): tile k in k&1
+  __shared__ float yp[2][TT * G * 64];  // per-wave partial readout per (t, wave, channel)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -107,23 +106,14 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   const int ntiles = (L + TT - 1) / TT;
   const int nfull = L / TT;              // tiles that lie entirely inside the sequence
   const int64_t row0 = (int64_t)b * L;   // row of (b, t) is row0 + t
-  // Rows of one tile handled by this lane in prep (PR) and readout (RO).  With twice as
-  // many waves as tile rows, waves [0, TT) prep and waves [TT, 2TT) read out, so both
-  // phases are spread over every wave; otherwise each wave does both for its rows.
-  constexpr bool SPLIT = (G == 2 * TT);
-  constexpr int EPL2 = SPLIT ? 1 : EPL;
-  const int prow = wave;                        // first prep row (+ G*i)
-  const int rrow = SPLIT ? wave - TT : wave;    // first readout row (+ G*i)
-  // byte offset of (row, channel d) inside a tile; padding lanes and rows beyond the
-  // tile get an offset >= 2^31, outside every resource
-  auto lane_off = [&](int row) __attribute__((always_inline)) {
-    return (dvalid && row >= 0 && row < TT) ? (uint32_t)((row * Dm + d) * ES) : kOutside;
-  };
-  uint32_t poff[EPL2], roff[EPL2];
+  // Rows wave + G*i of every tile are this wave's, for the prep and for the readout.
+  // Byte offset of (row, channel d) inside a tile; padding lanes and rows beyond the
+  // tile get an offset >= 2^31, outside every resource.
+  uint32_t loff[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL2; ++i) {
-    poff[i] = lane_off(prow + G * i);
-    roff[i] = lane_off(rrow + G * i);
+  for (int i = 0; i < EPL; ++i) {
+    const int row = wave + G * i;
+    loff[i] = (dvalid && row < TT) ? (uint32_t)((row * Dm + d) * ES) : kOutside;
   }
   // One resource per tensor over this batch element's slice of the sequence (its range
   // ends at the last row, so rows past the end read 0 / drop stores); the tile offset
@@ -139,24 +129,55 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
     return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * tile_bytes;
   };
 
-  // ---- B/C of a tile for this wave's states: wave-uniform, in SGPRs, double buffered
+  // ---- B (and C when a wave has several states) of a tile for this wave's states:
+  // wave-uniform, in SGPRs, double buffered
   float cb[2][TT][S], cc[2][TT][S];
   auto load_bc = [&](int j, int buf) __attribute__((always_inline)) {
     if (j < nfull) {  // whole tile inside the sequence: constant offsets from one base
-      const T* __restrict__ Bt = Bm + (row0 + (int64_t)j * TT) * N + n0;
-      const T* __restrict__ Ct = Cm + (row0 + (int64_t)j * TT) * N + n0;
+      const int64_t e = (row0 + (int64_t)j * TT) * N + n0;  // element (row of tile j, n0)
+      if (std::is_same<T, bf16_t>::value && !MASKED) {
+        // bf16 with even N: element e + t*N + s lies in dword (e >> 1) + ((par + t*N + s) >> 1);
+        // only one state per wave can start at an odd element (par = 1, then s = 0)
+        const int par = S == 1 ? (int)(e & 1) : 0;
+        const cu32_t* __restrict__ Bw = (const cu32_t*)Bm + (e >> 1);
+        const cu32_t* __restrict__ Cw = (const cu32_t*)Cm + (e >> 1);
+        auto half = [&](uint32_t w, bool hi) __attribute__((always_inline)) {
+          return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+        };
 #pragma unroll
-      for (int t = 0; t < TT; ++t)
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          if (MASKED) {
-            cb[buf][t][s] = s < nact ? ld_uniform<T>(Bt, t * N + s) : 0.f;
-            if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Ct, t * N + s) : 0.f;
-          } else {
-            cb[buf][t][s] = ld_uniform<T>(Bt, t * N + s);
-            if (S > 1) cc[buf][t][s] = ld_uniform<T>(Ct, t * N + s);
+          for (int s = 0; s < S; ++s) {
+            const int c = t * N + s;
+            const bool hi = S == 1 ? par != 0 : (c & 1) != 0;
+            cb[buf][t][s] = half(Bw[c >> 1], hi);
+            if (S > 1) cc[buf][t][s] = half(Cw[c >> 1], hi);
           }
-        }
+      } else if (std::is_same<T, bf16_t>::value) {  // bf16, any N: element by element
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            const int64_t o = e + t * N + (s < nact ? s : 0);
+            cb[buf][t][s] = s < nact ? ld_uniform<T>(Bm, o) : 0.f;
+            if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Cm, o) : 0.f;
+          }
+      } else {
+        const T* __restrict__ Bt = Bm + e;
+        const T* __restrict__ Ct = Cm + e;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            if (MASKED) {
+              cb[buf][t][s] = s < nact ? ld_uniform<T>(Bt, t * N + s) : 0.f;
+              if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Ct, t * N + s) : 0.f;
+            } else {
+              cb[buf][t][s] = ld_uniform<T>(Bt, t * N + s);
+              if (S > 1) cc[buf][t][s] = ld_uniform<T>(Ct, t * N + s);
+            }
+          }
+      }
     } else if (j < ntiles) {  // the partial last tile: rows clamped (padded steps have Delta = 0)
 #pragma unroll
       for (int t = 0; t < TT; ++t)
@@ -170,67 +191,69 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
     }
   };
 
-  // ---- activations of the tiles still to prep, in a ring of P register slots: the
-  // loads of tile j are issued P tiles before tile j is prepped (slot j % P)
-  float px[P][EPL2], pr[P][EPL2], pz[P][EPL2];
+  // ---- activations of this wave's rows, in a ring of R register slots (tile j in slot
+  // j % R).  Tile j is loaded while tile j-6 is scanned: the prep uses x and delta_raw
+  // of tile j five steps later, the readout x and z of tile j seven steps later.
+  float px[R][EPL], pr[R][EPL], pz[R][EPL];
   auto load_tile = [&](int j, int slot) __attribute__((always_inline)) {
     const uint32_t o = toff(j);
 #pragma unroll
-    for (int i = 0; i < EPL2; ++i) {
-      const uint32_t v = off_add(poff[i], o);
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t v = off_add(loff[i], o);
       px[slot][i] = buf_ld<T>(rx, v);
       pr[slot][i] = buf_ld<T>(rr, v);
       pz[slot][i] = GATED ? buf_ld<T>(rz, v) : 0.f;
     }
   };
-  // prep of tile k: Delta and Delta*x for the scan, D*x and silu(z) for the readout.
-  // Padded steps and channels get Delta = 0, which leaves the state as it is.
-  auto prep = [&](int k, int slot, int dbuf, int xbuf) __attribute__((always_inline)) {
+  // prep of tile k: Delta and Delta*x for the scan.  Padded steps and channels get
+  // Delta = 0, which leaves the state as it is.
+  auto prep = [&](int k, int slot, int dbuf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < EPL2; ++i) {
-      const int t = prow + G * i;
-      if (t >= 0 && t < TT) {
+    for (int i = 0; i < EPL; ++i) {
+      const int t = wave + G * i;
+      if (t < TT) {
         const bool v = dvalid && k * TT + t < L;
         const float delta = softplus_f(pr[slot][i] + bias);
         dd[dbuf][t * 64 + lane] = v ? make_float2(delta, delta * px[slot][i]) : make_float2(0.f, 0.f);
-        xz[xbuf][t * 64 + lane] = make_float2(dsk * px[slot][i], GATED ? silu_f(pz[slot][i]) : 1.f);
       }
     }
   };
-  // readout of tile k: wave partials added in fixed order, plus skip, times gate; rows
-  // outside the sequence (and k < 0) fall outside the store resource
-  auto readout = [&](int k, int pbuf, int xbuf) __attribute__((always_inline)) {
+  // readout of tile k: wave partials added in fixed order, plus skip, times gate.  With
+  // one state per wave the partials are the states and C[t][n] is applied here (scalar
+  // loads), which keeps that multiply out of the scan.  Rows outside the sequence (and
+  // k < 0) fall outside the store resource.
+  auto readout = [&](int k, int slot, int pbuf) __attribute__((always_inline)) {
     const uint32_t o = toff(k);
 #pragma unroll
-    for (int i = 0; i < EPL2; ++i) {
-      const int t = rrow + G * i;
+    for (int i = 0; i < EPL; ++i) {
+      const int t = wave + G * i;
       float out = 0.f;
-      if (t >= 0 && t < TT) {
-        // all partial reads first, one wait, then the fixed-order sum
-        const float2 q = xz[xbuf][t * 64 + lane];
-        float pv[G];
+      if (t < TT) {
+        float pv[G], cw[G];
 #pragma unroll
         for (int w = 0; w < G; ++w) pv[w] = yp[pbuf][(t * G + w) * 64 + lane];
-        float cw[G];
-        if (S == 1) {  // one state per wave: the partials are the states, weights C[t][n]
-          const int r = min(max(k * TT + t, 0), L - 1);  // row clamped into the sequence (value unused outside)
+        if (S == 1) {
+          const int r = min(max(k * TT + t, 0), L - 1);  // row clamped into the sequence
 #pragma unroll
           for (int w = 0; w < G; ++w) cw[w] = w < N ? ld_uniform<T>(Cm, (row0 + r) * N + w) : 0.f;
         }
+        // skip and gate from the activations in registers while the loads are in flight
+        const float skip = dsk * px[slot][i];
+        const float gate = GATED ? silu_f(pz[slot][i]) : 1.f;
         __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
-        float s = q.x;
+        float acc = skip;
         if (S == 1) {
 #pragma unroll
-          for (int w = 0; w < G; ++w) s = fmaf(cw[w], pv[w], s);
+          for (int w = 0; w < G; ++w) acc = fmaf(cw[w], pv[w], acc);
         } else {
 #pragma unroll
-          for (int w = 0; w < G; ++w) s += pv[w];
+          for (int w = 0; w < G; ++w) acc += pv[w];
         }
-        out = s * q.y;
+        out = acc * gate;
       }
       // the store is issued on every path (rows outside the tile have an outside offset),
       // so every iteration has the same memory operations
-      buf_st<T>(out, ry, off_add(roff[i], o));
+      buf_st<T>(out, ry, off_add(loff[i], o));
     }
   };
   // scan of tile k (B/C in buffer cbuf).  Scalar and LDS loads share one wait counter
@@ -263,27 +286,31 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
     }
   };
 
-  // prologue: tiles 0..P-1 in flight, B/C of tile 0, tile 0 prepped, tile P into slot 0
+  // prologue: B/C of tile 0, tiles 0..5 in flight, tile 0 prepped; slot 7 (tile -1,
+  // read out in the first step) holds zeros
   load_bc(0, 0);
 #pragma unroll
-  for (int u = 0; u < P; ++u) load_tile(u, u);
-  prep(0, 0, 0, 0);
-  load_tile(P, 0);
-  __syncthreads();
-  // main loop, unrolled by P = 4 so that every ring slot and buffer index is a constant
-  for (int kk = 0; kk < ntiles; kk += P) {
+  for (int u = 0; u < 6; ++u) load_tile(u, u);
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
+  for (int i = 0; i < EPL; ++i) px[7][i] = pr[7][i] = pz[7][i] = 0.f;
+  prep(0, 0, 0);
+  __syncthreads();
+  // Main loop, unrolled by 8 so that every ring slot and buffer index is a constant.
+  // Between two barriers a wave preps tile k+1, loads tile k+6, reads out tile k-1 and
+  // scans tile k; dd and yp alternate by tile parity.
+  for (int kk = 0; kk < ntiles; kk += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
       const int k = kk + u;
       if (k >= ntiles) break;
-      prep(k + 1, (u + 1) % P, (u + 1) & 1, (u + 1) & 3);
-      load_tile(k + 1 + P, (u + 1) % P);
-      readout(k - 1, (u + 1) & 1, (u + 3) & 3);
+      prep(k + 1, (u + 1) % R, (u + 1) & 1);
+      load_tile(k + 6, (u + 6) % R);
+      readout(k - 1, (u + R - 1) % R, (u + 1) & 1);
       scan(k, u & 1, u & 1, u & 1);
       __syncthreads();
     }
   }
-  readout(ntiles - 1, (ntiles - 1) & 1, (ntiles - 1) & 3);
+  readout(ntiles - 1, (ntiles - 1) % R, (ntiles - 1) & 1);
 
   if (h_final && dvalid) {
 #pragma unroll
@@ -294,11 +321,12 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
 
 template <typename T, int S, int G, bool GATED>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
-  // time tile: the B/C ring of a tile takes 2*TT*S SGPRs, so TT*S <= 16 (32 SGPRs);
-  // with 16 waves the LDS partials also cap TT at 8
-  constexpr int TT = G >= 16 ? 8 : (S == 1 ? 16 : (S == 2 ? 8 : 4));
-  // activation prefetch depth in tiles: about 64 steps ahead of the scan
-  constexpr int PF = 4;
+  // time tile: one state per wave scans 16 steps per barrier (LDS: dd 16 KB, partials
+  // 2*16*G*256 B); with several states per wave the B/C ring of a tile takes 4*TT*S
+  // SGPRs, so TT*S <= 16
+  constexpr int TT = S == 1 ? 16 : (S == 2 ? 8 : 4);
+  // ring of activation slots (tile mod 8)
+  constexpr int PF = 8;
   const int ngroups = (int)((a.dim + 63) / 64);
   const int64_t nblocks = (int64_t)ngroups * a.batch;
   if (a.dstate == S * G)
