@@ -8,11 +8,12 @@
  *   s_t[b,d]     = sum_n C[b,t,n] h_t[b,d,n] + D[d] x[b,t,d]    readout from the updated state
  *   y[b,t,d]     = s_t silu(z[b,t,d])   (y = s_t when z is NULL)  optional SiLU gate
  * Passages that define it: the selective_scan_kernel and its softplus device
- * function in the POPCORNBENCH transcript "FW-GLM-5-1 l2_p30" (recurrence order,
+ * function in the POPCORNBENCH transcript FW-GLM-5-1 l2_p30 (recurrence order,
  * readout after the update, skip term D*x); mamba-rs kernels.rs, MambaKernels
- * (ssm_step_fwd "single-step SSM forward (T=1 inference)", exp_negate,
- * softplus_fwd, split_gate_silu and gating_backward "y = ssm_out * gate_silu",
- * and the gradient shapes of ssm_reduce_d_B/_C/_D/_a_log).
+ * fields (ssm_step_fwd, the one-step forward used at inference; exp_negate;
+ * softplus_fwd; split_gate_silu and gating_backward, by which the SiLU gate
+ * multiplies the whole SSM output; the gradient shapes of
+ * ssm_reduce_d_B/_C/_D/_a_log).
  *
  * Conventions shared by every entry point
  *   Layout: contiguous row-major, last index fastest.

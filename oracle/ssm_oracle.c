@@ -13,12 +13,12 @@
  *   s_t[b,d]     = sum_n C[b,t,n] * h_t[b,d,n] + D[d] * x[b,t,d]
  *   y[b,t,d]     = s_t * silu(z[b,t,d])            (or s_t when there is no gate)
  * Sources:
- *   - the selective-scan kernel of the POPCORNBENCH transcript "FW-GLM-5-1 l2_p30"
+ *   - the selective-scan kernel of the POPCORNBENCH transcript FW-GLM-5-1 l2_p30
  *     (its selective_scan_kernel: A_val = -exp(A_log), dA = exp(delta*A),
  *     B scaled by delta, state updated first, readout from the updated state,
  *     skip term D*x added to the readout; its softplus device function);
- *   - mamba-rs kernels.rs (MambaKernels fields): ssm_step_fwd "single-step SSM
- *     forward", exp_negate (A = -exp(A_log)), softplus, split_gate_silu and
+ *   - mamba-rs kernels.rs (MambaKernels fields): ssm_step_fwd (the one-step
+ *     forward), exp_negate (A = -exp(A_log)), softplus, split_gate_silu and
  *     gating_backward (the gate multiplies the whole SSM output), and the
  *     gradient shapes of ssm_reduce_d_B/C/D/a_log;
  *   - deterministic_backward.py (ordered_cumsum): parameter-gradient sums are

@@ -1,9 +1,10 @@
 // ssm_bwd.hip -- backward of the selective scan for gfx950 (fp32 I/O).
 //
-// Gradients of the loss sum(dy * y) (mamba-rs kernels.rs lists the pieces:
-// ssm_backward_local "dh, du, d_delta contributions", ssm_reduce_d_B / _d_C
-// "[B*T*d_state]", ssm_reduce_d_D "[d_inner]", ssm_reduce_d_a_log
-// "[d_inner*d_state]", softplus_bwd, silu_bwd, gating_backward).  With
+// Gradients of the loss sum(dy * y) (mamba-rs kernels.rs, MambaKernels fields, lists
+// the pieces: ssm_backward_local for the per-element state, input and step-size
+// contributions; ssm_reduce_d_B / _d_C into [B*T*d_state] buffers; ssm_reduce_d_D over
+// d_inner; ssm_reduce_d_a_log over d_inner*d_state; softplus_bwd, silu_bwd,
+// gating_backward).  With
 // a_t = exp(Delta_t A), g_t = dy_t silu(z_t), and G_t = dLoss/dh_t:
 //   G_t = g_t C_t + a_{t+1} G_{t+1}
 //   dz_t = dy_t s_t silu'(z_t)                 dx_t = g_t D + Delta_t sum_n G_t B_t
@@ -13,9 +14,10 @@
 // The derivative of softplus is the logistic sigmoid (mamba3_preprocess_backward.slang
 // writes it 1 - exp(-softplus)).
 //
-// Determinism (deterministic_backward.py: only the order of shared-parameter sums
-// is fixed, ordered_cumsum adds per-(batch, chunk) partials in lexical order; the
-// Slang shader replaces a contended float atomic with a per-row partial): there are
+// Determinism (deterministic_backward.py keeps the forward as it is and fixes the
+// order in which shared-parameter gradients are summed -- its ordered_cumsum adds
+// per-(batch, chunk) partials batch by batch, chunk by chunk; the Slang shader writes
+// a per-row dt_bias partial instead of a float atomic): there are
 // no atomics.  Every sum is a fixed-order fp32 sum -- over the 64 channels of a
 // tile inside one wavefront, then over tiles / batch in ascending order in a
 // separate reduction kernel.

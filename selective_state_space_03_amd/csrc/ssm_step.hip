@@ -1,5 +1,6 @@
-// ssm_step.hip -- single-step decode update (mamba-rs kernels.rs, ssm_step_fwd:
-// "Single-step SSM forward (T=1 inference)"), state updated in place.
+// ssm_step.hip -- single-step decode update (mamba-rs kernels.rs, MambaKernels field
+// ssm_step_fwd: the SSM forward for one time step, used at inference), state updated
+// in place.
 //
 // The step is bound by HBM traffic of the state (read + write of batch*d_inner*d_state
 // fp32), so the layout is chosen for that stream: QL lanes share one (b, d) pair and
