@@ -4,12 +4,12 @@
 // the pieces: ssm_backward_local for the per-element state, input and step-size
 // contributions; ssm_reduce_d_B / _d_C into [B*T*d_state] buffers; ssm_reduce_d_D over
 // d_inner; ssm_reduce_d_a_log over d_inner*d_state; softplus_bwd, silu_bwd,
-// gating_backward).  With
-// a_t = exp(Delta_t A), g_t = dy_t silu(z_t), and G_t = dLoss/dh_t:
+// gating_backward).  With a_t = exp(Delta_t A), u_t = Delta_t x_t, g_t = dy_t silu(z_t)
+// and G_t = dLoss/dh_t:
 //   G_t = g_t C_t + a_{t+1} G_{t+1}
 //   dz_t = dy_t s_t silu'(z_t)                 dx_t = g_t D + Delta_t sum_n G_t B_t
 //   dDelta_t = sum_n G_t (A a_t h_{t-1} + B_t x_t),   ddelta_raw_t = dDelta_t sigmoid(r_t)
-//   dB_t = sum_d G_t Delta_t x_t   dC_t = sum_d g_t h_t   (sums over channels)
+//   dB_t = sum_d G_t u_t   dC_t = sum_d g_t h_t   (sums over channels)
 //   dA_log = A * sum_{b,t} G_t Delta_t a_t h_{t-1}, dD = sum g x, d_dt_bias = sum ddelta_raw
 // The derivative of softplus is the logistic sigmoid (mamba3_preprocess_backward.slang
 // writes it 1 - exp(-softplus)).
@@ -17,20 +17,31 @@
 // Determinism (deterministic_backward.py keeps the forward as it is and fixes the
 // order in which shared-parameter gradients are summed -- its ordered_cumsum adds
 // per-(batch, chunk) partials batch by batch, chunk by chunk; the Slang shader writes
-// a per-row dt_bias partial instead of a float atomic): there are
-// no atomics.  Every sum is a fixed-order fp32 sum -- over the 64 channels of a
-// tile inside one wavefront, then over tiles / batch in ascending order in a
-// separate reduction kernel.
+// a per-row dt_bias partial instead of a float atomic): there are no atomics.  Every
+// sum is a fixed-order fp32 sum -- over the 64 channels of a tile inside one
+// wavefront, over the wavefronts of a workgroup in wave order, then over tiles /
+// (batch, segment) in ascending order in a separate reduction kernel.
 //
-// Kernels, all on the caller's stream:
-//   1. chunk_state : per (b, time chunk, channel) the chunk's end state from a zero
-//                    start and the chunk's sum of Delta (chunks are independent);
-//   2. chunk_pass  : sequential over chunks per (b, d, n): the true start state of
-//                    every chunk (h0 for chunk 0);
-//   3. bwd_main    : per (b, 64-channel tile), chunks in reverse order; inside a
-//                    chunk the forward is recomputed from its start state with the
-//                    states kept in VGPRs, then the reverse recurrence runs;
-//   4. reduce_bc / reduce_params : ordered sums of the per-tile partials.
+// Parallel structure.  Both recurrences are linear, so time is cut into segments of
+// segc chunks of kChunk steps that are processed independently; what crosses a
+// segment boundary is a state (forward) and an adjoint carry (reverse), each an
+// affine function of its value at the other end of the segment, with decay
+// exp(A * sum of Delta over the segment):
+//   1. chunk_rel : per (b, 64-channel tile, segment), forward from a zero state:
+//                  the state at every chunk start relative to the segment start, the
+//                  sum of Delta up to it, and the segment's end state and Delta sum;
+//   2. seg_adj   : per (b, tile, segment), the reverse recurrence from a zero carry:
+//                  the carry leaving the segment's first step;
+//   3. seg_pass  : per (b, d, n), sequential over segments: the true state entering
+//                  every segment (h0 first) and the true carry entering it from the
+//                  right;
+//   4. bwd_main  : per (b, tile, segment), chunks in reverse order: the chunk's start
+//                  state from 1 and 3, its forward recomputed into VGPRs, then the
+//                  reverse recurrence and every gradient;
+//   5. reduce_bc / reduce_params : ordered sums of the per-tile partials.
+// Work layout (as in the forward): lane = channel, the G wavefronts of a workgroup
+// split the state axis (S states per wave), B and C are wave-uniform scalar loads,
+// per-element work is done once per (t, channel) and shared through LDS.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -38,10 +49,12 @@ namespace ssm {
 
 namespace {
 constexpr int kChunk = 16;  // time steps per chunk (recompute window held in VGPRs)
-constexpr int kSub = 8;     // reverse steps between channel reductions of dB/dC
+constexpr int kSub = 4;     // reverse steps between channel reductions of dB/dC
 constexpr int kRowPad = 66; // padded LDS row (float2) for the channel reduction
+constexpr int kS = 2;       // states per wavefront
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+int waves_for(int dstate) { return dstate <= 2 ? 1 : (dstate <= 4 ? 2 : (dstate <= 8 ? 4 : 8)); }
 }  // namespace
 
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
@@ -49,126 +62,262 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
   l.chunk = kChunk;
   l.nchunks = (seqlen + kChunk - 1) / kChunk;
   l.ngroups = (dim + 63) / 64;
+  // segments: enough (batch, tile, segment) workgroups to fill the chip several times
+  // over, but at least 4 chunks per segment
+  const int64_t want = (2048 + batch * l.ngroups - 1) / (batch * l.ngroups);
+  int64_t segc = (l.nchunks + want - 1) / want;
+  if (segc < 4) segc = 4;
+  if (segc > l.nchunks) segc = l.nchunks;
+  l.segc = segc;
+  l.nseg = (l.nchunks + segc - 1) / segc;
   const size_t f = sizeof(float);
+  const size_t N = (size_t)dstate;
   size_t off = 0;
-  l.off_hloc = off;     off = align256(off + (size_t)batch * l.nchunks * dim * dstate * f);
-  l.off_sumdelta = off; off = align256(off + (size_t)batch * l.nchunks * dim * f);
-  l.off_hstart = off;   off = align256(off + (size_t)batch * l.nchunks * dim * dstate * f);
-  l.off_dbc = off;      off = align256(off + 2 * (size_t)batch * l.ngroups * seqlen * dstate * f);
-  l.off_dparam = off;   off = align256(off + ((size_t)batch * dim * dstate + 2 * (size_t)batch * dim) * f);
+  l.off_hrel = off;   off = align256(off + (size_t)batch * l.nchunks * dim * N * f);
+  l.off_cumd = off;   off = align256(off + (size_t)batch * l.nchunks * dim * f);
+  l.off_hseg = off;   off = align256(off + (size_t)batch * l.nseg * dim * N * f);
+  l.off_sdseg = off;  off = align256(off + (size_t)batch * l.nseg * dim * f);
+  l.off_gseg = off;   off = align256(off + (size_t)batch * l.nseg * dim * N * f);
+  l.off_hin = off;    off = align256(off + (size_t)batch * l.nseg * dim * N * f);
+  l.off_gin = off;    off = align256(off + (size_t)batch * l.nseg * dim * N * f);
+  l.off_dbc = off;    off = align256(off + 2 * (size_t)batch * l.ngroups * seqlen * N * f);
+  l.off_dparam = off; off = align256(off + ((size_t)batch * l.nseg * dim * N + 2 * (size_t)batch * l.nseg * dim) * f);
   l.total = off;
   return l;
 }
 
 namespace {
 
-// ---- 1. chunk end states from a zero start; lane = channel, all states per lane
-template <int NS>
-__global__ void __launch_bounds__(64)
-chunk_state_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
-                   const float* __restrict__ Bm, const float* __restrict__ A_log,
-                   const float* __restrict__ dt_bias, float* __restrict__ hloc,
-                   float* __restrict__ sumdelta, int64_t L, int64_t Dm, int N, int64_t ngroups,
-                   int64_t nchunks) {
-  // block -> (b, chunk, group); the last chunk's end state is never needed
-  const int64_t per_b = (nchunks - 1) * ngroups;
-  const int64_t b = blockIdx.x / per_b;
-  const int64_t rem = blockIdx.x % per_b;
-  const int64_t k = rem / ngroups;
-  const int64_t d = (rem % ngroups) * 64 + threadIdx.x;
-  if (d >= Dm) return;  // no barriers in this kernel
-  const float bias = dt_bias ? dt_bias[d] : 0.f;
-  float A2[NS], h[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) {
-    A2[n] = n < N ? a2_from_alog(A_log[d * N + n]) : 0.f;
-    h[n] = 0.f;
-  }
-  const int64_t t0 = k * kChunk;
-  const int64_t t1 = (t0 + kChunk < L) ? t0 + kChunk : L;
-  float sd = 0.f;
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t idx = (b * L + t) * Dm + d;
-    const float delta = softplus_f(delta_raw[idx] + bias);
-    const float dxv = delta * x[idx];
-    sd += delta;
-    const float* __restrict__ Bt = Bm + (b * L + t) * N;
-#pragma unroll
-    for (int n = 0; n < NS; ++n)
-      if (n < N) h[n] = fmaf(exp2_hw(delta * A2[n]), h[n], dxv * Bt[n]);
-  }
-  const int64_t o = (b * nchunks + k) * Dm + d;
-#pragma unroll
-  for (int n = 0; n < NS; ++n)
-    if (n < N) hloc[o * N + n] = h[n];
-  sumdelta[o] = sd;
+// Common per-lane set-up: channel, states of this wave, and the segment's chunks.
+struct Lane {
+  int lane, wave;
+  int64_t b, grp, seg, d;
+  bool dvalid;
+  int n0, nact;
+  int64_t c_begin, c_end;
+};
+template <int S>
+__device__ __forceinline__ Lane lane_setup(int64_t ngroups, int64_t nseg, int64_t segc, int64_t nchunks, int N) {
+  Lane q;
+  q.lane = threadIdx.x & 63;
+  q.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // block -> (b, segment, group): the groups of one segment are neighbours
+  q.grp = blockIdx.x % ngroups;
+  const int64_t bs = blockIdx.x / ngroups;
+  q.seg = bs % nseg;
+  q.b = bs / nseg;
+  q.d = q.grp * 64 + q.lane;
+  q.n0 = q.wave * S;
+  q.nact = N - q.n0 < 0 ? 0 : (N - q.n0 > S ? S : N - q.n0);
+  q.c_begin = q.seg * segc;
+  q.c_end = q.c_begin + segc < nchunks ? q.c_begin + segc : nchunks;
+  q.dvalid = false;  // set by the caller (needs Dm)
+  return q;
 }
 
-// ---- 2. start state of every chunk, sequential over chunks per (b, d, n)
+// ---- 1. forward from a zero state per segment: chunk-start states relative to the
+// segment start, Delta sums, and the segment's end state
+template <int S, int G>
+__global__ void __launch_bounds__(64 * G)
+chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
+                 const float* __restrict__ Bm, const float* __restrict__ A_log,
+                 const float* __restrict__ dt_bias, float* __restrict__ hrel, float* __restrict__ cumd,
+                 float* __restrict__ hseg, float* __restrict__ sdseg, int64_t L, int64_t Dm, int N,
+                 int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
+  constexpr int TC = kChunk;
+  constexpr int EPL = (TC + G - 1) / G;
+  __shared__ float2 pd[TC * 64];  // (Delta, Delta*x) per (t, channel)
+  Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
+  q.dvalid = q.d < Dm;
+  const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
+  float A2[S], h[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    A2[j] = (q.dvalid && j < q.nact) ? a2_from_alog(A_log[q.d * N + q.n0 + j]) : 0.f;
+    h[j] = 0.f;
+  }
+  float sd = 0.f;
+  const int64_t row0 = q.b * L;
+  for (int64_t c = q.c_begin; c < q.c_end; ++c) {
+    const int64_t t0 = c * TC;
+    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
+    if (q.dvalid) {
+      const int64_t o = (q.b * nchunks + c) * Dm + q.d;
+#pragma unroll
+      for (int j = 0; j < S; ++j)
+        if (j < q.nact) hrel[o * N + q.n0 + j] = h[j];
+      if (q.wave == 0) cumd[o] = sd;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int t = q.wave + G * i;
+      if (t < TC) {
+        const bool v = q.dvalid && t < tvalid;
+        const int64_t idx = (row0 + t0 + t) * Dm + q.d;
+        const float delta = v ? softplus_f(delta_raw[idx] + bias) : 0.f;
+        pd[t * 64 + q.lane] = make_float2(delta, v ? delta * x[idx] : 0.f);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps have Delta = 0
+      const float2 v = pd[t * 64 + q.lane];
+      sd += v.x;
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        const float bj = j < q.nact ? ld_uniform<float>(Bm, (row0 + tr) * N + q.n0 + j) : 0.f;
+        h[j] = fmaf(exp2_hw(v.x * A2[j]), h[j], v.y * bj);
+      }
+    }
+    __syncthreads();
+  }
+  if (q.dvalid) {
+    const int64_t o = (q.b * nseg + q.seg) * Dm + q.d;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (j < q.nact) hseg[o * N + q.n0 + j] = h[j];
+    if (q.wave == 0) sdseg[o] = sd;
+  }
+}
+
+// ---- 2. reverse recurrence from a zero carry per segment: the carry a_t G_t leaving
+// the segment's first step
+template <int S, int G, bool GATED>
+__global__ void __launch_bounds__(64 * G)
+seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
+               const float* __restrict__ dy, const float* __restrict__ Cm,
+               const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+               float* __restrict__ gseg, int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks,
+               int64_t segc, int64_t nseg) {
+  constexpr int TC = kChunk;
+  constexpr int EPL = (TC + G - 1) / G;
+  __shared__ float2 pa[TC * 64];  // (Delta, g) per (t, channel)
+  Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
+  q.dvalid = q.d < Dm;
+  const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
+  float A2[S], gc[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    A2[j] = (q.dvalid && j < q.nact) ? a2_from_alog(A_log[q.d * N + q.n0 + j]) : 0.f;
+    gc[j] = 0.f;
+  }
+  const int64_t row0 = q.b * L;
+  for (int64_t c = q.c_end - 1; c >= q.c_begin; --c) {
+    const int64_t t0 = c * TC;
+    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int t = q.wave + G * i;
+      if (t < TC) {
+        const bool v = q.dvalid && t < tvalid;
+        const int64_t idx = (row0 + t0 + t) * Dm + q.d;
+        const float delta = v ? softplus_f(delta_raw[idx] + bias) : 0.f;
+        float g = v ? dy[idx] : 0.f;
+        if (GATED) g *= v ? silu_f(z[idx]) : 0.f;
+        pa[t * 64 + q.lane] = make_float2(delta, g);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = TC - 1; t >= 0; --t) {
+      const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps: Delta = g = 0
+      const float2 v = pa[t * 64 + q.lane];
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        const float cj = j < q.nact ? ld_uniform<float>(Cm, (row0 + tr) * N + q.n0 + j) : 0.f;
+        const float Gt = fmaf(v.y, cj, gc[j]);  // dLoss/dh_t
+        gc[j] = exp2_hw(v.x * A2[j]) * Gt;      // carry to h_{t-1}
+      }
+    }
+    __syncthreads();
+  }
+  if (q.dvalid) {
+    const int64_t o = (q.b * nseg + q.seg) * Dm + q.d;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (j < q.nact) gseg[o * N + q.n0 + j] = gc[j];
+  }
+}
+
+// ---- 3. sequential over segments per (b, d, n): state entering every segment
+// (forward) and carry entering it from the right (reverse)
 __global__ void __launch_bounds__(256)
-chunk_pass_kernel(const float* __restrict__ hloc, const float* __restrict__ sumdelta,
-                  const float* __restrict__ A_log, const float* __restrict__ h0,
-                  float* __restrict__ hstart, int64_t batch, int64_t Dm, int N, int64_t nchunks) {
+seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
+                const float* __restrict__ gseg, const float* __restrict__ A_log,
+                const float* __restrict__ h0, float* __restrict__ hin, float* __restrict__ gin,
+                int64_t batch, int64_t Dm, int N, int64_t nseg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
   if (i >= batch * Dm * N) return;
   const int64_t b = i / (Dm * N);
   const int64_t dn = i % (Dm * N);
   const int64_t d = dn / N;
+  const int n = (int)(dn % N);
   const float A2 = a2_from_alog(A_log[dn]);
   float h = h0 ? h0[i] : 0.f;
-  for (int64_t k = 0; k < nchunks; ++k) {
-    const int64_t o = (b * nchunks + k) * Dm + d;
-    hstart[o * N + (dn % N)] = h;
-    if (k + 1 < nchunks) h = fmaf(exp2_hw(A2 * sumdelta[o]), h, hloc[o * N + (dn % N)]);
+  for (int64_t s = 0; s < nseg; ++s) {
+    const int64_t o = (b * nseg + s) * Dm + d;
+    hin[o * N + n] = h;
+    h = fmaf(exp2_hw(A2 * sdseg[o]), h, hseg[o * N + n]);
+  }
+  float g = 0.f;
+  for (int64_t s = nseg - 1; s >= 0; --s) {
+    const int64_t o = (b * nseg + s) * Dm + d;
+    gin[o * N + n] = g;
+    g = fmaf(exp2_hw(A2 * sdseg[o]), g, gseg[o * N + n]);
   }
 }
 
-// ---- 3. main backward: recompute + reverse, per (b, 64-channel tile)
+// ---- 4. main backward per (b, tile, segment): chunks in reverse order
 template <int S, int G, bool GATED>
 __global__ void __launch_bounds__(64 * G)
 bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
                 const float* __restrict__ z, const float* __restrict__ Bm, const float* __restrict__ Cm,
                 const float* __restrict__ A_log, const float* __restrict__ D_skip,
                 const float* __restrict__ dt_bias, const float* __restrict__ dy,
-                const float* __restrict__ hstart, float* __restrict__ dx, float* __restrict__ ddelta_raw,
-                float* __restrict__ dz, float* __restrict__ pdB, float* __restrict__ pdC,
-                float* __restrict__ pdA, float* __restrict__ pdD, float* __restrict__ pdbias,
-                int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks) {
+                const float* __restrict__ hrel, const float* __restrict__ cumd,
+                const float* __restrict__ hin, const float* __restrict__ gin,
+                float* __restrict__ dx, float* __restrict__ ddelta_raw, float* __restrict__ dz,
+                float* __restrict__ pdB, float* __restrict__ pdC, float* __restrict__ pdA,
+                float* __restrict__ pdD, float* __restrict__ pdbias, int64_t L, int64_t Dm, int N,
+                int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   constexpr int NPAIR = kSub * S;      // (step, state) outputs per sub-tile and wave
   constexpr int LPP = 64 / NPAIR;      // lanes that share one output's channel sum
   static_assert(LPP >= 2 && 64 % NPAIR == 0, "sub-tile reduction layout");
   __shared__ float4 pd[TC * 64];                 // (Delta, Delta*x, g, -) per (t, channel)
-  __shared__ float2 pp[TC * G * 64];             // per-wave partials: .x readout, then (P1, P2)
+  __shared__ float yp[TC * G * 64];              // per-wave readout partials sum_j C h
+  __shared__ float2 pp[TC * G * 64];             // per-wave partials (sum G B, sum G A a h_{t-1})
   __shared__ float2 scr[G][NPAIR * kRowPad];     // per-wave dB/dC channel-reduction scratch
   __shared__ float2 fin[G * 64];                 // per-wave dD / d_dt_bias partials
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t b = blockIdx.x / ngroups;
-  const int64_t grp = blockIdx.x % ngroups;
-  const int64_t d = grp * 64 + lane;
-  const bool dvalid = d < Dm;
+  Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
+  q.dvalid = q.d < Dm;
+  const int lane = q.lane, wave = q.wave;
+  const int64_t b = q.b, d = q.d;
+  const bool dvalid = q.dvalid;
+  const int n0 = q.n0, nact = q.nact;
   const float bias = (dvalid && dt_bias) ? dt_bias[d] : 0.f;
   const float dsk = (dvalid && D_skip) ? D_skip[d] : 0.f;
-  const int n0 = wave * S;
-  const int nact = N - n0 < 0 ? 0 : (N - n0 > S ? S : N - n0);
 
-  float A2[S], Av[S], Gs[S], dA[S];
+  float A2[S], Av[S], Gc[S], dA[S], hi[S];
+  {
+    const int64_t o = ((b * nseg + q.seg) * Dm + d) * N + n0;
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    const bool v = dvalid && j < nact;
-    const float al = v ? A_log[d * N + n0 + j] : 0.f;
-    Av[j] = v ? -expf(al) : 0.f;
-    A2[j] = Av[j] * kLog2e;
-    Gs[j] = 0.f;
-    dA[j] = 0.f;
+    for (int j = 0; j < S; ++j) {
+      const bool v = dvalid && j < nact;
+      Av[j] = v ? -expf(A_log[d * N + n0 + j]) : 0.f;
+      A2[j] = Av[j] * kLog2e;
+      Gc[j] = v ? gin[o + j] : 0.f;  // carry entering the segment's last step
+      hi[j] = v ? hin[o + j] : 0.f;  // state entering the segment
+      dA[j] = 0.f;
+    }
   }
   float dD_acc = 0.f, db_acc = 0.f;
   const int64_t row0 = b * L;
 
-  for (int64_t k = nchunks - 1; k >= 0; --k) {
+  for (int64_t k = q.c_end - 1; k >= q.c_begin; --k) {
     const int64_t t0 = k * TC;
     const int tvalid = (int)((L - t0) < TC ? (L - t0) : TC);
     // ---- P: per-element values (each element once, spread over all waves)
@@ -192,74 +341,77 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
       ex[i] = xv; edelta[i] = delta; eg[i] = g; esig[i] = sigmoid_f(r); egz[i] = gz;
       if (t < TC) pd[t * 64 + lane] = make_float4(delta, delta * xv, g, 0.f);
     }
-    __syncthreads();
-    // ---- F: recompute this wave's states over the chunk, keep h_t and a_t
-    float H[TC][S], AS[TC][S], hs[S];
+    // start state of this chunk: relative state + decayed segment entry state
+    float hs[S];
     {
-      const float* __restrict__ hst = hstart + ((b * nchunks + k) * Dm + d) * N + n0;
+      const int64_t o = (b * nchunks + k) * Dm + d;
+      const float cd = dvalid ? cumd[o] : 0.f;
 #pragma unroll
-      for (int j = 0; j < S; ++j) hs[j] = (dvalid && j < nact) ? hst[j] : 0.f;
+      for (int j = 0; j < S; ++j)
+        hs[j] = (dvalid && j < nact) ? fmaf(exp2_hw(A2[j] * cd), hi[j], hrel[o * N + n0 + j]) : 0.f;
+    }
+    __syncthreads();
+    // ---- F: recompute this wave's states over the chunk, keep h_t, a_t and the
+    // chunk's (Delta, Delta*x, g) in registers
+    float H[TC][S], AS[TC][S];
+    float4 V[TC];
+    {
       float hc[S];
 #pragma unroll
       for (int j = 0; j < S; ++j) hc[j] = hs[j];
 #pragma unroll
       for (int t = 0; t < TC; ++t) {
-        const int64_t tr = (t0 + t < L) ? t0 + t : L - 1;  // clamp: invalid steps have Delta = 0
-        const float* __restrict__ Bt = Bm + (row0 + tr) * N + n0;
-        const float* __restrict__ Ct = Cm + (row0 + tr) * N + n0;
-        const float4 v = pd[t * 64 + lane];
+        const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps have Delta = 0
+        V[t] = pd[t * 64 + lane];
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < S; ++j) {
-          if (j < nact) {
-            const float a = exp2_hw(v.x * A2[j]);
-            hc[j] = fmaf(a, hc[j], v.y * Bt[j]);
-            acc = fmaf(Ct[j], hc[j], acc);
-            AS[t][j] = a;
-          } else {
-            AS[t][j] = 1.f;
-          }
+          const float bj = j < nact ? ld_uniform<float>(Bm, (row0 + tr) * N + n0 + j) : 0.f;
+          const float cj = j < nact ? ld_uniform<float>(Cm, (row0 + tr) * N + n0 + j) : 0.f;
+          const float a = exp2_hw(V[t].x * A2[j]);
+          hc[j] = fmaf(a, hc[j], V[t].y * bj);
+          acc = fmaf(cj, hc[j], acc);
+          AS[t][j] = a;
           H[t][j] = hc[j];
         }
-        pp[(t * G + wave) * 64 + lane].x = acc;
+        if (GATED) yp[(t * G + wave) * 64 + lane] = acc;
       }
     }
     __syncthreads();
     // ---- R1: readout s_t (fixed wave order) -> dz
+    if (GATED) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int t = wave + G * i;
-      if (GATED && t < tvalid && dvalid) {
-        float s = dsk * ex[i];
+      for (int i = 0; i < EPL; ++i) {
+        const int t = wave + G * i;
+        if (t < tvalid && dvalid) {
+          float s = dsk * ex[i];
 #pragma unroll
-        for (int w = 0; w < G; ++w) s += pp[(t * G + w) * 64 + lane].x;
-        dz[(row0 + t0 + t) * Dm + d] = egz[i] * s;
+          for (int w = 0; w < G; ++w) s += yp[(t * G + w) * 64 + lane];
+          dz[(row0 + t0 + t) * Dm + d] = egz[i] * s;
+        }
       }
     }
-    __syncthreads();
     // ---- V: reverse recurrence over the chunk
     float2* __restrict__ sw = scr[wave];
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {
-      const int64_t tr = (t0 + t < L) ? t0 + t : L - 1;
-      const float* __restrict__ Bt = Bm + (row0 + tr) * N + n0;
-      const float* __restrict__ Ct = Cm + (row0 + tr) * N + n0;
-      const float4 v = pd[t * 64 + lane];  // Delta, Delta*x, g
+      const int64_t tr = t < tvalid ? t0 + t : L - 1;
       float P1 = 0.f, P2 = 0.f;
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         float dBp = 0.f, dCp = 0.f;
         if (j < nact) {
-          const float bj = Bt[j];
-          Gs[j] = fmaf(v.z, Ct[j], Gs[j]);             // dLoss/dh_t
-          dCp = v.z * H[t][j];
-          dBp = Gs[j] * v.y;
-          P1 = fmaf(Gs[j], bj, P1);
+          const float bj = ld_uniform<float>(Bm, (row0 + tr) * N + n0 + j);
+          const float cj = ld_uniform<float>(Cm, (row0 + tr) * N + n0 + j);
+          const float Gt = fmaf(V[t].z, cj, Gc[j]);      // dLoss/dh_t
+          dCp = V[t].z * H[t][j];
+          dBp = Gt * V[t].y;
+          P1 = fmaf(Gt, bj, P1);
           const float hprev = t > 0 ? H[t - 1][j] : hs[j];
-          const float w = Gs[j] * (AS[t][j] * hprev);  // G a h_{t-1}
-          dA[j] = fmaf(w, v.x, dA[j]);
+          const float w = Gt * (AS[t][j] * hprev);       // G a h_{t-1}
+          dA[j] = fmaf(w, V[t].x, dA[j]);
           P2 = fmaf(w, Av[j], P2);
-          Gs[j] *= AS[t][j];                            // carry to h_{t-1}
+          Gc[j] = AS[t][j] * Gt;                          // carry to h_{t-1}
         }
         sw[((t % kSub) * S + j) * kRowPad + lane] = make_float2(dBp, dCp);
       }
@@ -273,9 +425,9 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         float sB = 0.f, sC = 0.f;
 #pragma unroll
         for (int i = 0; i < 64 / LPP; ++i) {
-          const float2 q = sw[p * kRowPad + part + LPP * i];
-          sB += q.x;
-          sC += q.y;
+          const float2 qv = sw[p * kRowPad + part + LPP * i];
+          sB += qv.x;
+          sC += qv.y;
         }
 #pragma unroll
         for (int m = 1; m < LPP; m <<= 1) {
@@ -285,7 +437,7 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         const int ts = t + p / S;  // absolute step inside the chunk
         const int j = p % S;
         if (part < 2 && j < nact && ts < tvalid) {
-          const int64_t o = ((b * ngroups + grp) * L + t0 + ts) * N + n0 + j;
+          const int64_t o = ((b * ngroups + q.grp) * L + t0 + ts) * N + n0 + j;
           if (part == 0) pdB[o] = sB; else pdC[o] = sC;
         }
         __builtin_amdgcn_wave_barrier();
@@ -300,9 +452,9 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         float P1 = 0.f, P2 = 0.f;
 #pragma unroll
         for (int w = 0; w < G; ++w) {
-          const float2 q = pp[(t * G + w) * 64 + lane];
-          P1 += q.x;
-          P2 += q.y;
+          const float2 qv = pp[(t * G + w) * 64 + lane];
+          P1 += qv.x;
+          P2 += qv.y;
         }
         const int64_t idx = (row0 + t0 + t) * Dm + d;
         dx[idx] = fmaf(eg[i], dsk, edelta[i] * P1);
@@ -314,11 +466,13 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
     }
     __syncthreads();
   }
-  // ---- per-(b, d) partials: dA raw sums, and dD / d_dt_bias joined over waves in order
+  // ---- per-(b, segment, d) partials: dA raw sums, and dD / d_dt_bias joined over
+  // waves in order
+  const int64_t po = (b * nseg + q.seg) * Dm + d;
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < S; ++j)
-      if (j < nact) pdA[(b * Dm + d) * N + n0 + j] = dA[j];
+      if (j < nact) pdA[po * N + n0 + j] = dA[j];
   }
   fin[wave * 64 + lane] = make_float2(dD_acc, db_acc);
   __syncthreads();
@@ -329,12 +483,12 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
       sD += fin[w * 64 + lane].x;
       sb += fin[w * 64 + lane].y;
     }
-    pdD[b * Dm + d] = sD;
-    pdbias[b * Dm + d] = sb;
+    pdD[po] = sD;
+    pdbias[po] = sb;
   }
 }
 
-// ---- 4a. dB, dC: sum of the channel-tile partials in ascending tile order
+// ---- 5a. dB, dC: sum of the channel-tile partials in ascending tile order
 __global__ void __launch_bounds__(256)
 reduce_bc_kernel(const float* __restrict__ pdB, const float* __restrict__ pdC, float* __restrict__ dB,
                  float* __restrict__ dC, int64_t batch, int64_t L, int N, int64_t ngroups) {
@@ -352,58 +506,75 @@ reduce_bc_kernel(const float* __restrict__ pdB, const float* __restrict__ pdC, f
   dC[i] = sC;
 }
 
-// ---- 4b. dA_log, dD, d_dt_bias: sums over batch in ascending order
+// ---- 5b. dA_log, dD, d_dt_bias: sums over (batch, segment) in lexical order
 __global__ void __launch_bounds__(256)
 reduce_params_kernel(const float* __restrict__ pdA, const float* __restrict__ pdD,
                      const float* __restrict__ pdbias, const float* __restrict__ A_log,
                      float* __restrict__ dA_log, float* __restrict__ dD, float* __restrict__ d_dt_bias,
-                     int64_t batch, int64_t Dm, int N) {
+                     int64_t nparts, int64_t Dm, int N) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (d, n)
   if (i < Dm * N && dA_log) {
     float s = 0.f;
-    for (int64_t b = 0; b < batch; ++b) s += pdA[b * Dm * N + i];
+    for (int64_t p = 0; p < nparts; ++p) s += pdA[p * Dm * N + i];
     dA_log[i] = s * -expf(A_log[i]);  // dA/dA_log = A
   }
   if (i < Dm) {
     float sD = 0.f, sb = 0.f;
-    for (int64_t b = 0; b < batch; ++b) {
-      sD += pdD[b * Dm + i];
-      sb += pdbias[b * Dm + i];
+    for (int64_t p = 0; p < nparts; ++p) {
+      sD += pdD[p * Dm + i];
+      sb += pdbias[p * Dm + i];
     }
     if (dD) dD[i] = sD;
     if (d_dt_bias) d_dt_bias[i] = sb;
   }
 }
 
-template <int S, int G>
-hipError_t launch_main(const BwdArgs& a, const BwdLayout& l, char* ws, hipStream_t stream) {
-  float* hstart = (float*)(ws + l.off_hstart);
+template <int G>
+hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipStream_t stream) {
+  constexpr int S = kS;
+  const unsigned blocks = (unsigned)(a.batch * l.nseg * l.ngroups);
+  float* hrel = (float*)(ws + l.off_hrel);
+  float* cumd = (float*)(ws + l.off_cumd);
+  float* hseg = (float*)(ws + l.off_hseg);
+  float* sdseg = (float*)(ws + l.off_sdseg);
+  float* gseg = (float*)(ws + l.off_gseg);
+  float* hin = (float*)(ws + l.off_hin);
+  float* gin = (float*)(ws + l.off_gin);
+  hipError_t e;
+  hipLaunchKernelGGL((chunk_rel_kernel<S, G>), dim3(blocks), dim3(64 * G), 0, stream, a.x, a.delta_raw, a.B,
+                     a.A_log, a.dt_bias, hrel, cumd, hseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
+                     l.nchunks, l.segc, l.nseg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.z)
+    hipLaunchKernelGGL((seg_adj_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
+                       a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
+                       l.segc, l.nseg);
+  else
+    hipLaunchKernelGGL((seg_adj_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
+                       a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
+                       l.segc, l.nseg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    const int64_t n = a.batch * a.dim * a.dstate;
+    hipLaunchKernelGGL(seg_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, hseg, sdseg,
+                       gseg, a.A_log, a.h0, hin, gin, a.batch, a.dim, a.dstate, l.nseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   float* pdB = (float*)(ws + l.off_dbc);
   float* pdC = pdB + (size_t)a.batch * l.ngroups * a.seqlen * a.dstate;
   float* pdA = (float*)(ws + l.off_dparam);
-  float* pdD = pdA + (size_t)a.batch * a.dim * a.dstate;
-  float* pdb = pdD + (size_t)a.batch * a.dim;
-  const unsigned blocks = (unsigned)(a.batch * l.ngroups);
+  float* pdD = pdA + (size_t)a.batch * l.nseg * a.dim * a.dstate;
+  float* pdb = pdD + (size_t)a.batch * l.nseg * a.dim;
   if (a.z)
     hipLaunchKernelGGL((bwd_main_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
-                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hstart, a.dx,
-                       a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
-                       l.ngroups, l.nchunks);
+                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
+                       a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
+                       l.ngroups, l.nchunks, l.segc, l.nseg);
   else
     hipLaunchKernelGGL((bwd_main_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
-                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hstart, a.dx,
-                       a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
-                       l.ngroups, l.nchunks);
-  return hipGetLastError();
-}
-
-template <int NS>
-hipError_t launch_state(const BwdArgs& a, const BwdLayout& l, char* ws, hipStream_t stream) {
-  const unsigned blocks = (unsigned)(a.batch * (l.nchunks - 1) * l.ngroups);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_state_kernel<NS>), dim3(blocks), dim3(64), 0, stream, a.x, a.delta_raw, a.B,
-                     a.A_log, a.dt_bias, (float*)(ws + l.off_hloc), (float*)(ws + l.off_sumdelta),
-                     a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks);
+                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
+                       a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
+                       l.ngroups, l.nchunks, l.segc, l.nseg);
   return hipGetLastError();
 }
 
@@ -413,20 +584,12 @@ hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
   const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate);
   char* ws = (char*)workspace;
   hipError_t e;
-  const int ns = a.dstate <= 4 ? 4 : (a.dstate <= 8 ? 8 : 16);
-  e = ns == 4 ? launch_state<4>(a, l, ws, stream)
-              : (ns == 8 ? launch_state<8>(a, l, ws, stream) : launch_state<16>(a, l, ws, stream));
-  if (e != hipSuccess) return e;
-  {
-    const int64_t n = a.batch * a.dim * a.dstate;
-    hipLaunchKernelGGL(chunk_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)(ws + l.off_hloc), (const float*)(ws + l.off_sumdelta), a.A_log, a.h0,
-                       (float*)(ws + l.off_hstart), a.batch, a.dim, a.dstate, l.nchunks);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  switch (waves_for(a.dstate)) {
+    case 1: e = launch_segments<1>(a, l, ws, stream); break;
+    case 2: e = launch_segments<2>(a, l, ws, stream); break;
+    case 4: e = launch_segments<4>(a, l, ws, stream); break;
+    default: e = launch_segments<8>(a, l, ws, stream); break;
   }
-  // four states per wave; 4, 2 or 1 wavefronts per tile for d_state <= 16, 8, 4
-  e = ns == 4 ? launch_main<4, 1>(a, l, ws, stream)
-              : (ns == 8 ? launch_main<4, 2>(a, l, ws, stream) : launch_main<4, 4>(a, l, ws, stream));
   if (e != hipSuccess) return e;
   {
     float* pdB = (float*)(ws + l.off_dbc);
@@ -438,11 +601,11 @@ hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
   }
   {
     float* pdA = (float*)(ws + l.off_dparam);
-    float* pdD = pdA + (size_t)a.batch * a.dim * a.dstate;
-    float* pdb = pdD + (size_t)a.batch * a.dim;
+    float* pdD = pdA + (size_t)a.batch * l.nseg * a.dim * a.dstate;
+    float* pdb = pdD + (size_t)a.batch * l.nseg * a.dim;
     const int64_t n = a.dim * a.dstate > a.dim ? a.dim * a.dstate : a.dim;
     hipLaunchKernelGGL(reduce_params_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pdA, pdD,
-                       pdb, a.A_log, a.dA_log, a.dD, a.d_dt_bias, a.batch, a.dim, a.dstate);
+                       pdb, a.A_log, a.dA_log, a.dD, a.d_dt_bias, a.batch * l.nseg, a.dim, a.dstate);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

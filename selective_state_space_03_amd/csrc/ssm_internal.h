@@ -66,10 +66,12 @@ struct BwdArgs {
 
 // Workspace layout of the backward (byte offsets into one caller buffer).
 struct BwdLayout {
-  int chunk;         // time steps per chunk
+  int chunk;         // time steps per chunk (the recompute window)
   int64_t nchunks;   // ceil(seqlen / chunk)
   int64_t ngroups;   // ceil(dim / 64) channel groups
-  size_t off_hloc, off_sumdelta, off_hstart, off_dbc, off_dparam, total;
+  int64_t segc;      // chunks per segment (segments are processed in parallel)
+  int64_t nseg;      // ceil(nchunks / segc)
+  size_t off_hrel, off_cumd, off_hseg, off_sdseg, off_gseg, off_hin, off_gin, off_dbc, off_dparam, total;
 };
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
 
