@@ -40,8 +40,10 @@
 //                  reverse recurrence and every gradient;
 //   5. reduce_bc / reduce_params : ordered sums of the per-tile partials.
 // Work layout (as in the forward): lane = channel, the G wavefronts of a workgroup
-// split the state axis (S states per wave), B and C are wave-uniform scalar loads,
-// per-element work is done once per (t, channel) and shared through LDS.
+// split the state axis (S states per wave), per-element work is done once per
+// (t, channel) and shared through LDS.  B and C of a chunk are staged in LDS too and
+// read with same-address (broadcast) loads: scalar loads inside the step loops would
+// share the LDS wait counter and complete out of order, forcing a full wait per step.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -127,6 +129,7 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   __shared__ float2 pd[TC * 64];  // (Delta, Delta*x) per (t, channel)
+  __shared__ float bs[TC * 16];   // B per (t, state), zero beyond d_state
   Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
   q.dvalid = q.d < Dm;
   const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
@@ -138,46 +141,64 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
   }
   float sd = 0.f;
   const int64_t row0 = q.b * L;
+  // this wave's rows of a chunk (x, delta_raw, B), loaded one chunk ahead
+  float lx[EPL], lr[EPL], lb[EPL];
+  auto load = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * TC;
+    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int t = q.wave + G * i;
+      const bool v = q.dvalid && t < tvalid;
+      const int64_t idx = (row0 + t0 + t) * Dm + q.d;
+      lx[i] = v ? x[idx] : 0.f;
+      lr[i] = v ? delta_raw[idx] : 0.f;
+      lb[i] = (t < tvalid && q.lane < N) ? Bm[(row0 + t0 + t) * N + q.lane] : 0.f;
+    }
+  };
+  load(q.c_begin);
   for (int64_t c = q.c_begin; c < q.c_end; ++c) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
-    if (q.dvalid) {
-      const int64_t o = (q.b * nchunks + c) * Dm + q.d;
+    if (q.dvalid) {  // state-major [b][chunk][n][d]: one coalesced row per state
 #pragma unroll
       for (int j = 0; j < S; ++j)
-        if (j < q.nact) hrel[o * N + q.n0 + j] = h[j];
-      if (q.wave == 0) cumd[o] = sd;
+        if (j < q.nact) hrel[((q.b * nchunks + c) * N + q.n0 + j) * Dm + q.d] = h[j];
+      if (q.wave == 0) cumd[(q.b * nchunks + c) * Dm + q.d] = sd;
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-        const float delta = v ? softplus_f(delta_raw[idx] + bias) : 0.f;
-        pd[t * 64 + q.lane] = make_float2(delta, v ? delta * x[idx] : 0.f);
+        const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
+        pd[t * 64 + q.lane] = make_float2(delta, delta * lx[i]);
+        if (q.lane < 16) bs[t * 16 + q.lane] = lb[i];
       }
     }
+    if (c + 1 < q.c_end) load(c + 1);
     __syncthreads();
+    float2 v[TC];
+    float bv[TC][S];
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps have Delta = 0
-      const float2 v = pd[t * 64 + q.lane];
-      sd += v.x;
+      v[t] = pd[t * 64 + q.lane];
 #pragma unroll
-      for (int j = 0; j < S; ++j) {
-        const float bj = j < q.nact ? ld_uniform<float>(Bm, (row0 + tr) * N + q.n0 + j) : 0.f;
-        h[j] = fmaf(exp2_hw(v.x * A2[j]), h[j], v.y * bj);
-      }
+      for (int j = 0; j < S; ++j) bv[t][j] = bs[t * 16 + q.n0 + j];  // same address on every lane
+    }
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {  // padded steps have Delta = 0 and B = 0
+      sd += v[t].x;
+#pragma unroll
+      for (int j = 0; j < S; ++j) h[j] = fmaf(exp2_hw(v[t].x * A2[j]), h[j], v[t].y * bv[t][j]);
     }
     __syncthreads();
   }
   if (q.dvalid) {
-    const int64_t o = (q.b * nseg + q.seg) * Dm + q.d;
 #pragma unroll
     for (int j = 0; j < S; ++j)
-      if (j < q.nact) hseg[o * N + q.n0 + j] = h[j];
-    if (q.wave == 0) sdseg[o] = sd;
+      if (j < q.nact) hseg[((q.b * nseg + q.seg) * N + q.n0 + j) * Dm + q.d] = h[j];
+    if (q.wave == 0) sdseg[(q.b * nseg + q.seg) * Dm + q.d] = sd;
   }
 }
 
@@ -193,6 +214,7 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   __shared__ float2 pa[TC * 64];  // (Delta, g) per (t, channel)
+  __shared__ float cs[TC * 16];   // C per (t, state), zero beyond d_state
   Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
   q.dvalid = q.d < Dm;
   const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
@@ -203,6 +225,23 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
     gc[j] = 0.f;
   }
   const int64_t row0 = q.b * L;
+  // this wave's rows of a chunk (delta_raw, dy, z, C), loaded one chunk ahead
+  float lr[EPL], ly[EPL], lz[EPL], lc[EPL];
+  auto load = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * TC;
+    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int t = q.wave + G * i;
+      const bool v = q.dvalid && t < tvalid;
+      const int64_t idx = (row0 + t0 + t) * Dm + q.d;
+      lr[i] = v ? delta_raw[idx] : 0.f;
+      ly[i] = v ? dy[idx] : 0.f;
+      lz[i] = (GATED && v) ? z[idx] : 0.f;
+      lc[i] = (t < tvalid && q.lane < N) ? Cm[(row0 + t0 + t) * N + q.lane] : 0.f;
+    }
+  };
+  load(q.c_end - 1);
   for (int64_t c = q.c_end - 1; c >= q.c_begin; --c) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
@@ -211,60 +250,65 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-        const float delta = v ? softplus_f(delta_raw[idx] + bias) : 0.f;
-        float g = v ? dy[idx] : 0.f;
-        if (GATED) g *= v ? silu_f(z[idx]) : 0.f;
+        const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
+        float g = ly[i];
+        if (GATED) g *= silu_f(lz[i]);
         pa[t * 64 + q.lane] = make_float2(delta, g);
+        if (q.lane < 16) cs[t * 16 + q.lane] = lc[i];
       }
     }
+    if (c > q.c_begin) load(c - 1);
     __syncthreads();
+    float2 v[TC];
+    float cv[TC][S];
 #pragma unroll
-    for (int t = TC - 1; t >= 0; --t) {
-      const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps: Delta = g = 0
-      const float2 v = pa[t * 64 + q.lane];
+    for (int t = 0; t < TC; ++t) {
+      v[t] = pa[t * 64 + q.lane];
+#pragma unroll
+      for (int j = 0; j < S; ++j) cv[t][j] = cs[t * 16 + q.n0 + j];  // same address on every lane
+    }
+#pragma unroll
+    for (int t = TC - 1; t >= 0; --t) {  // padded steps: Delta = g = 0
 #pragma unroll
       for (int j = 0; j < S; ++j) {
-        const float cj = j < q.nact ? ld_uniform<float>(Cm, (row0 + tr) * N + q.n0 + j) : 0.f;
-        const float Gt = fmaf(v.y, cj, gc[j]);  // dLoss/dh_t
-        gc[j] = exp2_hw(v.x * A2[j]) * Gt;      // carry to h_{t-1}
+        const float Gt = fmaf(v[t].y, cv[t][j], gc[j]);  // dLoss/dh_t
+        gc[j] = exp2_hw(v[t].x * A2[j]) * Gt;            // carry to h_{t-1}
       }
     }
     __syncthreads();
   }
   if (q.dvalid) {
-    const int64_t o = (q.b * nseg + q.seg) * Dm + q.d;
 #pragma unroll
     for (int j = 0; j < S; ++j)
-      if (j < q.nact) gseg[o * N + q.n0 + j] = gc[j];
+      if (j < q.nact) gseg[((q.b * nseg + q.seg) * N + q.n0 + j) * Dm + q.d] = gc[j];
   }
 }
 
 // ---- 3. sequential over segments per (b, d, n): state entering every segment
-// (forward) and carry entering it from the right (reverse)
+// (forward) and carry entering it from the right (reverse).  Segment values are
+// state-major, [b][segment][n][d].
 __global__ void __launch_bounds__(256)
 seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
                 const float* __restrict__ gseg, const float* __restrict__ A_log,
                 const float* __restrict__ h0, float* __restrict__ hin, float* __restrict__ gin,
                 int64_t batch, int64_t Dm, int N, int64_t nseg) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, d, n)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, n, d), d fastest
   if (i >= batch * Dm * N) return;
   const int64_t b = i / (Dm * N);
-  const int64_t dn = i % (Dm * N);
-  const int64_t d = dn / N;
-  const int n = (int)(dn % N);
-  const float A2 = a2_from_alog(A_log[dn]);
-  float h = h0 ? h0[i] : 0.f;
+  const int n = (int)((i / Dm) % N);
+  const int64_t d = i % Dm;
+  const float A2 = a2_from_alog(A_log[d * N + n]);
+  float h = h0 ? h0[(b * Dm + d) * N + n] : 0.f;
   for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t o = (b * nseg + s) * Dm + d;
-    hin[o * N + n] = h;
-    h = fmaf(exp2_hw(A2 * sdseg[o]), h, hseg[o * N + n]);
+    const int64_t o = ((b * nseg + s) * N + n) * Dm + d;
+    hin[o] = h;
+    h = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), h, hseg[o]);
   }
   float g = 0.f;
   for (int64_t s = nseg - 1; s >= 0; --s) {
-    const int64_t o = (b * nseg + s) * Dm + d;
-    gin[o * N + n] = g;
-    g = fmaf(exp2_hw(A2 * sdseg[o]), g, gseg[o * N + n]);
+    const int64_t o = ((b * nseg + s) * N + n) * Dm + d;
+    gin[o] = g;
+    g = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), g, gseg[o]);
   }
 }
 
@@ -291,6 +335,7 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
   __shared__ float2 pp[TC * G * 64];             // per-wave partials (sum G B, sum G A a h_{t-1})
   __shared__ float2 scr[G][NPAIR * kRowPad];     // per-wave dB/dC channel-reduction scratch
   __shared__ float2 fin[G * 64];                 // per-wave dD / d_dt_bias partials
+  __shared__ float2 bcs[TC * 16];                // (B, C) per (t, state), zero beyond d_state
 
   Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
   q.dvalid = q.d < Dm;
@@ -302,20 +347,40 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
   const float dsk = (dvalid && D_skip) ? D_skip[d] : 0.f;
 
   float A2[S], Av[S], Gc[S], dA[S], hi[S];
-  {
-    const int64_t o = ((b * nseg + q.seg) * Dm + d) * N + n0;
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const bool v = dvalid && j < nact;
-      Av[j] = v ? -expf(A_log[d * N + n0 + j]) : 0.f;
-      A2[j] = Av[j] * kLog2e;
-      Gc[j] = v ? gin[o + j] : 0.f;  // carry entering the segment's last step
-      hi[j] = v ? hin[o + j] : 0.f;  // state entering the segment
-      dA[j] = 0.f;
-    }
+  for (int j = 0; j < S; ++j) {
+    const bool v = dvalid && j < nact;
+    const int64_t o = ((b * nseg + q.seg) * N + n0 + j) * Dm + d;
+    Av[j] = v ? -expf(A_log[d * N + n0 + j]) : 0.f;
+    A2[j] = Av[j] * kLog2e;
+    Gc[j] = v ? gin[o] : 0.f;  // carry entering the segment's last step
+    hi[j] = v ? hin[o] : 0.f;  // state entering the segment
+    dA[j] = 0.f;
   }
   float dD_acc = 0.f, db_acc = 0.f;
   const int64_t row0 = b * L;
+  // this wave's rows of a chunk (x, delta_raw, dy, z, and B, C for lanes < d_state),
+  // loaded one chunk ahead
+  float lx[EPL], lr[EPL], ly[EPL], lz[EPL];
+  float2 lbc[EPL];
+  auto load = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * TC;
+    const int tvalid = (int)((L - t0) < TC ? (L - t0) : TC);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int t = wave + G * i;
+      const bool v = dvalid && t < tvalid;
+      const int64_t idx = (row0 + t0 + t) * Dm + d;
+      lx[i] = v ? x[idx] : 0.f;
+      lr[i] = v ? delta_raw[idx] : 0.f;
+      ly[i] = v ? dy[idx] : 0.f;
+      lz[i] = (GATED && v) ? z[idx] : 0.f;
+      const bool ok = t < tvalid && lane < N;
+      const int64_t o = (row0 + t0 + t) * N + lane;
+      lbc[i] = ok ? make_float2(Bm[o], Cm[o]) : make_float2(0.f, 0.f);
+    }
+  };
+  load(q.c_end - 1);
 
   for (int64_t k = q.c_end - 1; k >= q.c_begin; --k) {
     const int64_t t0 = k * TC;
@@ -326,29 +391,33 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
     for (int i = 0; i < EPL; ++i) {
       const int t = wave + G * i;
       const bool v = dvalid && t < tvalid;
-      const int64_t idx = (row0 + t0 + t) * Dm + d;
-      const float xv = v ? x[idx] : 0.f;
-      const float r = (v ? delta_raw[idx] : 0.f) + bias;
-      const float dyv = v ? dy[idx] : 0.f;
+      const float xv = lx[i];
+      const float r = lr[i] + bias;
+      const float dyv = ly[i];
       const float delta = v ? softplus_f(r) : 0.f;
       float g = dyv, gz = 0.f;
       if (GATED) {
-        const float zv = v ? z[idx] : 0.f;
+        const float zv = lz[i];
         const float sz = sigmoid_f(zv);
         g = dyv * zv * sz;
         gz = dyv * sz * fmaf(zv, 1.f - sz, 1.f);
       }
       ex[i] = xv; edelta[i] = delta; eg[i] = g; esig[i] = sigmoid_f(r); egz[i] = gz;
-      if (t < TC) pd[t * 64 + lane] = make_float4(delta, delta * xv, g, 0.f);
+      if (t < TC) {
+        pd[t * 64 + lane] = make_float4(delta, delta * xv, g, 0.f);
+        if (lane < 16) bcs[t * 16 + lane] = lbc[i];
+      }
     }
+    if (k > q.c_begin) load(k - 1);
     // start state of this chunk: relative state + decayed segment entry state
     float hs[S];
     {
-      const int64_t o = (b * nchunks + k) * Dm + d;
-      const float cd = dvalid ? cumd[o] : 0.f;
+      const float cd = dvalid ? cumd[(b * nchunks + k) * Dm + d] : 0.f;
 #pragma unroll
       for (int j = 0; j < S; ++j)
-        hs[j] = (dvalid && j < nact) ? fmaf(exp2_hw(A2[j] * cd), hi[j], hrel[o * N + n0 + j]) : 0.f;
+        hs[j] = (dvalid && j < nact)
+                    ? fmaf(exp2_hw(A2[j] * cd), hi[j], hrel[((b * nchunks + k) * N + n0 + j) * Dm + d])
+                    : 0.f;
     }
     __syncthreads();
     // ---- F: recompute this wave's states over the chunk, keep h_t, a_t and the
@@ -360,14 +429,14 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
 #pragma unroll
       for (int j = 0; j < S; ++j) hc[j] = hs[j];
 #pragma unroll
-      for (int t = 0; t < TC; ++t) {
-        const int64_t tr = t < tvalid ? t0 + t : L - 1;  // padded steps have Delta = 0
-        V[t] = pd[t * 64 + lane];
+      for (int t = 0; t < TC; ++t) V[t] = pd[t * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {  // padded steps have Delta = 0 and B = C = 0
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < S; ++j) {
-          const float bj = j < nact ? ld_uniform<float>(Bm, (row0 + tr) * N + n0 + j) : 0.f;
-          const float cj = j < nact ? ld_uniform<float>(Cm, (row0 + tr) * N + n0 + j) : 0.f;
+          const float2 bc = bcs[t * 16 + n0 + j];  // same address on every lane
+          const float bj = bc.x, cj = bc.y;
           const float a = exp2_hw(V[t].x * A2[j]);
           hc[j] = fmaf(a, hc[j], V[t].y * bj);
           acc = fmaf(cj, hc[j], acc);
@@ -395,14 +464,13 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
     float2* __restrict__ sw = scr[wave];
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {
-      const int64_t tr = t < tvalid ? t0 + t : L - 1;
       float P1 = 0.f, P2 = 0.f;
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         float dBp = 0.f, dCp = 0.f;
         if (j < nact) {
-          const float bj = ld_uniform<float>(Bm, (row0 + tr) * N + n0 + j);
-          const float cj = ld_uniform<float>(Cm, (row0 + tr) * N + n0 + j);
+          const float2 bc = bcs[t * 16 + n0 + j];
+          const float bj = bc.x, cj = bc.y;
           const float Gt = fmaf(V[t].z, cj, Gc[j]);      // dLoss/dh_t
           dCp = V[t].z * H[t][j];
           dBp = Gt * V[t].y;
@@ -472,7 +540,7 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
   if (dvalid) {
 #pragma unroll
     for (int j = 0; j < S; ++j)
-      if (j < nact) pdA[po * N + n0 + j] = dA[j];
+      if (j < nact) pdA[((b * nseg + q.seg) * N + n0 + j) * Dm + d] = dA[j];
   }
   fin[wave * 64 + lane] = make_float2(dD_acc, db_acc);
   __syncthreads();
@@ -512,14 +580,17 @@ reduce_params_kernel(const float* __restrict__ pdA, const float* __restrict__ pd
                      const float* __restrict__ pdbias, const float* __restrict__ A_log,
                      float* __restrict__ dA_log, float* __restrict__ dD, float* __restrict__ d_dt_bias,
                      int64_t nparts, int64_t Dm, int N) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (d, n)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (n, d), d fastest
   if (i < Dm * N && dA_log) {
+    const int64_t n = i / Dm, d = i % Dm;
     float s = 0.f;
-    for (int64_t p = 0; p < nparts; ++p) s += pdA[p * Dm * N + i];
-    dA_log[i] = s * -expf(A_log[i]);  // dA/dA_log = A
+#pragma unroll 8
+    for (int64_t p = 0; p < nparts; ++p) s += pdA[p * Dm * N + i];  // partials are [part][n][d]
+    dA_log[d * N + n] = s * -expf(A_log[d * N + n]);                // dA/dA_log = A
   }
   if (i < Dm) {
     float sD = 0.f, sb = 0.f;
+#pragma unroll 8
     for (int64_t p = 0; p < nparts; ++p) {
       sD += pdD[p * Dm + i];
       sb += pdbias[p * Dm + i];
