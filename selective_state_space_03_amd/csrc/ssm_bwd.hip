@@ -52,10 +52,22 @@ namespace ssm {
 namespace {
 constexpr int kChunk = 16;  // time steps per chunk (recompute window held in VGPRs)
 constexpr int kSub = 4;     // reverse steps between channel reductions of dB/dC
-constexpr int kRowPad = 66; // padded LDS row (float2) for the channel reduction
+constexpr int kRowPad = 72; // padded LDS row (float2): the column reads of the channel
+                             // reduction hit every bank equally
 constexpr int kS = 2;       // states per wavefront
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// v of lane i + k within its row of 16 lanes (DPP row_shl; lanes without a source get 0)
+__device__ __forceinline__ float dpp_shl(float v, int k) {
+  const int b = __float_as_int(v);
+  int r;
+  if (k == 8) r = __builtin_amdgcn_update_dpp(0, b, 0x108, 0xF, 0xF, true);
+  else if (k == 4) r = __builtin_amdgcn_update_dpp(0, b, 0x104, 0xF, 0xF, true);
+  else if (k == 2) r = __builtin_amdgcn_update_dpp(0, b, 0x102, 0xF, 0xF, true);
+  else r = __builtin_amdgcn_update_dpp(0, b, 0x101, 0xF, 0xF, true);
+  return __int_as_float(r);
+}
 int waves_for(int dstate) { return dstate <= 2 ? 1 : (dstate <= 4 ? 2 : (dstate <= 8 ? 4 : 8)); }
 }  // namespace
 
@@ -486,7 +498,8 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
       pp[(t * G + wave) * 64 + lane] = make_float2(P1, P2);
       if (t % kSub == 0) {
         // channel sums of this sub-tile: output pair p = (step, state), LPP lanes each
-        // add 64/LPP channels in ascending order, then a fixed butterfly joins them
+        // add 64/LPP channels in ascending order, then a fixed halving tree (DPP row
+        // shifts inside the LPP-lane group) leaves the total in the group's first lane
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         const int p = lane / LPP, part = lane % LPP;
@@ -497,16 +510,18 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
           sB += qv.x;
           sC += qv.y;
         }
+        static_assert(LPP <= 16, "the halving tree stays inside a row of 16 lanes");
 #pragma unroll
-        for (int m = 1; m < LPP; m <<= 1) {
-          sB += __shfl_xor(sB, m, LPP);
-          sC += __shfl_xor(sC, m, LPP);
+        for (int k = LPP / 2; k >= 1; k >>= 1) {
+          sB += dpp_shl(sB, k);
+          sC += dpp_shl(sC, k);
         }
         const int ts = t + p / S;  // absolute step inside the chunk
         const int j = p % S;
-        if (part < 2 && j < nact && ts < tvalid) {
+        if (part == 0 && j < nact && ts < tvalid) {
           const int64_t o = ((b * ngroups + q.grp) * L + t0 + ts) * N + n0 + j;
-          if (part == 0) pdB[o] = sB; else pdC[o] = sC;
+          pdB[o] = sB;
+          pdC[o] = sC;
         }
         __builtin_amdgcn_wave_barrier();
       }
