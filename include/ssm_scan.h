@@ -27,8 +27,7 @@
  *   dy, dx, ddelta_raw, dz in the backward).  Parameters, states and all
  *   arithmetic are fp32.  bf16 results are rounded to nearest even.
  *   Pointers are device pointers (hipMalloc / torch CUDA tensors), naturally
- *   aligned for their element type; B and C of ssm_scan_fwd are also 4-byte
- *   aligned in bf16 (SSM_ERR_ALIGN otherwise).  Outputs must not overlap inputs, except
+ *   aligned for their element type.  Outputs must not overlap inputs, except
  *   `state` of ssm_scan_step, which is read and written in place.
  *   Ownership: the caller allocates and frees every buffer, including any
  *   workspace; the library allocates no device memory and keeps no pointer
@@ -83,7 +82,10 @@ const char* ssm_status_string(int status);
  *            few channels use; ssm_scan_fwd_workspace_bytes() gives the size that
  *            enables it (0 when it is never used).  NULL or a smaller buffer is
  *            not an error: the scan then runs unsplit.
- *   io_dtype: SSM_F32 or SSM_BF16. */
+ *   io_dtype: SSM_F32 or SSM_BF16.
+ *   Limits: one batch element's slice, seqlen * max(d_inner, d_state) elements of
+ *   io_dtype, must be below 2^31 bytes (SSM_ERR_UNSUPPORTED otherwise); d_inner
+ *   <= 2^24 and seqlen <= 2^30 (SSM_ERR_DIM otherwise). */
 size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                     int64_t d_state, int io_dtype);
 int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void* B,

@@ -66,13 +66,13 @@ int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void
   // batch element must stay below 2^31 bytes
   if (d_inner > ((int64_t)1 << 24) || seqlen > ((int64_t)1 << 30)) return SSM_ERR_DIM;
   const size_t es = esize(io_dtype);
-  // the forward addresses one batch element's [seqlen, d_inner] slice with 31-bit offsets
-  if ((uint64_t)seqlen * (uint64_t)d_inner * es >= ((uint64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
+  // the forward addresses one batch element's [seqlen, d_inner] and [seqlen, d_state]
+  // slices with 31-bit offsets
+  if ((uint64_t)seqlen * (uint64_t)(d_inner > d_state ? d_inner : d_state) * es >= ((uint64_t)1 << 31))
+    return SSM_ERR_UNSUPPORTED;
   const void* io_in[] = {x, delta_raw, z, B, C};
   for (const void* p : io_in)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  // B and C are read by the scalar unit in whole dwords (bf16 included)
-  if (!aligned(B, 4) || !aligned(C, 4)) return SSM_ERR_ALIGN;
   const void* f_in[] = {A_log, D_skip, dt_bias, h0, h_final};
   for (const void* p : f_in)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;

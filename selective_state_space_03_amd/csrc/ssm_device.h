@@ -61,28 +61,6 @@ template <> struct io<bf16_t> {
   __device__ __forceinline__ static void st(bf16_t* __restrict__ p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-// Wave-uniform read of memory that no kernel of the launch writes (B, C): through the
-// constant address space the load is a scalar (SMEM) load into an SGPR, whatever the
-// compiler can prove about aliasing.
-// (fp32 is read as its bit pattern: a plain float copy from constant memory into a
-// register array can be turned into a memory copy, which keeps the array in scratch.)
-typedef __attribute__((address_space(4))) const uint32_t cu32_t;
-template <typename T> __device__ __forceinline__ float ld_uniform(const T* p, int64_t i);
-template <> __device__ __forceinline__ float ld_uniform<float>(const float* p, int64_t i) {
-  return __uint_as_float(((cu32_t*)p)[i]);
-}
-// Scalar loads read whole dwords, so a bf16 element is taken from the aligned dword
-// that holds it: p must be a 4-byte aligned tensor base and i the element index from
-// it (the low half for even i, the high half for odd i).  Where the parity of i is
-// known at compile time the select folds away and neighbouring elements share one load.
-// (The dword holding the last element of a tensor with an odd element count reaches 2
-// bytes past its end, never past the aligned 4-byte word, hence never into another page.)
-template <> __device__ __forceinline__ float ld_uniform<bf16_t>(const bf16_t* p, int64_t i) {
-  const uint32_t w = ((cu32_t*)p)[i >> 1];
-  const uint32_t sh = (i & 1) ? 0u : 16u;
-  return __uint_as_float((w << sh) & 0xffff0000u);
-}
-
 // A[d,n] = -exp(A_log[d,n]) folded with log2(e), so that exp(Delta*A) = exp2(Delta*A2)
 // (mamba-rs exp_negate: out = -exp(a_log)).  Computed once per state per kernel with the
 // accurate library exp.

@@ -13,21 +13,22 @@
 //     contiguous 256 B (fp32) or 128 B (bf16) row segment per wavefront;
 //   * the G wavefronts of the workgroup split the state axis: wave w owns states
 //     [w*S, w*S + S) of all 64 channels and keeps them in VGPRs for the whole
-//     sequence.  All 64 lanes of a wave need the same B[b,t,n] and C[b,t,n], so
-//     those are wave-uniform scalar loads (SGPR operands, no VALU or LDS cost);
-//   * per-(t,d) work (softplus, Delta*x, D*x, silu(z)) is done once per element
-//     in a "prep" phase spread over all waves and shared through LDS, and the
-//     readout sum over states is a per-wave partial in LDS that a "readout"
-//     phase adds in fixed wave order -- so the result is deterministic.
-// Time is walked in tiles of TT steps with one barrier per tile: between two
-// barriers a wave preps tile k+1, reads out tile k-1 and scans tile k (LDS buffers
-// are double / quadruple buffered for that).  Activation loads run P tiles ahead of
-// the prep through per-tile buffer resources: out-of-range rows and padding channels
-// read 0 and drop their stores in hardware, so the loop has no branch around memory
-// operations and the compiler can wait for exactly the tile it needs.  B/C of the
-// next tile are scalar loads issued at the start of each scan into the other half of
-// a double-buffered SGPR set.  The scalar unit is shared by the four SIMDs of a CU, so
-// address arithmetic is kept off it: B/C of a tile are immediate offsets from one base.
+//     sequence.  All 64 lanes of a wave need the same B[b,t,n] and C[b,t,n]: the rows
+//     of a time tile are staged in LDS and read with same-address (broadcast) loads;
+//   * per-(t,d) work (softplus, Delta*x) is done once per element in a "prep" phase
+//     spread over all waves and shared through LDS; the readout sum over states is a
+//     per-wave partial in LDS that a "readout" phase adds in fixed wave order -- so the
+//     result is deterministic.  With one state per wave the partial is the state
+//     itself and the readout applies C[t][n], which keeps that multiply out of the
+//     scan loop; the readout also takes D*x and silu(z) from the activations it holds.
+// Time is walked in tiles of TT steps with one barrier per tile: between two barriers a
+// wave preps tile k+1, loads tiles ahead, reads out tile k-1 and scans tile k (LDS
+// buffers are double / quadruple buffered for that).  All global traffic goes through
+// per-batch-element buffer resources and a ring of register slots: out-of-range rows
+// and padding channels read 0 and drop their stores in hardware, so the loop has no
+// branch around memory operations and the compiler waits for exactly the tile it
+// needs.  The loop issues no scalar memory loads: they would share the LDS wait
+// counter and complete out of order, forcing full waits.
 #include <type_traits>
 
 #include "ssm_device.h"
@@ -82,6 +83,8 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   const int N = MASKED ? N_rt : S * G;
   __shared__ float2 dd[2][TT * 64];     // (Delta, Delta*x) per (t, channel): tile k in k&1
   __shared__ float yp[2][TT * G * 64];  // per-wave partial readout per (t, wave, channel)
+  __shared__ float bsT[2][16 * TT];     // B per (state, t), transposed: tile k in k&1
+  __shared__ float csm[4][TT * 16];     // C per (t, state): tile k in k&3
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,7 +107,6 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   }
 
   const int ntiles = (L + TT - 1) / TT;
-  const int nfull = L / TT;              // tiles that lie entirely inside the sequence
   const int64_t row0 = (int64_t)b * L;   // row of (b, t) is row0 + t
   // Rows wave + G*i of every tile are this wave's, for the prep and for the readout.
   // Byte offset of (row, channel d) inside a tile; padding lanes and rows beyond the
@@ -123,72 +125,23 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   const __amdgpu_buffer_rsrc_t rr = tile_rsrc(delta_raw + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t rz = tile_rsrc(GATED ? z + row0 * Dm : x + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t ry = tile_rsrc(y + row0 * Dm, slice);
+  // B and C rows of the same tiles: lane n < d_state of a row loads element n
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(Bm + row0 * N, (int64_t)L * N * ES);
+  const __amdgpu_buffer_rsrc_t rc = tile_rsrc(Cm + row0 * N, (int64_t)L * N * ES);
+  uint32_t boff[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int row = wave + G * i;
+    boff[i] = (lane < N && row < TT) ? (uint32_t)((row * N + lane) * ES) : kOutside;
+  }
   const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);
+  const uint32_t btile_bytes = (uint32_t)(TT * N * ES);
   // offset of tile j (j may be -1 or past the end: then every access is outside)
   auto toff = [&](int j) __attribute__((always_inline)) {
     return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * tile_bytes;
   };
-
-  // ---- B (and C when a wave has several states) of a tile for this wave's states:
-  // wave-uniform, in SGPRs, double buffered
-  float cb[2][TT][S], cc[2][TT][S];
-  auto load_bc = [&](int j, int buf) __attribute__((always_inline)) {
-    if (j < nfull) {  // whole tile inside the sequence: constant offsets from one base
-      const int64_t e = (row0 + (int64_t)j * TT) * N + n0;  // element (row of tile j, n0)
-      if (std::is_same<T, bf16_t>::value && !MASKED) {
-        // bf16 with even N: element e + t*N + s lies in dword (e >> 1) + ((par + t*N + s) >> 1);
-        // only one state per wave can start at an odd element (par = 1, then s = 0)
-        const int par = S == 1 ? (int)(e & 1) : 0;
-        const cu32_t* __restrict__ Bw = (const cu32_t*)Bm + (e >> 1);
-        const cu32_t* __restrict__ Cw = (const cu32_t*)Cm + (e >> 1);
-        auto half = [&](uint32_t w, bool hi) __attribute__((always_inline)) {
-          return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
-        };
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const int c = t * N + s;
-            const bool hi = S == 1 ? par != 0 : (c & 1) != 0;
-            cb[buf][t][s] = half(Bw[c >> 1], hi);
-            if (S > 1) cc[buf][t][s] = half(Cw[c >> 1], hi);
-          }
-      } else if (std::is_same<T, bf16_t>::value) {  // bf16, any N: element by element
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const int64_t o = e + t * N + (s < nact ? s : 0);
-            cb[buf][t][s] = s < nact ? ld_uniform<T>(Bm, o) : 0.f;
-            if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Cm, o) : 0.f;
-          }
-      } else {
-        const T* __restrict__ Bt = Bm + e;
-        const T* __restrict__ Ct = Cm + e;
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            if (MASKED) {
-              cb[buf][t][s] = s < nact ? ld_uniform<T>(Bt, t * N + s) : 0.f;
-              if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Ct, t * N + s) : 0.f;
-            } else {
-              cb[buf][t][s] = ld_uniform<T>(Bt, t * N + s);
-              if (S > 1) cc[buf][t][s] = ld_uniform<T>(Ct, t * N + s);
-            }
-          }
-      }
-    } else if (j < ntiles) {  // the partial last tile: rows clamped (padded steps have Delta = 0)
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int r = j * TT + t < L ? j * TT + t : L - 1;
-          const int64_t o = (row0 + r) * N + n0 + (s < nact ? s : 0);
-          cb[buf][t][s] = s < nact ? ld_uniform<T>(Bm, o) : 0.f;
-          if (S > 1) cc[buf][t][s] = s < nact ? ld_uniform<T>(Cm, o) : 0.f;
-        }
-    }
+  auto btoff = [&](int j) __attribute__((always_inline)) {
+    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * btile_bytes;
   };
 
   // ---- activations of this wave's rows, in a ring of R register slots (tile j in slot
@@ -205,9 +158,23 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
       pz[slot][i] = GATED ? buf_ld<T>(rz, v) : 0.f;
     }
   };
-  // prep of tile k: Delta and Delta*x for the scan.  Padded steps and channels get
-  // Delta = 0, which leaves the state as it is.
-  auto prep = [&](int k, int slot, int dbuf) __attribute__((always_inline)) {
+  // B and C rows of tile j (small and shared by every channel tile, so mostly L2 hits):
+  // loaded one step before their prep, in a ring of 2 slots (tile j in slot j & 1)
+  float pb[2][EPL], pc[2][EPL];
+  auto load_bc = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint32_t ob = btoff(j);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t vb = off_add(boff[i], ob);
+      pb[slot][i] = buf_ld<T>(rb, vb);
+      pc[slot][i] = buf_ld<T>(rc, vb);
+    }
+  };
+  // prep of tile k: Delta and Delta*x for the scan, and the tile's B and C rows
+  // (lanes < 16; zero past d_state and past the sequence).  Padded steps and channels
+  // get Delta = 0, which leaves the state as it is.
+  auto prep = [&](int k, int slot, int dbuf, int cbuf) __attribute__((always_inline)) {
+    const int bslot = dbuf;  // B/C ring slot of tile k is k & 1, like dd
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int t = wave + G * i;
@@ -215,14 +182,18 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
         const bool v = dvalid && k * TT + t < L;
         const float delta = softplus_f(pr[slot][i] + bias);
         dd[dbuf][t * 64 + lane] = v ? make_float2(delta, delta * px[slot][i]) : make_float2(0.f, 0.f);
+        if (lane < 16) {
+          bsT[dbuf][lane * TT + t] = pb[bslot][i];
+          csm[cbuf][t * 16 + lane] = pc[bslot][i];
+        }
       }
     }
   };
   // readout of tile k: wave partials added in fixed order, plus skip, times gate.  With
-  // one state per wave the partials are the states and C[t][n] is applied here (scalar
-  // loads), which keeps that multiply out of the scan.  Rows outside the sequence (and
-  // k < 0) fall outside the store resource.
-  auto readout = [&](int k, int slot, int pbuf) __attribute__((always_inline)) {
+  // one state per wave the partials are the states and C[t][n] is applied here, which
+  // keeps that multiply out of the scan.  Rows outside the sequence (and k < 0) fall
+  // outside the store resource.
+  auto readout = [&](int k, int slot, int pbuf, int cbuf) __attribute__((always_inline)) {
     const uint32_t o = toff(k);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -233,14 +204,12 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
 #pragma unroll
         for (int w = 0; w < G; ++w) pv[w] = yp[pbuf][(t * G + w) * 64 + lane];
         if (S == 1) {
-          const int r = min(max(k * TT + t, 0), L - 1);  // row clamped into the sequence
 #pragma unroll
-          for (int w = 0; w < G; ++w) cw[w] = w < N ? ld_uniform<T>(Cm, (row0 + r) * N + w) : 0.f;
+          for (int w = 0; w < G; ++w) cw[w] = csm[cbuf][t * 16 + w];  // same address on every lane
         }
         // skip and gate from the activations in registers while the loads are in flight
         const float skip = dsk * px[slot][i];
         const float gate = GATED ? silu_f(pz[slot][i]) : 1.f;
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
         float acc = skip;
         if (S == 1) {
 #pragma unroll
@@ -256,61 +225,76 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
       buf_st<T>(out, ry, off_add(loff[i], o));
     }
   };
-  // scan of tile k (B/C in buffer cbuf).  Scalar and LDS loads share one wait counter
-  // and scalar loads complete out of order, so the tile's LDS reads are waited for
-  // first; then the B/C of tile k+1 go out (into the other buffer) and have the whole
-  // scan to arrive before the closing barrier waits for them.
-  auto scan = [&](int k, int dbuf, int pbuf, int cbuf) __attribute__((always_inline)) {
-    float2 v[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) v[t] = dd[dbuf][t * 64 + lane];
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // s_waitcnt lgkmcnt(0)
-    load_bc(k + 1, cbuf ^ 1);
+  // scan of tile k: (Delta, Delta*x) per lane and this wave's B (and C) per step, all
+  // from LDS -- B and C with same-address (broadcast) reads
+  // (in two halves of the tile, so that the loaded operands of only half of it are
+  // live at a time)
+  auto scan = [&](int dbuf, int pbuf, int cbuf) __attribute__((always_inline)) {
+    constexpr int TH = TT / 2;
     float* __restrict__ ypw = yp[pbuf] + wave * 64 + lane;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
+    for (int half = 0; half < 2; ++half) {
+    float2 v[TH];
+    float bv[TH][S], cv[TH][S];
+#pragma unroll
+    for (int tt = 0; tt < TH; ++tt) v[tt] = dd[dbuf][(half * TH + tt) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+#pragma unroll
+      for (int tt = 0; tt < TH; ++tt) {
+        bv[tt][j] = bsT[dbuf][(n0 + j) * TT + half * TH + tt];
+        if (S > 1) cv[tt][j] = csm[cbuf][(half * TH + tt) * 16 + n0 + j];
+      }
+#pragma unroll
+    for (int tt = 0; tt < TH; ++tt) {
+      const int t = half * TH + tt;
       if (S == 1) {  // store the state; the readout applies C
-        const float a = exp2_hw(v[t].x * A2[0]);
-        h[0] = fmaf(a, h[0], v[t].y * cb[cbuf][t][0]);
+        const float a = exp2_hw(v[tt].x * A2[0]);
+        h[0] = fmaf(a, h[0], v[tt].y * bv[tt][0]);
         ypw[t * G * 64] = h[0];
       } else {
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < S; ++j) {
-          const float a = exp2_hw(v[t].x * A2[j]);
-          h[j] = fmaf(a, h[j], v[t].y * cb[cbuf][t][j]);
-          acc = fmaf(cc[cbuf][t][j], h[j], acc);
+          const float a = exp2_hw(v[tt].x * A2[j]);
+          h[j] = fmaf(a, h[j], v[tt].y * bv[tt][j]);
+          acc = fmaf(cv[tt][j], h[j], acc);
         }
         ypw[t * G * 64] = acc;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // prologue: B/C of tile 0, tiles 0..5 in flight, tile 0 prepped; slot 7 (tile -1,
-  // read out in the first step) holds zeros
+  // prologue: B/C of tiles 0 and 1 and tiles 0..5 in flight, tile 0 prepped; slot 7
+  // (tile -1, read out in the first step) holds zeros
   load_bc(0, 0);
+  load_bc(1, 1);
 #pragma unroll
   for (int u = 0; u < 6; ++u) load_tile(u, u);
 #pragma unroll
   for (int i = 0; i < EPL; ++i) px[7][i] = pr[7][i] = pz[7][i] = 0.f;
-  prep(0, 0, 0);
+  prep(0, 0, 0, 0);
   __syncthreads();
   // Main loop, unrolled by 8 so that every ring slot and buffer index is a constant.
-  // Between two barriers a wave preps tile k+1, loads tile k+6, reads out tile k-1 and
-  // scans tile k; dd and yp alternate by tile parity.
+  // Between two barriers a wave preps tile k+1, loads B/C of tile k+2 and the tile
+  // k+6, reads out tile k-1 and scans tile k; dd, bsT and yp alternate by tile parity,
+  // csm by tile mod 4.
   for (int kk = 0; kk < ntiles; kk += R) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int k = kk + u;
       if (k >= ntiles) break;
-      prep(k + 1, (u + 1) % R, (u + 1) & 1);
+      prep(k + 1, (u + 1) % R, (u + 1) & 1, (u + 1) & 3);
+      load_bc(k + 2, u & 1);
       load_tile(k + 6, (u + 6) % R);
-      readout(k - 1, (u + R - 1) % R, (u + 1) & 1);
-      scan(k, u & 1, u & 1, u & 1);
+      readout(k - 1, (u + R - 1) % R, (u + 1) & 1, (u + 3) & 3);
+      scan(u & 1, u & 1, u & 3);
       __syncthreads();
     }
   }
-  readout(ntiles - 1, (ntiles - 1) % R, (ntiles - 1) & 1);
+  readout(ntiles - 1, (ntiles - 1) % R, (ntiles - 1) & 1, (ntiles - 1) & 3);
 
   if (h_final && dvalid) {
 #pragma unroll
@@ -321,10 +305,9 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
 
 template <typename T, int S, int G, bool GATED>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
-  // time tile: one state per wave scans 16 steps per barrier (LDS: dd 16 KB, partials
-  // 2*16*G*256 B); with several states per wave the B/C ring of a tile takes 4*TT*S
-  // SGPRs, so TT*S <= 16
-  constexpr int TT = S == 1 ? 16 : (S == 2 ? 8 : 4);
+  // time tile: 16 steps per barrier (LDS: dd 16 KB, partials 2*16*G*256 B); with 8 or
+  // 16 states per wave the per-step operands of a tile half would not fit in VGPRs
+  constexpr int TT = (S <= 4 && G > 1) ? 16 : 4;
   // ring of activation slots (tile mod 8)
   constexpr int PF = 8;
   const int ngroups = (int)((a.dim + 63) / 64);
