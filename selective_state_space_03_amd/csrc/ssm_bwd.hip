@@ -52,21 +52,51 @@ namespace ssm {
 namespace {
 constexpr int kChunk = 16;  // time steps per chunk (recompute window held in VGPRs)
 constexpr int kSub = 4;     // reverse steps between channel reductions of dB/dC
-constexpr int kRowPad = 72; // padded LDS row (float2): the column reads of the channel
-                             // reduction hit every bank equally
 constexpr int kS = 2;       // states per wavefront
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// v of lane i + k within its row of 16 lanes (DPP row_shl; lanes without a source get 0)
-__device__ __forceinline__ float dpp_shl(float v, int k) {
-  const int b = __float_as_int(v);
-  int r;
-  if (k == 8) r = __builtin_amdgcn_update_dpp(0, b, 0x108, 0xF, 0xF, true);
-  else if (k == 4) r = __builtin_amdgcn_update_dpp(0, b, 0x104, 0xF, 0xF, true);
-  else if (k == 2) r = __builtin_amdgcn_update_dpp(0, b, 0x102, 0xF, 0xF, true);
-  else r = __builtin_amdgcn_update_dpp(0, b, 0x101, 0xF, 0xF, true);
-  return __int_as_float(r);
+// DPP lane permutations inside rows of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sums of 16 values over the 64 lanes of a wavefront (a transpose-reduce): every
+// stage pairs each lane with one in the other half of a lane group, each lane keeps
+// one half of its values and adds the partner's copy of that half.  Lanes 32-63 /
+// 0-31 and odd / even 16-lane rows are exchanged by the gfx950 permlane swaps, the
+// 8- and 4-lane halves of a row by DPP mirrors, the last two quad steps are plain
+// DPP butterflies.  Lane i ends with the sum of value (i >> 2) & 15; the tree is
+// fixed, so the result is deterministic.
+__device__ __forceinline__ float transpose_reduce16(float (&v)[16], int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {  // lanes 0-31 keep v[k], lanes 32-63 keep v[k + 8]
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 8]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // even rows keep v[k], odd rows keep v[k + 4]
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 4]), false, false);
+    v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool h3 = (lane & 8) != 0, h2 = (lane & 4) != 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // row halves (lane 15 - i is the partner): keep v[k] / v[k + 2]
+    const float keep = h3 ? v[k + 2] : v[k], send = h3 ? v[k] : v[k + 2];
+    v[k] = keep + dpp<kDppRowMirror>(send);
+  }
+  {  // quarters of a row (lane 7 - i within 8): keep v[0] / v[1]
+    const float keep = h2 ? v[1] : v[0], send = h2 ? v[0] : v[1];
+    v[0] = keep + dpp<kDppRowHalfMirror>(send);
+  }
+  v[0] += dpp<kDppQuadXor2>(v[0]);
+  v[0] += dpp<kDppQuadXor1>(v[0]);
+  return v[0];
 }
 int waves_for(int dstate) { return dstate <= 2 ? 1 : (dstate <= 4 ? 2 : (dstate <= 8 ? 4 : 8)); }
 }  // namespace
@@ -339,13 +369,10 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
                 int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
-  constexpr int NPAIR = kSub * S;      // (step, state) outputs per sub-tile and wave
-  constexpr int LPP = 64 / NPAIR;      // lanes that share one output's channel sum
-  static_assert(LPP >= 2 && 64 % NPAIR == 0, "sub-tile reduction layout");
+  static_assert(2 * kSub * S == 16, "a sub-tile's dB/dC values fill one transpose-reduce");
   __shared__ float4 pd[TC * 64];                 // (Delta, Delta*x, g, -) per (t, channel)
   __shared__ float yp[TC * G * 64];              // per-wave readout partials sum_j C h
   __shared__ float2 pp[TC * G * 64];             // per-wave partials (sum G B, sum G A a h_{t-1})
-  __shared__ float2 scr[G][NPAIR * kRowPad];     // per-wave dB/dC channel-reduction scratch
   __shared__ float2 fin[G * 64];                 // per-wave dD / d_dt_bias partials
   __shared__ float2 bcs[TC * 16];                // (B, C) per (t, state), zero beyond d_state
 
@@ -375,9 +402,14 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
   // loaded one chunk ahead
   float lx[EPL], lr[EPL], ly[EPL], lz[EPL];
   float2 lbc[EPL];
+  float lhr[S], lcd;  // the chunk's relative start state and Delta sum up to it
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)((L - t0) < TC ? (L - t0) : TC);
+    lcd = dvalid ? cumd[(b * nchunks + c) * Dm + d] : 0.f;
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      lhr[j] = (dvalid && j < nact) ? hrel[((b * nchunks + c) * N + n0 + j) * Dm + d] : 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int t = wave + G * i;
@@ -420,17 +452,11 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         if (lane < 16) bcs[t * 16 + lane] = lbc[i];
       }
     }
-    if (k > q.c_begin) load(k - 1);
     // start state of this chunk: relative state + decayed segment entry state
     float hs[S];
-    {
-      const float cd = dvalid ? cumd[(b * nchunks + k) * Dm + d] : 0.f;
 #pragma unroll
-      for (int j = 0; j < S; ++j)
-        hs[j] = (dvalid && j < nact)
-                    ? fmaf(exp2_hw(A2[j] * cd), hi[j], hrel[((b * nchunks + k) * N + n0 + j) * Dm + d])
-                    : 0.f;
-    }
+    for (int j = 0; j < S; ++j) hs[j] = fmaf(exp2_hw(A2[j] * lcd), hi[j], lhr[j]);
+    if (k > q.c_begin) load(k - 1);
     __syncthreads();
     // ---- F: recompute this wave's states over the chunk, keep h_t, a_t and the
     // chunk's (Delta, Delta*x, g) in registers
@@ -472,8 +498,9 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         }
       }
     }
-    // ---- V: reverse recurrence over the chunk
-    float2* __restrict__ sw = scr[wave];
+    // ---- V: reverse recurrence over the chunk; every kSub steps the (dB, dC) values
+    // of the sub-tile are summed over the 64 channels in registers
+    float red[16];
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {
       float P1 = 0.f, P2 = 0.f;
@@ -493,37 +520,20 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
           P2 = fmaf(w, Av[j], P2);
           Gc[j] = AS[t][j] * Gt;                          // carry to h_{t-1}
         }
-        sw[((t % kSub) * S + j) * kRowPad + lane] = make_float2(dBp, dCp);
+        red[2 * ((t % kSub) * S + j)] = dBp;
+        red[2 * ((t % kSub) * S + j) + 1] = dCp;
       }
       pp[(t * G + wave) * 64 + lane] = make_float2(P1, P2);
       if (t % kSub == 0) {
-        // channel sums of this sub-tile: output pair p = (step, state), LPP lanes each
-        // add 64/LPP channels in ascending order, then a fixed halving tree (DPP row
-        // shifts inside the LPP-lane group) leaves the total in the group's first lane
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        const int p = lane / LPP, part = lane % LPP;
-        float sB = 0.f, sC = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64 / LPP; ++i) {
-          const float2 qv = sw[p * kRowPad + part + LPP * i];
-          sB += qv.x;
-          sC += qv.y;
-        }
-        static_assert(LPP <= 16, "the halving tree stays inside a row of 16 lanes");
-#pragma unroll
-        for (int k = LPP / 2; k >= 1; k >>= 1) {
-          sB += dpp_shl(sB, k);
-          sC += dpp_shl(sC, k);
-        }
-        const int ts = t + p / S;  // absolute step inside the chunk
-        const int j = p % S;
-        if (part == 0 && j < nact && ts < tvalid) {
+        // lane i holds the channel sum of value (i >> 2) & 15 = 2 * (step * S + state) + (0: dB, 1: dC)
+        const float sum = transpose_reduce16(red, lane);
+        const int o16 = (lane >> 2) & 15;
+        const int pidx = o16 >> 1, j = pidx % S;
+        const int ts = t + pidx / S;  // absolute step inside the chunk
+        if ((lane & 3) == 0 && j < nact && ts < tvalid) {
           const int64_t o = ((b * ngroups + q.grp) * L + t0 + ts) * N + n0 + j;
-          pdB[o] = sB;
-          pdC[o] = sC;
+          ((o16 & 1) ? pdC : pdB)[o] = sum;
         }
-        __builtin_amdgcn_wave_barrier();
       }
     }
     __syncthreads();
