@@ -160,7 +160,9 @@ __device__ __forceinline__ Lane lane_setup(int64_t ngroups, int64_t nseg, int64_
 }
 
 // ---- 1. forward from a zero state per segment: chunk-start states relative to the
-// segment start, Delta sums, and the segment's end state
+// segment start, Delta sums, and the segment's end state.  One barrier per chunk:
+// the prep of chunk c+1 goes to the other half of double-buffered LDS while chunk c
+// is scanned from registers.
 template <int S, int G>
 __global__ void __launch_bounds__(64 * G)
 chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
@@ -170,8 +172,8 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
                  int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
-  __shared__ float2 pd[TC * 64];  // (Delta, Delta*x) per (t, channel)
-  __shared__ float bs[TC * 16];   // B per (t, state), zero beyond d_state
+  __shared__ float2 pd[2][TC * 64];  // (Delta, Delta*x) per (t, channel)
+  __shared__ float bs[2][TC * 16];   // B per (t, state), zero beyond d_state
   Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
   q.dvalid = q.d < Dm;
   const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
@@ -183,7 +185,7 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
   }
   float sd = 0.f;
   const int64_t row0 = q.b * L;
-  // this wave's rows of a chunk (x, delta_raw, B), loaded one chunk ahead
+  // this wave's rows of a chunk (x, delta_raw, B), loaded one chunk ahead of the prep
   float lx[EPL], lr[EPL], lb[EPL];
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
@@ -198,35 +200,42 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
       lb[i] = (t < tvalid && q.lane < N) ? Bm[(row0 + t0 + t) * N + q.lane] : 0.f;
     }
   };
-  load(q.c_begin);
-  for (int64_t c = q.c_begin; c < q.c_end; ++c) {
-    const int64_t t0 = c * TC;
-    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
-    if (q.dvalid) {  // state-major [b][chunk][n][d]: one coalesced row per state
-#pragma unroll
-      for (int j = 0; j < S; ++j)
-        if (j < q.nact) hrel[((q.b * nchunks + c) * N + q.n0 + j) * Dm + q.d] = h[j];
-      if (q.wave == 0) cumd[(q.b * nchunks + c) * Dm + q.d] = sd;
-    }
+  auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
+    const int tvalid = (int)(L - c * TC < TC ? L - c * TC : TC);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
         const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
-        pd[t * 64 + q.lane] = make_float2(delta, delta * lx[i]);
-        if (q.lane < 16) bs[t * 16 + q.lane] = lb[i];
+        pd[buf][t * 64 + q.lane] = make_float2(delta, delta * lx[i]);
+        if (q.lane < 16) bs[buf][t * 16 + q.lane] = lb[i];
       }
     }
-    if (c + 1 < q.c_end) load(c + 1);
-    __syncthreads();
+  };
+  load(q.c_begin);
+  prep(q.c_begin, 0);
+  if (q.c_begin + 1 < q.c_end) load(q.c_begin + 1);
+  __syncthreads();
+  for (int64_t c = q.c_begin; c < q.c_end; ++c) {
+    const int buf = (int)((c - q.c_begin) & 1);
+    if (q.dvalid) {  // state-major [b][chunk][n][d]: one coalesced row per state
+#pragma unroll
+      for (int j = 0; j < S; ++j)
+        if (j < q.nact) hrel[((q.b * nchunks + c) * N + q.n0 + j) * Dm + q.d] = h[j];
+      if (q.wave == 0) cumd[(q.b * nchunks + c) * Dm + q.d] = sd;
+    }
     float2 v[TC];
     float bv[TC][S];
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      v[t] = pd[t * 64 + q.lane];
+      v[t] = pd[buf][t * 64 + q.lane];
 #pragma unroll
-      for (int j = 0; j < S; ++j) bv[t][j] = bs[t * 16 + q.n0 + j];  // same address on every lane
+      for (int j = 0; j < S; ++j) bv[t][j] = bs[buf][t * 16 + q.n0 + j];  // same address on every lane
+    }
+    if (c + 1 < q.c_end) {
+      prep(c + 1, buf ^ 1);
+      if (c + 2 < q.c_end) load(c + 2);
     }
 #pragma unroll
     for (int t = 0; t < TC; ++t) {  // padded steps have Delta = 0 and B = 0
@@ -245,7 +254,7 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
 }
 
 // ---- 2. reverse recurrence from a zero carry per segment: the carry a_t G_t leaving
-// the segment's first step
+// the segment's first step (same double-buffered one-barrier-per-chunk structure)
 template <int S, int G, bool GATED>
 __global__ void __launch_bounds__(64 * G)
 seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
@@ -255,8 +264,8 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
                int64_t segc, int64_t nseg) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
-  __shared__ float2 pa[TC * 64];  // (Delta, g) per (t, channel)
-  __shared__ float cs[TC * 16];   // C per (t, state), zero beyond d_state
+  __shared__ float2 pa[2][TC * 64];  // (Delta, g) per (t, channel)
+  __shared__ float cs[2][TC * 16];   // C per (t, state), zero beyond d_state
   Lane q = lane_setup<S>(ngroups, nseg, segc, nchunks, N);
   q.dvalid = q.d < Dm;
   const float bias = (q.dvalid && dt_bias) ? dt_bias[q.d] : 0.f;
@@ -267,7 +276,7 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
     gc[j] = 0.f;
   }
   const int64_t row0 = q.b * L;
-  // this wave's rows of a chunk (delta_raw, dy, z, C), loaded one chunk ahead
+  // this wave's rows of a chunk (delta_raw, dy, z, C), loaded one chunk ahead of the prep
   float lr[EPL], ly[EPL], lz[EPL], lc[EPL];
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
@@ -283,10 +292,8 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
       lc[i] = (t < tvalid && q.lane < N) ? Cm[(row0 + t0 + t) * N + q.lane] : 0.f;
     }
   };
-  load(q.c_end - 1);
-  for (int64_t c = q.c_end - 1; c >= q.c_begin; --c) {
-    const int64_t t0 = c * TC;
-    const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
+  auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
+    const int tvalid = (int)(L - c * TC < TC ? L - c * TC : TC);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int t = q.wave + G * i;
@@ -295,19 +302,28 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
         const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
         float g = ly[i];
         if (GATED) g *= silu_f(lz[i]);
-        pa[t * 64 + q.lane] = make_float2(delta, g);
-        if (q.lane < 16) cs[t * 16 + q.lane] = lc[i];
+        pa[buf][t * 64 + q.lane] = make_float2(delta, g);
+        if (q.lane < 16) cs[buf][t * 16 + q.lane] = lc[i];
       }
     }
-    if (c > q.c_begin) load(c - 1);
-    __syncthreads();
+  };
+  load(q.c_end - 1);
+  prep(q.c_end - 1, 0);
+  if (q.c_end - 2 >= q.c_begin) load(q.c_end - 2);
+  __syncthreads();
+  for (int64_t c = q.c_end - 1; c >= q.c_begin; --c) {
+    const int buf = (int)((q.c_end - 1 - c) & 1);
     float2 v[TC];
     float cv[TC][S];
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      v[t] = pa[t * 64 + q.lane];
+      v[t] = pa[buf][t * 64 + q.lane];
 #pragma unroll
-      for (int j = 0; j < S; ++j) cv[t][j] = cs[t * 16 + q.n0 + j];  // same address on every lane
+      for (int j = 0; j < S; ++j) cv[t][j] = cs[buf][t * 16 + q.n0 + j];  // same address on every lane
+    }
+    if (c - 1 >= q.c_begin) {
+      prep(c - 1, buf ^ 1);
+      if (c - 2 >= q.c_begin) load(c - 2);
     }
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {  // padded steps: Delta = g = 0
