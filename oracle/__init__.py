@@ -9,11 +9,15 @@ gcc, no GPU headers), this module only marshals numpy arrays.
 Every input is widened to float64 before the call: fp32 inputs widen exactly,
 and bf16 inputs are passed as the float values they represent (also exact).
 
-Functions (definitions and citations are in the header of ``ssm_oracle.c``):
+Functions (definitions and citations are in the headers of ``ssm_oracle.c`` and
+``conv1d_oracle.c``):
   fwd(...)  -> {"y", "h_final"}          forward scan, sequential in t
   step(...) -> {"y", "state"}            single decode step (separate code)
   bwd(...)  -> {"dx", "ddelta_raw", "dz", "dB", "dC", "dA_log", "dD", "d_dt_bias"}
   softplus / sigmoid / silu / silu_grad  scalar helpers, exposed for pinning
+  conv_fwd(...)  -> out                  depthwise causal conv1d (+ SiLU)
+  conv_step(...) -> {"out", "state"}     one decode step of it (separate code)
+  conv_bwd(...)  -> {"dx", "dw", "dbias"}
 """
 from __future__ import annotations
 
@@ -25,18 +29,18 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_SRCS = [os.path.join(_HERE, "ssm_oracle.c"), os.path.join(_HERE, "conv1d_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libssm_oracle.so")
 _lib = None
 _lock = threading.Lock()
 
 
 def build(force: bool = False) -> str:
-    """Compile ssm_oracle.c with gcc into libssm_oracle.so (no fast-math)."""
+    """Compile the oracle's C sources with gcc into libssm_oracle.so (no fast-math)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-shared", "-fPIC",
-               "-std=c99", "-D_POSIX_C_SOURCE=200809L", _SRC, "-o", tmp, "-lm", "-lpthread"]
+               "-std=c99", "-D_POSIX_C_SOURCE=200809L"] + _SRCS + ["-o", tmp, "-lm", "-lpthread"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -58,6 +62,12 @@ def _load():
         lib.ssm_oracle_step.restype = ctypes.c_int
         lib.ssm_oracle_bwd.argtypes = [P] * 18 + [L] * 4 + [ctypes.c_int]
         lib.ssm_oracle_bwd.restype = ctypes.c_int
+        lib.conv1d_oracle_fwd.argtypes = [P] * 4 + [L] * 4 + [ctypes.c_int]
+        lib.conv1d_oracle_fwd.restype = ctypes.c_int
+        lib.conv1d_oracle_step.argtypes = [P] * 5 + [L] * 3 + [ctypes.c_int]
+        lib.conv1d_oracle_step.restype = ctypes.c_int
+        lib.conv1d_oracle_bwd.argtypes = [P] * 7 + [L] * 4 + [ctypes.c_int]
+        lib.conv1d_oracle_bwd.restype = ctypes.c_int
         for name in ("softplus", "sigmoid", "silu", "silu_grad"):
             f = getattr(lib, "ssm_oracle_" + name)
             f.argtypes = [ctypes.c_double]
@@ -169,3 +179,51 @@ def silu(z: float) -> float:
 
 def silu_grad(z: float) -> float:
     return _load().ssm_oracle_silu_grad(float(z))
+
+
+# ---------------------------------------------------------------- conv1d
+
+def conv_fwd(x, w, bias=None, silu=True):
+    x = _f64(x)
+    b, l, d = x.shape
+    w = _f64(w)
+    k = w.shape[1]
+    w = _f64(w, (d, k))
+    bias = _f64(bias, (d,))
+    out = np.empty((b, l, d), np.float64)
+    rc = _load().conv1d_oracle_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), b, l, d, k, int(bool(silu)))
+    if rc != 0:
+        raise RuntimeError("conv1d_oracle_fwd failed with %d" % rc)
+    return out
+
+
+def conv_step(state, x, w, bias=None, silu=True):
+    x = _f64(x)
+    b, d = x.shape
+    w = _f64(w)
+    k = w.shape[1]
+    w = _f64(w, (d, k))
+    bias = _f64(bias, (d,))
+    state = np.array(state, dtype=np.float64, copy=True, order="C").reshape(b, d, k - 1)
+    out = np.empty((b, d), np.float64)
+    rc = _load().conv1d_oracle_step(_ptr(state) if k > 1 else None, _ptr(x), _ptr(w), _ptr(bias), _ptr(out),
+                                    b, d, k, int(bool(silu)))
+    if rc != 0:
+        raise RuntimeError("conv1d_oracle_step failed with %d" % rc)
+    return {"out": out, "state": state}
+
+
+def conv_bwd(x, w, dout, bias=None, silu=True):
+    x = _f64(x)
+    b, l, d = x.shape
+    w = _f64(w)
+    k = w.shape[1]
+    w = _f64(w, (d, k))
+    bias = _f64(bias, (d,))
+    dout = _f64(dout, (b, l, d))
+    out = {"dx": np.empty((b, l, d)), "dw": np.empty((d, k)), "dbias": np.empty((d,))}
+    rc = _load().conv1d_oracle_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(dout), _ptr(out["dx"]), _ptr(out["dw"]),
+                                   _ptr(out["dbias"]), b, l, d, k, int(bool(silu)))
+    if rc != 0:
+        raise RuntimeError("conv1d_oracle_bwd failed with %d" % rc)
+    return out

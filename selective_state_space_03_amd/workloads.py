@@ -127,3 +127,62 @@ def make_inputs(w: Workload, *, batch: Optional[int] = None, seqlen: Optional[in
         out["h0"] = (0.1 * rng.standard_normal((b, d, n))).astype(np.float32) if random_h0 else None
         out["dy"] = rng.standard_normal((b, l, d)).astype(np.float32) if want_dy else None
     return out
+
+
+# ---------------------------------------------------------------- depthwise causal conv1d
+#
+# The conv1d that precedes the scan in a Mamba block.  Recipe: numpy PCG64(seed); draw
+# order x, w, bias, dout, state; x, dout, state ~ N(0, 1); w and bias ~ U(-1/sqrt(K),
+# 1/sqrt(K)) (the default initialisation of a depthwise conv with K taps); values
+# rounded to fp32 (and to bf16 for bf16 I/O) like the scan inputs.
+
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    kind: str      # "conv" (sequence) or "conv_step" (one decode step)
+    batch: int
+    seqlen: int
+    dim: int
+    width: int     # K, taps per channel
+    io: str
+    silu: bool
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+
+CONV_WORKLOADS = {
+    "conv_small": ConvWorkload("conv_small", "conv", 1, 64, 16, 4, "f32", True, 2001),
+    "conv_b8_l2048_d1536_k4": ConvWorkload("conv_b8_l2048_d1536_k4", "conv", 8, 2048, 1536, 4, "f32", True, 2002),
+    "conv_bf16_b4_l4096_d4096_k4": ConvWorkload("conv_bf16_b4_l4096_d4096_k4", "conv", 4, 4096, 4096, 4, "bf16",
+                                                True, 2003),
+    "conv_step_b256_d5120_k4": ConvWorkload("conv_step_b256_d5120_k4", "conv_step", 256, 1, 5120, 4, "f32", True,
+                                            2004),
+}
+
+
+def make_conv_inputs(w: ConvWorkload, *, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                     dim: Optional[int] = None, width: Optional[int] = None, silu: Optional[bool] = None,
+                     seed: Optional[int] = None, io: Optional[str] = None) -> dict:
+    """Seeded conv1d inputs: x ([b, l, d], or [b, d] for a step), weight [d, K], bias [d],
+    dout like x, and for a step the state [b, d, K-1]."""
+    b = w.batch if batch is None else batch
+    l = w.seqlen if seqlen is None else seqlen
+    d = w.dim if dim is None else dim
+    k = w.width if width is None else width
+    io_ = w.io if io is None else io
+    step = w.kind == "conv_step"
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    act = (b, d) if step else (b, l, d)
+    bound = 1.0 / np.sqrt(k)
+    x = round_to_io(rng.standard_normal(act), io_)
+    weight = rng.uniform(-bound, bound, size=(d, k)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=d).astype(np.float32)
+    dout = rng.standard_normal(act).astype(np.float32)
+    out = {"io": io_, "batch": b, "seqlen": 1 if step else l, "dim": d, "width": k,
+           "silu": w.silu if silu is None else silu, "x": x, "weight": weight, "bias": bias, "dout": dout}
+    if step:
+        out["state"] = round_to_io(rng.standard_normal((b, d, k - 1)), io_)
+    return out
