@@ -1,10 +1,12 @@
-// ssm_api.hip -- the extern "C" entry points declared in include/ssm_scan.h.
+// ssm_api.hip -- the extern "C" entry points declared in include/ssm_scan.h and
+// include/ssm_conv1d.h.
 // Every argument is validated before anything is enqueued; launch errors are mapped
 // to SSM_ERR_HIP.  No exception crosses the boundary.
 #include <stdint.h>
 
 #include <new>
 
+#include "../../include/ssm_conv1d.h"
 #include "../../include/ssm_scan.h"
 #include "ssm_internal.h"
 
@@ -29,6 +31,16 @@ bool dims_ok(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
 }
 
 size_t esize(int io_dtype) { return io_dtype == SSM_BF16 ? 2 : 4; }
+
+bool conv_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
+  if (batch < 1 || seqlen < 1 || dim < 1 || width < 1 || width > 8) return false;
+  const int64_t lim = (int64_t)1 << 40;
+  if (batch > lim / seqlen) return false;
+  if (batch * seqlen > lim / dim) return false;
+  // grids are 1-D: channel groups x time groups x batch (and batch * dim for a step)
+  if ((dim + 63) / 64 * ((seqlen + 63) / 64) * batch > ((int64_t)1 << 31) - 1) return false;
+  return true;
+}
 
 }  // namespace
 
@@ -176,6 +188,95 @@ int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void
   a.dz = z ? (float*)dz : nullptr; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
   a.d_dt_bias = d_dt_bias; a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
   return ssm::launch_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- conv1d
+
+int ssm_conv1d_fwd(const void* x, const float* weight, const float* bias, void* out, int64_t batch,
+                   int64_t seqlen, int64_t dim, int64_t width, int activation, int io_dtype,
+                   hipStream_t stream) {
+  if (!x || !weight || !out) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!conv_dims_ok(batch, seqlen, dim, width)) return SSM_ERR_DIM;
+  const size_t es = esize(io_dtype);
+  if (!aligned(x, es) || !aligned(out, es) || !aligned(weight, 4) || (bias && !aligned(bias, 4)))
+    return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * seqlen * dim;
+  const Range o = rng(out, E * es);
+  if (overlap(o, rng(x, E * es)) || overlap(o, rng(weight, (size_t)dim * width * 4)) ||
+      overlap(o, rng(bias, bias ? dim * 4 : 0)))
+    return SSM_ERR_ALIAS;
+  ssm::ConvArgs a{};
+  a.x = x; a.w = weight; a.bias = bias; a.out = out;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.width = (int)width;
+  a.silu = activation == SSM_ACT_SILU; a.bf16 = io_dtype == SSM_BF16;
+  return ssm::launch_conv_fwd(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_conv1d_step(void* conv_state, const void* x, const float* weight, const float* bias, void* out,
+                    int64_t batch, int64_t dim, int64_t width, int activation, int io_dtype,
+                    hipStream_t stream) {
+  if (!x || !weight || !out || (width > 1 && !conv_state)) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!conv_dims_ok(batch, 1, dim, width)) return SSM_ERR_DIM;
+  if (batch * dim > ((int64_t)1 << 31) * 255) return SSM_ERR_DIM;  // grid limit
+  const size_t es = esize(io_dtype);
+  if (!aligned(x, es) || !aligned(out, es) || !aligned(conv_state, es) || !aligned(weight, 4) ||
+      (bias && !aligned(bias, 4)))
+    return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * dim;
+  const Range ins[] = {rng(x, E * es), rng(weight, (size_t)dim * width * 4), rng(bias, bias ? dim * 4 : 0)};
+  const Range outs[] = {rng(out, E * es), rng(conv_state, width > 1 ? E * (width - 1) * es : 0)};
+  for (const Range& r : outs)
+    for (const Range& i : ins)
+      if (overlap(r, i)) return SSM_ERR_ALIAS;
+  if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+  ssm::ConvArgs a{};
+  a.x = x; a.w = weight; a.bias = bias; a.out = out; a.state = conv_state;
+  a.batch = batch; a.seqlen = 1; a.dim = dim; a.width = (int)width;
+  a.silu = activation == SSM_ACT_SILU; a.bf16 = io_dtype == SSM_BF16;
+  return ssm::launch_conv_step(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+size_t ssm_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int io_dtype) {
+  (void)io_dtype;
+  if (!conv_dims_ok(batch, seqlen, dim, width)) return 0;
+  return ssm::conv_bwd_layout(batch, seqlen, dim, width).total;
+}
+
+int ssm_conv1d_bwd(const void* x, const float* weight, const float* bias, const void* dout, void* dx,
+                   float* dweight, float* dbias, void* workspace, size_t workspace_bytes, int64_t batch,
+                   int64_t seqlen, int64_t dim, int64_t width, int activation, int io_dtype,
+                   hipStream_t stream) {
+  if (!x || !weight || !dout || !dx) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!conv_dims_ok(batch, seqlen, dim, width)) return SSM_ERR_DIM;
+  if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
+  if (!workspace) return SSM_ERR_WORKSPACE;
+  const ssm::ConvBwdLayout l = ssm::conv_bwd_layout(batch, seqlen, dim, width);
+  if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
+  const void* all[] = {x, weight, bias, dout, dx, dweight, dbias};
+  for (const void* p : all)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * seqlen * dim, W = (size_t)dim * width;
+  const Range ins[] = {rng(x, E * 4), rng(weight, W * 4), rng(bias, bias ? dim * 4 : 0), rng(dout, E * 4)};
+  const Range outs[] = {rng(dx, E * 4), rng(dweight, dweight ? W * 4 : 0), rng(dbias, dbias ? dim * 4 : 0),
+                        rng(workspace, l.total)};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  ssm::ConvArgs a{};
+  a.x = x; a.w = weight; a.bias = bias; a.dout = dout; a.dx = dx; a.dw = dweight; a.dbias = dbias;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.width = (int)width;
+  a.silu = activation == SSM_ACT_SILU; a.bf16 = false;
+  return ssm::launch_conv_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -75,6 +75,30 @@ struct BwdLayout {
 };
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
 
+// depthwise causal conv1d (+ SiLU)
+struct ConvArgs {
+  const void* x;       // [B, L, D] io dtype (a step: [B, D])
+  const float* w;      // [D, K]
+  const float* bias;   // [D], nullable
+  void* out;           // like x
+  void* state;         // step only: [B, D, K-1] io dtype, read and written
+  const void* dout;    // backward only, fp32
+  void* dx;            // backward only, fp32
+  float* dw;           // backward only, [D, K], nullable
+  float* dbias;        // backward only, [D], nullable
+  int64_t batch, seqlen, dim;
+  int width;
+  bool silu, bf16;
+};
+struct ConvBwdLayout {
+  int64_t ntiles;      // time tiles per batch element
+  size_t off_dw, off_db, total;
+};
+ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t width);
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_step(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_bwd(const ConvArgs& a, void* workspace, hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);

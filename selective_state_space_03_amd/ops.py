@@ -27,7 +27,9 @@ SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPORTED",
           4: "SSM_ERR_ALIGN", 5: "SSM_ERR_WORKSPACE", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_HIP"}
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_conv1d_fwd", "ssm_conv1d_step",
+           "ssm_conv1d_bwd_workspace_bytes", "ssm_conv1d_bwd")
+SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
 
 _lib = None
 _lock = threading.Lock()
@@ -62,6 +64,14 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.restype = SZ
         L.ssm_scan_bwd.argtypes = [P] * 18 + [P, SZ] + [I64] * 4 + [I, P]
         L.ssm_scan_bwd.restype = I
+        L.ssm_conv1d_fwd.argtypes = [P] * 4 + [I64] * 4 + [I, I, P]
+        L.ssm_conv1d_fwd.restype = I
+        L.ssm_conv1d_step.argtypes = [P] * 5 + [I64] * 3 + [I, I, P]
+        L.ssm_conv1d_step.restype = I
+        L.ssm_conv1d_bwd_workspace_bytes.argtypes = [I64] * 4 + [I]
+        L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
+        L.ssm_conv1d_bwd.argtypes = [P] * 7 + [P, SZ] + [I64] * 4 + [I, I, P]
+        L.ssm_conv1d_bwd.restype = I
         _lib = L
         return L
 
@@ -194,3 +204,72 @@ def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=Non
                             _ptr(workspace), ws_bytes, b, l, d, n, io, _stream())
     _check("ssm_scan_bwd", st)
     return out
+
+
+# ---------------------------------------------------------------- conv1d
+
+def conv1d_fwd(x, weight, bias=None, silu=True, out=None):
+    """Depthwise causal conv1d (+ SiLU) over [batch, seqlen, dim]; weight [dim, K] fp32."""
+    b, l, d = x.shape
+    k = weight.shape[1]
+    dev = x.device
+    io = _io_dtype(x)
+    _req(x, "x", (b, l, d), x.dtype, dev)
+    _req(weight, "weight", (d, k), torch.float32, dev)
+    _req(bias, "bias", (d,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", (b, l, d), x.dtype, dev)
+    _check("ssm_conv1d_fwd", lib().ssm_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), b, l, d, k,
+                                                  SSM_ACT_SILU if silu else SSM_ACT_NONE, io, _stream()))
+    return out
+
+
+def conv1d_step(conv_state, x, weight, bias=None, silu=True, out=None):
+    """One decode step; conv_state [batch, dim, K-1] (io dtype) is updated in place."""
+    b, d = x.shape
+    k = weight.shape[1]
+    dev = x.device
+    io = _io_dtype(x)
+    _req(x, "x", (b, d), x.dtype, dev)
+    _req(weight, "weight", (d, k), torch.float32, dev)
+    _req(bias, "bias", (d,), torch.float32, dev)
+    if k > 1:
+        _req(conv_state, "conv_state", (b, d, k - 1), x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", (b, d), x.dtype, dev)
+    _check("ssm_conv1d_step", lib().ssm_conv1d_step(_ptr(conv_state) if k > 1 else None, _ptr(x), _ptr(weight),
+                                                    _ptr(bias), _ptr(out), b, d, k,
+                                                    SSM_ACT_SILU if silu else SSM_ACT_NONE, io, _stream()))
+    return out
+
+
+def conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, io_dtype=SSM_F32):
+    return int(lib().ssm_conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, io_dtype))
+
+
+def conv1d_bwd(x, weight, dout, bias=None, silu=True, workspace=None, dx=None, dweight=None, dbias=None,
+               want_params=True):
+    """Backward (fp32): returns {"dx", "dweight", "dbias"} (the last two None unless wanted)."""
+    b, l, d = x.shape
+    k = weight.shape[1]
+    dev = x.device
+    f = torch.float32
+    _req(x, "x", (b, l, d), f, dev)
+    _req(weight, "weight", (d, k), f, dev)
+    _req(bias, "bias", (d,), f, dev)
+    _req(dout, "dout", (b, l, d), f, dev)
+    if dx is None:
+        dx = torch.empty((b, l, d), dtype=f, device=dev)
+    if want_params and dweight is None:
+        dweight = torch.empty((d, k), dtype=f, device=dev)
+    if want_params and dbias is None:
+        dbias = torch.empty((d,), dtype=f, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(conv1d_bwd_workspace_bytes(b, l, d, k), 1),), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("ssm_conv1d_bwd", lib().ssm_conv1d_bwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(dout), _ptr(dx),
+                                                  _ptr(dweight), _ptr(dbias), _ptr(workspace), ws_bytes, b, l, d,
+                                                  k, SSM_ACT_SILU if silu else SSM_ACT_NONE, SSM_F32, _stream()))
+    return {"dx": dx, "dweight": dweight, "dbias": dbias}

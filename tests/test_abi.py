@@ -1,5 +1,5 @@
 """CPU checks of the C ABI: the library loads, exports every function that
-include/ssm_scan.h declares, and rejects invalid arguments with the documented
+include/*.h declares, and rejects invalid arguments with the documented
 status codes *before* enqueueing anything.  Every call here fails validation, so
 no HIP call is made and no GPU is needed (pointer values are fake addresses that
 are never dereferenced)."""
@@ -19,15 +19,18 @@ no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
                                  reason="fake-pointer validation checks run only where no GPU is visible")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, DIM, UNSUP, ALIGN, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ssm_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -160,3 +163,38 @@ def test_bwd_validation():
     assert bwd_call(ws=addr(9)) == ALIAS             # workspace == dx
     assert bwd_call(dB=addr(13)) == ALIAS            # dB == dC
     assert bwd_call(dA_log=addr(14, 2)) == ALIGN
+
+
+# ---------------------------------------------------------------- conv1d
+
+def conv_call(x=addr(0), w=addr(5), bias=addr(6), out=addr(9), b=2, l=64, d=32, k=4, act=1, io=0):
+    return ops.lib().ssm_conv1d_fwd(x, w, bias, out, b, l, d, k, act, io, None)
+
+
+@no_gpu_only
+def test_conv_fwd_validation():
+    assert conv_call(x=None) == NULL
+    assert conv_call(w=None) == NULL
+    assert conv_call(k=0) == DIM and conv_call(k=9) == DIM and conv_call(l=0) == DIM
+    assert conv_call(act=2) == UNSUP and conv_call(io=5) == UNSUP
+    assert conv_call(x=addr(0, 2)) == ALIGN
+    assert conv_call(out=addr(0)) == ALIAS
+
+
+@no_gpu_only
+def test_conv_step_and_bwd_validation():
+    L = ops.lib()
+    # step: a width > 1 needs a state; in-place state may not overlap x
+    assert L.ssm_conv1d_step(None, addr(0), addr(5), None, addr(9), 2, 32, 4, 1, 0, None) == NULL
+    assert L.ssm_conv1d_step(addr(0), addr(0), addr(5), None, addr(9), 2, 32, 4, 1, 0, None) == ALIAS
+    # bwd: fp32 only, and the workspace is required and large enough
+    wsb = L.ssm_conv1d_bwd_workspace_bytes(2, 64, 32, 4, 0)
+    assert wsb > 0
+    assert L.ssm_conv1d_bwd(addr(0), addr(5), None, addr(1), addr(9), None, None, addr(11), wsb, 2, 64, 32, 4, 1,
+                            1, None) == UNSUP
+    assert L.ssm_conv1d_bwd(addr(0), addr(5), None, addr(1), addr(9), None, None, None, wsb, 2, 64, 32, 4, 1, 0,
+                            None) == WS
+    assert L.ssm_conv1d_bwd(addr(0), addr(5), None, addr(1), addr(9), None, None, addr(11), wsb - 1, 2, 64, 32, 4,
+                            1, 0, None) == WS
+    assert L.ssm_conv1d_bwd(addr(0), addr(5), None, addr(1), addr(0), None, None, addr(11), wsb, 2, 64, 32, 4, 1,
+                            0, None) == ALIAS
