@@ -4,12 +4,13 @@
 // conv1d_burnin_fwd, the multi-step forward; conv1d_step_bwd / conv1d_burnin_bwd).
 //   p[b,t,d] = sum_{k<K} w[d,k] x[b,t-(K-1)+k,d] + bias[d]   (no history before t = 0)
 //   out      = silu(p) or p
-// The weight and bias gradients are fixed-order sums of per-(batch, time tile)
+// The weight and bias gradients are fixed-order sums of per-(batch, time segment)
 // partials, added in lexical order (deterministic_backward.py, ordered_conv: per-batch
 // partials summed in batch order, no atomics).
 //
-// All three kernels are HBM streams: lane = channel, so every load and store of a
-// [B, L, D] row is one contiguous 256 B (fp32) / 128 B (bf16) segment per wavefront,
+// All three kernels are HBM streams: lane = channel (two neighbouring channels per
+// lane in the forward when d_inner is even), so every load and store of a [B, L, D]
+// row is one contiguous segment per wavefront,
 // and each lane walks a tile of TL time steps keeping the K-tap window in registers
 // (the halo of K-1 rows per tile is the only re-read).  All loads of a tile are
 // issued before any arithmetic.
@@ -23,36 +24,82 @@ constexpr int kFwdTile = 32;  // time steps per lane in the forward
 constexpr int kBwdTile = 16;  // time steps per lane in the backward
 constexpr int kWaves = 4;     // wavefronts per workgroup, one time tile each
 
-template <typename T, int K, bool SILU>
+// V neighbouring channels per lane in one access: 2 or 4 elements of T
+template <typename T, int V> struct vec_io;
+template <> struct vec_io<float, 2> {
+  __device__ __forceinline__ static void ld(const float* p, int64_t i, float* o) {
+    const float2 q = *reinterpret_cast<const float2*>(p + i);
+    o[0] = q.x; o[1] = q.y;
+  }
+  __device__ __forceinline__ static void st(float* p, int64_t i, const float* o) {
+    *reinterpret_cast<float2*>(p + i) = make_float2(o[0], o[1]);
+  }
+};
+template <> struct vec_io<bf16_t, 4> {
+  __device__ __forceinline__ static void ld(const bf16_t* p, int64_t i, float* o) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+    o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+  __device__ __forceinline__ static void st(bf16_t* p, int64_t i, const float* o) {
+    *reinterpret_cast<uint2*>(p + i) =
+        make_uint2((uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+                   (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16));
+  }
+};
+// V channels per lane: 1, or an 8-byte access (2 fp32 / 4 bf16) when d_inner is a
+// multiple of V and the rows are aligned for it
+template <typename T, int K, bool SILU, int V>
 __global__ void __launch_bounds__(64 * kWaves)
 conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
                 T* __restrict__ out, int64_t L, int64_t Dm, int64_t ngroups, int64_t ntg) {
-  constexpr int TL = kFwdTile;
+  constexpr int TL = V == 4 ? kFwdTile / 2 : kFwdTile;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // block -> (b, time group, channel group), channel groups fastest
   const int64_t grp = blockIdx.x % ngroups;
   const int64_t r = blockIdx.x / ngroups;
   const int64_t tg = r % ntg, b = r / ntg;
-  const int64_t d = grp * 64 + lane;
+  const int64_t d = (grp * 64 + lane) * V;
   const int64_t t0 = (tg * kWaves + wave) * TL;
-  if (d >= Dm || t0 >= L) return;  // no barriers in this kernel
-  float wk[K];
+  if (d >= Dm || t0 >= L) return;  // no barriers in this kernel (Dm is a multiple of V)
+  float wk[V][K], bs[V];
 #pragma unroll
-  for (int k = 0; k < K; ++k) wk[k] = w[d * K + k];
-  const float bs = bias ? bias[d] : 0.f;
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[v][k] = w[(d + v) * K + k];
+    bs[v] = bias ? bias[d + v] : 0.f;
+  }
   // x[t0-K+1 .. t0+TL-1], zero before t = 0 and past the end
-  float xr[TL + K - 1];
+  float xr[TL + K - 1][V];
 #pragma unroll
   for (int i = 0; i < TL + K - 1; ++i) {
     const int64_t t = t0 - (K - 1) + i;
-    xr[i] = (t >= 0 && t < L) ? io<T>::ld(x, (b * L + t) * Dm + d) : 0.f;
+    const bool in = t >= 0 && t < L;
+    if constexpr (V > 1) {
+      if (in) {
+        vec_io<T, V>::ld(x, (b * L + t) * Dm + d, xr[i]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) xr[i][v] = 0.f;
+      }
+    } else {
+      xr[i][0] = in ? io<T>::ld(x, (b * L + t) * Dm + d) : 0.f;
+    }
   }
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    float p = bs;
+    float o[V];
 #pragma unroll
-    for (int k = 0; k < K; ++k) p = fmaf(wk[k], xr[i + k], p);
-    if (t0 + i < L) io<T>::st(out, (b * L + t0 + i) * Dm + d, SILU ? silu_f(p) : p);
+    for (int v = 0; v < V; ++v) {
+      float p = bs[v];
+#pragma unroll
+      for (int k = 0; k < K; ++k) p = fmaf(wk[v][k], xr[i + k][v], p);
+      o[v] = SILU ? silu_f(p) : p;
+    }
+    if (t0 + i < L) {
+      if constexpr (V > 1) vec_io<T, V>::st(out, (b * L + t0 + i) * Dm + d, o);
+      else io<T>::st(out, (b * L + t0 + i) * Dm + d, o[0]);
+    }
   }
 }
 
@@ -75,74 +122,92 @@ conv_step_kernel(T* __restrict__ state, const T* __restrict__ x, const float* __
   for (int k = 0; k < K - 1; ++k) io<T>::st(state, i * (K - 1) + k, win[k + 1]);
 }
 
-// backward of one (b, time tile, channel): dx for the tile, and the tile's partial
-// dw[k] = sum_t dp[t] x[t-K+1+k] and dbias = sum_t dp[t], stored [b][tile][k][d]
+// backward of one (b, time segment, channel group): each wave walks its time tiles of
+// the segment in ascending order, writes dx, and accumulates the tile's
+// dw[k] = sum_t dp[t] x[t-K+1+k] and dbias = sum_t dp[t]; the waves' sums are then
+// added in wave order through LDS and stored as the segment's partial, [b][seg][k][d]
 template <int K, bool SILU>
 __global__ void __launch_bounds__(64 * kWaves)
 conv_bwd_kernel(const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
                 const float* __restrict__ dout, float* __restrict__ dx, float* __restrict__ pdw,
-                float* __restrict__ pdb, int64_t L, int64_t Dm, int64_t ngroups, int64_t ntg, int64_t ntiles) {
+                float* __restrict__ pdb, int64_t L, int64_t Dm, int64_t ngroups, int64_t ntg, int64_t tgs,
+                int64_t nseg) {
   constexpr int TL = kBwdTile;
+  __shared__ float red[kWaves][K + 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t grp = blockIdx.x % ngroups;
   const int64_t r = blockIdx.x / ngroups;
-  const int64_t tg = r % ntg, b = r / ntg;
+  const int64_t seg = r % nseg, b = r / nseg;
   const int64_t d = grp * 64 + lane;
-  const int64_t tile = tg * kWaves + wave;
-  const int64_t t0 = tile * TL;
-  if (d >= Dm || t0 >= L) return;  // no barriers in this kernel
+  const bool dvalid = d < Dm;
   float wk[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) wk[k] = w[d * K + k];
-  const float bs = bias ? bias[d] : 0.f;
-  // x[t0-K+1 .. t0+TL+K-2] and dout[t0 .. t0+TL+K-2], zero outside the sequence
-  constexpr int NX = TL + 2 * (K - 1), NG = TL + K - 1;
-  float xr[NX], gr[NG];
-#pragma unroll
-  for (int i = 0; i < NX; ++i) {
-    const int64_t t = t0 - (K - 1) + i;
-    xr[i] = (t >= 0 && t < L) ? x[(b * L + t) * Dm + d] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int64_t t = t0 + i;
-    gr[i] = t < L ? dout[(b * L + t) * Dm + d] : 0.f;
-  }
-  // dp[t0 + i] for i < TL + K - 1 (dp = 0 past the end since dout = 0 there)
-  float dp[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    if (SILU) {
-      float p = bs;
-#pragma unroll
-      for (int k = 0; k < K; ++k) p = fmaf(wk[k], xr[i + k], p);
-      const float sg = sigmoid_f(p);
-      dp[i] = gr[i] * sg * fmaf(p, 1.f - sg, 1.f);
-    } else {
-      dp[i] = gr[i];
-    }
-  }
+  for (int k = 0; k < K; ++k) wk[k] = dvalid ? w[d * K + k] : 0.f;
+  const float bs = (dvalid && bias) ? bias[d] : 0.f;
   float sw[K], sb = 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) sw[k] = 0.f;
+  const int64_t tg_end = (seg + 1) * tgs < ntg ? (seg + 1) * tgs : ntg;
+  for (int64_t tg = seg * tgs; tg < tg_end; ++tg) {
+    const int64_t t0 = (tg * kWaves + wave) * TL;
+    if (!dvalid || t0 >= L) continue;  // uniform per wave; the barrier below is outside the loop
+    // x[t0-K+1 .. t0+TL+K-2] and dout[t0 .. t0+TL+K-2], zero outside the sequence
+    constexpr int NX = TL + 2 * (K - 1), NG = TL + K - 1;
+    float xr[NX], gr[NG];
 #pragma unroll
-  for (int i = 0; i < TL; ++i) {
-    float g = 0.f;
+    for (int i = 0; i < NX; ++i) {
+      const int64_t t = t0 - (K - 1) + i;
+      xr[i] = (t >= 0 && t < L) ? x[(b * L + t) * Dm + d] : 0.f;
+    }
 #pragma unroll
-    for (int k = 0; k < K; ++k) g = fmaf(wk[k], dp[i + K - 1 - k], g);
-    if (t0 + i < L) dx[(b * L + t0 + i) * Dm + d] = g;
-    // the tile's own steps only (dp of the halo belongs to the next tile)
+    for (int i = 0; i < NG; ++i) {
+      const int64_t t = t0 + i;
+      gr[i] = t < L ? dout[(b * L + t) * Dm + d] : 0.f;
+    }
+    // dp[t0 + i] for i < TL + K - 1 (dp = 0 past the end since dout = 0 there)
+    float dp[NG];
 #pragma unroll
-    for (int k = 0; k < K; ++k) sw[k] = fmaf(dp[i], xr[i + k], sw[k]);
-    sb += dp[i];
+    for (int i = 0; i < NG; ++i) {
+      if (SILU) {
+        float p = bs;
+#pragma unroll
+        for (int k = 0; k < K; ++k) p = fmaf(wk[k], xr[i + k], p);
+        const float sg = sigmoid_f(p);
+        dp[i] = gr[i] * sg * fmaf(p, 1.f - sg, 1.f);
+      } else {
+        dp[i] = gr[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+      float g = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) g = fmaf(wk[k], dp[i + K - 1 - k], g);
+      if (t0 + i < L) dx[(b * L + t0 + i) * Dm + d] = g;
+      // the tile's own steps only (dp of the halo belongs to the next tile)
+#pragma unroll
+      for (int k = 0; k < K; ++k) sw[k] = fmaf(dp[i], xr[i + k], sw[k]);
+      sb += dp[i];
+    }
   }
-  const int64_t o = (b * ntiles + tile) * K;
+  // the waves' sums, added in wave order
 #pragma unroll
-  for (int k = 0; k < K; ++k) pdw[(o + k) * Dm + d] = sw[k];
-  pdb[(b * ntiles + tile) * Dm + d] = sb;
+  for (int k = 0; k < K; ++k) red[wave][k][lane] = sw[k];
+  red[wave][K][lane] = sb;
+  __syncthreads();
+  if (wave == 0 && dvalid) {
+    const int64_t o = (b * nseg + seg) * K;
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+      float s = red[0][k][lane];
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) s += red[v][k][lane];
+      if (k < K) pdw[(o + k) * Dm + d] = s; else pdb[(b * nseg + seg) * Dm + d] = s;
+    }
+  }
 }
 
-// dw[d,k] and dbias[d]: sums of the partials over (b, tile) in lexical order
+// dw[d,k] and dbias[d]: sums of the partials over (b, segment) in lexical order
 template <int K>
 __global__ void __launch_bounds__(256)
 conv_reduce_kernel(const float* __restrict__ pdw, const float* __restrict__ pdb, float* __restrict__ dw,
@@ -163,18 +228,29 @@ conv_reduce_kernel(const float* __restrict__ pdw, const float* __restrict__ pdb,
   }
 }
 
-template <typename T, int K>
-hipError_t fwd_k(const ConvArgs& a, hipStream_t stream) {
-  const int64_t ngroups = (a.dim + 63) / 64;
-  const int64_t ntg = (a.seqlen + kFwdTile * kWaves - 1) / (kFwdTile * kWaves);
+template <typename T, int K, int V>
+hipError_t fwd_kv(const ConvArgs& a, hipStream_t stream) {
+  constexpr int TL = V == 4 ? kFwdTile / 2 : kFwdTile;
+  const int64_t ngroups = (a.dim + 64 * V - 1) / (64 * V);
+  const int64_t ntg = (a.seqlen + TL * kWaves - 1) / (TL * kWaves);
   const dim3 grid((unsigned)(ngroups * ntg * a.batch));
   if (a.silu)
-    hipLaunchKernelGGL((conv_fwd_kernel<T, K, true>), grid, dim3(64 * kWaves), 0, stream, (const T*)a.x, a.w,
+    hipLaunchKernelGGL((conv_fwd_kernel<T, K, true, V>), grid, dim3(64 * kWaves), 0, stream, (const T*)a.x, a.w,
                        a.bias, (T*)a.out, a.seqlen, a.dim, ngroups, ntg);
   else
-    hipLaunchKernelGGL((conv_fwd_kernel<T, K, false>), grid, dim3(64 * kWaves), 0, stream, (const T*)a.x, a.w,
+    hipLaunchKernelGGL((conv_fwd_kernel<T, K, false, V>), grid, dim3(64 * kWaves), 0, stream, (const T*)a.x, a.w,
                        a.bias, (T*)a.out, a.seqlen, a.dim, ngroups, ntg);
   return hipGetLastError();
+}
+
+template <typename T, int K>
+hipError_t fwd_k(const ConvArgs& a, hipStream_t stream) {
+  // 8-byte accesses (2 fp32 or 4 bf16 channels per lane) when every row starts on
+  // an 8-byte boundary
+  constexpr int V = sizeof(T) == 4 ? 2 : 4;
+  if (a.dim % V == 0 && (uintptr_t)a.x % 8 == 0 && (uintptr_t)a.out % 8 == 0)
+    return fwd_kv<T, K, V>(a, stream);
+  return fwd_kv<T, K, 1>(a, stream);
 }
 
 template <typename T, int K>
@@ -196,21 +272,20 @@ hipError_t bwd_k(const ConvArgs& a, void* ws, hipStream_t stream) {
   float* pdw = (float*)((char*)ws + l.off_dw);
   float* pdb = (float*)((char*)ws + l.off_db);
   const int64_t ngroups = (a.dim + 63) / 64;
-  const int64_t ntg = (l.ntiles + kWaves - 1) / kWaves;
-  const dim3 grid((unsigned)(ngroups * ntg * a.batch));
+  const dim3 grid((unsigned)(ngroups * l.nseg * a.batch));
   if (a.silu)
     hipLaunchKernelGGL((conv_bwd_kernel<K, true>), grid, dim3(64 * kWaves), 0, stream, (const float*)a.x, a.w,
-                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, ntg,
-                       l.ntiles);
+                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg,
+                       l.tgs, l.nseg);
   else
     hipLaunchKernelGGL((conv_bwd_kernel<K, false>), grid, dim3(64 * kWaves), 0, stream, (const float*)a.x, a.w,
-                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, ntg,
-                       l.ntiles);
+                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg,
+                       l.tgs, l.nseg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = K * a.dim;
   hipLaunchKernelGGL((conv_reduce_kernel<K>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pdw, pdb,
-                     a.dw, a.dbias, a.batch * l.ntiles, a.dim);
+                     a.dw, a.dbias, a.batch * l.nseg, a.dim);
   return hipGetLastError();
 }
 
@@ -245,8 +320,14 @@ hipError_t step_t(const ConvArgs& a, hipStream_t s) {
 
 ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
   ConvBwdLayout l;
-  l.ntiles = (seqlen + kBwdTile - 1) / kBwdTile;
-  const size_t parts = (size_t)batch * l.ntiles;
+  // time groups of kWaves tiles; a workgroup walks tgs of them (a segment), with tgs
+  // chosen for about 1536 workgroups in all
+  l.ntg = (seqlen + kBwdTile * kWaves - 1) / (kBwdTile * kWaves);
+  const int64_t units = l.ntg * ((dim + 63) / 64) * batch;
+  l.tgs = (units + 1535) / 1536;
+  if (l.tgs < 1) l.tgs = 1;
+  l.nseg = (l.ntg + l.tgs - 1) / l.tgs;
+  const size_t parts = (size_t)batch * l.nseg;
   l.off_dw = 0;
   l.off_db = (parts * width * dim * sizeof(float) + 255) & ~(size_t)255;
   l.total = (l.off_db + parts * dim * sizeof(float) + 255) & ~(size_t)255;

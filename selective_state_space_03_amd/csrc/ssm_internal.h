@@ -91,7 +91,9 @@ struct ConvArgs {
   bool silu, bf16;
 };
 struct ConvBwdLayout {
-  int64_t ntiles;      // time tiles per batch element
+  int64_t ntg;         // time groups (one tile per wave) per batch element
+  int64_t tgs;         // time groups per segment (one workgroup)
+  int64_t nseg;        // segments per batch element
   size_t off_dw, off_db, total;
 };
 ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t width);

@@ -51,6 +51,8 @@ FWD_CASES = [
     ("ragged_k4", "conv_b8_l2048_d1536_k4", dict(batch=2, seqlen=301, dim=130)),
     ("no_silu", "conv_b8_l2048_d1536_k4", dict(batch=2, seqlen=77, dim=70, silu=False)),
     ("bf16", "conv_bf16_b4_l4096_d4096_k4", dict(batch=2, seqlen=200, dim=192)),
+    ("bf16_odd_dim_one_channel_per_lane", "conv_bf16_b4_l4096_d4096_k4", dict(batch=2, seqlen=50, dim=77)),
+    ("odd_dim_one_channel_per_lane", "conv_b8_l2048_d1536_k4", dict(batch=2, seqlen=130, dim=129)),
     ("seqlen_one", "conv_b8_l2048_d1536_k4", dict(batch=3, seqlen=1, dim=65)),
 ] + [("width%d" % k, "conv_b8_l2048_d1536_k4", dict(batch=2, seqlen=150, dim=100, width=k)) for k in range(1, 9)]
 
