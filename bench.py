@@ -1,6 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|bf16|step|fwd5|bwd|copy] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                  [--only fwd|bf16|step|fwd5|bwd|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -59,6 +60,21 @@ def bwd_bytes(b, l, d, n, gated):
     return reads + writes
 
 
+def conv_bytes(b, l, d, k, es):
+    """depthwise causal conv1d: x read, out written, weight and bias read"""
+    return 2 * b * l * d * es + d * k * 4 + d * 4
+
+
+def conv_step_bytes(b, d, k, es):
+    """one decode step: state read and written, x read, out written, weight and bias read"""
+    return 2 * b * d * (k - 1) * es + 2 * b * d * es + d * k * 4 + d * 4
+
+
+def conv_bwd_bytes(b, l, d, k):
+    """x and dout read, dx written; weight and bias read, their gradients written"""
+    return 3 * b * l * d * 4 + 2 * (d * k * 4 + d * 4)
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -112,7 +128,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "copy"])
+    ap.add_argument("--only", default="all",
+                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                             "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -219,6 +237,59 @@ def main():
             ("bwd_b4_l2048_d2048", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, workspace_bytes=wsb)
 
+    def conv_case(name, min_bytes_rotation=1.2e9):
+        w = W.CONV_WORKLOADS[name]
+        inp = W.make_conv_inputs(w)
+        es = 2 if w.io == "bf16" else 4
+        step = w.kind == "conv_step"
+        nb = conv_step_bytes(w.batch, w.dim, w.width, es) if step else conv_bytes(w.batch, w.seqlen, w.dim, w.width, es)
+        nsets = max(2, int(np.ceil(min_bytes_rotation / nb)))
+        base = {"x": tio(inp["x"], w.io)}
+        if step:
+            base["st"] = tio(inp["state"], w.io)
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        wt, bias = t32(inp["weight"]), t32(inp["bias"])
+        outs = [torch.empty_like(base["x"]) for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            if step:
+                ops.conv1d_step(s["st"], s["x"], wt, bias, silu=w.silu, out=outs[i])
+            else:
+                ops.conv1d_fwd(s["x"], wt, bias, silu=w.silu, out=outs[i])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
+    def conv_bwd_case(name="conv_b8_l2048_d1536_k4"):
+        w = W.CONV_WORKLOADS[name]
+        inp = W.make_conv_inputs(w)
+        nb = conv_bwd_bytes(w.batch, w.seqlen, w.dim, w.width)
+        nsets = max(2, int(np.ceil(1.2e9 / nb)))
+        base = {"x": t32(inp["x"]), "dout": t32(inp["dout"])}
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        wt, bias = t32(inp["weight"]), t32(inp["bias"])
+        f = torch.float32
+        outs = [{"dx": torch.empty_like(base["x"]), "dw": torch.empty((w.dim, w.width), dtype=f, device=dev),
+                 "db": torch.empty((w.dim,), dtype=f, device=dev)} for _ in range(nsets)]
+        wsb = ops.conv1d_bwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.width)
+        wss = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+
+        def fn(i):
+            s, o = sets[i], outs[i]
+            ops.conv1d_bwd(s["x"], wt, s["dout"], bias, silu=w.silu, workspace=wss[i], dx=o["dx"], dweight=o["dw"],
+                           dbias=o["db"])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            ("conv_bwd_b8_l2048_d1536_k4", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS,
+             nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
     if args.only == "copy":
         # calibration kernel for the HBM byte counters: a plain 1 GiB device-to-device copy
         nbytes = 1 << 30
@@ -240,6 +311,14 @@ def main():
         results["step_b256_d5120"] = step_case()
     if args.only in ("all", "bwd"):
         results["bwd_b4_l2048_d2048"] = bwd_case()
+    if args.only in ("all", "conv"):
+        results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
+    if args.only in ("all", "conv_bf16"):
+        results["conv_bf16_b4_l4096_d4096_k4"] = conv_case("conv_bf16_b4_l4096_d4096_k4")
+    if args.only in ("all", "conv_step"):
+        results["conv_step_b256_d5120_k4"] = conv_case("conv_step_b256_d5120_k4")
+    if args.only in ("all", "conv_bwd"):
+        results["conv_bwd_b8_l2048_d1536_k4"] = conv_bwd_case()
 
     if head is None:
         # profiling runs of a single secondary case print a short line
@@ -278,7 +357,7 @@ def main():
         secondary[k] = {"gbs": round(v["gbs"], 1), "frac_of_8tbs": round(v["gbs"] / HBM_PEAK_GBS, 4),
                         "us_per_launch": round(v["ev_ms"] * 1e3, 1), "algorithmic_bytes": v["bytes"],
                         "elements_per_s": round(v["workload"].elements / (v["ev_ms"] * 1e-3), 1)}
-        if v["workload"].kind != "step":
+        if v["workload"].kind in ("fwd", "fwdbwd"):
             secondary[k]["state_updates_per_s"] = round(v["workload"].state_updates / (v["ev_ms"] * 1e-3), 1)
 
     out = {
