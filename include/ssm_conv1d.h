@@ -53,8 +53,8 @@ int ssm_conv1d_step(void* conv_state, const void* x, const float* weight, const 
 
 /* Backward of ssm_conv1d_fwd for dout = dLoss/dout (fp32):
  *   dx required; dweight, dbias optional (NULL: not written).  Outputs are
- *   overwritten.  dweight and dbias are fixed-order sums of per-(batch, time tile)
- *   partials, added in lexical order, without atomics.
+ *   overwritten.  dweight and dbias are fixed-order sums of per-(batch, time
+ *   segment) partials, added in lexical order, without atomics.
  *   workspace: at least ssm_conv1d_bwd_workspace_bytes() bytes, 256-byte aligned. */
 size_t ssm_conv1d_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
                                       int io_dtype);
