@@ -30,6 +30,7 @@
 // needs.  The loop issues no scalar memory loads: they would share the LDS wait
 // counter and complete out of order, forcing full waits.
 #include <type_traits>
+#include <utility>
 
 #include "ssm_device.h"
 #include "ssm_internal.h"
@@ -303,6 +304,253 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// States across lanes.  One wavefront holds 4 channels x 16 states: lane = 16*c + n
+// (row c of the wave is channel c, position n in the row is state n), so a whole
+// (b, d) recurrence lives in one row and every state is one VGPR of one lane.  A
+// workgroup is 4 waves = 16 channels.  Per time tile of 16 steps:
+//   * prep: lane 16*c + t computes Delta and Delta*x of step t of channel c once;
+//   * scan: step t reads those two values from lane t of its row with a DPP row
+//     broadcast folded into the multiply that consumes them (no LDS, no extra
+//     instruction), and B[t][n], C[t][n] from a wave-private LDS copy of the tile's
+//     rows, transposed so that 4 steps come in one 16-byte read;
+//   * readout: the 16 products C[t][n] h_t[n] of a lane are summed over the 16 lanes
+//     of the row by a transpose-reduce (halving exchanges over lane distances 8, 7
+//     (mirror), 2 and 1), which leaves the sum for step t in lane 16*c + t -- the
+//     lane that prepped step t and holds its x and z, so the skip, the gate and the
+//     store follow without data movement.
+// Nothing is shared between waves, so the loop has no barrier.  The sums are taken in
+// a fixed order: results are deterministic.
+
+// lane i of each 16-lane row gets row lane i^8 (rows rotate by 8); lanes 0-7 of a row
+// return lo + partner's lo, lanes 8-15 hi + partner's hi.  The bank masks make each
+// DPP add write only its half of the row, so one register holds both halves' results.
+__device__ __forceinline__ float row_keep_half_ror8(float lo, float hi) {
+  float r;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(r)
+      : "v"(lo), "v"(hi));
+  return r;
+}
+// partner = the mirror lane inside each half row (lane i^7); lanes with bit 2 clear
+// (banks 0 and 2) keep lo, the others hi
+__device__ __forceinline__ float row_keep_half_mirror8(float lo, float hi) {
+  float r;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(r)
+      : "v"(lo), "v"(hi));
+  return r;
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_amdgcn_update_dpp(0.f, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppRowBcast0 = 0x150;  // row_newbcast:0 (+t: every lane of a row reads its lane t)
+
+// p[j] in every lane of a 16-lane row -> lane i of the row returns sum over the row of
+// p[i].  Exchanges halve the values held at lane distances 8, 7, 2, 1; lane i keeps
+// the half that its bit 3, 2, 1, 0 selects, so the index it ends with is i itself.
+__device__ __forceinline__ float row_transpose_sum16(const float (&p)[16], int lane) {
+  float q[8], r[4], s[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = row_keep_half_ror8(p[j], p[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = row_keep_half_mirror8(q[j], q[j + 4]);
+  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = b1 ? r[j] : r[j + 2];
+    const float keep = b1 ? r[j + 2] : r[j];
+    s[j] = keep + dpp_f<kDppQuadXor2>(send);
+  }
+  const float send = b0 ? s[0] : s[1];
+  const float keep = b0 ? s[1] : s[0];
+  return keep + dpp_f<kDppQuadXor1>(send);
+}
+
+// one step of the recurrence in a state lane: Delta and Delta*x of step T come from
+// lane T of the row
+template <int T>
+__device__ __forceinline__ void lane_step(float& h, float dl, float dlx, float A2, float b, float& c) {
+  const float a = exp2_hw(dpp_f<kDppRowBcast0 + T>(dl) * A2);
+  h = fmaf(a, h, dpp_f<kDppRowBcast0 + T>(dlx) * b);
+  c *= h;  // C[t][n] h_t[n], summed over the row by the readout
+}
+template <int... I>
+__device__ __forceinline__ void lane_scan16(std::integer_sequence<int, I...>, float& h, float dl, float dlx,
+                                            float A2, const float (&bv)[16], float (&cv)[16]) {
+  (lane_step<I>(h, dl, dlx, A2, bv[I], cv[I]), ...);
+}
+
+template <typename T, bool GATED>
+__global__ void __launch_bounds__(256)
+fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
+                 const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
+                 const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
+                 const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_final, int L, int Dm,
+                 int N, int ngroups, int nblocks) {
+  constexpr int TT = 16;  // steps per tile = lanes per row
+  constexpr int R = 8;    // ring of loaded tiles (tile mod 8); the loop is unrolled by 8
+  constexpr int P = 6;    // tiles loaded ahead
+  constexpr int NB = 4;   // LDS tile buffers (tile mod 4)
+  constexpr int SP = 20;  // LDS row stride in floats (16 + 4: conflict-free column reads)
+  constexpr int ES = (int)sizeof(T);
+  // Global memory is read and written only in whole 64-byte rows of the group's 16
+  // channels: wave w moves rows 4w..4w+3 of every tile (lane 16*i + j: row 4w+i,
+  // channel or state j) and the rows pass through LDS to the lanes that use them:
+  //   act[buf][x | delta_raw | z][t][channel], bct[buf][B | C][n][t] (transposed),
+  //   yb[buf][t][channel].  Tile j lives in buffer j % NB (yb: j % 2).
+  __shared__ __attribute__((aligned(16))) float act[NB][3][TT * SP];
+  __shared__ __attribute__((aligned(16))) float bct[NB][2][16 * SP];
+  __shared__ float yb[2][TT * SP];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane >> 4;  // channel of the wave (scan / prep), row of the quarter (loads)
+  const int li = lane & 15;   // state (scan), step (prep, readout), channel or state (loads)
+  // Blocks are dispatched to the 8 XCDs round robin; give the blocks of one XCD
+  // consecutive channel groups, so groups that share lines are read through one L2.
+  const int xcd = blockIdx.x & 7, per = nblocks >> 3, rem = nblocks & 7;
+  const int lb = xcd * per + (xcd < rem ? xcd : rem) + (int)(blockIdx.x >> 3);
+  const int b = lb / ngroups;
+  const int g0 = (lb % ngroups) * 16;  // first channel of the group
+  const int d = g0 + wave * 4 + row;   // channel of this lane in the scan / prep layout
+  const bool dvalid = d < Dm;
+
+  // state lane: A2 and h of state li of channel d (states >= N stay 0: B = C = 0)
+  const bool nvalid = dvalid && li < N;
+  const float A2 = nvalid ? a2_from_alog(A_log[(int64_t)d * N + li]) : 0.f;
+  const int64_t hb = ((int64_t)b * Dm + d) * N + li;
+  float h = (nvalid && h0) ? h0[hb] : 0.f;
+  // prep lane: parameters of channel d
+  const float bias = (dvalid && dt_bias) ? dt_bias[d] : 0.f;
+  const float dsk = (dvalid && D_skip) ? D_skip[d] : 0.f;
+
+  const int ntiles = (L + TT - 1) / TT;
+  const int64_t row0 = (int64_t)b * L;
+  const int64_t slice = (int64_t)L * Dm * ES;
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rr = tile_rsrc(delta_raw + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rz = tile_rsrc(GATED ? z + row0 * Dm : x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t ry = tile_rsrc(y + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(Bm + row0 * N, (int64_t)L * N * ES);
+  const __amdgpu_buffer_rsrc_t rc = tile_rsrc(Cm + row0 * N, (int64_t)L * N * ES);
+  // load / store lane: row qt = 4*wave + row of the tile, channel g0 + li, state li
+  const int qt = wave * 4 + row;
+  const uint32_t aoff = (g0 + li < Dm) ? (uint32_t)((qt * Dm + g0 + li) * ES) : kOutside;
+  const uint32_t boff = (li < N) ? (uint32_t)((qt * N + li) * ES) : kOutside;
+  const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);
+  const uint32_t btile_bytes = (uint32_t)(TT * N * ES);
+  auto toff = [&](int j) __attribute__((always_inline)) {
+    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * tile_bytes;
+  };
+  auto btoff = [&](int j) __attribute__((always_inline)) {
+    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * btile_bytes;
+  };
+
+  // this wave's quarter of tile j, in ring slot j % R
+  float qx[R], qr[R], qz[R], qb[R], qc[R];
+  auto load_tile = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint32_t o = off_add(aoff, toff(j));
+    const uint32_t ob = off_add(boff, btoff(j));
+    qx[slot] = buf_ld<T>(rx, o);
+    qr[slot] = buf_ld<T>(rr, o);
+    qz[slot] = GATED ? buf_ld<T>(rz, o) : 0.f;
+    qb[slot] = buf_ld<T>(rb, ob);
+    qc[slot] = buf_ld<T>(rc, ob);
+  };
+  auto stage_tile = [&](int slot, int buf) __attribute__((always_inline)) {
+    act[buf][0][qt * SP + li] = qx[slot];
+    act[buf][1][qt * SP + li] = qr[slot];
+    if (GATED) act[buf][2][qt * SP + li] = qz[slot];
+    bct[buf][0][li * SP + qt] = qb[slot];
+    bct[buf][1][li * SP + qt] = qc[slot];
+  };
+  // B[t][li] and C[t][li] of the 16 steps of the tile in buffer buf (state lane)
+  float bv[16], cv[16];
+  auto read_bc = [&](int buf) __attribute__((always_inline)) {
+    const float* const pb = &bct[buf][0][li * SP];
+    const float* const pc = &bct[buf][1][li * SP];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 vb = *(const float4*)(pb + 4 * i);
+      const float4 vc = *(const float4*)(pc + 4 * i);
+      bv[4 * i] = vb.x; bv[4 * i + 1] = vb.y; bv[4 * i + 2] = vb.z; bv[4 * i + 3] = vb.w;
+      cv[4 * i] = vc.x; cv[4 * i + 1] = vc.y; cv[4 * i + 2] = vc.z; cv[4 * i + 3] = vc.w;
+    }
+  };
+  // prep of tile k in the prep lane (step li, channel d): Delta and Delta*x; padded
+  // steps and channels get Delta = 0, which leaves the state unchanged
+  const int pcol = li * SP + wave * 4 + row;
+  auto prep = [&](int k, int buf, float& dl, float& dlx, float& xk) __attribute__((always_inline)) {
+    const bool v = dvalid && k * TT + li < L;
+    xk = act[buf][0][pcol];
+    const float delta = softplus_f(act[buf][1][pcol] + bias);
+    dl = v ? delta : 0.f;
+    dlx = v ? delta * xk : 0.f;
+  };
+  // y of tile j from LDS, stored as 64-byte rows (rows past the end and k < 0 outside)
+  auto store_y = [&](int j, int ybuf) __attribute__((always_inline)) {
+    buf_st<T>(yb[ybuf][qt * SP + li], ry, off_add(aoff, toff(j)));
+  };
+
+  // prologue: tiles 0..P-1 in flight; tiles 0 and 1 staged; tile 0 prepped
+#pragma unroll
+  for (int u = 0; u < P; ++u) load_tile(u, u);
+  stage_tile(0, 0);
+  stage_tile(1, 1);
+  __syncthreads();
+  float dl, dlx, xk;
+  prep(0, 0, dl, dlx, xk);
+
+  // Iteration k (one barrier, at its end): load tile k+P; read B/C of tile k and
+  // prep tile k+1 from LDS (staged two iterations earlier); stage tile k+2 (its
+  // buffer last held tile k-2, done with before the previous barrier); store y of
+  // tile k-1; scan, read out and write y of tile k to LDS.
+  for (int kk = 0; kk < ntiles; kk += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = kk + u;
+      if (k >= ntiles) break;
+      load_tile(k + P, (u + P) % R);
+      read_bc(u % NB);
+      float dln, dlxn, xkn;
+      prep(k + 1, (u + 1) % NB, dln, dlxn, xkn);
+      const float zk = GATED ? act[u % NB][2][pcol] : 0.f;
+      stage_tile((u + 2) % R, (u + 2) % NB);
+      store_y(k - 1, (u + 1) & 1);
+      lane_scan16(std::make_integer_sequence<int, 16>(), h, dl, dlx, A2, bv, cv);
+      // readout of tile k in the prep lane of step li
+      const float s = row_transpose_sum16(cv, lane);
+      const float gate = GATED ? silu_f(zk) : 1.f;
+      yb[u & 1][pcol] = fmaf(dsk, xk, s) * gate;
+      dl = dln;
+      dlx = dlxn;
+      xk = xkn;
+      __syncthreads();
+    }
+  }
+  store_y(ntiles - 1, (ntiles - 1) & 1);
+  if (h_final && nvalid) h_final[hb] = h;
+}
+
+template <typename T, bool GATED>
+hipError_t launch_lanes(const FwdArgs& a, hipStream_t stream) {
+  const int ngroups = (int)((a.dim + 15) / 16);
+  const int64_t nblocks = (int64_t)ngroups * a.batch;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_lanes_kernel<T, GATED>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+                     (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C, a.A_log,
+                     a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen, (int)a.dim, a.dstate, ngroups,
+                     (int)nblocks);
+  return hipGetLastError();
+}
+
 template <typename T, int S, int G, bool GATED>
 hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   // time tile: 16 steps per barrier (LDS: dd 16 KB, partials 2*16*G*256 B); with 8 or
@@ -339,6 +587,7 @@ int pick_states_per_wave(const FwdArgs& a, int ns) {
 template <typename T, bool GATED>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int ns = a.dstate <= 4 ? 4 : (a.dstate <= 8 ? 8 : 16);
+  if (ns == 16 && !getenv("SSM_FWD_STATES_PER_WAVE")) return launch_lanes<T, GATED>(a, stream);
   const int s = pick_states_per_wave(a, ns);
   if (ns == 16) {
     switch (s) {
