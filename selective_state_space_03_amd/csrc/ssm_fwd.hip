@@ -61,6 +61,18 @@ template <> __device__ __forceinline__ float buf_ld<float>(__amdgpu_buffer_rsrc_
 template <> __device__ __forceinline__ float buf_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
+// raw element bits (zero-extended), converted to fp32 only where the value is used, so
+// that a load's wait is not pulled up to the load
+template <typename T> __device__ __forceinline__ uint32_t buf_ld_raw(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ uint32_t buf_ld_raw<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ uint32_t buf_ld_raw<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <typename T> __device__ __forceinline__ float raw_f32(uint32_t v) {
+  return std::is_same<T, float>::value ? __uint_as_float(v) : __uint_as_float(v << 16);
+}
 template <typename T> __device__ __forceinline__ void buf_st(float v, __amdgpu_buffer_rsrc_t r, uint32_t off);
 template <> __device__ __forceinline__ void buf_st<float>(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);  // bits, not a value cast
@@ -322,28 +334,48 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
 // Nothing is shared between waves, so the loop has no barrier.  The sums are taken in
 // a fixed order: results are deterministic.
 
-// lane i of each 16-lane row gets row lane i^8 (rows rotate by 8); lanes 0-7 of a row
-// return lo + partner's lo, lanes 8-15 hi + partner's hi.  The bank masks make each
-// DPP add write only its half of the row, so one register holds both halves' results.
-__device__ __forceinline__ float row_keep_half_ror8(float lo, float hi) {
-  float r;
+// Halving exchanges of the in-row transpose-reduce, written as DPP adds whose bank
+// masks make each instruction write only half of the row, so one register holds both
+// halves' results.  One s_nop covers the DPP read-after-VALU-write wait for the whole
+// block (its sources are not written inside it).
+// Stage 1: partner lane i^8 (rows rotate by 8); lanes 0-7 of a row keep p[j] + partner's
+// p[j], lanes 8-15 p[j+8] + partner's p[j+8] (j < 8).
+__device__ __forceinline__ void row_halve_ror8(const float (&p)[16], float (&q)[8]) {
   asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xc"
-      : "=&v"(r)
-      : "v"(lo), "v"(hi));
-  return r;
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(p[8]),
+        "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
 }
-// partner = the mirror lane inside each half row (lane i^7); lanes with bit 2 clear
-// (banks 0 and 2) keep lo, the others hi
-__device__ __forceinline__ float row_keep_half_mirror8(float lo, float hi) {
-  float r;
+// Stage 2: partner = the mirror lane inside each half row (lane i^7); lanes with bit 2
+// clear (banks 0 and 2) keep q[j] + partner's q[j], the others q[j+4] + partner's (j < 4).
+__device__ __forceinline__ void row_halve_mirror8(const float (&q)[8], float (&r)[4]) {
   asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
-      : "=&v"(r)
-      : "v"(lo), "v"(hi));
-  return r;
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
 }
 template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_amdgcn_update_dpp(0.f, v, CTRL, 0xf, 0xf, false);
@@ -357,10 +389,8 @@ constexpr int kDppRowBcast0 = 0x150;  // row_newbcast:0 (+t: every lane of a row
 // the half that its bit 3, 2, 1, 0 selects, so the index it ends with is i itself.
 __device__ __forceinline__ float row_transpose_sum16(const float (&p)[16], int lane) {
   float q[8], r[4], s[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = row_keep_half_ror8(p[j], p[j + 8]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = row_keep_half_mirror8(q[j], q[j + 4]);
+  row_halve_ror8(p, q);
+  row_halve_mirror8(q, r);
   const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -387,8 +417,8 @@ __device__ __forceinline__ void lane_scan16(std::integer_sequence<int, I...>, fl
   (lane_step<I>(h, dl, dlx, A2, bv[I], cv[I]), ...);
 }
 
-template <typename T, bool GATED>
-__global__ void __launch_bounds__(256)
+template <typename T, int W, bool GATED>
+__global__ void __launch_bounds__(64 * W)
 fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
                  const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
                  const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
@@ -398,16 +428,20 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   constexpr int R = 8;    // ring of loaded tiles (tile mod 8); the loop is unrolled by 8
   constexpr int P = 6;    // tiles loaded ahead
   constexpr int NB = 4;   // LDS tile buffers (tile mod 4)
-  constexpr int SP = 20;  // LDS row stride in floats (16 + 4: conflict-free column reads)
+  constexpr int CG = 4 * W;      // channels per group (4 per wave)
+  constexpr int RW = TT / W;     // tile rows moved by each wave
+  constexpr int SA = CG + 4;     // LDS row stride of activation tiles (conflict-free columns)
+  constexpr int SP = 20;         // LDS row stride of the transposed B/C tiles
   constexpr int ES = (int)sizeof(T);
-  // Global memory is read and written only in whole 64-byte rows of the group's 16
-  // channels: wave w moves rows 4w..4w+3 of every tile (lane 16*i + j: row 4w+i,
-  // channel or state j) and the rows pass through LDS to the lanes that use them:
+  static_assert(W == 4 || W == 8, "4 or 8 waves per group");
+  // Global memory is read and written only in whole rows of the group's CG channels
+  // (CG * ES bytes): wave w moves rows RW*w .. RW*w+RW-1 of every tile (lane CG*i + j:
+  // row RW*w + i, channel j) and the rows pass through LDS to the lanes that use them:
   //   act[buf][x | delta_raw | z][t][channel], bct[buf][B | C][n][t] (transposed),
   //   yb[buf][t][channel].  Tile j lives in buffer j % NB (yb: j % 2).
-  __shared__ __attribute__((aligned(16))) float act[NB][3][TT * SP];
+  __shared__ __attribute__((aligned(16))) float act[NB][3][TT * SA];
   __shared__ __attribute__((aligned(16))) float bct[NB][2][16 * SP];
-  __shared__ float yb[2][TT * SP];
+  __shared__ float yb[2][TT * SA];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -418,7 +452,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   const int xcd = blockIdx.x & 7, per = nblocks >> 3, rem = nblocks & 7;
   const int lb = xcd * per + (xcd < rem ? xcd : rem) + (int)(blockIdx.x >> 3);
   const int b = lb / ngroups;
-  const int g0 = (lb % ngroups) * 16;  // first channel of the group
+  const int g0 = (lb % ngroups) * CG;  // first channel of the group
   const int d = g0 + wave * 4 + row;   // channel of this lane in the scan / prep layout
   const bool dvalid = d < Dm;
 
@@ -433,6 +467,8 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
 
   const int ntiles = (L + TT - 1) / TT;
   const int64_t row0 = (int64_t)b * L;
+  // one resource per tensor over this batch element's slice; rows past the end of the
+  // sequence read 0 and drop their stores, padding channels have an offset >= 2^31
   const int64_t slice = (int64_t)L * Dm * ES;
   const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t rr = tile_rsrc(delta_raw + row0 * Dm, slice);
@@ -440,36 +476,38 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   const __amdgpu_buffer_rsrc_t ry = tile_rsrc(y + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t rb = tile_rsrc(Bm + row0 * N, (int64_t)L * N * ES);
   const __amdgpu_buffer_rsrc_t rc = tile_rsrc(Cm + row0 * N, (int64_t)L * N * ES);
-  // load / store lane: row qt = 4*wave + row of the tile, channel g0 + li, state li
-  const int qt = wave * 4 + row;
-  const uint32_t aoff = (g0 + li < Dm) ? (uint32_t)((qt * Dm + g0 + li) * ES) : kOutside;
-  const uint32_t boff = (li < N) ? (uint32_t)((qt * N + li) * ES) : kOutside;
-  const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);
+  const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);  // j * tile_bytes < 2^31 for j < ntiles
   const uint32_t btile_bytes = (uint32_t)(TT * N * ES);
-  auto toff = [&](int j) __attribute__((always_inline)) {
-    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * tile_bytes;
-  };
-  auto btoff = [&](int j) __attribute__((always_inline)) {
-    return (j < 0 || j >= ntiles) ? kOutside : (uint32_t)j * btile_bytes;
-  };
+  // load / store lane of the activations: row qt of the tile, channel g0 + qc
+  const int qt = wave * RW + lane / CG, qc = lane % CG;
+  const uint32_t aoff = (g0 + qc < Dm) ? (uint32_t)((qt * Dm + g0 + qc) * ES) : kOutside;
+  // B/C lane: row bqt, state li (lanes 0 .. 16*RW-1; the others load nothing)
+  const int bqt = wave * RW + row;
+  const bool bl = lane < 16 * RW;
+  const uint32_t boff = (bl && li < N) ? (uint32_t)((bqt * N + li) * ES) : kOutside;
 
   // this wave's quarter of tile j, in ring slot j % R
-  float qx[R], qr[R], qz[R], qb[R], qc[R];
+  uint32_t qx[R], qr[R], qz[R], qb[R], qcv[R];
+  // (loads ahead of the last tile re-read the last tile -- cache hits, never scanned --
+  // so the loop has no branch and the tile offset stays below 2^31)
   auto load_tile = [&](int j, int slot) __attribute__((always_inline)) {
-    const uint32_t o = off_add(aoff, toff(j));
-    const uint32_t ob = off_add(boff, btoff(j));
-    qx[slot] = buf_ld<T>(rx, o);
-    qr[slot] = buf_ld<T>(rr, o);
-    qz[slot] = GATED ? buf_ld<T>(rz, o) : 0.f;
-    qb[slot] = buf_ld<T>(rb, ob);
-    qc[slot] = buf_ld<T>(rc, ob);
+    const int jc = j < ntiles ? j : ntiles - 1;
+    const uint32_t o = aoff + (uint32_t)jc * tile_bytes;
+    const uint32_t ob = boff + (uint32_t)jc * btile_bytes;
+    qx[slot] = buf_ld_raw<T>(rx, o);
+    qr[slot] = buf_ld_raw<T>(rr, o);
+    qz[slot] = GATED ? buf_ld_raw<T>(rz, o) : 0u;
+    qb[slot] = buf_ld_raw<T>(rb, ob);
+    qcv[slot] = buf_ld_raw<T>(rc, ob);
   };
   auto stage_tile = [&](int slot, int buf) __attribute__((always_inline)) {
-    act[buf][0][qt * SP + li] = qx[slot];
-    act[buf][1][qt * SP + li] = qr[slot];
-    if (GATED) act[buf][2][qt * SP + li] = qz[slot];
-    bct[buf][0][li * SP + qt] = qb[slot];
-    bct[buf][1][li * SP + qt] = qc[slot];
+    act[buf][0][qt * SA + qc] = raw_f32<T>(qx[slot]);
+    act[buf][1][qt * SA + qc] = raw_f32<T>(qr[slot]);
+    if (GATED) act[buf][2][qt * SA + qc] = raw_f32<T>(qz[slot]);
+    if (bl) {
+      bct[buf][0][li * SP + bqt] = raw_f32<T>(qb[slot]);
+      bct[buf][1][li * SP + bqt] = raw_f32<T>(qcv[slot]);
+    }
   };
   // B[t][li] and C[t][li] of the 16 steps of the tile in buffer buf (state lane)
   float bv[16], cv[16];
@@ -486,17 +524,18 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   };
   // prep of tile k in the prep lane (step li, channel d): Delta and Delta*x; padded
   // steps and channels get Delta = 0, which leaves the state unchanged
-  const int pcol = li * SP + wave * 4 + row;
+  const int pcol = li * SA + wave * 4 + row;
+  // (padding channels have x = 0, so their state stays 0 without a mask; steps past the
+  // end of the sequence occur only in the last tile)
   auto prep = [&](int k, int buf, float& dl, float& dlx, float& xk) __attribute__((always_inline)) {
-    const bool v = dvalid && k * TT + li < L;
     xk = act[buf][0][pcol];
-    const float delta = softplus_f(act[buf][1][pcol] + bias);
-    dl = v ? delta : 0.f;
-    dlx = v ? delta * xk : 0.f;
+    dl = softplus_f(act[buf][1][pcol] + bias);
+    if ((k + 1) * TT > L) dl = k * TT + li < L ? dl : 0.f;
+    dlx = dl * xk;
   };
   // y of tile j from LDS, stored as 64-byte rows (rows past the end and k < 0 outside)
   auto store_y = [&](int j, int ybuf) __attribute__((always_inline)) {
-    buf_st<T>(yb[ybuf][qt * SP + li], ry, off_add(aoff, toff(j)));
+    if (j >= 0) buf_st<T>(yb[ybuf][qt * SA + qc], ry, aoff + (uint32_t)j * tile_bytes);
   };
 
   // prologue: tiles 0..P-1 in flight; tiles 0 and 1 staged; tile 0 prepped
@@ -539,16 +578,23 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   if (h_final && nvalid) h_final[hb] = h;
 }
 
-template <typename T, bool GATED>
-hipError_t launch_lanes(const FwdArgs& a, hipStream_t stream) {
-  const int ngroups = (int)((a.dim + 15) / 16);
+template <typename T, int W, bool GATED>
+hipError_t launch_lanes_w(const FwdArgs& a, hipStream_t stream) {
+  const int ngroups = (int)((a.dim + 4 * W - 1) / (4 * W));
   const int64_t nblocks = (int64_t)ngroups * a.batch;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_lanes_kernel<T, GATED>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_lanes_kernel<T, W, GATED>), dim3((unsigned)nblocks), dim3(64 * W), 0, stream,
                      (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C, a.A_log,
                      a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen, (int)a.dim, a.dstate, ngroups,
                      (int)nblocks);
   return hipGetLastError();
+}
+
+template <typename T, bool GATED>
+hipError_t launch_lanes(const FwdArgs& a, hipStream_t stream) {
+  const char* e = getenv("SSM_FWD_LANES_WAVES");
+  if (e && atoi(e) == 8) return launch_lanes_w<T, 8, GATED>(a, stream);
+  return launch_lanes_w<T, 4, GATED>(a, stream);
 }
 
 template <typename T, int S, int G, bool GATED>
