@@ -13,7 +13,8 @@ Functions (definitions and citations are in the headers of ``ssm_oracle.c`` and
 ``conv1d_oracle.c``):
   fwd(...)  -> {"y", "h_final"}          forward scan, sequential in t
   step(...) -> {"y", "state"}            single decode step (separate code)
-  bwd(...)  -> {"dx", "ddelta_raw", "dz", "dB", "dC", "dA_log", "dD", "d_dt_bias"}
+  bwd(...)  -> {"dx", "ddelta_raw", "dz", "dB", "dC", "dA_log", "dD", "d_dt_bias", "dh0"}
+  (fwd, step and bwd take the step-size clamp dt_min, dt_max; bwd takes dh_final)
   softplus / sigmoid / silu / silu_grad  scalar helpers, exposed for pinning
   conv_fwd(...)  -> out                  depthwise causal conv1d (+ SiLU)
   conv_step(...) -> {"out", "state"}     one decode step of it (separate code)
@@ -56,11 +57,12 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         L = ctypes.c_long
-        lib.ssm_oracle_fwd.argtypes = [P] * 11 + [L] * 4 + [ctypes.c_int]
+        Dbl = ctypes.c_double
+        lib.ssm_oracle_fwd.argtypes = [P] * 11 + [L] * 4 + [Dbl, Dbl, ctypes.c_int]
         lib.ssm_oracle_fwd.restype = ctypes.c_int
-        lib.ssm_oracle_step.argtypes = [P] * 10 + [L] * 3 + [ctypes.c_int]
+        lib.ssm_oracle_step.argtypes = [P] * 10 + [L] * 3 + [Dbl, Dbl, ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
-        lib.ssm_oracle_bwd.argtypes = [P] * 18 + [L] * 4 + [ctypes.c_int]
+        lib.ssm_oracle_bwd.argtypes = [P] * 20 + [L] * 4 + [Dbl, Dbl, ctypes.c_int]
         lib.ssm_oracle_bwd.restype = ctypes.c_int
         lib.conv1d_oracle_fwd.argtypes = [P] * 4 + [L] * 4 + [ctypes.c_int]
         lib.conv1d_oracle_fwd.restype = ctypes.c_int
@@ -94,7 +96,8 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def fwd(x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, h0=None, nthreads=None):
+def fwd(x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, h0=None, nthreads=None,
+        dt_min=0.0, dt_max=float("inf")):
     x = _f64(x)
     b, l, d = x.shape
     n = np.asarray(A_log).shape[1]
@@ -110,13 +113,14 @@ def fwd(x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, h0=None, nthrea
     h_final = np.empty((b, d, n), np.float64)
     rc = _load().ssm_oracle_fwd(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
                                 _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
-                                b, l, d, n, nthreads or default_threads())
+                                b, l, d, n, float(dt_min), float(dt_max), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("ssm_oracle_fwd failed with %d" % rc)
     return {"y": y, "h_final": h_final}
 
 
-def step(state, x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, nthreads=None):
+def step(state, x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, nthreads=None,
+         dt_min=0.0, dt_max=float("inf")):
     state = np.array(state, dtype=np.float64, copy=True, order="C")
     b, d, n = state.shape
     x = _f64(x, (b, d))
@@ -130,13 +134,14 @@ def step(state, x, delta_raw, B, C, A_log, D=None, dt_bias=None, z=None, nthread
     y = np.empty((b, d), np.float64)
     rc = _load().ssm_oracle_step(_ptr(state), _ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C),
                                  _ptr(A_log), _ptr(D), _ptr(dt_bias), _ptr(y), b, d, n,
-                                 nthreads or default_threads())
+                                 float(dt_min), float(dt_max), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("ssm_oracle_step failed with %d" % rc)
     return {"y": y, "state": state}
 
 
-def bwd(x, delta_raw, B, C, A_log, dy, D=None, dt_bias=None, z=None, h0=None, nthreads=None):
+def bwd(x, delta_raw, B, C, A_log, dy, D=None, dt_bias=None, z=None, h0=None, nthreads=None,
+        dt_min=0.0, dt_max=float("inf"), dh_final=None):
     x = _f64(x)
     b, l, d = x.shape
     n = np.asarray(A_log).shape[1]
@@ -149,17 +154,20 @@ def bwd(x, delta_raw, B, C, A_log, dy, D=None, dt_bias=None, z=None, h0=None, nt
     dt_bias = _f64(dt_bias, (d,))
     h0 = _f64(h0, (b, d, n))
     dy = _f64(dy, (b, l, d))
+    dh_final = _f64(dh_final, (b, d, n))
     out = {
         "dx": np.empty((b, l, d)), "ddelta_raw": np.empty((b, l, d)),
         "dz": np.empty((b, l, d)) if z is not None else None,
         "dB": np.empty((b, l, n)), "dC": np.empty((b, l, n)),
         "dA_log": np.empty((d, n)), "dD": np.empty((d,)), "d_dt_bias": np.empty((d,)),
+        "dh0": np.empty((b, d, n)),
     }
     rc = _load().ssm_oracle_bwd(
         _ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log), _ptr(D), _ptr(dt_bias),
-        _ptr(h0), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta_raw"]), _ptr(out["dz"]),
+        _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddelta_raw"]), _ptr(out["dz"]),
         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA_log"]), _ptr(out["dD"]),
-        _ptr(out["d_dt_bias"]), b, l, d, n, nthreads or default_threads())
+        _ptr(out["d_dt_bias"]), _ptr(out["dh0"]), b, l, d, n, float(dt_min), float(dt_max),
+        nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("ssm_oracle_bwd failed with %d" % rc)
     return out

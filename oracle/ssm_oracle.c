@@ -25,7 +25,16 @@
  *     plain fp32-or-better sums taken in lexical (batch, chunk) order; here they
  *     are fp64 sums in (batch, time) order.
  *   - mamba3_preprocess_backward.slang (dt adjoint): d softplus / d r = 1 - exp(-softplus(r)),
- *     i.e. the logistic sigmoid of r.
+ *     i.e. the logistic sigmoid of r; and its optional step-size clamp: Delta is
+ *     softplus clamped to [dt_min, dt_max], and the gradient reaching delta_raw is
+ *     masked to steps whose softplus lies inside the bounds (bounds included).
+ *     dt_min = 0, dt_max = +inf (the default dt_limit of deterministic_backward.py's
+ *     ordered_cumsum) is no clamp at all, since softplus > 0.
+ *   - deterministic_backward.py (ordered_conv's initial_states / dfinal_states
+ *     arguments): a sequence may start from a given state and receive a gradient on
+ *     its final state; the backward then also returns the gradient of the initial
+ *     state.  Here: dh_final = dLoss/dh_final enters the reverse pass as the carry
+ *     beyond the last step, and dh0 = dLoss/dh0 is the carry leaving step 0.
  *
  * Layouts (row-major, last index fastest):
  *   x, delta_raw, z, y, dy, dx, ddelta_raw, dz : [batch, seqlen, dim]
@@ -34,8 +43,9 @@
  *   D, dt_bias, dD, d_dt_bias                  : [dim]
  *   h0, h_final, state                         : [batch, dim, dstate]
  * Optional inputs may be NULL: z (no gate), D (zero skip), dt_bias (zero bias),
- * h0 (zero initial state).  Optional outputs may be NULL: h_final, and in the
- * backward dz (required when z is given), dB, dC, dA_log, dD, d_dt_bias.
+ * h0 (zero initial state), dh_final (zero).  Optional outputs may be NULL: h_final,
+ * and in the backward dz (required when z is given), dB, dC, dA_log, dD, d_dt_bias,
+ * dh0.  dt_min <= dt_max are the clamp bounds (0 and +inf: no clamp).
  *
  * Threads: independent channels d are split statically across nthreads POSIX
  * threads (nthreads <= 0 means 1).  Each channel's scan is sequential in t.
@@ -76,14 +86,23 @@ double ssm_oracle_silu_grad(double z) {
 /* ---- problem description shared by the thread workers ---- */
 
 typedef struct {
-  const double *x, *delta_raw, *z, *B, *C, *A_log, *D, *dt_bias, *h0, *dy;
+  const double *x, *delta_raw, *z, *B, *C, *A_log, *D, *dt_bias, *h0, *dy, *dh_final;
   double *y, *h_final, *state;
-  double *dx, *ddelta_raw, *dz, *dB, *dC, *dA_log, *dD, *d_dt_bias;
+  double *dx, *ddelta_raw, *dz, *dB, *dC, *dA_log, *dD, *d_dt_bias, *dh0;
+  double dt_min, dt_max; /* clamp of Delta */
   long batch, seqlen, dim, dstate;
   long d_begin, d_end;  /* channel range owned by one worker */
   double *dB_part, *dC_part; /* per-worker [batch, seqlen, dstate] partial sums */
   int status;
 } ssm_job;
+
+/* ---- discretisation: Delta = clamp(softplus(r), dt_min, dt_max); *inside is 1 when
+ * softplus(r) lies in [dt_min, dt_max] (the gradient mask), else 0 ---- */
+static double discretise(const ssm_job *j, double r, double *inside) {
+  const double sp = ssm_oracle_softplus(r);
+  if (inside) *inside = (sp >= j->dt_min && sp <= j->dt_max) ? 1.0 : 0.0;
+  return sp < j->dt_min ? j->dt_min : (sp > j->dt_max ? j->dt_max : sp);
+}
 
 /* ---- forward: one channel d of one batch element b ---- */
 
@@ -100,7 +119,7 @@ static void fwd_channel(const ssm_job *j, long b, long d, double *h, double *A) 
     const double *Bt = j->B + (b * L + t) * N; /* [b, t, :] */
     const double *Ct = j->C + (b * L + t) * N;
     const double xv = j->x[i];
-    const double delta = ssm_oracle_softplus(j->delta_raw[i] + bias);
+    const double delta = discretise(j, j->delta_raw[i] + bias, NULL);
     double s = 0.0;
     for (long n = 0; n < N; ++n) {
       h[n] = exp(delta * A[n]) * h[n] + delta * Bt[n] * xv;
@@ -132,7 +151,7 @@ static void step_channel(const ssm_job *j, long b, long d) {
   double *st = j->state + (b * Dm + d) * N;    /* [b, d, :] */
   const double *Bb = j->B + b * N, *Cb = j->C + b * N;
   const double xv = j->x[i];
-  const double delta = ssm_oracle_softplus(j->delta_raw[i] + (j->dt_bias ? j->dt_bias[d] : 0.0));
+  const double delta = discretise(j, j->delta_raw[i] + (j->dt_bias ? j->dt_bias[d] : 0.0), NULL);
   double s = 0.0;
   for (long n = 0; n < N; ++n) {
     const double A = -exp(j->A_log[d * N + n]);
@@ -162,10 +181,12 @@ static void *step_worker(void *arg) {
  *   dB[b,t,n]        += G_t[n] Delta_t x_t                (summed over d)
  *   dx_t              = g_t D + Delta_t sum_n G_t[n] B_t[n]
  *   dDelta_t          = sum_n G_t[n] (A[n] a_t[n] h_{t-1}[n] + B_t[n] x_t)
- *   ddelta_raw_t      = dDelta_t * sigmoid(delta_raw_t + dt_bias)
+ *   ddelta_raw_t      = dDelta_t * mask_t * sigmoid(delta_raw_t + dt_bias)
+ *                       (mask_t = 1 when softplus lies inside the clamp bounds, else 0)
  *   dA[n]            += G_t[n] Delta_t a_t[n] h_{t-1}[n];  dA_log = dA * A  (dA/dA_log = A)
  *   dD               += g_t x_t;   d_dt_bias += ddelta_raw_t
- * The gradient of h_final is taken as zero and no gradient of h0 is produced.
+ * The carry starts at G = dh_final (zero when absent); after step 0 it is a_0 G_0 =
+ * dLoss/dh0, written to dh0.
  */
 static int bwd_channel(ssm_job *j, long b, long d, double *hs, double *s_pre, double *A,
                        double *G, double *dA_acc) {
@@ -181,7 +202,7 @@ static int bwd_channel(ssm_job *j, long b, long d, double *hs, double *s_pre, do
     const long i = (b * L + t) * Dm + d;
     const double *Bt = j->B + (b * L + t) * N, *Ct = j->C + (b * L + t) * N;
     const double xv = j->x[i];
-    const double delta = ssm_oracle_softplus(j->delta_raw[i] + bias);
+    const double delta = discretise(j, j->delta_raw[i] + bias, NULL);
     double s = 0.0;
     for (long n = 0; n < N; ++n) {
       const double hn = exp(delta * A[n]) * hs[t * N + n] + delta * Bt[n] * xv;
@@ -191,7 +212,7 @@ static int bwd_channel(ssm_job *j, long b, long d, double *hs, double *s_pre, do
     s_pre[t] = s + Dd * xv;
   }
   /* reverse */
-  for (long n = 0; n < N; ++n) G[n] = 0.0;
+  for (long n = 0; n < N; ++n) G[n] = j->dh_final ? j->dh_final[(b * Dm + d) * N + n] : 0.0;
   double dD_acc = 0.0, dbias_acc = 0.0;
   for (long t = L - 1; t >= 0; --t) {
     const long i = (b * L + t) * Dm + d;
@@ -199,7 +220,8 @@ static int bwd_channel(ssm_job *j, long b, long d, double *hs, double *s_pre, do
     const double *Bt = j->B + bt, *Ct = j->C + bt;
     const double xv = j->x[i];
     const double r = j->delta_raw[i] + bias;
-    const double delta = ssm_oracle_softplus(r);
+    double inside;
+    const double delta = discretise(j, r, &inside);
     const double dyv = j->dy[i];
     double g;
     if (j->z) {
@@ -223,12 +245,14 @@ static int bwd_channel(ssm_job *j, long b, long d, double *hs, double *s_pre, do
       G[n] *= a; /* contribution to dLoss/dh_{t-1}[n] through h_t */
     }
     j->dx[i] = g * Dd + dxacc;
-    const double dr = ddelta * ssm_oracle_sigmoid(r);
+    const double dr = ddelta * inside * ssm_oracle_sigmoid(r);
     j->ddelta_raw[i] = dr;
     dbias_acc += dr;
   }
   if (j->dD) j->dD[d] += dD_acc;
   if (j->d_dt_bias) j->d_dt_bias[d] += dbias_acc;
+  if (j->dh0)
+    for (long n = 0; n < N; ++n) j->dh0[(b * Dm + d) * N + n] = G[n];
   return 0;
 }
 
@@ -291,42 +315,49 @@ static int dims_ok(long batch, long seqlen, long dim, long dstate) {
   return batch > 0 && seqlen > 0 && dim > 0 && dstate > 0;
 }
 
+static int clamp_ok(double dt_min, double dt_max) {
+  return dt_min >= 0.0 && dt_min <= dt_max; /* false for NaN */
+}
+
 int ssm_oracle_fwd(const double *x, const double *delta_raw, const double *z, const double *B,
                    const double *C, const double *A_log, const double *D, const double *dt_bias,
                    const double *h0, double *y, double *h_final, long batch, long seqlen, long dim,
-                   long dstate, int nthreads) {
+                   long dstate, double dt_min, double dt_max, int nthreads) {
   if (!x || !delta_raw || !B || !C || !A_log || !y) return -1;
-  if (!dims_ok(batch, seqlen, dim, dstate)) return -1;
+  if (!dims_ok(batch, seqlen, dim, dstate) || !clamp_ok(dt_min, dt_max)) return -1;
   ssm_job j;
   memset(&j, 0, sizeof(j));
   j.x = x; j.delta_raw = delta_raw; j.z = z; j.B = B; j.C = C; j.A_log = A_log; j.D = D;
   j.dt_bias = dt_bias; j.h0 = h0; j.y = y; j.h_final = h_final;
   j.batch = batch; j.seqlen = seqlen; j.dim = dim; j.dstate = dstate;
+  j.dt_min = dt_min; j.dt_max = dt_max;
   return run_split(&j, dim, nthreads, fwd_worker);
 }
 
 int ssm_oracle_step(double *state, const double *x, const double *delta_raw, const double *z,
                     const double *B, const double *C, const double *A_log, const double *D,
                     const double *dt_bias, double *y, long batch, long dim, long dstate,
-                    int nthreads) {
+                    double dt_min, double dt_max, int nthreads) {
   if (!state || !x || !delta_raw || !B || !C || !A_log || !y) return -1;
-  if (!dims_ok(batch, 1, dim, dstate)) return -1;
+  if (!dims_ok(batch, 1, dim, dstate) || !clamp_ok(dt_min, dt_max)) return -1;
   ssm_job j;
   memset(&j, 0, sizeof(j));
   j.state = state; j.x = x; j.delta_raw = delta_raw; j.z = z; j.B = B; j.C = C;
   j.A_log = A_log; j.D = D; j.dt_bias = dt_bias; j.y = y;
   j.batch = batch; j.seqlen = 1; j.dim = dim; j.dstate = dstate;
+  j.dt_min = dt_min; j.dt_max = dt_max;
   return run_split(&j, dim, nthreads, step_worker);
 }
 
 int ssm_oracle_bwd(const double *x, const double *delta_raw, const double *z, const double *B,
                    const double *C, const double *A_log, const double *D, const double *dt_bias,
-                   const double *h0, const double *dy, double *dx, double *ddelta_raw, double *dz,
-                   double *dB, double *dC, double *dA_log, double *dD, double *d_dt_bias,
-                   long batch, long seqlen, long dim, long dstate, int nthreads) {
+                   const double *h0, const double *dy, const double *dh_final, double *dx,
+                   double *ddelta_raw, double *dz, double *dB, double *dC, double *dA_log,
+                   double *dD, double *d_dt_bias, double *dh0, long batch, long seqlen, long dim,
+                   long dstate, double dt_min, double dt_max, int nthreads) {
   if (!x || !delta_raw || !B || !C || !A_log || !dy || !dx || !ddelta_raw) return -1;
   if (z && !dz) return -1;
-  if (!dims_ok(batch, seqlen, dim, dstate)) return -1;
+  if (!dims_ok(batch, seqlen, dim, dstate) || !clamp_ok(dt_min, dt_max)) return -1;
   if (nthreads <= 0) nthreads = 1;
   if (nthreads > dim) nthreads = (int)dim;
   const size_t S = (size_t)batch * seqlen * dstate;
@@ -341,9 +372,10 @@ int ssm_oracle_bwd(const double *x, const double *delta_raw, const double *z, co
   for (int k = 0; k < nthreads; ++k) {
     ssm_job *j = &jobs[k];
     j->x = x; j->delta_raw = delta_raw; j->z = z; j->B = B; j->C = C; j->A_log = A_log;
-    j->D = D; j->dt_bias = dt_bias; j->h0 = h0; j->dy = dy;
+    j->D = D; j->dt_bias = dt_bias; j->h0 = h0; j->dy = dy; j->dh_final = dh_final;
     j->dx = dx; j->ddelta_raw = ddelta_raw; j->dz = dz; j->dA_log = dA_log; j->dD = dD;
-    j->d_dt_bias = d_dt_bias;
+    j->d_dt_bias = d_dt_bias; j->dh0 = dh0;
+    j->dt_min = dt_min; j->dt_max = dt_max;
     j->batch = batch; j->seqlen = seqlen; j->dim = dim; j->dstate = dstate;
     j->d_begin = dim * k / nthreads;
     j->d_end = dim * (k + 1) / nthreads;

@@ -9,9 +9,16 @@ a wrong sign or index, readout from the stale state, a transposed operand):
   * composition: scan(L1+L2) == scan(L2, h0 = h_final(scan(L1)));
   * linearity in x (ungated, h0 = 0);
   * hand-derived worked examples (tests/golden/hand_cases.json);
-  * backward: central finite differences of sum(dy*y) for every input and
+  * backward: central finite differences of sum(dy*y) (and of sum(dy*y) +
+    sum(dh_final*h_final), giving dh0) for every input and
     parameter element, gated and ungated; special case C = 0; an adjoint
-    (directional-derivative) identity; thread-count independence.
+    (directional-derivative) identity; thread-count independence;
+  * a backward split in two segments (dh0 of the second part as dh_final of the
+    first) equals the backward of the whole sequence;
+  * step-size clamp: central differences with steps clamped below, above and not
+    at all (clamped steps pass no gradient to delta_raw); dt_min = dt_max = c gives
+    the constant-step closed form whatever delta_raw is; a clamp that never binds
+    changes nothing; the clamped L=1 scan equals the clamped step.
 The oracle's scalar helpers are pinned to library routines (numpy logaddexp,
 the logistic function) and to the softplus identity sigma(r) = 1 - exp(-softplus(r)).
 """
@@ -318,3 +325,188 @@ def test_backward_thread_count_consistent():
             np.testing.assert_allclose(g1[k], g4[k], rtol=1e-13, atol=1e-13)
         else:
             assert np.array_equal(g1[k], g4[k]), k
+
+
+# ------------------------------------------- sequences carried across segments
+
+def _fd_grads(p, loss, names):
+    """central differences of a scalar loss for every element of the named inputs"""
+    out = {}
+    for name in names:
+        base = p[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            hstep = 1e-6 * max(1.0, abs(base[idx]))
+            q = dict(p)
+            up = base.copy(); up[idx] += hstep
+            dn = base.copy(); dn[idx] -= hstep
+            q[name] = up
+            lp = loss(q)
+            q[name] = dn
+            lm = loss(q)
+            fd[idx] = (lp - lm) / (2 * hstep)
+        out[name] = fd
+    return out
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_with_final_state_gradient_matches_central_differences(gated):
+    """Loss sum(dy*y) + sum(dh_final*h_final): every gradient, and dh0, against central
+    differences (initial_states / dfinal_states of deterministic_backward.py)."""
+    rng = np.random.default_rng(61 if gated else 62)
+    b, l, d, n = 2, 5, 3, 2
+    p = rand_problem(rng, b, l, d, n, gated=gated, h0=True)
+    dy = rng.standard_normal((b, l, d))
+    dhf = rng.standard_normal((b, d, n))
+    g = run_bwd(p, dy, dh_final=dhf)
+
+    def loss(q):
+        r = run_fwd(q)
+        return float(np.sum(dy * r["y"]) + np.sum(dhf * r["h_final"]))
+
+    names = [k for k in list(GRAD_OF) + ["h0"] if p.get(k) is not None]
+    fd = _fd_grads(p, loss, names)
+    for name in names:
+        gname = GRAD_OF.get(name, "dh0")
+        scale = max(1.0, np.abs(fd[name]).max())
+        np.testing.assert_allclose(g[gname], fd[name], rtol=1e-6, atol=1e-6 * scale, err_msg=name)
+
+
+def test_backward_composes_over_segments():
+    """Backward of a whole sequence = backward of its second part (started from the
+    first part's final state) followed by backward of the first part with the second
+    part's dh0 as its dh_final: per-step gradients match, parameter gradients add."""
+    rng = np.random.default_rng(63)
+    b, d, n, L1, L2 = 2, 5, 4, 23, 41
+    p = rand_problem(rng, b, L1 + L2, d, n, gated=True, h0=True)
+    dy = rng.standard_normal((b, L1 + L2, d))
+    dhf = rng.standard_normal((b, d, n))
+    full = run_bwd(p, dy, dh_final=dhf)
+    seq = ("x", "delta_raw", "B", "C", "z")
+    p1 = {k: (v[:, :L1] if k in seq else v) for k, v in p.items()}
+    p2 = {k: (v[:, L1:] if k in seq else v) for k, v in p.items()}
+    p2["h0"] = run_fwd(p1)["h_final"]
+    g2 = run_bwd(p2, dy[:, L1:], dh_final=dhf)
+    g1 = run_bwd(p1, dy[:, :L1], dh_final=g2["dh0"])
+    for k in ("dx", "ddelta_raw", "dz", "dB", "dC"):
+        np.testing.assert_allclose(np.concatenate([g1[k], g2[k]], 1), full[k], rtol=1e-11, atol=1e-12, err_msg=k)
+    for k in ("dA_log", "dD", "d_dt_bias"):
+        np.testing.assert_allclose(g1[k] + g2[k], full[k], rtol=1e-11, atol=1e-12, err_msg=k)
+    np.testing.assert_allclose(g1["dh0"], full["dh0"], rtol=1e-11, atol=1e-12)
+
+
+def test_zero_final_gradient_is_the_default():
+    rng = np.random.default_rng(64)
+    p = rand_problem(rng, 2, 9, 3, 4)
+    dy = rng.standard_normal((2, 9, 3))
+    a = run_bwd(p, dy)
+    z = run_bwd(p, dy, dh_final=np.zeros((2, 3, 4)))
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], z[k]), k
+
+
+# ------------------------------------------------------------- step-size clamp
+
+def _clamp_bounds(p, lo_q=0.3, hi_q=0.7, gap=1e-4):
+    """bounds at quantiles of softplus over the problem, nudged so that no step's
+    softplus lies within `gap` of a bound (central differences never cross a kink)"""
+    sp = softplus_ref(p["delta_raw"] + p["dt_bias"][None, None, :]).ravel()
+    lo, hi = np.quantile(sp, lo_q), np.quantile(sp, hi_q)
+    for _ in range(100):
+        if np.min(np.abs(sp - lo)) > gap and np.min(np.abs(sp - hi)) > gap:
+            break
+        lo *= 1.0 + 3 * gap
+        hi *= 1.0 - 3 * gap
+    assert np.min(np.abs(sp - lo)) > gap and np.min(np.abs(sp - hi)) > gap
+    assert np.any(sp < lo) and np.any(sp > hi) and np.any((sp > lo) & (sp < hi))
+    return float(lo), float(hi)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_clamped_backward_matches_central_differences(gated):
+    """Delta = clamp(softplus, dt_min, dt_max) with some steps below, some above and
+    some inside the bounds (mamba3_preprocess_backward.slang's dt clamp and mask)."""
+    rng = np.random.default_rng(71 if gated else 72)
+    b, l, d, n = 2, 6, 3, 2
+    p = rand_problem(rng, b, l, d, n, gated=gated, h0=True, dscale=2.0)
+    lo, hi = _clamp_bounds(p)
+    dy = rng.standard_normal((b, l, d))
+    dhf = rng.standard_normal((b, d, n))
+    g = run_bwd(p, dy, dh_final=dhf, dt_min=lo, dt_max=hi)
+
+    def loss(q):
+        r = run_fwd(q, dt_min=lo, dt_max=hi)
+        return float(np.sum(dy * r["y"]) + np.sum(dhf * r["h_final"]))
+
+    names = [k for k in list(GRAD_OF) + ["h0"] if p.get(k) is not None]
+    fd = _fd_grads(p, loss, names)
+    for name in names:
+        gname = GRAD_OF.get(name, "dh0")
+        scale = max(1.0, np.abs(fd[name]).max())
+        np.testing.assert_allclose(g[gname], fd[name], rtol=1e-6, atol=1e-6 * scale, err_msg=name)
+    # the clamped steps pass no gradient to delta_raw
+    sp = softplus_ref(p["delta_raw"] + p["dt_bias"][None, None, :])
+    assert np.all(g["ddelta_raw"][(sp < lo) | (sp > hi)] == 0.0)
+
+
+@pytest.mark.parametrize("L", [1, 300])
+def test_clamp_to_one_value_gives_the_constant_step_closed_form(L):
+    """dt_min = dt_max = c makes Delta = c whatever delta_raw is: with x, B, C, z
+    constant in time the scan is the geometric sum with a = exp(c A)."""
+    rng = np.random.default_rng(80 + L)
+    b, d, n, c = 2, 3, 4, 0.037
+    xc = rng.standard_normal((b, d))
+    zc = rng.standard_normal((b, d))
+    Bc = rng.standard_normal((b, n))
+    Cc = rng.standard_normal((b, n))
+    A_log = np.log(rng.uniform(0.05, 3.0, (d, n)))
+    Dsk = rng.standard_normal(d)
+    h0 = rng.standard_normal((b, d, n))
+    rep = lambda a: np.repeat(a[:, None, :], L, axis=1)
+    raw = 3.0 * rng.standard_normal((b, L, d))  # varies in time; the clamp removes it
+    res = oracle.fwd(rep(xc), raw, rep(Bc), rep(Cc), A_log, D=Dsk, dt_bias=rng.standard_normal(d),
+                     z=rep(zc), h0=h0, dt_min=c, dt_max=c)
+    A = -np.exp(A_log)
+    a = np.exp(c * A)[None]                                       # [1, d, n]
+    u = c * Bc[:, None, :] * xc[:, :, None]                       # [b, d, n]
+    ak = a[:, None] ** np.arange(1, L + 1)[None, :, None, None]   # [b?, L, d, n]
+    h = ak * h0[:, None] + u[:, None] * (1 - ak) / (1 - a[:, None])
+    s = np.einsum("bldn,bn->bld", h, Cc) + Dsk[None, None, :] * xc[:, None, :]
+    y = s * silu_ref(zc)[:, None, :]
+    np.testing.assert_allclose(res["y"], y, rtol=1e-11, atol=1e-12 * np.abs(y).max())
+    np.testing.assert_allclose(res["h_final"], h[:, -1], rtol=1e-11, atol=1e-12)
+
+
+def test_clamp_that_never_binds_changes_nothing():
+    rng = np.random.default_rng(90)
+    p = rand_problem(rng, 2, 40, 5, 3)
+    sp = softplus_ref(p["delta_raw"] + p["dt_bias"][None, None, :])
+    lo, hi = 0.5 * sp.min(), 2.0 * sp.max()
+    dy = rng.standard_normal((2, 40, 5))
+    a, c = run_fwd(p), run_fwd(p, dt_min=lo, dt_max=hi)
+    assert np.array_equal(a["y"], c["y"]) and np.array_equal(a["h_final"], c["h_final"])
+    ga, gc = run_bwd(p, dy), run_bwd(p, dy, dt_min=lo, dt_max=hi)
+    for k in ga:
+        if ga[k] is not None:
+            assert np.array_equal(ga[k], gc[k]), k
+
+
+def test_clamped_scan_of_length_one_equals_clamped_step():
+    rng = np.random.default_rng(91)
+    p = rand_problem(rng, 3, 1, 7, 5, dscale=2.0)
+    sp = softplus_ref(p["delta_raw"] + p["dt_bias"][None, None, :])
+    lo, hi = np.quantile(sp, 0.3), np.quantile(sp, 0.7)
+    sc = run_fwd(p, dt_min=lo, dt_max=hi)
+    st = oracle.step(p["h0"], p["x"][:, 0], p["delta_raw"][:, 0], p["B"][:, 0], p["C"][:, 0], p["A_log"],
+                     D=p["D"], dt_bias=p["dt_bias"], z=p["z"][:, 0], dt_min=lo, dt_max=hi)
+    np.testing.assert_allclose(st["y"], sc["y"][:, 0], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(st["state"], sc["h_final"], rtol=1e-15, atol=1e-15)
+
+
+def test_invalid_clamp_bounds_are_rejected():
+    rng = np.random.default_rng(92)
+    p = rand_problem(rng, 1, 3, 2, 2)
+    for lo, hi in ((0.2, 0.1), (-0.1, 1.0), (float("nan"), 1.0)):
+        with pytest.raises(RuntimeError):
+            run_fwd(p, dt_min=lo, dt_max=hi)
