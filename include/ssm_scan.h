@@ -63,7 +63,8 @@ typedef enum {
   SSM_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size        */
   SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input                         */
-  SSM_ERR_HIP = 7          /* the HIP runtime reported an error at launch         */
+  SSM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch         */
+  SSM_ERR_ARG = 8          /* an option value is out of range                     */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -112,7 +113,7 @@ int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void
  *     not written).  dD and d_dt_bias are the gradients as if D_skip / dt_bias
  *     were present (they are when NULL, with value zero).
  *   The gradient flowing into h_final is taken as zero and no gradient of h0 is
- *   produced.
+ *   produced (ssm_scan_bwd_ex takes the one and returns the other).
  *   workspace: required, at least ssm_scan_bwd_workspace_bytes() bytes, 256-byte
  *   aligned; its contents on entry are ignored.
  *   Reductions: dB and dC (sums over channels), dA_log, dD and d_dt_bias (sums
@@ -130,6 +131,48 @@ int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void
                  float* dB, float* dC, float* dA_log, float* dD, float* d_dt_bias,
                  void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
                  int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream);
+
+/* ---- Variants of the same path: the step-size clamp, and sequences carried across
+ * segments.  The _ex entry points take the arguments of the entry points above plus
+ * an options pointer; NULL (or a zero-initialised struct) gives exactly the results
+ * of the plain entry points, which are the _ex calls with NULL options. */
+typedef struct {
+  /* Step-size clamp (mamba3_preprocess_backward.slang: dt clamp and dt mask):
+   *   Delta = clamp(softplus(delta_raw + dt_bias), dt_min, dt_max),
+   * and the backward passes dLoss/dDelta on to delta_raw (and dt_bias) only at steps
+   * whose softplus lies inside [dt_min, dt_max], bounds included.
+   * dt_min >= 0; dt_max <= 0 means no upper bound; otherwise dt_min <= dt_max.
+   * A NaN bound, a negative dt_min or dt_min > dt_max > 0 gives SSM_ERR_ARG. */
+  float dt_min;
+  float dt_max;
+  /* Backward only (NULL for the forward and the step, SSM_ERR_ARG otherwise); the
+   * initial / final state gradients of a sequence carried across segments
+   * (deterministic_backward.py: initial_states, dfinal_states):
+   *   dh_final [batch, d_inner, d_state] fp32, read: dLoss/dh_final, the gradient that
+   *            reaches the state after the last step from outside; NULL means zero.
+   *   dh0      [batch, d_inner, d_state] fp32, written: dLoss/dh0; NULL: not written.
+   * Both naturally aligned; dh_final must not overlap an output, dh0 nothing else. */
+  const float* dh_final;
+  float* dh0;
+} ssm_scan_options;
+
+int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const void* B,
+                    const void* C, const float* A_log, const float* D_skip, const float* dt_bias,
+                    const float* h0, void* y, float* h_final, int64_t batch, int64_t seqlen,
+                    int64_t d_inner, int64_t d_state, int io_dtype, void* workspace,
+                    size_t workspace_bytes, const ssm_scan_options* options, hipStream_t stream);
+int ssm_scan_step_ex(float* state, const void* x, const void* delta_raw, const void* z,
+                     const void* B, const void* C, const float* A_log, const float* D_skip,
+                     const float* dt_bias, void* y, int64_t batch, int64_t d_inner,
+                     int64_t d_state, int io_dtype, const ssm_scan_options* options,
+                     hipStream_t stream);
+int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const void* B,
+                    const void* C, const float* A_log, const float* D_skip, const float* dt_bias,
+                    const float* h0, const void* dy, void* dx, void* ddelta_raw, void* dz,
+                    float* dB, float* dC, float* dA_log, float* dD, float* d_dt_bias,
+                    void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                    int64_t d_inner, int64_t d_state, int io_dtype,
+                    const ssm_scan_options* options, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,22 @@ bool conv_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
   return true;
 }
 
+// Options of the _ex entry points: clamp bounds (dt_max <= 0: no upper bound) and the
+// backward-only state gradients.  NULL options are the defaults.
+bool options_ok(const ssm_scan_options* o, bool backward, float* lo, float* hi) {
+  *lo = 0.f;
+  *hi = __builtin_inff();
+  if (!o) return true;
+  if (!(o->dt_min >= 0.f) || o->dt_max != o->dt_max) return false;  // negative or NaN
+  if (o->dt_max > 0.f) {
+    if (o->dt_min > o->dt_max) return false;
+    *hi = o->dt_max;
+  }
+  *lo = o->dt_min;
+  if (!backward && (o->dh_final || o->dh0)) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +72,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported an error";
+    case SSM_ERR_ARG: return "SSM_ERR_ARG: an option value is out of range";
     default: return "unknown ssm_status";
   }
 }
@@ -70,8 +87,19 @@ int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void
                  const float* A_log, const float* D_skip, const float* dt_bias, const float* h0, void* y,
                  float* h_final, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                  int io_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ssm_scan_fwd_ex(x, delta_raw, z, B, C, A_log, D_skip, dt_bias, h0, y, h_final, batch, seqlen,
+                         d_inner, d_state, io_dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const void* B, const void* C,
+                    const float* A_log, const float* D_skip, const float* dt_bias, const float* h0, void* y,
+                    float* h_final, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                    int io_dtype, void* workspace, size_t workspace_bytes, const ssm_scan_options* options,
+                    hipStream_t stream) {
   (void)workspace; (void)workspace_bytes;
   if (!x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
+  float dt_lo, dt_hi;
+  if (!options_ok(options, false, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
   // per-tile buffer offsets of the forward kernel are 32-bit: a 16-row tile of one
@@ -106,13 +134,24 @@ int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void
   a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
   a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
   a.bf16 = io_dtype == SSM_BF16;
+  a.dt_lo = dt_lo; a.dt_hi = dt_hi;
   return ssm::launch_fwd(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void* z, const void* B,
                   const void* C, const float* A_log, const float* D_skip, const float* dt_bias, void* y,
                   int64_t batch, int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream) {
+  return ssm_scan_step_ex(state, x, delta_raw, z, B, C, A_log, D_skip, dt_bias, y, batch, d_inner, d_state,
+                          io_dtype, nullptr, stream);
+}
+
+int ssm_scan_step_ex(float* state, const void* x, const void* delta_raw, const void* z, const void* B,
+                     const void* C, const float* A_log, const float* D_skip, const float* dt_bias, void* y,
+                     int64_t batch, int64_t d_inner, int64_t d_state, int io_dtype,
+                     const ssm_scan_options* options, hipStream_t stream) {
   if (!state || !x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
+  float dt_lo, dt_hi;
+  if (!options_ok(options, false, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, 1, d_inner, d_state)) return SSM_ERR_DIM;
   if (batch * d_inner * 4 >= ((int64_t)1 << 31) * 256) return SSM_ERR_DIM;  // grid limit
@@ -137,6 +176,7 @@ int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void
   a.state = state; a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log;
   a.D_skip = D_skip; a.dt_bias = dt_bias; a.y = y;
   a.batch = batch; a.dim = d_inner; a.dstate = (int)d_state; a.bf16 = io_dtype == SSM_BF16;
+  a.dt_lo = dt_lo; a.dt_hi = dt_hi;
   return ssm::launch_step(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -152,8 +192,23 @@ int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void
                  const void* dy, void* dx, void* ddelta_raw, void* dz, float* dB, float* dC, float* dA_log,
                  float* dD, float* d_dt_bias, void* workspace, size_t workspace_bytes, int64_t batch,
                  int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, hipStream_t stream) {
+  return ssm_scan_bwd_ex(x, delta_raw, z, B, C, A_log, D_skip, dt_bias, h0, dy, dx, ddelta_raw, dz, dB, dC,
+                         dA_log, dD, d_dt_bias, workspace, workspace_bytes, batch, seqlen, d_inner, d_state,
+                         io_dtype, nullptr, stream);
+}
+
+int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const void* B, const void* C,
+                    const float* A_log, const float* D_skip, const float* dt_bias, const float* h0,
+                    const void* dy, void* dx, void* ddelta_raw, void* dz, float* dB, float* dC, float* dA_log,
+                    float* dD, float* d_dt_bias, void* workspace, size_t workspace_bytes, int64_t batch,
+                    int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype,
+                    const ssm_scan_options* options, hipStream_t stream) {
   if (!x || !delta_raw || !B || !C || !A_log || !dy || !dx || !ddelta_raw || !dB || !dC) return SSM_ERR_NULL;
   if (z && !dz) return SSM_ERR_NULL;
+  float dt_lo, dt_hi;
+  if (!options_ok(options, true, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
+  const float* dh_final = options ? options->dh_final : nullptr;
+  float* dh0 = options ? options->dh0 : nullptr;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
   if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
@@ -161,18 +216,19 @@ int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void
   const ssm::BwdLayout l = ssm::bwd_layout(batch, seqlen, d_inner, (int)d_state);
   if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
   const void* all[] = {x, delta_raw, z, B, C, A_log, D_skip, dt_bias, h0, dy,
-                       dx, ddelta_raw, dz, dB, dC, dA_log, dD, d_dt_bias};
+                       dx, ddelta_raw, dz, dB, dC, dA_log, dD, d_dt_bias, dh_final, dh0};
   for (const void* p : all)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
   const size_t H = (size_t)batch * d_inner * d_state, P = (size_t)d_inner * d_state;
   const Range ins[] = {rng(x, E * 4), rng(delta_raw, E * 4), rng(z, z ? E * 4 : 0), rng(B, S * 4),
                        rng(C, S * 4), rng(A_log, P * 4), rng(D_skip, D_skip ? d_inner * 4 : 0),
-                       rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * 4)};
+                       rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * 4),
+                       rng(dh_final, dh_final ? H * 4 : 0)};
   const Range outs[] = {rng(dx, E * 4), rng(ddelta_raw, E * 4), rng(dz, dz && z ? E * 4 : 0),
                         rng(dB, S * 4), rng(dC, S * 4), rng(dA_log, dA_log ? P * 4 : 0),
                         rng(dD, dD ? d_inner * 4 : 0), rng(d_dt_bias, d_dt_bias ? d_inner * 4 : 0),
-                        rng(workspace, l.total)};
+                        rng(workspace, l.total), rng(dh0, dh0 ? H * 4 : 0)};
   const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
   for (int i = 0; i < nout; ++i) {
     for (const Range& r : ins)
@@ -187,6 +243,7 @@ int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void
   a.h0 = h0; a.dy = (const float*)dy; a.dx = (float*)dx; a.ddelta_raw = (float*)ddelta_raw;
   a.dz = z ? (float*)dz : nullptr; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
   a.d_dt_bias = d_dt_bias; a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
+  a.dh_final = dh_final; a.dh0 = dh0; a.dt_lo = dt_lo; a.dt_hi = dt_hi;
   return ssm::launch_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -169,7 +169,7 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
                  const float* __restrict__ Bm, const float* __restrict__ A_log,
                  const float* __restrict__ dt_bias, float* __restrict__ hrel, float* __restrict__ cumd,
                  float* __restrict__ hseg, float* __restrict__ sdseg, int64_t L, int64_t Dm, int N,
-                 int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
+                 int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   __shared__ float2 pd[2][TC * 64];  // (Delta, Delta*x) per (t, channel)
@@ -207,7 +207,7 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
+        const float delta = v ? clamp_delta(softplus_f(lr[i] + bias), dt_lo, dt_hi) : 0.f;
         pd[buf][t * 64 + q.lane] = make_float2(delta, delta * lx[i]);
         if (q.lane < 16) bs[buf][t * 16 + q.lane] = lb[i];
       }
@@ -261,7 +261,7 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
                const float* __restrict__ dy, const float* __restrict__ Cm,
                const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                float* __restrict__ gseg, int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks,
-               int64_t segc, int64_t nseg) {
+               int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   __shared__ float2 pa[2][TC * 64];  // (Delta, g) per (t, channel)
@@ -299,7 +299,7 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const float delta = v ? softplus_f(lr[i] + bias) : 0.f;
+        const float delta = v ? clamp_delta(softplus_f(lr[i] + bias), dt_lo, dt_hi) : 0.f;
         float g = ly[i];
         if (GATED) g *= silu_f(lz[i]);
         pa[buf][t * 64 + q.lane] = make_float2(delta, g);
@@ -348,7 +348,8 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
 __global__ void __launch_bounds__(256)
 seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
                 const float* __restrict__ gseg, const float* __restrict__ A_log,
-                const float* __restrict__ h0, float* __restrict__ hin, float* __restrict__ gin,
+                const float* __restrict__ h0, const float* __restrict__ dh_final,
+                float* __restrict__ hin, float* __restrict__ gin, float* __restrict__ dh0,
                 int64_t batch, int64_t Dm, int N, int64_t nseg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, n, d), d fastest
   if (i >= batch * Dm * N) return;
@@ -362,12 +363,15 @@ seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
     hin[o] = h;
     h = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), h, hseg[o]);
   }
-  float g = 0.f;
+  // the carry beyond the last step is the gradient reaching h_final from outside; the
+  // carry leaving the first segment is a_0 G_0 = dLoss/dh0
+  float g = dh_final ? dh_final[(b * Dm + d) * N + n] : 0.f;
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t o = ((b * nseg + s) * N + n) * Dm + d;
     gin[o] = g;
     g = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), g, gseg[o]);
   }
+  if (dh0) dh0[(b * Dm + d) * N + n] = g;
 }
 
 // ---- 4. main backward per (b, tile, segment): chunks in reverse order
@@ -382,7 +386,7 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
                 float* __restrict__ dx, float* __restrict__ ddelta_raw, float* __restrict__ dz,
                 float* __restrict__ pdB, float* __restrict__ pdC, float* __restrict__ pdA,
                 float* __restrict__ pdD, float* __restrict__ pdbias, int64_t L, int64_t Dm, int N,
-                int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg) {
+                int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
   static_assert(2 * kSub * S == 16, "a sub-tile's dB/dC values fill one transpose-reduce");
@@ -454,7 +458,8 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
       const float xv = lx[i];
       const float r = lr[i] + bias;
       const float dyv = ly[i];
-      const float delta = v ? softplus_f(r) : 0.f;
+      const float sp = softplus_f(r);
+      const float delta = v ? clamp_delta(sp, dt_lo, dt_hi) : 0.f;
       float g = dyv, gz = 0.f;
       if (GATED) {
         const float zv = lz[i];
@@ -462,7 +467,8 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
         g = dyv * zv * sz;
         gz = dyv * sz * fmaf(zv, 1.f - sz, 1.f);
       }
-      ex[i] = xv; edelta[i] = delta; eg[i] = g; esig[i] = sigmoid_f(r); egz[i] = gz;
+      // d Delta / d delta_raw: the sigmoid, where the clamp lets the gradient through
+      ex[i] = xv; edelta[i] = delta; eg[i] = g; esig[i] = sigmoid_f(r) * clamp_mask(sp, dt_lo, dt_hi); egz[i] = gz;
       if (t < TC) {
         pd[t * 64 + lane] = make_float4(delta, delta * xv, g, 0.f);
         if (lane < 16) bcs[t * 16 + lane] = lbc[i];
@@ -655,21 +661,21 @@ hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipSt
   hipError_t e;
   hipLaunchKernelGGL((chunk_rel_kernel<S, G>), dim3(blocks), dim3(64 * G), 0, stream, a.x, a.delta_raw, a.B,
                      a.A_log, a.dt_bias, hrel, cumd, hseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
-                     l.nchunks, l.segc, l.nseg);
+                     l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.z)
     hipLaunchKernelGGL((seg_adj_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
                        a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
-                       l.segc, l.nseg);
+                       l.segc, l.nseg, a.dt_lo, a.dt_hi);
   else
     hipLaunchKernelGGL((seg_adj_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
                        a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
-                       l.segc, l.nseg);
+                       l.segc, l.nseg, a.dt_lo, a.dt_hi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const int64_t n = a.batch * a.dim * a.dstate;
     hipLaunchKernelGGL(seg_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, hseg, sdseg,
-                       gseg, a.A_log, a.h0, hin, gin, a.batch, a.dim, a.dstate, l.nseg);
+                       gseg, a.A_log, a.h0, a.dh_final, hin, gin, a.dh0, a.batch, a.dim, a.dstate, l.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   float* pdB = (float*)(ws + l.off_dbc);
@@ -681,12 +687,12 @@ hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipSt
     hipLaunchKernelGGL((bwd_main_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
                        a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
                        a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
-                       l.ngroups, l.nchunks, l.segc, l.nseg);
+                       l.ngroups, l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   else
     hipLaunchKernelGGL((bwd_main_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
                        a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
                        a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
-                       l.ngroups, l.nchunks, l.segc, l.nseg);
+                       l.ngroups, l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

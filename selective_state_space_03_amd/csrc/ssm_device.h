@@ -34,6 +34,19 @@ __device__ __forceinline__ float softplus_f(float r) {
   return fmaxf(r, 0.0f) + fmaf(log2_hw(u), kLn2, -c);
 }
 
+// The optional step-size clamp (mamba3_preprocess_backward.slang clamps softplus to
+// [dt_min, dt_max] and masks the gradient of the clamped steps): Delta = softplus
+// clamped to [lo, hi].  lo = 0, hi = +inf is no clamp at all, since softplus >= 0.
+// Written with comparisons so that a NaN stays NaN.
+__device__ __forceinline__ float clamp_delta(float sp, float lo, float hi) {
+  return sp < lo ? lo : (sp > hi ? hi : sp);
+}
+// 1 where the clamp lets the gradient through (softplus inside [lo, hi], bounds
+// included), else 0
+__device__ __forceinline__ float clamp_mask(float sp, float lo, float hi) {
+  return (sp >= lo && sp <= hi) ? 1.f : 0.f;
+}
+
 // logistic sigmoid, the derivative of softplus (mamba3_preprocess_backward.slang writes
 // it as 1 - exp(-softplus(r))).  exp2 saturates to +inf for r << 0 and rcp(inf) = 0.
 __device__ __forceinline__ float sigmoid_f(float r) { return rcp_hw(1.0f + exp2_hw(-r * kLog2e)); }

@@ -87,7 +87,7 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
                 const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
                 const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
                 const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_final,
-                int L, int Dm, int N_rt, int ngroups) {
+                int L, int Dm, int N_rt, int ngroups, float dt_lo, float dt_hi) {
   static_assert(R == 8, "ring slots are tile mod 8; the main loop is unrolled by 8");
   constexpr int EPL = (TT + G - 1) / G;  // prep/readout rows per lane per tile
   constexpr int ES = (int)sizeof(T);
@@ -193,7 +193,7 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
       const int t = wave + G * i;
       if (t < TT) {
         const bool v = dvalid && k * TT + t < L;
-        const float delta = softplus_f(pr[slot][i] + bias);
+        const float delta = clamp_delta(softplus_f(pr[slot][i] + bias), dt_lo, dt_hi);
         dd[dbuf][t * 64 + lane] = v ? make_float2(delta, delta * px[slot][i]) : make_float2(0.f, 0.f);
         if (lane < 16) {
           bsT[dbuf][lane * TT + t] = pb[bslot][i];
@@ -423,7 +423,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
                  const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
                  const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
                  const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_final, int L, int Dm,
-                 int N, int ngroups, int nblocks) {
+                 int N, int ngroups, int nblocks, float dt_lo, float dt_hi) {
   constexpr int TT = 16;  // steps per tile = lanes per row
   constexpr int R = 8;    // ring of loaded tiles (tile mod 8); the loop is unrolled by 8
   constexpr int P = 6;    // tiles loaded ahead
@@ -529,7 +529,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   // end of the sequence occur only in the last tile)
   auto prep = [&](int k, int buf, float& dl, float& dlx, float& xk) __attribute__((always_inline)) {
     xk = act[buf][0][pcol];
-    dl = softplus_f(act[buf][1][pcol] + bias);
+    dl = clamp_delta(softplus_f(act[buf][1][pcol] + bias), dt_lo, dt_hi);
     if ((k + 1) * TT > L) dl = k * TT + li < L ? dl : 0.f;
     dlx = dl * xk;
   };
@@ -586,7 +586,7 @@ hipError_t launch_lanes_w(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_lanes_kernel<T, W, GATED>), dim3((unsigned)nblocks), dim3(64 * W), 0, stream,
                      (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C, a.A_log,
                      a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen, (int)a.dim, a.dstate, ngroups,
-                     (int)nblocks);
+                     (int)nblocks, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 
@@ -610,12 +610,12 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_scan_kernel<T, S, G, TT, PF, GATED, false>), dim3((unsigned)nblocks), dim3(64 * G), 0,
                        stream, (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B,
                        (const T*)a.C, a.A_log, a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen,
-                       (int)a.dim, a.dstate, ngroups);
+                       (int)a.dim, a.dstate, ngroups, a.dt_lo, a.dt_hi);
   else
     hipLaunchKernelGGL((fwd_scan_kernel<T, S, G, TT, PF, GATED, true>), dim3((unsigned)nblocks), dim3(64 * G), 0,
                        stream, (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B,
                        (const T*)a.C, a.A_log, a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen,
-                       (int)a.dim, a.dstate, ngroups);
+                       (int)a.dim, a.dstate, ngroups, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct FwdArgs {
   int64_t batch, seqlen, dim;
   int dstate;
   int bf16;  // io dtype is bf16
+  float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
 };
 
 struct StepArgs {
@@ -39,6 +40,7 @@ struct StepArgs {
   int64_t batch, dim;
   int dstate;
   int bf16;
+  float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
 };
 
 struct BwdArgs {
@@ -60,8 +62,11 @@ struct BwdArgs {
   float* dA_log;     // nullable
   float* dD;         // nullable
   float* d_dt_bias;  // nullable
+  const float* dh_final = nullptr;  // [B, D, N]: gradient reaching h_final (nullable: zero)
+  float* dh0 = nullptr;             // [B, D, N]: gradient of h0 (nullable: not written)
   int64_t batch, seqlen, dim;
   int dstate;
+  float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
 };
 
 // Workspace layout of the backward (byte offsets into one caller buffer).

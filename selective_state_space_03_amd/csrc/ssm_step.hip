@@ -18,7 +18,8 @@ __global__ void __launch_bounds__(256)
 step_kernel(float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ delta_raw,
             const T* __restrict__ z, const T* __restrict__ Bm, const T* __restrict__ Cm,
             const float* __restrict__ A_log, const float* __restrict__ D_skip,
-            const float* __restrict__ dt_bias, T* __restrict__ y, int64_t batch, int64_t Dm, int N) {
+            const float* __restrict__ dt_bias, T* __restrict__ y, int64_t batch, int64_t Dm, int N,
+            float dt_lo, float dt_hi) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t pair = gid / QL;  // (b, d) flattened: b * Dm + d
   const int q = (int)(gid % QL);
@@ -63,7 +64,7 @@ step_kernel(float* __restrict__ state, const T* __restrict__ x, const T* __restr
       }
     }
   }
-  const float delta = softplus_f(rv + bias);
+  const float delta = clamp_delta(softplus_f(rv + bias), dt_lo, dt_hi);
   const float dx = delta * xv;
   float acc = 0.f;
 #pragma unroll
@@ -97,11 +98,11 @@ hipError_t launch_ql(const StepArgs& a, bool vec, hipStream_t stream) {
   if (vec)
     hipLaunchKernelGGL((step_kernel<T, QL, true, GATED>), dim3(blocks), dim3(256), 0, stream, a.state,
                        (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C,
-                       a.A_log, a.D_skip, a.dt_bias, (T*)a.y, a.batch, a.dim, a.dstate);
+                       a.A_log, a.D_skip, a.dt_bias, (T*)a.y, a.batch, a.dim, a.dstate, a.dt_lo, a.dt_hi);
   else
     hipLaunchKernelGGL((step_kernel<T, QL, false, GATED>), dim3(blocks), dim3(256), 0, stream, a.state,
                        (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C,
-                       a.A_log, a.D_skip, a.dt_bias, (T*)a.y, a.batch, a.dim, a.dstate);
+                       a.A_log, a.D_skip, a.dt_bias, (T*)a.y, a.batch, a.dim, a.dstate, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
 

@@ -7,10 +7,14 @@ fallback: if the library is missing or a call fails, an exception is raised.
 
 Functions mirror the C entry points:
   ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h0=None,
-               y=None, h_final=None, return_final_state=True) -> (y, h_final)
-  ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, y=None) -> y
+               y=None, h_final=None, return_final_state=True, dt_min=None, dt_max=None) -> (y, h_final)
+  ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, y=None,
+                dt_min=None, dt_max=None) -> y
   ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=None, h0=None,
-               workspace=None, out=None) -> dict of gradients
+               workspace=None, out=None, dt_min=None, dt_max=None, dh_final=None,
+               return_dh0=False) -> dict of gradients (with "dh0" when asked for)
+The step-size clamp (dt_min, dt_max) and the state gradients go through the _ex entry
+points and their ssm_scan_options struct; without them the calls are the plain ones.
 """
 from __future__ import annotations
 
@@ -25,10 +29,18 @@ LIB_PATH = os.path.join(HERE, "lib", "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPORTED",
-          4: "SSM_ERR_ALIGN", 5: "SSM_ERR_WORKSPACE", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_HIP"}
+          4: "SSM_ERR_ALIGN", 5: "SSM_ERR_WORKSPACE", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_HIP",
+          8: "SSM_ERR_ARG"}
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_conv1d_fwd", "ssm_conv1d_step",
-           "ssm_conv1d_bwd_workspace_bytes", "ssm_conv1d_bwd")
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
+           "ssm_scan_bwd_ex", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
+           "ssm_conv1d_bwd")
+
+
+class ScanOptions(ctypes.Structure):
+    """ssm_scan_options of include/ssm_scan.h"""
+    _fields_ = [("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("dh_final", ctypes.c_void_p), ("dh0", ctypes.c_void_p)]
 SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
 
 _lib = None
@@ -64,6 +76,13 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.restype = SZ
         L.ssm_scan_bwd.argtypes = [P] * 18 + [P, SZ] + [I64] * 4 + [I, P]
         L.ssm_scan_bwd.restype = I
+        OP = ctypes.POINTER(ScanOptions)
+        L.ssm_scan_fwd_ex.argtypes = [P] * 11 + [I64] * 4 + [I, P, SZ, OP, P]
+        L.ssm_scan_fwd_ex.restype = I
+        L.ssm_scan_step_ex.argtypes = [P] * 10 + [I64] * 3 + [I, OP, P]
+        L.ssm_scan_step_ex.restype = I
+        L.ssm_scan_bwd_ex.argtypes = [P] * 18 + [P, SZ] + [I64] * 4 + [I, OP, P]
+        L.ssm_scan_bwd_ex.restype = I
         L.ssm_conv1d_fwd.argtypes = [P] * 4 + [I64] * 4 + [I, I, P]
         L.ssm_conv1d_fwd.restype = I
         L.ssm_conv1d_step.argtypes = [P] * 5 + [I64] * 3 + [I, I, P]
@@ -113,6 +132,15 @@ def _req(t, name, shape, dtype, device):
     return t
 
 
+def _options(dt_min, dt_max, dh_final=None, dh0=None):
+    """ssm_scan_options for the _ex entry points (None when nothing is set)"""
+    if dt_min is None and dt_max is None and dh_final is None and dh0 is None:
+        return None
+    o = ScanOptions(0.0 if dt_min is None else float(dt_min), 0.0 if dt_max is None else float(dt_max),
+                    None if dh_final is None else dh_final.data_ptr(), None if dh0 is None else dh0.data_ptr())
+    return ctypes.pointer(o)
+
+
 def fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=SSM_F32):
     return int(lib().ssm_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype))
 
@@ -122,7 +150,7 @@ def bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=SSM_F32):
 
 
 def ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h0=None,
-                 y=None, h_final=None, return_final_state=True, workspace=None):
+                 y=None, h_final=None, return_final_state=True, workspace=None, dt_min=None, dt_max=None):
     b, l, d = x.shape
     n = B.shape[-1]
     dev, dt = x.device, x.dtype
@@ -142,14 +170,15 @@ def ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h
         h_final = torch.empty((b, d, n), dtype=f32, device=dev)
     _req(h_final, "h_final", (b, d, n), f32, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ssm_scan_fwd(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
-                            _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
-                            b, l, d, n, io, _ptr(workspace), ws_bytes, _stream())
-    _check("ssm_scan_fwd", st)
+    st = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
+                               _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
+                               b, l, d, n, io, _ptr(workspace), ws_bytes, _options(dt_min, dt_max), _stream())
+    _check("ssm_scan_fwd_ex", st)
     return y, h_final
 
 
-def ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, y=None):
+def ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, y=None,
+                  dt_min=None, dt_max=None):
     b, d, n = state.shape
     dev, dt = x.device, x.dtype
     io = _io_dtype(x)
@@ -164,14 +193,15 @@ def ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z
     if y is None:
         y = torch.empty((b, d), dtype=dt, device=dev)
     _req(y, "y", (b, d), dt, dev)
-    st = lib().ssm_scan_step(_ptr(state), _ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C),
-                             _ptr(A_log), _ptr(D_skip), _ptr(dt_bias), _ptr(y), b, d, n, io, _stream())
-    _check("ssm_scan_step", st)
+    st = lib().ssm_scan_step_ex(_ptr(state), _ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C),
+                                _ptr(A_log), _ptr(D_skip), _ptr(dt_bias), _ptr(y), b, d, n, io,
+                                _options(dt_min, dt_max), _stream())
+    _check("ssm_scan_step_ex", st)
     return y
 
 
 def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=None, h0=None,
-                 workspace=None, out=None):
+                 workspace=None, out=None, dt_min=None, dt_max=None, dh_final=None, return_dh0=False):
     b, l, d = x.shape
     n = B.shape[-1]
     dev, dt = x.device, x.dtype
@@ -197,12 +227,18 @@ def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=Non
         nbytes = bwd_workspace_bytes(b, l, d, n, io)
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().ssm_scan_bwd(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
-                            _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(out["dx"]),
-                            _ptr(out["ddelta_raw"]), _ptr(out.get("dz")), _ptr(out["dB"]), _ptr(out["dC"]),
-                            _ptr(out.get("dA_log")), _ptr(out.get("dD")), _ptr(out.get("d_dt_bias")),
-                            _ptr(workspace), ws_bytes, b, l, d, n, io, _stream())
-    _check("ssm_scan_bwd", st)
+    _req(dh_final, "dh_final", (b, d, n), f32, dev)
+    if return_dh0 and out.get("dh0") is None:
+        out["dh0"] = torch.empty((b, d, n), dtype=f32, device=dev)
+    dh0 = out.get("dh0") if return_dh0 else None
+    _req(dh0, "dh0", (b, d, n), f32, dev)
+    st = lib().ssm_scan_bwd_ex(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
+                               _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(out["dx"]),
+                               _ptr(out["ddelta_raw"]), _ptr(out.get("dz")), _ptr(out["dB"]), _ptr(out["dC"]),
+                               _ptr(out.get("dA_log")), _ptr(out.get("dD")), _ptr(out.get("d_dt_bias")),
+                               _ptr(workspace), ws_bytes, b, l, d, n, io,
+                               _options(dt_min, dt_max, dh_final, dh0), _stream())
+    _check("ssm_scan_bwd_ex", st)
     return out
 
 

@@ -198,3 +198,54 @@ def test_conv_step_and_bwd_validation():
                             1, 0, None) == WS
     assert L.ssm_conv1d_bwd(addr(0), addr(5), None, addr(1), addr(0), None, None, addr(11), wsb, 2, 64, 32, 4, 1,
                             0, None) == ALIAS
+
+
+# ------------------------------------------------ options of the _ex entry points
+
+def _opts(dt_min=0.0, dt_max=0.0, dh_final=None, dh0=None):
+    return ctypes.pointer(ops.ScanOptions(dt_min, dt_max, dh_final, dh0))
+
+
+ARG = 8
+
+
+def call_fwd_ex(a, opts):
+    return ops.lib().ssm_scan_fwd_ex(a["x"], a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"], a["D"],
+                                     a["dt_bias"], a["h0"], a["y"], a["h_final"], a["b"], a["l"], a["d"],
+                                     a["n"], a["io"], a["ws"], a["wsb"], opts, a["stream"])
+
+
+def bwd_ex_call(opts, **over):
+    a = dict(x=addr(0), delta_raw=addr(1), z=addr(2), B=addr(3), C=addr(4), A_log=addr(5), D=addr(6),
+             dt_bias=addr(7), h0=None, dy=addr(8), dx=addr(9), ddelta_raw=addr(10), dz=addr(11), dB=addr(12),
+             dC=addr(13), dA_log=addr(14), dD=addr(15), d_dt_bias=addr(16), ws=addr(17), b=2, l=64, d=128, n=16)
+    a.update(over)
+    wsb = ops.lib().ssm_scan_bwd_workspace_bytes(a["b"], a["l"], a["d"], a["n"], 0)
+    return ops.lib().ssm_scan_bwd_ex(a["x"], a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"], a["D"],
+                                     a["dt_bias"], a["h0"], a["dy"], a["dx"], a["ddelta_raw"], a["dz"], a["dB"],
+                                     a["dC"], a["dA_log"], a["dD"], a["d_dt_bias"], a["ws"], wsb, a["b"],
+                                     a["l"], a["d"], a["n"], ops.SSM_F32, opts, None)
+
+
+@no_gpu_only
+def test_options_validation():
+    a = fwd_args()
+    nan = float("nan")
+    assert call_fwd_ex(a, _opts(0.2, 0.1)) == ARG            # dt_min > dt_max
+    assert call_fwd_ex(a, _opts(-0.1, 1.0)) == ARG           # negative lower bound
+    assert call_fwd_ex(a, _opts(nan, 1.0)) == ARG
+    assert call_fwd_ex(a, _opts(0.0, nan)) == ARG
+    assert call_fwd_ex(a, _opts(dh_final=BASE + 20 * STRIDE)) == ARG   # backward-only field
+    assert call_fwd_ex(a, _opts(dh0=BASE + 20 * STRIDE)) == ARG
+    assert call_fwd_ex(fwd_args(x=None), _opts(0.2, 0.1)) == NULL  # pointer checks come first
+    L = ops.lib()
+    st = L.ssm_scan_step_ex(addr(0), addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7), addr(8),
+                            addr(9), 4, 64, 16, ops.SSM_F32, _opts(1.0, 0.5), None)
+    assert st == ARG
+    # backward: the state gradients are validated like every other buffer
+    assert bwd_ex_call(_opts(0.3, 0.2)) == ARG
+    assert bwd_ex_call(_opts(dh0=BASE + 0 * STRIDE)) == ALIAS            # dh0 == x
+    assert bwd_ex_call(_opts(dh0=BASE + 9 * STRIDE)) == ALIAS            # dh0 == dx
+    assert bwd_ex_call(_opts(dh_final=BASE + 9 * STRIDE)) == ALIAS       # dh_final == dx
+    assert bwd_ex_call(_opts(dh0=BASE + 20 * STRIDE + 2)) == ALIGN
+    assert bwd_ex_call(_opts(dh_final=BASE + 20 * STRIDE + 1)) == ALIGN
