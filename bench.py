@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|step|fwd5|bwd|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -53,10 +53,12 @@ def step_bytes(b, d, n, es, gated):
     return 2 * H * 4 + E * es * (3 if gated else 2) + E * es + 2 * b * n * es + d * n * 4 + 2 * d * 4
 
 
-def bwd_bytes(b, l, d, n, gated):
+def bwd_bytes(b, l, d, n, gated, es=4):
+    """activations (x, delta_raw, z, dy in; dx, ddelta_raw, dz out) and B, C at the I/O
+    size es; dB, dC and the parameter gradients in fp32"""
     E, S = b * l * d, b * l * n
-    reads = E * 4 * (4 if gated else 3) + 2 * S * 4 + d * n * 4 + 2 * d * 4
-    writes = E * 4 * (3 if gated else 2) + 2 * S * 4 + d * n * 4 + 2 * d * 4
+    reads = E * es * (4 if gated else 3) + 2 * S * es + d * n * 4 + 2 * d * 4
+    writes = E * es * (3 if gated else 2) + 2 * S * 4 + d * n * 4 + 2 * d * 4
     return reads + writes
 
 
@@ -129,7 +131,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "conv", "conv_bf16", "conv_step", "conv_bwd",
                              "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -207,23 +209,25 @@ def main():
             (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
 
-    def bwd_case(name="fwdbwd_b4_l2048_d2048"):
+    def bwd_case(name="fwdbwd_b4_l2048_d2048", io="fp32"):
+        # io = "bf16": the same workload with its activations, B, C and dy rounded to bf16
         w = W.WORKLOADS[name]
         inp = W.make_inputs(w)
         b, l, d, n = w.batch, w.seqlen, w.dim, w.dstate
-        nb = bwd_bytes(b, l, d, n, w.gated)
+        nb = bwd_bytes(b, l, d, n, w.gated, 2 if io == "bf16" else 4)
         nsets = 2
-        base = dict(x=t32(inp["x"]), dr=t32(inp["delta_raw"]), z=t32(inp["z"]), B=t32(inp["B"]), C=t32(inp["C"]),
-                    dy=t32(inp["dy"]))
+        base = dict(x=tio(inp["x"], io), dr=tio(inp["delta_raw"], io), z=tio(inp["z"], io), B=tio(inp["B"], io),
+                    C=tio(inp["C"], io), dy=tio(inp["dy"], io))
         sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
         A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
         f = torch.float32
-        outs = [{"dx": torch.empty((b, l, d), dtype=f, device=dev), "ddelta_raw": torch.empty((b, l, d), dtype=f, device=dev),
-                 "dz": torch.empty((b, l, d), dtype=f, device=dev), "dB": torch.empty((b, l, n), dtype=f, device=dev),
+        a = torch.bfloat16 if io == "bf16" else f
+        outs = [{"dx": torch.empty((b, l, d), dtype=a, device=dev), "ddelta_raw": torch.empty((b, l, d), dtype=a, device=dev),
+                 "dz": torch.empty((b, l, d), dtype=a, device=dev), "dB": torch.empty((b, l, n), dtype=f, device=dev),
                  "dC": torch.empty((b, l, n), dtype=f, device=dev), "dA_log": torch.empty((d, n), dtype=f, device=dev),
                  "dD": torch.empty((d,), dtype=f, device=dev), "d_dt_bias": torch.empty((d,), dtype=f, device=dev)}
                 for _ in range(nsets)]
-        wsb = ops.bwd_workspace_bytes(b, l, d, n)
+        wsb = ops.bwd_workspace_bytes(b, l, d, n, ops.SSM_BF16 if io == "bf16" else ops.SSM_F32)
         wss = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nsets)]
 
         def fn(i):
@@ -234,7 +238,7 @@ def main():
         wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
         gbs = nb / (ev_ms * 1e-3) / 1e9
         log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  workspace %.1f MB" %
-            ("bwd_b4_l2048_d2048", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
+            ("bwd_b4_l2048_d2048" if io == "fp32" else "bwd_bf16_b4_l2048_d2048", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, workspace_bytes=wsb)
 
     def conv_case(name, min_bytes_rotation=1.2e9):
@@ -311,6 +315,8 @@ def main():
         results["step_b256_d5120"] = step_case()
     if args.only in ("all", "bwd"):
         results["bwd_b4_l2048_d2048"] = bwd_case()
+    if args.only in ("all", "bwd_bf16"):
+        results["bwd_bf16_b4_l2048_d2048"] = bwd_case(io="bf16")
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):

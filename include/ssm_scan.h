@@ -122,7 +122,9 @@ int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void
  *   deterministic_backward.py (ordered_cumsum: partials added in lexical
  *   (batch, chunk) order) and the deterministic row partial of
  *   mamba3_preprocess_backward.slang (dt_bias_partial).
- *   This build supports io_dtype = SSM_F32 only (SSM_ERR_UNSUPPORTED otherwise). */
+ *   io_dtype SSM_F32 or SSM_BF16: x, delta_raw, z, B, C, dy are read and dx, ddelta_raw,
+ *   dz written in io_dtype (bf16 rounded to nearest even); dB, dC and the parameter
+ *   gradients are fp32 in both cases, as are the state and all arithmetic. */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                     int64_t d_state, int io_dtype);
 int ssm_scan_bwd(const void* x, const void* delta_raw, const void* z, const void* B,

@@ -211,21 +211,23 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   float* dh0 = options ? options->dh0 : nullptr;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
-  if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
   if (!workspace) return SSM_ERR_WORKSPACE;
   const ssm::BwdLayout l = ssm::bwd_layout(batch, seqlen, d_inner, (int)d_state);
   if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
-  const void* all[] = {x, delta_raw, z, B, C, A_log, D_skip, dt_bias, h0, dy,
-                       dx, ddelta_raw, dz, dB, dC, dA_log, dD, d_dt_bias, dh_final, dh0};
-  for (const void* p : all)
+  const size_t es = esize(io_dtype);
+  const void* io_ptrs[] = {x, delta_raw, z, B, C, dy, dx, ddelta_raw, dz};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f32_ptrs[] = {A_log, D_skip, dt_bias, h0, dB, dC, dA_log, dD, d_dt_bias, dh_final, dh0};
+  for (const void* p : f32_ptrs)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
   const size_t H = (size_t)batch * d_inner * d_state, P = (size_t)d_inner * d_state;
-  const Range ins[] = {rng(x, E * 4), rng(delta_raw, E * 4), rng(z, z ? E * 4 : 0), rng(B, S * 4),
-                       rng(C, S * 4), rng(A_log, P * 4), rng(D_skip, D_skip ? d_inner * 4 : 0),
-                       rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * 4),
+  const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
+                       rng(C, S * es), rng(A_log, P * 4), rng(D_skip, D_skip ? d_inner * 4 : 0),
+                       rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * es),
                        rng(dh_final, dh_final ? H * 4 : 0)};
-  const Range outs[] = {rng(dx, E * 4), rng(ddelta_raw, E * 4), rng(dz, dz && z ? E * 4 : 0),
+  const Range outs[] = {rng(dx, E * es), rng(ddelta_raw, E * es), rng(dz, dz && z ? E * es : 0),
                         rng(dB, S * 4), rng(dC, S * 4), rng(dA_log, dA_log ? P * 4 : 0),
                         rng(dD, dD ? d_inner * 4 : 0), rng(d_dt_bias, d_dt_bias ? d_inner * 4 : 0),
                         rng(workspace, l.total), rng(dh0, dh0 ? H * 4 : 0)};
@@ -238,10 +240,9 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   }
 
   ssm::BwdArgs a;
-  a.x = (const float*)x; a.delta_raw = (const float*)delta_raw; a.z = (const float*)z;
-  a.B = (const float*)B; a.C = (const float*)C; a.A_log = A_log; a.D_skip = D_skip; a.dt_bias = dt_bias;
-  a.h0 = h0; a.dy = (const float*)dy; a.dx = (float*)dx; a.ddelta_raw = (float*)ddelta_raw;
-  a.dz = z ? (float*)dz : nullptr; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
+  a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log; a.D_skip = D_skip;
+  a.dt_bias = dt_bias; a.h0 = h0; a.dy = dy; a.dx = dx; a.ddelta_raw = ddelta_raw;
+  a.dz = z ? dz : nullptr; a.bf16 = io_dtype == SSM_BF16; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
   a.d_dt_bias = d_dt_bias; a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
   a.dh_final = dh_final; a.dh0 = dh0; a.dt_lo = dt_lo; a.dt_hi = dt_hi;
   return ssm::launch_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;

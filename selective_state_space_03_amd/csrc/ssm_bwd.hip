@@ -1,4 +1,5 @@
-// ssm_bwd.hip -- backward of the selective scan for gfx950 (fp32 I/O).
+// ssm_bwd.hip -- backward of the selective scan for gfx950 (fp32 or bf16 I/O; state,
+// arithmetic and dB, dC and the parameter gradients in fp32).
 //
 // Gradients of the loss sum(dy * y) (mamba-rs kernels.rs, MambaKernels fields, lists
 // the pieces: ssm_backward_local for the per-element state, input and step-size
@@ -163,10 +164,10 @@ __device__ __forceinline__ Lane lane_setup(int64_t ngroups, int64_t nseg, int64_
 // segment start, Delta sums, and the segment's end state.  One barrier per chunk:
 // the prep of chunk c+1 goes to the other half of double-buffered LDS while chunk c
 // is scanned from registers.
-template <int S, int G>
+template <typename T, int S, int G>
 __global__ void __launch_bounds__(64 * G)
-chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
-                 const float* __restrict__ Bm, const float* __restrict__ A_log,
+chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
+                 const T* __restrict__ Bm, const float* __restrict__ A_log,
                  const float* __restrict__ dt_bias, float* __restrict__ hrel, float* __restrict__ cumd,
                  float* __restrict__ hseg, float* __restrict__ sdseg, int64_t L, int64_t Dm, int N,
                  int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
@@ -195,9 +196,9 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
       const int t = q.wave + G * i;
       const bool v = q.dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-      lx[i] = v ? x[idx] : 0.f;
-      lr[i] = v ? delta_raw[idx] : 0.f;
-      lb[i] = (t < tvalid && q.lane < N) ? Bm[(row0 + t0 + t) * N + q.lane] : 0.f;
+      lx[i] = v ? io<T>::ld(x, idx) : 0.f;
+      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
+      lb[i] = (t < tvalid && q.lane < N) ? io<T>::ld(Bm, (row0 + t0 + t) * N + q.lane) : 0.f;
     }
   };
   auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
@@ -255,10 +256,10 @@ chunk_rel_kernel(const float* __restrict__ x, const float* __restrict__ delta_ra
 
 // ---- 2. reverse recurrence from a zero carry per segment: the carry a_t G_t leaving
 // the segment's first step (same double-buffered one-barrier-per-chunk structure)
-template <int S, int G, bool GATED>
+template <typename T, int S, int G, bool GATED>
 __global__ void __launch_bounds__(64 * G)
-seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
-               const float* __restrict__ dy, const float* __restrict__ Cm,
+seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
+               const T* __restrict__ dy, const T* __restrict__ Cm,
                const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                float* __restrict__ gseg, int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks,
                int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
@@ -286,10 +287,10 @@ seg_adj_kernel(const float* __restrict__ delta_raw, const float* __restrict__ z,
       const int t = q.wave + G * i;
       const bool v = q.dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-      lr[i] = v ? delta_raw[idx] : 0.f;
-      ly[i] = v ? dy[idx] : 0.f;
-      lz[i] = (GATED && v) ? z[idx] : 0.f;
-      lc[i] = (t < tvalid && q.lane < N) ? Cm[(row0 + t0 + t) * N + q.lane] : 0.f;
+      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
+      ly[i] = v ? io<T>::ld(dy, idx) : 0.f;
+      lz[i] = (GATED && v) ? io<T>::ld(z, idx) : 0.f;
+      lc[i] = (t < tvalid && q.lane < N) ? io<T>::ld(Cm, (row0 + t0 + t) * N + q.lane) : 0.f;
     }
   };
   auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
@@ -375,15 +376,15 @@ seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
 }
 
 // ---- 4. main backward per (b, tile, segment): chunks in reverse order
-template <int S, int G, bool GATED>
+template <typename T, int S, int G, bool GATED>
 __global__ void __launch_bounds__(64 * G)
-bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw,
-                const float* __restrict__ z, const float* __restrict__ Bm, const float* __restrict__ Cm,
+bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
+                const T* __restrict__ z, const T* __restrict__ Bm, const T* __restrict__ Cm,
                 const float* __restrict__ A_log, const float* __restrict__ D_skip,
-                const float* __restrict__ dt_bias, const float* __restrict__ dy,
+                const float* __restrict__ dt_bias, const T* __restrict__ dy,
                 const float* __restrict__ hrel, const float* __restrict__ cumd,
                 const float* __restrict__ hin, const float* __restrict__ gin,
-                float* __restrict__ dx, float* __restrict__ ddelta_raw, float* __restrict__ dz,
+                T* __restrict__ dx, T* __restrict__ ddelta_raw, T* __restrict__ dz,
                 float* __restrict__ pdB, float* __restrict__ pdC, float* __restrict__ pdA,
                 float* __restrict__ pdD, float* __restrict__ pdbias, int64_t L, int64_t Dm, int N,
                 int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
@@ -435,13 +436,13 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
       const int t = wave + G * i;
       const bool v = dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + d;
-      lx[i] = v ? x[idx] : 0.f;
-      lr[i] = v ? delta_raw[idx] : 0.f;
-      ly[i] = v ? dy[idx] : 0.f;
-      lz[i] = (GATED && v) ? z[idx] : 0.f;
+      lx[i] = v ? io<T>::ld(x, idx) : 0.f;
+      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
+      ly[i] = v ? io<T>::ld(dy, idx) : 0.f;
+      lz[i] = (GATED && v) ? io<T>::ld(z, idx) : 0.f;
       const bool ok = t < tvalid && lane < N;
       const int64_t o = (row0 + t0 + t) * N + lane;
-      lbc[i] = ok ? make_float2(Bm[o], Cm[o]) : make_float2(0.f, 0.f);
+      lbc[i] = ok ? make_float2(io<T>::ld(Bm, o), io<T>::ld(Cm, o)) : make_float2(0.f, 0.f);
     }
   };
   load(q.c_end - 1);
@@ -516,7 +517,7 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
           float s = dsk * ex[i];
 #pragma unroll
           for (int w = 0; w < G; ++w) s += yp[(t * G + w) * 64 + lane];
-          dz[(row0 + t0 + t) * Dm + d] = egz[i] * s;
+          io<T>::st(dz, (row0 + t0 + t) * Dm + d, egz[i] * s);
         }
       }
     }
@@ -572,9 +573,9 @@ bwd_main_kernel(const float* __restrict__ x, const float* __restrict__ delta_raw
           P2 += qv.y;
         }
         const int64_t idx = (row0 + t0 + t) * Dm + d;
-        dx[idx] = fmaf(eg[i], dsk, edelta[i] * P1);
+        io<T>::st(dx, idx, fmaf(eg[i], dsk, edelta[i] * P1));
         const float dr = fmaf(ex[i], P1, P2) * esig[i];
-        ddelta_raw[idx] = dr;
+        io<T>::st(ddelta_raw, idx, dr);
         dD_acc = fmaf(eg[i], ex[i], dD_acc);
         db_acc += dr;
       }
@@ -647,8 +648,11 @@ reduce_params_kernel(const float* __restrict__ pdA, const float* __restrict__ pd
   }
 }
 
-template <int G>
+template <typename T, int G>
 hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipStream_t stream) {
+  const T *x = (const T*)a.x, *dr = (const T*)a.delta_raw, *z = (const T*)a.z, *dy = (const T*)a.dy;
+  const T *Bm = (const T*)a.B, *Cm = (const T*)a.C;
+  T *dx = (T*)a.dx, *ddr = (T*)a.ddelta_raw, *dz = (T*)a.dz;
   constexpr int S = kS;
   const unsigned blocks = (unsigned)(a.batch * l.nseg * l.ngroups);
   float* hrel = (float*)(ws + l.off_hrel);
@@ -659,17 +663,17 @@ hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipSt
   float* hin = (float*)(ws + l.off_hin);
   float* gin = (float*)(ws + l.off_gin);
   hipError_t e;
-  hipLaunchKernelGGL((chunk_rel_kernel<S, G>), dim3(blocks), dim3(64 * G), 0, stream, a.x, a.delta_raw, a.B,
+  hipLaunchKernelGGL((chunk_rel_kernel<T, S, G>), dim3(blocks), dim3(64 * G), 0, stream, x, dr, Bm,
                      a.A_log, a.dt_bias, hrel, cumd, hseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
                      l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.z)
-    hipLaunchKernelGGL((seg_adj_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
-                       a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
+    hipLaunchKernelGGL((seg_adj_kernel<T, S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, dr, z,
+                       dy, Cm, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
                        l.segc, l.nseg, a.dt_lo, a.dt_hi);
   else
-    hipLaunchKernelGGL((seg_adj_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.delta_raw, a.z,
-                       a.dy, a.C, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
+    hipLaunchKernelGGL((seg_adj_kernel<T, S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, dr, z,
+                       dy, Cm, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
                        l.segc, l.nseg, a.dt_lo, a.dt_hi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
@@ -684,14 +688,14 @@ hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipSt
   float* pdD = pdA + (size_t)a.batch * l.nseg * a.dim * a.dstate;
   float* pdb = pdD + (size_t)a.batch * l.nseg * a.dim;
   if (a.z)
-    hipLaunchKernelGGL((bwd_main_kernel<S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
-                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
-                       a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
+    hipLaunchKernelGGL((bwd_main_kernel<T, S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, x,
+                       dr, z, Bm, Cm, a.A_log, a.D_skip, a.dt_bias, dy, hrel, cumd, hin, gin,
+                       dx, ddr, dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
                        l.ngroups, l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, a.x,
-                       a.delta_raw, a.z, a.B, a.C, a.A_log, a.D_skip, a.dt_bias, a.dy, hrel, cumd, hin, gin,
-                       a.dx, a.ddelta_raw, a.dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
+    hipLaunchKernelGGL((bwd_main_kernel<T, S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, x,
+                       dr, z, Bm, Cm, a.A_log, a.D_skip, a.dt_bias, dy, hrel, cumd, hin, gin,
+                       dx, ddr, dz, pdB, pdC, pdA, pdD, pdb, a.seqlen, a.dim, a.dstate,
                        l.ngroups, l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   return hipGetLastError();
 }
@@ -703,10 +707,10 @@ hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
   char* ws = (char*)workspace;
   hipError_t e;
   switch (waves_for(a.dstate)) {
-    case 1: e = launch_segments<1>(a, l, ws, stream); break;
-    case 2: e = launch_segments<2>(a, l, ws, stream); break;
-    case 4: e = launch_segments<4>(a, l, ws, stream); break;
-    default: e = launch_segments<8>(a, l, ws, stream); break;
+    case 1: e = a.bf16 ? launch_segments<bf16_t, 1>(a, l, ws, stream) : launch_segments<float, 1>(a, l, ws, stream); break;
+    case 2: e = a.bf16 ? launch_segments<bf16_t, 2>(a, l, ws, stream) : launch_segments<float, 2>(a, l, ws, stream); break;
+    case 4: e = a.bf16 ? launch_segments<bf16_t, 4>(a, l, ws, stream) : launch_segments<float, 4>(a, l, ws, stream); break;
+    default: e = a.bf16 ? launch_segments<bf16_t, 8>(a, l, ws, stream) : launch_segments<float, 8>(a, l, ws, stream); break;
   }
   if (e != hipSuccess) return e;
   {

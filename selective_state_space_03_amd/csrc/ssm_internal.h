@@ -44,19 +44,19 @@ struct StepArgs {
 };
 
 struct BwdArgs {
-  const float* x;
-  const float* delta_raw;
-  const float* z;  // nullable
-  const float* B;
-  const float* C;
+  const void* x;  // x, delta_raw, z, B, C, dy, dx, ddelta_raw, dz: io dtype
+  const void* delta_raw;
+  const void* z;  // nullable
+  const void* B;
+  const void* C;
   const float* A_log;
   const float* D_skip;   // nullable
   const float* dt_bias;  // nullable
   const float* h0;       // nullable
-  const float* dy;
-  float* dx;
-  float* ddelta_raw;
-  float* dz;  // non-null iff z
+  const void* dy;
+  void* dx;
+  void* ddelta_raw;
+  void* dz;  // non-null iff z
   float* dB;
   float* dC;
   float* dA_log;     // nullable
@@ -66,6 +66,7 @@ struct BwdArgs {
   float* dh0 = nullptr;             // [B, D, N]: gradient of h0 (nullable: not written)
   int64_t batch, seqlen, dim;
   int dstate;
+  int bf16;  // io dtype is bf16
   float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
 };
 

@@ -125,7 +125,7 @@ def make_inputs(w: Workload, *, batch: Optional[int] = None, seqlen: Optional[in
         out["state"] = (0.1 * rng.standard_normal((b, d, n))).astype(np.float32)
     else:
         out["h0"] = (0.1 * rng.standard_normal((b, d, n))).astype(np.float32) if random_h0 else None
-        out["dy"] = rng.standard_normal((b, l, d)).astype(np.float32) if want_dy else None
+        out["dy"] = round_to_io(rng.standard_normal((b, l, d)), io) if want_dy else None
     return out
 
 

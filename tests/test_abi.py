@@ -155,7 +155,9 @@ def test_bwd_validation():
     assert bwd_call(dz=None) == NULL                 # z given, dz missing
     assert bwd_call(dB=None) == NULL
     assert bwd_call(n=0) == DIM
-    assert bwd_call(io=ops.SSM_BF16) == UNSUP
+    assert bwd_call(io=7) == UNSUP
+    assert bwd_call(io=ops.SSM_BF16, dy=addr(8, 1)) == ALIGN   # bf16 needs 2 B
+    assert bwd_call(io=ops.SSM_BF16, dB=addr(12, 2)) == ALIGN  # dB stays fp32
     assert bwd_call(ws=None) == WS
     assert bwd_call(wsb=1024) == WS
     assert bwd_call(ws=addr(17, 64)) == WS           # workspace must be 256 B aligned
