@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -131,7 +131,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "train", "conv", "conv_bf16", "conv_step", "conv_bwd",
                              "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -161,7 +161,9 @@ def main():
         t = t32(a)
         return t.to(torch.bfloat16) if (t is not None and io == "bf16") else t
 
-    def fwd_case(name, min_bytes_rotation=1.2e9):
+    def fwd_case(name, min_bytes_rotation=1.2e9, save=False):
+        # save: also write the chunk states for the backward (same algorithmic bytes;
+        # the states are an implementation overhead of the training path)
         w = W.WORKLOADS[name]
         inp = W.make_inputs(w, with_dy=False)
         io = w.io
@@ -174,16 +176,18 @@ def main():
         A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
         ys = [torch.empty_like(base["x"]) for _ in range(nsets)]
         hfs = [torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in range(nsets)]
+        css = [torch.empty(ops.chunk_states_shape(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.float32,
+                           device=dev) if save else None for _ in range(nsets)]
 
         def fn(i):
             s = sets[i]
             ops.ssm_scan_fwd(s["x"], s["dr"], s["B"], s["C"], A_log, D_skip=Dsk, dt_bias=dtb, z=s["z"],
-                             y=ys[i], h_final=hfs[i])
+                             y=ys[i], h_final=hfs[i], chunk_states=css[i])
 
         wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
         gbs = nb / (ev_ms * 1e-3) / 1e9
         log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
-            (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+            (name + ("_save" if save else ""), ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs,
                     wall_gbs=nb / (wall_ms * 1e-3) / 1e9, inp=inp)
 
@@ -209,8 +213,9 @@ def main():
             (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
 
-    def bwd_case(name="fwdbwd_b4_l2048_d2048", io="fp32"):
+    def bwd_case(name="fwdbwd_b4_l2048_d2048", io="fp32", saved=False):
         # io = "bf16": the same workload with its activations, B, C and dy rounded to bf16
+        # saved: the backward reuses chunk states written by the forward (made untimed)
         w = W.WORKLOADS[name]
         inp = W.make_inputs(w)
         b, l, d, n = w.batch, w.seqlen, w.dim, w.dstate
@@ -229,16 +234,24 @@ def main():
                 for _ in range(nsets)]
         wsb = ops.bwd_workspace_bytes(b, l, d, n, ops.SSM_BF16 if io == "bf16" else ops.SSM_F32)
         wss = [torch.empty((wsb,), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        css = [None] * nsets
+        if saved:
+            for i, s in enumerate(sets):
+                css[i] = torch.empty(ops.chunk_states_shape(b, l, d, n), dtype=torch.float32, device=dev)
+                ops.ssm_scan_fwd(s["x"], s["dr"], s["B"], s["C"], A_log, D_skip=Dsk, dt_bias=dtb, z=s["z"],
+                                 return_final_state=False, chunk_states=css[i])
+            torch.cuda.synchronize()
 
         def fn(i):
             s = sets[i]
             ops.ssm_scan_bwd(s["x"], s["dr"], s["B"], s["C"], A_log, s["dy"], D_skip=Dsk, dt_bias=dtb, z=s["z"],
-                             workspace=wss[i], out=outs[i])
+                             workspace=wss[i], out=outs[i], chunk_states=css[i])
 
         wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
         gbs = nb / (ev_ms * 1e-3) / 1e9
+        label = ("bwd_b4_l2048_d2048" if io == "fp32" else "bwd_bf16_b4_l2048_d2048") + ("_saved" if saved else "")
         log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  workspace %.1f MB" %
-            ("bwd_b4_l2048_d2048" if io == "fp32" else "bwd_bf16_b4_l2048_d2048", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
+            (label, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, workspace_bytes=wsb)
 
     def conv_case(name, min_bytes_rotation=1.2e9):
@@ -317,6 +330,10 @@ def main():
         results["bwd_b4_l2048_d2048"] = bwd_case()
     if args.only in ("all", "bwd_bf16"):
         results["bwd_bf16_b4_l2048_d2048"] = bwd_case(io="bf16")
+    if args.only in ("all", "train"):
+        # the training pair with the forward's chunk states reused by the backward
+        results["fwd_save_b4_l2048_d2048"] = fwd_case("fwdbwd_b4_l2048_d2048", save=True)
+        results["bwd_saved_b4_l2048_d2048"] = bwd_case(saved=True)
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):

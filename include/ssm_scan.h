@@ -156,7 +156,17 @@ typedef struct {
    * Both naturally aligned; dh_final must not overlap an output, dh0 nothing else. */
   const float* dh_final;
   float* dh0;
+  /* Chunk states [batch, ceil(seqlen / 16), d_state, d_inner] fp32 (not allowed in the
+   * step): the state entering every 16-step chunk, h_{16k-1} (h0 for k = 0), the
+   * forward's states saved for reuse by the backward.  ssm_scan_fwd_ex writes them
+   * (d_state 9..16 only, SSM_ERR_UNSUPPORTED otherwise); ssm_scan_bwd_ex given them
+   * skips recomputing the forward states.  The backward must get the states its own
+   * inputs and options produce.  ssm_scan_chunk_states_bytes() gives the size; one
+   * batch element's part must stay below 2^31 bytes (SSM_ERR_UNSUPPORTED). */
+  float* chunk_states;
 } ssm_scan_options;
+
+size_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
 
 int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const void* B,
                     const void* C, const float* A_log, const float* D_skip, const float* dt_bias,

@@ -44,7 +44,7 @@ bool conv_dims_ok(int64_t batch, int64_t seqlen, int64_t dim, int64_t width) {
 
 // Options of the _ex entry points: clamp bounds (dt_max <= 0: no upper bound) and the
 // backward-only state gradients.  NULL options are the defaults.
-bool options_ok(const ssm_scan_options* o, bool backward, float* lo, float* hi) {
+bool options_ok(const ssm_scan_options* o, bool backward, float* lo, float* hi, bool step = false) {
   *lo = 0.f;
   *hi = __builtin_inff();
   if (!o) return true;
@@ -55,7 +55,14 @@ bool options_ok(const ssm_scan_options* o, bool backward, float* lo, float* hi) 
   }
   *lo = o->dt_min;
   if (!backward && (o->dh_final || o->dh0)) return false;
+  if (step && o->chunk_states) return false;
   return true;
+}
+
+int64_t state_chunks(int64_t seqlen) { return (seqlen + ssm::kStateChunk - 1) / ssm::kStateChunk; }
+// one batch element's chunk states are addressed with 31-bit offsets
+bool chunk_states_fit(int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  return (uint64_t)state_chunks(seqlen) * (uint64_t)d_state * (uint64_t)d_inner * 4 < ((uint64_t)1 << 31);
 }
 
 }  // namespace
@@ -75,6 +82,11 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_ARG: return "SSM_ERR_ARG: an option value is out of range";
     default: return "unknown ssm_status";
   }
+}
+
+size_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (!dims_ok(batch, seqlen, d_inner, d_state)) return 0;
+  return (size_t)batch * state_chunks(seqlen) * d_state * d_inner * 4;
 }
 
 size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
@@ -113,7 +125,10 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
   const void* io_in[] = {x, delta_raw, z, B, C};
   for (const void* p : io_in)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  const void* f_in[] = {A_log, D_skip, dt_bias, h0, h_final};
+  float* chunk_states = options ? options->chunk_states : nullptr;
+  // saved chunk states come from the states-across-lanes kernel (d_state 9..16)
+  if (chunk_states && (d_state < 9 || !chunk_states_fit(seqlen, d_inner, d_state))) return SSM_ERR_UNSUPPORTED;
+  const void* f_in[] = {A_log, D_skip, dt_bias, h0, h_final, chunk_states};
   for (const void* p : f_in)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   if (!aligned(y, es)) return SSM_ERR_ALIGN;
@@ -123,18 +138,22 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
                        rng(C, S * es), rng(A_log, (size_t)d_inner * d_state * 4),
                        rng(D_skip, D_skip ? d_inner * 4 : 0), rng(dt_bias, dt_bias ? d_inner * 4 : 0),
                        rng(h0, h0 ? H * 4 : 0)};
-  const Range outs[] = {rng(y, E * es), rng(h_final, h_final ? H * 4 : 0)};
-  for (const Range& o : outs)
-    for (const Range& i : ins)
-      if (overlap(o, i)) return SSM_ERR_ALIAS;
-  if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+  const Range outs[] = {rng(y, E * es), rng(h_final, h_final ? H * 4 : 0),
+                        rng(chunk_states, chunk_states ? ssm_scan_chunk_states_bytes(batch, seqlen, d_inner, d_state) : 0)};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
 
   ssm::FwdArgs a;
   a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log; a.D_skip = D_skip;
   a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
   a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
   a.bf16 = io_dtype == SSM_BF16;
-  a.dt_lo = dt_lo; a.dt_hi = dt_hi;
+  a.dt_lo = dt_lo; a.dt_hi = dt_hi; a.chunk_states = chunk_states;
   return ssm::launch_fwd(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -151,7 +170,7 @@ int ssm_scan_step_ex(float* state, const void* x, const void* delta_raw, const v
                      const ssm_scan_options* options, hipStream_t stream) {
   if (!state || !x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
   float dt_lo, dt_hi;
-  if (!options_ok(options, false, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
+  if (!options_ok(options, false, &dt_lo, &dt_hi, true)) return SSM_ERR_ARG;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, 1, d_inner, d_state)) return SSM_ERR_DIM;
   if (batch * d_inner * 4 >= ((int64_t)1 << 31) * 256) return SSM_ERR_DIM;  // grid limit
@@ -209,6 +228,7 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   if (!options_ok(options, true, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
   const float* dh_final = options ? options->dh_final : nullptr;
   float* dh0 = options ? options->dh0 : nullptr;
+  const float* chunk_states = options ? options->chunk_states : nullptr;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
   if (!workspace) return SSM_ERR_WORKSPACE;
@@ -218,7 +238,8 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   const void* io_ptrs[] = {x, delta_raw, z, B, C, dy, dx, ddelta_raw, dz};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  const void* f32_ptrs[] = {A_log, D_skip, dt_bias, h0, dB, dC, dA_log, dD, d_dt_bias, dh_final, dh0};
+  if (chunk_states && !chunk_states_fit(seqlen, d_inner, d_state)) return SSM_ERR_UNSUPPORTED;
+  const void* f32_ptrs[] = {A_log, D_skip, dt_bias, h0, dB, dC, dA_log, dD, d_dt_bias, dh_final, dh0, chunk_states};
   for (const void* p : f32_ptrs)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
@@ -226,7 +247,8 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
                        rng(C, S * es), rng(A_log, P * 4), rng(D_skip, D_skip ? d_inner * 4 : 0),
                        rng(dt_bias, dt_bias ? d_inner * 4 : 0), rng(h0, h0 ? H * 4 : 0), rng(dy, E * es),
-                       rng(dh_final, dh_final ? H * 4 : 0)};
+                       rng(dh_final, dh_final ? H * 4 : 0),
+                       rng(chunk_states, chunk_states ? ssm_scan_chunk_states_bytes(batch, seqlen, d_inner, d_state) : 0)};
   const Range outs[] = {rng(dx, E * es), rng(ddelta_raw, E * es), rng(dz, dz && z ? E * es : 0),
                         rng(dB, S * 4), rng(dC, S * 4), rng(dA_log, dA_log ? P * 4 : 0),
                         rng(dD, dD ? d_inner * 4 : 0), rng(d_dt_bias, d_dt_bias ? d_inner * 4 : 0),
@@ -244,7 +266,7 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   a.dt_bias = dt_bias; a.h0 = h0; a.dy = dy; a.dx = dx; a.ddelta_raw = ddelta_raw;
   a.dz = z ? dz : nullptr; a.bf16 = io_dtype == SSM_BF16; a.dB = dB; a.dC = dC; a.dA_log = dA_log; a.dD = dD;
   a.d_dt_bias = d_dt_bias; a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
-  a.dh_final = dh_final; a.dh0 = dh0; a.dt_lo = dt_lo; a.dt_hi = dt_hi;
+  a.dh_final = dh_final; a.dh0 = dh0; a.dt_lo = dt_lo; a.dt_hi = dt_hi; a.chunk_states = chunk_states;
   return ssm::launch_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

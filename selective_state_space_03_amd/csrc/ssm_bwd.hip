@@ -30,9 +30,10 @@
 // exp(A * sum of Delta over the segment):
 //   1. chunk_rel : per (b, 64-channel tile, segment), forward from a zero state:
 //                  the state at every chunk start relative to the segment start, the
-//                  sum of Delta up to it, and the segment's end state and Delta sum;
+//                  sum of Delta up to it, and the segment's end state (skipped when the
+//                  forward saved the true chunk start states);
 //   2. seg_adj   : per (b, tile, segment), the reverse recurrence from a zero carry:
-//                  the carry leaving the segment's first step;
+//                  the carry leaving the segment's first step, and the segment's Delta sum;
 //   3. seg_pass  : per (b, d, n), sequential over segments: the true state entering
 //                  every segment (h0 first) and the true carry entering it from the
 //                  right;
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(64 * G)
 chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
                  const T* __restrict__ Bm, const float* __restrict__ A_log,
                  const float* __restrict__ dt_bias, float* __restrict__ hrel, float* __restrict__ cumd,
-                 float* __restrict__ hseg, float* __restrict__ sdseg, int64_t L, int64_t Dm, int N,
+                 float* __restrict__ hseg, int64_t L, int64_t Dm, int N,
                  int64_t ngroups, int64_t nchunks, int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
@@ -250,7 +251,6 @@ chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
 #pragma unroll
     for (int j = 0; j < S; ++j)
       if (j < q.nact) hseg[((q.b * nseg + q.seg) * N + q.n0 + j) * Dm + q.d] = h[j];
-    if (q.wave == 0) sdseg[(q.b * nseg + q.seg) * Dm + q.d] = sd;
   }
 }
 
@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(64 * G)
 seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
                const T* __restrict__ dy, const T* __restrict__ Cm,
                const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-               float* __restrict__ gseg, int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks,
+               float* __restrict__ gseg, float* __restrict__ sdseg, int64_t L, int64_t Dm, int N, int64_t ngroups, int64_t nchunks,
                int64_t segc, int64_t nseg, float dt_lo, float dt_hi) {
   constexpr int TC = kChunk;
   constexpr int EPL = (TC + G - 1) / G;
@@ -276,6 +276,7 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
     A2[j] = (q.dvalid && j < q.nact) ? a2_from_alog(A_log[q.d * N + q.n0 + j]) : 0.f;
     gc[j] = 0.f;
   }
+  float sd = 0.f;  // sum of Delta over the segment
   const int64_t row0 = q.b * L;
   // this wave's rows of a chunk (delta_raw, dy, z, C), loaded one chunk ahead of the prep
   float lr[EPL], ly[EPL], lz[EPL], lc[EPL];
@@ -328,6 +329,7 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
     }
 #pragma unroll
     for (int t = TC - 1; t >= 0; --t) {  // padded steps: Delta = g = 0
+      sd += v[t].x;
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         const float Gt = fmaf(v[t].y, cv[t][j], gc[j]);  // dLoss/dh_t
@@ -340,6 +342,8 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
 #pragma unroll
     for (int j = 0; j < S; ++j)
       if (j < q.nact) gseg[((q.b * nseg + q.seg) * N + q.n0 + j) * Dm + q.d] = gc[j];
+    // the segment's sum of Delta (its decay is exp(A * sum)), for the segment pass
+    if (q.wave == 0) sdseg[(q.b * nseg + q.seg) * Dm + q.d] = sd;
   }
 }
 
@@ -358,11 +362,13 @@ seg_pass_kernel(const float* __restrict__ hseg, const float* __restrict__ sdseg,
   const int n = (int)((i / Dm) % N);
   const int64_t d = i % Dm;
   const float A2 = a2_from_alog(A_log[d * N + n]);
-  float h = h0 ? h0[(b * Dm + d) * N + n] : 0.f;
-  for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t o = ((b * nseg + s) * N + n) * Dm + d;
-    hin[o] = h;
-    h = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), h, hseg[o]);
+  if (hin) {  // (skipped when the forward saved the chunk states)
+    float h = h0 ? h0[(b * Dm + d) * N + n] : 0.f;
+    for (int64_t s = 0; s < nseg; ++s) {
+      const int64_t o = ((b * nseg + s) * N + n) * Dm + d;
+      hin[o] = h;
+      h = fmaf(exp2_hw(A2 * sdseg[(b * nseg + s) * Dm + d]), h, hseg[o]);
+    }
   }
   // the carry beyond the last step is the gradient reaching h_final from outside; the
   // carry leaving the first segment is a_0 G_0 = dLoss/dh0
@@ -414,7 +420,8 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
     Av[j] = v ? -expf(A_log[d * N + n0 + j]) : 0.f;
     A2[j] = Av[j] * kLog2e;
     Gc[j] = v ? gin[o] : 0.f;  // carry entering the segment's last step
-    hi[j] = v ? hin[o] : 0.f;  // state entering the segment
+    // state entering the segment (zero when hrel holds the forward's true chunk states)
+    hi[j] = (v && hin) ? hin[o] : 0.f;
     dA[j] = 0.f;
   }
   float dD_acc = 0.f, db_acc = 0.f;
@@ -427,7 +434,7 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)((L - t0) < TC ? (L - t0) : TC);
-    lcd = dvalid ? cumd[(b * nchunks + c) * Dm + d] : 0.f;
+    lcd = (dvalid && cumd) ? cumd[(b * nchunks + c) * Dm + d] : 0.f;
 #pragma unroll
     for (int j = 0; j < S; ++j)
       lhr[j] = (dvalid && j < nact) ? hrel[((b * nchunks + c) * N + n0 + j) * Dm + d] : 0.f;
@@ -655,26 +662,33 @@ hipError_t launch_segments(const BwdArgs& a, const BwdLayout& l, char* ws, hipSt
   T *dx = (T*)a.dx, *ddr = (T*)a.ddelta_raw, *dz = (T*)a.dz;
   constexpr int S = kS;
   const unsigned blocks = (unsigned)(a.batch * l.nseg * l.ngroups);
-  float* hrel = (float*)(ws + l.off_hrel);
-  float* cumd = (float*)(ws + l.off_cumd);
-  float* hseg = (float*)(ws + l.off_hseg);
+  // With the forward's saved chunk states (the true state entering every chunk, in
+  // hrel's layout) the chunk-relative forward pass and the state half of the segment
+  // pass are skipped: bwd_main reads the saved states as start states, with a zero
+  // Delta sum and a zero segment entry state.
+  const bool saved = a.chunk_states != nullptr;
+  float* hrel = saved ? const_cast<float*>(a.chunk_states) : (float*)(ws + l.off_hrel);
+  float* cumd = saved ? nullptr : (float*)(ws + l.off_cumd);
+  float* hseg = saved ? nullptr : (float*)(ws + l.off_hseg);
   float* sdseg = (float*)(ws + l.off_sdseg);
   float* gseg = (float*)(ws + l.off_gseg);
-  float* hin = (float*)(ws + l.off_hin);
+  float* hin = saved ? nullptr : (float*)(ws + l.off_hin);
   float* gin = (float*)(ws + l.off_gin);
   hipError_t e;
-  hipLaunchKernelGGL((chunk_rel_kernel<T, S, G>), dim3(blocks), dim3(64 * G), 0, stream, x, dr, Bm,
-                     a.A_log, a.dt_bias, hrel, cumd, hseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
-                     l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!saved) {
+    hipLaunchKernelGGL((chunk_rel_kernel<T, S, G>), dim3(blocks), dim3(64 * G), 0, stream, x, dr, Bm,
+                       a.A_log, a.dt_bias, hrel, cumd, hseg, a.seqlen, a.dim, a.dstate, l.ngroups,
+                       l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.z)
     hipLaunchKernelGGL((seg_adj_kernel<T, S, G, true>), dim3(blocks), dim3(64 * G), 0, stream, dr, z,
-                       dy, Cm, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
-                       l.segc, l.nseg, a.dt_lo, a.dt_hi);
+                       dy, Cm, a.A_log, a.dt_bias, gseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
+                       l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   else
     hipLaunchKernelGGL((seg_adj_kernel<T, S, G, false>), dim3(blocks), dim3(64 * G), 0, stream, dr, z,
-                       dy, Cm, a.A_log, a.dt_bias, gseg, a.seqlen, a.dim, a.dstate, l.ngroups, l.nchunks,
-                       l.segc, l.nseg, a.dt_lo, a.dt_hi);
+                       dy, Cm, a.A_log, a.dt_bias, gseg, sdseg, a.seqlen, a.dim, a.dstate, l.ngroups,
+                       l.nchunks, l.segc, l.nseg, a.dt_lo, a.dt_hi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const int64_t n = a.batch * a.dim * a.dstate;

@@ -417,13 +417,13 @@ __device__ __forceinline__ void lane_scan16(std::integer_sequence<int, I...>, fl
   (lane_step<I>(h, dl, dlx, A2, bv[I], cv[I]), ...);
 }
 
-template <typename T, int W, bool GATED>
+template <typename T, int W, bool GATED, bool SAVE>
 __global__ void __launch_bounds__(64 * W)
 fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
                  const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
                  const float* __restrict__ D_skip, const float* __restrict__ dt_bias,
                  const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_final, int L, int Dm,
-                 int N, int ngroups, int nblocks, float dt_lo, float dt_hi) {
+                 int N, int ngroups, int nblocks, float dt_lo, float dt_hi, float* __restrict__ chunk_states) {
   constexpr int TT = 16;  // steps per tile = lanes per row
   constexpr int R = 8;    // ring of loaded tiles (tile mod 8); the loop is unrolled by 8
   constexpr int P = 6;    // tiles loaded ahead
@@ -442,6 +442,9 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   __shared__ __attribute__((aligned(16))) float act[NB][3][TT * SA];
   __shared__ __attribute__((aligned(16))) float bct[NB][2][16 * SP];
   __shared__ float yb[2][TT * SA];
+  // SAVE: the state entering tile k, hs[k & 1][state][channel], stored one iteration
+  // later as whole rows of chunk_states[b][k][state][channel]
+  __shared__ float hsv[SAVE ? 2 : 1][SAVE ? 16 * SA : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -537,6 +540,15 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   auto store_y = [&](int j, int ybuf) __attribute__((always_inline)) {
     if (j >= 0) buf_st<T>(yb[ybuf][qt * SA + qc], ry, aoff + (uint32_t)j * tile_bytes);
   };
+  // chunk states of this batch element: tile j at rows [j*N, j*N + N) of [*, Dm]; this
+  // lane stores state row qt (when qt < N) of channel g0 + qc
+  const __amdgpu_buffer_rsrc_t rcs =
+      tile_rsrc(SAVE ? chunk_states + (int64_t)b * ntiles * N * Dm : nullptr, (int64_t)ntiles * N * Dm * 4);
+  const uint32_t csoff = (SAVE && qt < N && g0 + qc < Dm) ? (uint32_t)((qt * Dm + g0 + qc) * 4) : kOutside;
+  const uint32_t cs_tile_bytes = (uint32_t)(N * Dm * 4);
+  auto store_state = [&](int j) __attribute__((always_inline)) {
+    if (SAVE && j >= 0) buf_st<float>(hsv[j & 1][qt * SA + qc], rcs, csoff + (uint32_t)j * cs_tile_bytes);
+  };
 
   // prologue: tiles 0..P-1 in flight; tiles 0 and 1 staged; tile 0 prepped
 #pragma unroll
@@ -563,6 +575,10 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
       const float zk = GATED ? act[u % NB][2][pcol] : 0.f;
       stage_tile((u + 2) % R, (u + 2) % NB);
       store_y(k - 1, (u + 1) & 1);
+      if (SAVE) {
+        store_state(k - 1);
+        hsv[u & 1][li * SA + wave * 4 + row] = h;  // the state entering tile k
+      }
       lane_scan16(std::make_integer_sequence<int, 16>(), h, dl, dlx, A2, bv, cv);
       // readout of tile k in the prep lane of step li
       const float s = row_transpose_sum16(cv, lane);
@@ -575,6 +591,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     }
   }
   store_y(ntiles - 1, (ntiles - 1) & 1);
+  store_state(ntiles - 1);
   if (h_final && nvalid) h_final[hb] = h;
 }
 
@@ -583,10 +600,11 @@ hipError_t launch_lanes_w(const FwdArgs& a, hipStream_t stream) {
   const int ngroups = (int)((a.dim + 4 * W - 1) / (4 * W));
   const int64_t nblocks = (int64_t)ngroups * a.batch;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_lanes_kernel<T, W, GATED>), dim3((unsigned)nblocks), dim3(64 * W), 0, stream,
+  auto kern = a.chunk_states ? fwd_lanes_kernel<T, W, GATED, true> : fwd_lanes_kernel<T, W, GATED, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(64 * W), 0, stream,
                      (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B, (const T*)a.C, a.A_log,
                      a.D_skip, a.dt_bias, a.h0, (T*)a.y, a.h_final, (int)a.seqlen, (int)a.dim, a.dstate, ngroups,
-                     (int)nblocks, a.dt_lo, a.dt_hi);
+                     (int)nblocks, a.dt_lo, a.dt_hi, a.chunk_states);
   return hipGetLastError();
 }
 
@@ -633,7 +651,8 @@ int pick_states_per_wave(const FwdArgs& a, int ns) {
 template <typename T, bool GATED>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int ns = a.dstate <= 4 ? 4 : (a.dstate <= 8 ? 8 : 16);
-  if (ns == 16 && !getenv("SSM_FWD_STATES_PER_WAVE")) return launch_lanes<T, GATED>(a, stream);
+  // (saving chunk states is done by the states-across-lanes kernel only)
+  if (ns == 16 && (a.chunk_states || !getenv("SSM_FWD_STATES_PER_WAVE"))) return launch_lanes<T, GATED>(a, stream);
   const int s = pick_states_per_wave(a, ns);
   if (ns == 16) {
     switch (s) {

@@ -24,7 +24,9 @@ struct FwdArgs {
   int dstate;
   int bf16;  // io dtype is bf16
   float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
+  float* chunk_states = nullptr;  // [B, ceil(L/16), N, D]: state entering each 16-step chunk
 };
+constexpr int kStateChunk = 16;  // steps per saved chunk state (forward tile = backward chunk)
 
 struct StepArgs {
   float* state;
@@ -64,6 +66,7 @@ struct BwdArgs {
   float* d_dt_bias;  // nullable
   const float* dh_final = nullptr;  // [B, D, N]: gradient reaching h_final (nullable: zero)
   float* dh0 = nullptr;             // [B, D, N]: gradient of h0 (nullable: not written)
+  const float* chunk_states = nullptr;  // the forward's saved chunk states (nullable: recomputed)
   int64_t batch, seqlen, dim;
   int dstate;
   int bf16;  // io dtype is bf16

@@ -12,7 +12,9 @@ Functions mirror the C entry points:
                 dt_min=None, dt_max=None) -> y
   ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=None, h0=None,
                workspace=None, out=None, dt_min=None, dt_max=None, dh_final=None,
-               return_dh0=False) -> dict of gradients (with "dh0" when asked for)
+               return_dh0=False, chunk_states=None) -> dict of gradients (with "dh0" when asked for)
+  (ssm_scan_fwd also takes chunk_states=: a [B, ceil(L/16), N, D] fp32 tensor it fills
+   with the state entering every 16-step chunk, which ssm_scan_bwd then reuses)
 The step-size clamp (dt_min, dt_max) and the state gradients go through the _ex entry
 points and their ssm_scan_options struct; without them the calls are the plain ones.
 """
@@ -33,14 +35,14 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPOR
           8: "SSM_ERR_ARG"}
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
-           "ssm_scan_bwd_ex", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
+           "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
            "ssm_conv1d_bwd")
 
 
 class ScanOptions(ctypes.Structure):
     """ssm_scan_options of include/ssm_scan.h"""
     _fields_ = [("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
-                ("dh_final", ctypes.c_void_p), ("dh0", ctypes.c_void_p)]
+                ("dh_final", ctypes.c_void_p), ("dh0", ctypes.c_void_p), ("chunk_states", ctypes.c_void_p)]
 SSM_ACT_NONE, SSM_ACT_SILU = 0, 1
 
 _lib = None
@@ -83,6 +85,8 @@ def lib():
         L.ssm_scan_step_ex.restype = I
         L.ssm_scan_bwd_ex.argtypes = [P] * 18 + [P, SZ] + [I64] * 4 + [I, OP, P]
         L.ssm_scan_bwd_ex.restype = I
+        L.ssm_scan_chunk_states_bytes.argtypes = [I64] * 4
+        L.ssm_scan_chunk_states_bytes.restype = SZ
         L.ssm_conv1d_fwd.argtypes = [P] * 4 + [I64] * 4 + [I, I, P]
         L.ssm_conv1d_fwd.restype = I
         L.ssm_conv1d_step.argtypes = [P] * 5 + [I64] * 3 + [I, I, P]
@@ -132,13 +136,19 @@ def _req(t, name, shape, dtype, device):
     return t
 
 
-def _options(dt_min, dt_max, dh_final=None, dh0=None):
+def _options(dt_min, dt_max, dh_final=None, dh0=None, chunk_states=None):
     """ssm_scan_options for the _ex entry points (None when nothing is set)"""
-    if dt_min is None and dt_max is None and dh_final is None and dh0 is None:
+    if dt_min is None and dt_max is None and dh_final is None and dh0 is None and chunk_states is None:
         return None
     o = ScanOptions(0.0 if dt_min is None else float(dt_min), 0.0 if dt_max is None else float(dt_max),
-                    None if dh_final is None else dh_final.data_ptr(), None if dh0 is None else dh0.data_ptr())
+                    None if dh_final is None else dh_final.data_ptr(), None if dh0 is None else dh0.data_ptr(),
+                    None if chunk_states is None else chunk_states.data_ptr())
     return ctypes.pointer(o)
+
+
+def chunk_states_shape(batch, seqlen, d_inner, d_state):
+    """shape of the saved chunk states: the state entering every 16-step chunk"""
+    return (batch, (seqlen + 15) // 16, d_state, d_inner)
 
 
 def fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=SSM_F32):
@@ -150,7 +160,8 @@ def bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=SSM_F32):
 
 
 def ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h0=None,
-                 y=None, h_final=None, return_final_state=True, workspace=None, dt_min=None, dt_max=None):
+                 y=None, h_final=None, return_final_state=True, workspace=None, dt_min=None, dt_max=None,
+                 chunk_states=None):
     b, l, d = x.shape
     n = B.shape[-1]
     dev, dt = x.device, x.dtype
@@ -172,7 +183,10 @@ def ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
                                _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
-                               b, l, d, n, io, _ptr(workspace), ws_bytes, _options(dt_min, dt_max), _stream())
+                               b, l, d, n, io, _ptr(workspace), ws_bytes,
+                               _options(dt_min, dt_max, chunk_states=_req(chunk_states, "chunk_states",
+                                                                          chunk_states_shape(b, l, d, n), f32, dev)),
+                               _stream())
     _check("ssm_scan_fwd_ex", st)
     return y, h_final
 
@@ -201,7 +215,8 @@ def ssm_scan_step(state, x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z
 
 
 def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=None, h0=None,
-                 workspace=None, out=None, dt_min=None, dt_max=None, dh_final=None, return_dh0=False):
+                 workspace=None, out=None, dt_min=None, dt_max=None, dh_final=None, return_dh0=False,
+                 chunk_states=None):
     b, l, d = x.shape
     n = B.shape[-1]
     dev, dt = x.device, x.dtype
@@ -228,6 +243,7 @@ def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=Non
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _req(dh_final, "dh_final", (b, d, n), f32, dev)
+    _req(chunk_states, "chunk_states", chunk_states_shape(b, l, d, n), f32, dev)
     if return_dh0 and out.get("dh0") is None:
         out["dh0"] = torch.empty((b, d, n), dtype=f32, device=dev)
     dh0 = out.get("dh0") if return_dh0 else None
@@ -237,7 +253,7 @@ def ssm_scan_bwd(x, delta_raw, B, C, A_log, dy, D_skip=None, dt_bias=None, z=Non
                                _ptr(out["ddelta_raw"]), _ptr(out.get("dz")), _ptr(out["dB"]), _ptr(out["dC"]),
                                _ptr(out.get("dA_log")), _ptr(out.get("dD")), _ptr(out.get("d_dt_bias")),
                                _ptr(workspace), ws_bytes, b, l, d, n, io,
-                               _options(dt_min, dt_max, dh_final, dh0), _stream())
+                               _options(dt_min, dt_max, dh_final, dh0, chunk_states), _stream())
     _check("ssm_scan_bwd_ex", st)
     return out
 

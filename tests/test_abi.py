@@ -251,3 +251,26 @@ def test_options_validation():
     assert bwd_ex_call(_opts(dh_final=BASE + 9 * STRIDE)) == ALIAS       # dh_final == dx
     assert bwd_ex_call(_opts(dh0=BASE + 20 * STRIDE + 2)) == ALIGN
     assert bwd_ex_call(_opts(dh_final=BASE + 20 * STRIDE + 1)) == ALIGN
+
+
+@no_gpu_only
+def test_chunk_states_validation():
+    L = ops.lib()
+    assert L.ssm_scan_chunk_states_bytes(2, 33, 64, 16) == 2 * 3 * 16 * 64 * 4   # ceil(33/16) chunks
+    assert L.ssm_scan_chunk_states_bytes(2, 33, 64, 17) == 0
+    cs = BASE + 20 * STRIDE
+
+    def opt(p):
+        o = ops.ScanOptions(0.0, 0.0, None, None, p)
+        return ctypes.pointer(o)
+
+    assert call_fwd_ex(fwd_args(n=8), opt(cs)) == UNSUP            # saved by the d_state 9..16 kernel only
+    assert call_fwd_ex(fwd_args(), opt(BASE + 8 * STRIDE)) == ALIAS  # chunk states == y
+    assert call_fwd_ex(fwd_args(), opt(BASE + 0 * STRIDE)) == ALIAS  # chunk states == x
+    assert call_fwd_ex(fwd_args(), opt(cs + 2)) == ALIGN
+    assert call_fwd_ex(fwd_args(b=1, l=1 << 20, d=1024), opt(cs)) == UNSUP  # one batch element's part >= 2^31 B
+    st = L.ssm_scan_step_ex(addr(0), addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7), addr(8),
+                            addr(9), 4, 64, 16, ops.SSM_F32, opt(cs), None)
+    assert st == ARG                                                  # not a step option
+    assert bwd_ex_call(opt(BASE + 9 * STRIDE)) == ALIAS              # chunk states == dx
+    assert bwd_ex_call(opt(cs + 1)) == ALIGN

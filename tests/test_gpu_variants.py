@@ -210,3 +210,74 @@ def test_bwd_split_in_two_segments_matches_whole():
     for k in ("dA_log", "dD", "d_dt_bias"):
         assert rel_err(g1[k] + g2[k], whole[k]) <= 1e-4, k
     assert rel_err(g1["dh0"], whole["dh0"]) <= 1e-4
+
+
+# ------------------------------------------------------- saved chunk states
+
+def gpu_fwd_save(inp, lo=None, hi=None):
+    io = inp["io"]
+    b, l, d, n = inp["batch"], inp["seqlen"], inp["dim"], inp["dstate"]
+    cs = torch.empty(ops().chunk_states_shape(b, l, d, n), dtype=torch.float32, device="cuda")
+    y, hf = ops().ssm_scan_fwd(to_dev(inp["x"], io), to_dev(inp["delta_raw"], io), to_dev(inp["B"], io),
+                               to_dev(inp["C"], io), to_dev32(inp["A_log"]), D_skip=to_dev32(inp["D"]),
+                               dt_bias=to_dev32(inp["dt_bias"]), z=to_dev(inp["z"], io),
+                               h0=to_dev32(inp.get("h0")), dt_min=lo, dt_max=hi, chunk_states=cs)
+    torch.cuda.synchronize()
+    return host(y), host(hf), cs
+
+
+@pytest.mark.parametrize("over", [dict(batch=2, seqlen=100, dim=70, random_h0=True),
+                                  dict(batch=1, seqlen=48, dim=40, dstate=12)], ids=["n16_ragged", "n12"])
+def test_saved_chunk_states_are_the_states_entering_each_chunk(over):
+    inp = W.make_inputs(W.WORKLOADS["fwd_b8_l2048_d1536"], **over)
+    b, l, d, n = inp["batch"], inp["seqlen"], inp["dim"], inp["dstate"]
+    say("fwd saving chunk states B=%d L=%d D=%d N=%d" % (b, l, d, n))
+    y, hf, cs = gpu_fwd_save(inp)
+    cs = host(cs)                                     # [b, chunk, n, d]
+    y0, hf0 = gpu_fwd(inp, None, None)
+    assert np.array_equal(y, y0) and np.array_equal(hf, hf0)   # saving changes nothing else
+    seq = ("x", "delta_raw", "z", "B", "C")
+    for k in range((l + 15) // 16):
+        if k == 0:
+            ref = inp["h0"] if inp.get("h0") is not None else np.zeros((b, d, n))
+        else:
+            pre = {kk: (vv[:, : 16 * k] if kk in seq and vv is not None else vv) for kk, vv in inp.items()}
+            ref = oracle.fwd(pre["x"], pre["delta_raw"], pre["B"], pre["C"], inp["A_log"], D=inp["D"],
+                             dt_bias=inp["dt_bias"], z=pre["z"], h0=inp.get("h0"))["h_final"]
+        assert rel_err(cs[:, k].transpose(0, 2, 1), ref) <= 1e-4, k
+
+
+BWD_SAVED = [
+    ("plain", "fwdbwd_b4_l2048_d2048", dict(batch=3, seqlen=300, dim=130, random_h0=True), False, False),
+    ("many_segments", "fwdbwd_b4_l2048_d2048", dict(batch=1, seqlen=3000, dim=64, random_h0=True), False, False),
+    ("clamp_and_final_gradient", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=200, dim=100, random_h0=True),
+     True, True),
+    ("bf16", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=150, dim=96, random_h0=True, with_dy=True),
+     False, True),
+]
+
+
+@pytest.mark.parametrize("name,wl,over,clamp,final", BWD_SAVED, ids=[c[0] for c in BWD_SAVED])
+def test_bwd_with_saved_chunk_states(name, wl, over, clamp, final):
+    inp = W.make_inputs(W.WORKLOADS[wl], **over)
+    io = inp["io"]
+    lo, hi = clamp_bounds(inp) if clamp else (None, None)
+    dhf = np.random.default_rng(23).standard_normal((inp["batch"], inp["dim"], inp["dstate"])).astype(np.float32) \
+        if final else None
+    say("bwd with saved chunk states %s B=%d L=%d D=%d io=%s" % (name, inp["batch"], inp["seqlen"], inp["dim"], io))
+    _, _, cs = gpu_fwd_save(inp, lo, hi)
+
+    def run(states):
+        g = ops().ssm_scan_bwd(to_dev(inp["x"], io), to_dev(inp["delta_raw"], io), to_dev(inp["B"], io),
+                               to_dev(inp["C"], io), to_dev32(inp["A_log"]), to_dev(inp["dy"], io),
+                               D_skip=to_dev32(inp["D"]), dt_bias=to_dev32(inp["dt_bias"]), z=to_dev(inp["z"], io),
+                               h0=to_dev32(inp.get("h0")), dt_min=lo, dt_max=hi, dh_final=to_dev32(dhf),
+                               return_dh0=True, chunk_states=states)
+        torch.cuda.synchronize()
+        return {k: (host(v) if v is not None else None) for k, v in g.items()}
+
+    g = run(cs)
+    r = oracle_bwd(inp, 0.0 if lo is None else lo, float("inf") if hi is None else hi, dhf)
+    check(g, r, tol(io))
+    again = run(None)   # the backward that recomputes the states agrees closely
+    check(g, again, 1e-5 if io == "fp32" else tol(io))
