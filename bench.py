@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|mamba3|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -60,6 +60,16 @@ def bwd_bytes(b, l, d, n, gated, es=4):
     reads = E * es * (4 if gated else 3) + 2 * S * es + d * n * 4 + 2 * d * 4
     writes = E * es * (3 if gated else 2) + 2 * S * 4 + d * n * 4 + 2 * d * 4
     return reads + writes
+
+
+def mamba3_bytes(rows, inner, state, heads, angles, bc):
+    """Mamba-3 preprocess adjoint: the read parts of the projected rows (B, C, dd_dt,
+    dd_a) and dt_bias, every incoming gradient, the written gradient row, the row
+    partials and d_dt_bias (fp32)"""
+    width = 2 * inner + 2 * bc * state + 3 * heads + angles
+    reads = rows * (2 * bc * state + 2 * heads) + heads + rows * (2 * inner + 2 * bc * state + 3 * heads + angles)
+    writes = rows * width + rows * heads + heads
+    return 4 * (reads + writes)
 
 
 def conv_bytes(b, l, d, k, es):
@@ -131,7 +141,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "train", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
                              "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -254,6 +264,31 @@ def main():
             (label, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, wsb / 1e6))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, workspace_bytes=wsb)
 
+    def mamba3_case(name="m3_b8_l2048_d2048"):
+        w = W.MAMBA3_WORKLOADS[name]
+        inp = W.make_mamba3_inputs(w)
+        nb = mamba3_bytes(w.rows, w.inner, w.state, w.heads, w.rope_angles, w.bc_rows)
+        nsets = 2
+        g = inp["grads"]
+        base = {"p": t32(inp["projected"]), **{k: t32(v) for k, v in g.items()}}
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        dtb = t32(inp["dt_bias"])
+        outs = [(torch.empty_like(base["p"]), torch.empty((w.rows, w.heads), dtype=torch.float32, device=dev),
+                 torch.empty((w.heads,), dtype=torch.float32, device=dev)) for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            ops.mamba3_preprocess_bwd(s["p"], dtb, s["z"], s["x"], s["B"], s["C"], s["dt"], s["adt"], s["trap"],
+                                      s["angles"], w.inner, w.state, w.heads, w.rope_angles, w.bc_rows, w.epsilon,
+                                      w.dt_min, w.dt_max, w.a_floor, projected_grad=outs[i][0],
+                                      dt_bias_partial=outs[i][1], d_dt_bias=outs[i][2])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
     def conv_case(name, min_bytes_rotation=1.2e9):
         w = W.CONV_WORKLOADS[name]
         inp = W.make_conv_inputs(w)
@@ -334,6 +369,8 @@ def main():
         # the training pair with the forward's chunk states reused by the backward
         results["fwd_save_b4_l2048_d2048"] = fwd_case("fwdbwd_b4_l2048_d2048", save=True)
         results["bwd_saved_b4_l2048_d2048"] = bwd_case(saved=True)
+    if args.only in ("all", "mamba3"):
+        results["mamba3_preprocess_bwd_m3_b8_l2048_d2048"] = mamba3_case()
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):

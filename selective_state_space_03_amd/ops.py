@@ -36,7 +36,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPOR
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
-           "ssm_conv1d_bwd")
+           "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd")
 
 
 class ScanOptions(ctypes.Structure):
@@ -95,6 +95,11 @@ def lib():
         L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
         L.ssm_conv1d_bwd.argtypes = [P] * 7 + [P, SZ] + [I64] * 4 + [I, I, P]
         L.ssm_conv1d_bwd.restype = I
+        F = ctypes.c_float
+        L.ssm_mamba3_preprocess_bwd_workspace_bytes.argtypes = [I64, I64]
+        L.ssm_mamba3_preprocess_bwd_workspace_bytes.restype = SZ
+        L.ssm_mamba3_preprocess_bwd.argtypes = [P] * 13 + [P, SZ] + [I64] * 6 + [F] * 4 + [P]
+        L.ssm_mamba3_preprocess_bwd.restype = I
         _lib = L
         return L
 
@@ -325,3 +330,46 @@ def conv1d_bwd(x, weight, dout, bias=None, silu=True, workspace=None, dx=None, d
                                                   _ptr(dweight), _ptr(dbias), _ptr(workspace), ws_bytes, b, l, d,
                                                   k, SSM_ACT_SILU if silu else SSM_ACT_NONE, SSM_F32, _stream()))
     return {"dx": dx, "dweight": dweight, "dbias": dbias}
+
+
+# ---------------------------------------------------------------- Mamba-3 preprocess
+
+def mamba3_row_width(inner, state, heads, rope_angles, bc_rows):
+    """width of one projected row: z, x, B and C groups, dd_dt, dd_a, trap, angles"""
+    return 2 * inner + 2 * bc_rows * state + 3 * heads + rope_angles
+
+
+def mamba3_preprocess_bwd(projected, dt_bias, z_grad, x_grad, b_grad, c_grad, dt_grad, adt_grad, trap_grad,
+                          angle_grad, inner, state, heads, rope_angles, bc_rows, epsilon, dt_min, dt_max, a_floor,
+                          projected_grad=None, dt_bias_partial=None, d_dt_bias=True, workspace=None):
+    """Adjoint of the Mamba-3 projection preprocess (include/ssm_mamba3.h).
+
+    Returns (projected_grad [rows, width], dt_bias_partial [rows, heads], d_dt_bias [heads] or None)."""
+    rows = projected.shape[0]
+    width = mamba3_row_width(inner, state, heads, rope_angles, bc_rows)
+    dev, f32 = projected.device, torch.float32
+    _req(projected, "projected", (rows, width), f32, dev)
+    _req(dt_bias, "dt_bias", (heads,), f32, dev)
+    for name, t, w in (("z_grad", z_grad, inner), ("x_grad", x_grad, inner), ("b_grad", b_grad, bc_rows * state),
+                       ("c_grad", c_grad, bc_rows * state), ("dt_grad", dt_grad, heads), ("adt_grad", adt_grad, heads),
+                       ("trap_grad", trap_grad, heads), ("angle_grad", angle_grad, rope_angles)):
+        _req(t, name, (rows, w), f32, dev)
+    if projected_grad is None:
+        projected_grad = torch.empty((rows, width), dtype=f32, device=dev)
+    if dt_bias_partial is None:
+        dt_bias_partial = torch.empty((rows, heads), dtype=f32, device=dev)
+    dbias = torch.empty((heads,), dtype=f32, device=dev) if d_dt_bias is True else d_dt_bias
+    _req(projected_grad, "projected_grad", (rows, width), f32, dev)
+    _req(dt_bias_partial, "dt_bias_partial", (rows, heads), f32, dev)
+    _req(dbias, "d_dt_bias", (heads,), f32, dev)
+    if dbias is not None and workspace is None:
+        nbytes = int(lib().ssm_mamba3_preprocess_bwd_workspace_bytes(rows, heads))
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_mamba3_preprocess_bwd(
+        _ptr(projected), _ptr(dt_bias), _ptr(z_grad), _ptr(x_grad), _ptr(b_grad), _ptr(c_grad), _ptr(dt_grad),
+        _ptr(adt_grad), _ptr(trap_grad), _ptr(angle_grad), _ptr(projected_grad), _ptr(dt_bias_partial), _ptr(dbias),
+        _ptr(workspace), ws_bytes, rows, inner, state, heads, rope_angles, bc_rows, float(epsilon), float(dt_min), float(dt_max),
+        float(a_floor), _stream())
+    _check("ssm_mamba3_preprocess_bwd", st)
+    return projected_grad, dt_bias_partial, dbias

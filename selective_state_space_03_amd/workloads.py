@@ -186,3 +186,71 @@ def make_conv_inputs(w: ConvWorkload, *, batch: Optional[int] = None, seqlen: Op
     if step:
         out["state"] = round_to_io(rng.standard_normal((b, d, k - 1)), io_)
     return out
+
+
+# ---------------------------------------------------------- Mamba-3 preprocess adjoint
+
+@dataclasses.dataclass(frozen=True)
+class Mamba3Workload:
+    """Adjoint of the Mamba-3 projection preprocess over `rows` token rows.  The page
+    gives no sizes; these are a layer with d_model 2048 (inner 4096 = 64 heads of 64),
+    state 128 in one B/C group and 64 rotary angles, over 8 x 2048 tokens."""
+    name: str
+    rows: int
+    inner: int
+    state: int
+    heads: int
+    rope_angles: int
+    bc_rows: int
+    epsilon: float = 1e-6
+    dt_min: float = 1e-3
+    dt_max: float = 1e-1
+    a_floor: float = 1e-4
+    seed: int = 2100
+
+    @property
+    def width(self):
+        return 2 * self.inner + 2 * self.bc_rows * self.state + 3 * self.heads + self.rope_angles
+
+    @property
+    def kind(self):
+        return "mamba3"
+
+    @property
+    def elements(self) -> int:  # elements of the gradient row written per launch
+        return self.rows * self.width
+
+
+MAMBA3_WORKLOADS = {
+    "m3_small": Mamba3Workload("m3_small", rows=37, inner=70, state=16, heads=5, rope_angles=8, bc_rows=2, seed=2101),
+    "m3_b8_l2048_d2048": Mamba3Workload("m3_b8_l2048_d2048", rows=8 * 2048, inner=4096, state=128, heads=64,
+                                        rope_angles=64, bc_rows=1, seed=2102),
+}
+
+
+def make_mamba3_inputs(w: Mamba3Workload, *, rows: Optional[int] = None, inner: Optional[int] = None,
+                       state: Optional[int] = None, heads: Optional[int] = None,
+                       rope_angles: Optional[int] = None, bc_rows: Optional[int] = None,
+                       seed: Optional[int] = None) -> dict:
+    """Seeded fp32 inputs: projected rows ~ N(0, 1) (the dd_dt part shifted by the
+    dt_bias draw as in the scan workloads), dt_bias = log(expm1(u)), u ~ U[1e-3, 1e-1],
+    and every incoming gradient ~ N(0, 1).  Draw order: projected, u, z, x, B, C, dt,
+    adt, trap, angles gradients."""
+    r = w.rows if rows is None else rows
+    inn = w.inner if inner is None else inner
+    st = w.state if state is None else state
+    hd = w.heads if heads is None else heads
+    ang = w.rope_angles if rope_angles is None else rope_angles
+    bc = w.bc_rows if bc_rows is None else bc_rows
+    width = 2 * inn + 2 * bc * st + 3 * hd + ang
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    f = np.float32
+    projected = rng.standard_normal((r, width)).astype(f)
+    u = rng.uniform(1e-3, 1e-1, hd)
+    dt_bias = np.log(np.expm1(u)).astype(f)
+    g = {k: rng.standard_normal((r, n)).astype(f) for k, n in
+         (("z", inn), ("x", inn), ("B", bc * st), ("C", bc * st), ("dt", hd), ("adt", hd), ("trap", hd),
+          ("angles", ang))}
+    return {"rows": r, "inner": inn, "state": st, "heads": hd, "rope_angles": ang, "bc_rows": bc,
+            "epsilon": w.epsilon, "dt_min": w.dt_min, "dt_max": w.dt_max, "a_floor": w.a_floor,
+            "projected": projected, "dt_bias": dt_bias, "grads": g}

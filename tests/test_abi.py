@@ -274,3 +274,30 @@ def test_chunk_states_validation():
     assert st == ARG                                                  # not a step option
     assert bwd_ex_call(opt(BASE + 9 * STRIDE)) == ALIAS              # chunk states == dx
     assert bwd_ex_call(opt(cs + 1)) == ALIGN
+
+
+@no_gpu_only
+def test_mamba3_validation():
+    L = ops.lib()
+
+    def call(rows=4, inner=8, state=4, heads=2, angles=2, bc=1, eps=1e-6, lo=1e-3, hi=0.1, floor=1e-4, **over):
+        p = dict(projected=addr(0), dt_bias=addr(1), zg=addr(2), xg=addr(3), bg=addr(4), cg=addr(5), dtg=addr(6),
+                 adtg=addr(7), trapg=addr(8), angg=addr(9), out=addr(10), part=addr(11), dbias=addr(12))
+        p.update(over)
+        ws = p.get("ws", addr(13))
+        wsb = p.get("wsb", L.ssm_mamba3_preprocess_bwd_workspace_bytes(rows, heads))
+        return L.ssm_mamba3_preprocess_bwd(p["projected"], p["dt_bias"], p["zg"], p["xg"], p["bg"], p["cg"],
+                                           p["dtg"], p["adtg"], p["trapg"], p["angg"], p["out"], p["part"],
+                                           p["dbias"], ws, wsb, rows, inner, state, heads, angles, bc, eps, lo, hi,
+                                           floor, None)
+    assert call(rows=0) == DIM and call(inner=-1) == DIM and call(state=0) == DIM
+    assert call(projected=None) == NULL and call(out=None) == NULL and call(part=None) == NULL
+    assert call(angg=None) == NULL
+    assert call(eps=-1.0) == ARG and call(lo=0.2, hi=0.1) == ARG and call(lo=-1.0) == ARG
+    assert call(floor=float("nan")) == ARG
+    assert call(out=addr(0)) == ALIAS and call(part=addr(10)) == ALIAS and call(dbias=addr(1)) == ALIAS
+    assert call(out=addr(10, 2)) == ALIGN
+    assert call(ws=None) == WS and call(wsb=16) == WS and call(ws=addr(13, 64)) == WS
+    assert call(ws=addr(10)) == ALIAS                    # workspace == projected_grad
+    assert L.ssm_mamba3_preprocess_bwd_workspace_bytes(130, 64) == 768            # 3 chunks x 64 heads x 4 B
+    assert L.ssm_mamba3_preprocess_bwd_workspace_bytes(130, 3) == 256             # rounded up to 256 B
