@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|mamba3|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|mamba3|ssd|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -70,6 +70,16 @@ def mamba3_bytes(rows, inner, state, heads, angles, bc):
     reads = rows * (2 * bc * state + 2 * heads) + heads + rows * (2 * inner + 2 * bc * state + 3 * heads + angles)
     writes = rows * width + rows * heads + heads
     return 4 * (reads + writes)
+
+
+def ssd_fwd_bytes(b, l, h, nc, w):
+    """SSD chunk cumsum: dt read, A and dt_bias read, dA_cumsum and dt_out written (fp32)"""
+    return 4 * (b * l * h + 2 * h + 2 * b * h * nc * w)
+
+
+def ssd_bwd_bytes(b, l, h, nc, w):
+    """its backward: ddA, ddt_out, dt, A, dt_bias read; ddt, dA, d_dt_bias written (fp32)"""
+    return 4 * (2 * b * h * nc * w + b * l * h + 2 * h + b * l * h + 2 * h)
 
 
 def conv_bytes(b, l, d, k, es):
@@ -142,7 +152,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
                     choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
-                             "copy"])
+                             "ssd", "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -289,6 +299,43 @@ def main():
             (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
 
+    def ssd_case(name="ssd_b8_l2048_h64_w256", bwd=False):
+        w = W.SSD_WORKLOADS[name]
+        inp = W.make_ssd_inputs(w)
+        nb = (ssd_bwd_bytes if bwd else ssd_fwd_bytes)(w.batch, w.seqlen, w.heads, w.nchunks, w.chunk)
+        nsets = max(2, int(np.ceil(1.2e9 / nb)))
+        keys = ("dt", "ddA", "ddt_out") if bwd else ("dt",)
+        base = {k: t32(inp[k]) for k in keys}
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        A, dtb = t32(inp["A"]), t32(inp["dt_bias"])
+        f = torch.float32
+        if bwd:
+            wsb = ops.ssd_chunk_cumsum_bwd_workspace_bytes(w.batch, w.seqlen, w.heads, w.chunk)
+            outs = [{"ddt": torch.empty_like(base["dt"]), "dA": torch.empty((w.heads,), dtype=f, device=dev),
+                     "db": torch.empty((w.heads,), dtype=f, device=dev),
+                     "ws": torch.empty((wsb,), dtype=torch.uint8, device=dev)} for _ in range(nsets)]
+        else:
+            shp = (w.batch, w.heads, w.nchunks, w.chunk)
+            outs = [{"cs": torch.empty(shp, dtype=f, device=dev), "dto": torch.empty(shp, dtype=f, device=dev)}
+                    for _ in range(nsets)]
+
+        def fn(i):
+            s, o = sets[i], outs[i]
+            if bwd:
+                ops.ssd_chunk_cumsum_bwd(s["ddA"], s["ddt_out"], s["dt"], A, dt_bias=dtb, dt_softplus=w.dt_softplus,
+                                         dt_min=w.dt_min, dt_max=w.dt_max, ddt=o["ddt"], workspace=o["ws"],
+                                         dA=o["dA"], d_dt_bias=o["db"])
+            else:
+                ops.ssd_chunk_cumsum_fwd(s["dt"], A, w.chunk, dt_bias=dtb, dt_softplus=w.dt_softplus,
+                                         dt_min=w.dt_min, dt_max=w.dt_max, dA_cumsum=o["cs"], dt_out=o["dto"])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        label = ("ssd_cumsum_bwd_" if bwd else "ssd_cumsum_fwd_") + name[4:]
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
+            (label, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
     def conv_case(name, min_bytes_rotation=1.2e9):
         w = W.CONV_WORKLOADS[name]
         inp = W.make_conv_inputs(w)
@@ -371,6 +418,9 @@ def main():
         results["bwd_saved_b4_l2048_d2048"] = bwd_case(saved=True)
     if args.only in ("all", "mamba3"):
         results["mamba3_preprocess_bwd_m3_b8_l2048_d2048"] = mamba3_case()
+    if args.only in ("all", "ssd"):
+        results["ssd_cumsum_fwd_b8_l2048_h64_w256"] = ssd_case()
+        results["ssd_cumsum_bwd_b8_l2048_h64_w256"] = ssd_case(bwd=True)
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):

@@ -2,7 +2,7 @@
 
 Sources: csrc/ssm_api.hip (C ABI of include/ssm_scan.h and include/ssm_conv1d.h)
 and the kernels in csrc/ssm_fwd.hip, csrc/ssm_step.hip, csrc/ssm_bwd.hip and
-csrc/ssm_conv1d.hip.  Each source is compiled separately (in parallel) and linked
+csrc/ssm_conv1d.hip, csrc/ssm_mamba3.hip and csrc/ssm_ssd.hip.  Each source is compiled separately (in parallel) and linked
 into lib/libssmscan.so.  No fast-math; packed
 fp32 instructions are disabled for the device code.
 """
@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIBDIR, "libssmscan.so")
-SOURCES = ["ssm_api.hip", "ssm_fwd.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_conv1d.hip", "ssm_mamba3.hip"]
+SOURCES = ["ssm_api.hip", "ssm_fwd.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_conv1d.hip", "ssm_mamba3.hip", "ssm_ssd.hip"]
 ARCH = "gfx950"
 
 

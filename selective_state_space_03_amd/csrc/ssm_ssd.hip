@@ -1,0 +1,386 @@
+// ssm_ssd.hip -- the Mamba-2 SSD chunk cumsum and its ordered backward for gfx950.
+//
+// What is computed (deterministic_backward.py, ordered_cumsum, and the chunk cumsum
+// whose backward it reorders): per (batch, head, chunk) the clamped step sizes
+// dt_out = clamp(g(dt + dt_bias), dt_min, dt_max) and their running sum times A inside
+// the chunk; backward, the reverse running sum of ddA times A added to ddt_out, masked
+// by the clamp and scaled by g', plus the per-(batch, chunk) partials of dA and
+// d_dt_bias, which a second kernel adds in ascending (batch, chunk) order (the page's
+// lexical order, with no atomics).
+//
+// Work layout (our own).  dt and ddt are [batch, seqlen, heads] (head fastest) while the
+// chunk tensors are [batch, heads, chunks, chunk] (step fastest), so every workgroup
+// transposes through LDS: one workgroup per (batch, chunk, 16 heads), 4 waves, the
+// chunk walked in sub-tiles of 256 steps.  The [256 steps x 16 heads] slab of dt is
+// read in 64-byte head rows into LDS; then each wave takes 4 heads and handles one
+// 256-step row per head with 4 consecutive steps per lane: a sequential 4-term scan in
+// the lane, a 64-lane Hillis-Steele scan of the lane totals, and the carry of the
+// previous sub-tile.  Rows of the chunk tensors move as 16-byte vectors when the chunk
+// width and pointers allow.  Every scan and sum has a fixed order.
+#include "ssm_device.h"
+#include "ssm_scan.h"
+#include "ssm_ssd.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kHeads = 16;   // heads per workgroup
+constexpr int kSub = 256;    // steps per sub-tile (64 lanes x 4)
+constexpr int kPad = 4;      // LDS row padding (keeps 16-byte row alignment)
+
+struct SsdDims {
+  int64_t L, W, nc;
+  int H;
+  int softplus;
+  float lo, hi;
+};
+
+__device__ __forceinline__ float g_of(float r, int softplus) { return softplus ? softplus_f(r) : r; }
+
+// inclusive scan over the 64 lanes, in increasing lane order (fixed tree)
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+// inclusive scan from the right (lane 63 down to lane 0)
+__device__ __forceinline__ float wave_incl_rscan(float v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_down(v, d, 64);
+    if (lane + d < 64) v += o;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// 4 consecutive row entries starting at p (entries at or beyond n read as 0)
+template <bool VEC>
+__device__ __forceinline__ void ld4(const float* __restrict__ p, int n, float (&v)[4]) {
+  if (VEC && n >= 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = q < n ? p[q] : 0.f;
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void st4(float* __restrict__ p, int n, const float (&v)[4]) {
+  if (VEC && n >= 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < n) p[q] = v[q];
+  }
+}
+
+constexpr int kStage = kSub * kHeads / 256;  // slab elements per thread
+
+// element i of a [256 steps x 16 heads] slab (step i / 16, head i % 16) lies inside the
+// chunk, the sequence and the head range
+__device__ __forceinline__ bool valid(int64_t t0, int n, int h0, int i, const SsdDims& m) {
+  const int r = i >> 4, h = h0 + (i & 15);
+  return r < n && t0 + r < m.L && h < m.H;
+}
+
+// dt + dt_bias of a thread's kStage slab elements (0 outside), all loads issued first
+__device__ __forceinline__ void stage_load(const float* __restrict__ dt, const float* __restrict__ dt_bias, int64_t b,
+                                           int64_t t0, int n, int h0, int tid, const SsdDims& m,
+                                           float (&raw)[kStage]) {
+  const int h = h0 + (tid & 15);  // the same head for every j (256 is a multiple of 16)
+  const float bias = (dt_bias && h < m.H) ? dt_bias[h] : 0.f;
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int i = tid + 256 * j;
+    raw[j] = valid(t0, n, h0, i, m) ? dt[(b * m.L + t0 + (i >> 4)) * m.H + h] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) raw[j] += bias;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+ssd_cumsum_fwd_kernel(const float* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
+                      float* __restrict__ dA_cs, float* __restrict__ dt_out, SsdDims m) {
+  __shared__ __align__(16) float tile[kHeads][kSub + kPad];
+  const int64_t bc = blockIdx.x;  // (batch, chunk), chunk fastest
+  const int64_t b = bc / m.nc, c = bc - b * m.nc;
+  const int h0 = blockIdx.y * kHeads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float carry[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t l0 = 0; l0 < m.W; l0 += kSub) {
+    const int n = (int)(m.W - l0 < kSub ? m.W - l0 : kSub);
+    // stage dt_out of [n steps x 16 heads], read in 64-byte head rows; all of a
+    // thread's loads are issued before any of them is used
+    float raw[kStage];
+    stage_load(dt, dt_bias, b, c * m.W + l0, n, h0, tid, m, raw);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = tid + 256 * j, r = i >> 4, hh = i & 15;
+      tile[hh][r] = valid(c * m.W + l0, n, h0, i, m) ? clamp_delta(g_of(raw[j], m.softplus), m.lo, m.hi) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int hh = wave * 4 + k, h = h0 + hh;
+      if (h >= m.H) break;  // wave-uniform
+      const float a = A[h];
+      const float4 q = *reinterpret_cast<const float4*>(&tile[hh][4 * lane]);
+      float p[4];
+      p[0] = q.x * a;
+      p[1] = fmaf(q.y, a, p[0]);
+      p[2] = fmaf(q.z, a, p[1]);
+      p[3] = fmaf(q.w, a, p[2]);
+      const float s = wave_incl_scan(p[3], lane);
+      float ex = __shfl_up(s, 1, 64);
+      ex = lane == 0 ? 0.f : ex;
+      const float off = carry[k] + ex;
+      float o[4] = {off + p[0], off + p[1], off + p[2], off + p[3]};
+      float d[4] = {q.x, q.y, q.z, q.w};
+      carry[k] += __shfl(s, 63, 64);
+      const int64_t row = ((b * m.H + h) * m.nc + c) * m.W + l0 + 4 * lane;
+      const int nl = n - 4 * lane;
+      if (nl > 0) {
+        st4<VEC>(dA_cs + row, nl, o);
+        st4<VEC>(dt_out + row, nl, d);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ ddt_out, const float* __restrict__ dt,
+                      const float* __restrict__ A, const float* __restrict__ dt_bias, float* __restrict__ ddt,
+                      float* __restrict__ part_a, float* __restrict__ part_b, SsdDims m) {
+  __shared__ __align__(16) float tile[kHeads][kSub + kPad];
+  const int64_t bc = blockIdx.x;
+  const int64_t b = bc / m.nc, c = bc - b * m.nc;
+  const int h0 = blockIdx.y * kHeads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float carry[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+  const int64_t nsub = (m.W + kSub - 1) / kSub;
+  for (int64_t s_i = nsub - 1; s_i >= 0; --s_i) {  // sub-tiles from the end of the chunk
+    const int64_t l0 = s_i * kSub;
+    const int n = (int)(m.W - l0 < kSub ? m.W - l0 : kSub);
+    // stage raw = dt + dt_bias of [n steps x 16 heads]
+    {
+      float raw[kStage];
+      stage_load(dt, dt_bias, b, c * m.W + l0, n, h0, tid, m, raw);
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) {
+        const int i = tid + 256 * j;
+        tile[i & 15][i >> 4] = raw[j];
+      }
+    }
+    __syncthreads();
+    // the ddA and ddt_out rows of the wave's 4 heads, all loads issued first
+    const int nl = n - 4 * lane;
+    float dA4s[4][4], dO4s[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = h0 + wave * 4 + k;
+      const int64_t row = ((b * m.H + h) * m.nc + c) * m.W + l0 + 4 * lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dA4s[k][q] = dO4s[k][q] = 0.f;
+      if (nl > 0 && h < m.H) {
+        ld4<VEC>(ddA + row, nl, dA4s[k]);
+        ld4<VEC>(ddt_out + row, nl, dO4s[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int hh = wave * 4 + k, h = h0 + hh;
+      if (h >= m.H) break;  // wave-uniform
+      const float a = A[h];
+      const float(&dA4)[4] = dA4s[k];
+      const float(&dO4)[4] = dO4s[k];
+      // reverse running sums: inside the lane, across lanes, then the later sub-tiles
+      float r4[4];
+      r4[3] = dA4[3];
+      r4[2] = dA4[2] + r4[3];
+      r4[1] = dA4[1] + r4[2];
+      r4[0] = dA4[0] + r4[1];
+      const float S = wave_incl_rscan(r4[0], lane);
+      float ex = __shfl_down(S, 1, 64);
+      ex = lane == 63 ? 0.f : ex;
+      const float off = carry[k] + ex;
+      carry[k] += __shfl(S, 0, 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int li = 4 * lane + q;
+        if (li >= n) break;
+        const float rev = off + r4[q];
+        const int64_t t = c * m.W + l0 + li;
+        if (t < m.L) {
+          const float raw = tile[hh][li];
+          const float gv = g_of(raw, m.softplus);
+          const float v = clamp_delta(gv, m.lo, m.hi);
+          pa[k] = fmaf(v, rev, pa[k]);
+          const float gp = m.softplus ? sigmoid_f(raw) : 1.f;
+          const float d = fmaf(a, rev, dO4[q]) * clamp_mask(gv, m.lo, m.hi) * gp;
+          pb[k] += d;
+          tile[hh][li] = d;
+        }
+      }
+    }
+    __syncthreads();
+    // ddt of the slab, written in 64-byte head rows
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = tid + 256 * j;
+      if (valid(c * m.W + l0, n, h0, i, m)) ddt[(b * m.L + c * m.W + l0 + (i >> 4)) * m.H + h0 + (i & 15)] = tile[i & 15][i >> 4];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int h = h0 + wave * 4 + k;
+    if (h >= m.H) break;
+    const float sa = wave_sum(pa[k]), sb = wave_sum(pb[k]);
+    if (lane == 0) {
+      part_a[bc * m.H + h] = sa;
+      part_b[bc * m.H + h] = sb;
+    }
+  }
+}
+
+// dA[h], d_dt_bias[h]: the per-(batch, chunk) partials added in ascending (batch, chunk)
+// order, one lane per head
+__global__ void __launch_bounds__(64)
+ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restrict__ part_b, float* __restrict__ dA,
+                        float* __restrict__ d_dt_bias, int64_t nbc, int H) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= H) return;
+  float sa = 0.f, sb = 0.f;
+#pragma unroll 8
+  for (int64_t i = 0; i < nbc; ++i) {
+    sa += part_a[i * H + h];
+    sb += part_b[i * H + h];
+  }
+  dA[h] = sa;
+  if (d_dt_bias) d_dt_bias[h] = sb;
+}
+
+struct Rng {
+  uintptr_t lo, hi;
+};
+bool overlaps(Rng a, Rng b) { return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi; }
+Rng span(const void* p, size_t bytes) { return Rng{(uintptr_t)p, (uintptr_t)p + (p ? bytes : 0)}; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// shared checks of sizes and clamp bounds; fills m
+int ssd_dims(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int softplus, float lo, float hi,
+             SsdDims& m) {
+  if (batch < 1 || seqlen < 1 || heads < 1 || chunk < 1) return SSM_ERR_DIM;
+  if (heads > ((int64_t)1 << 20)) return SSM_ERR_DIM;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t nc = (seqlen + chunk - 1) / chunk;
+  if (seqlen >= lim || chunk >= lim || batch >= lim) return SSM_ERR_DIM;
+  if ((double)batch * (double)seqlen * (double)heads >= (double)lim || batch * nc >= lim) return SSM_ERR_DIM;
+  if ((double)batch * (double)heads * (double)nc * (double)chunk >= (double)lim) return SSM_ERR_DIM;
+  if (!(lo >= 0.f) || !(lo <= hi)) return SSM_ERR_ARG;  // also rejects NaN bounds
+  m.L = seqlen;
+  m.W = chunk;
+  m.nc = nc;
+  m.H = (int)heads;
+  m.softplus = softplus ? 1 : 0;
+  m.lo = lo;
+  m.hi = hi;
+  return SSM_OK;
+}
+
+size_t ws_part_bytes(int64_t batch, int64_t nc, int64_t heads) {
+  return ((size_t)batch * (size_t)nc * (size_t)heads * 4 + 255) & ~(size_t)255;
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" int ssm_ssd_chunk_cumsum_fwd(const float* dt, const float* A, const float* dt_bias, float* dA_cumsum,
+                                        float* dt_out, int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk,
+                                        int dt_softplus, float dt_min, float dt_max, hipStream_t stream) {
+  using namespace ssm;
+  SsdDims m;
+  const int st = ssd_dims(batch, seqlen, heads, chunk, dt_softplus, dt_min, dt_max, m);
+  if (st != SSM_OK) return st;
+  if (!dt || !A || !dA_cumsum || !dt_out) return SSM_ERR_NULL;
+  const void* all[] = {dt, A, dt_bias, dA_cumsum, dt_out};
+  for (const void* p : all)
+    if (p && !aligned4(p)) return SSM_ERR_ALIGN;
+  const size_t f = 4, nch = (size_t)batch * heads * m.nc * chunk * f;
+  const Rng ins[] = {span(dt, (size_t)batch * seqlen * heads * f), span(A, heads * f), span(dt_bias, heads * f)};
+  const Rng outs[] = {span(dA_cumsum, nch), span(dt_out, nch)};
+  for (const Rng& o : outs)
+    for (const Rng& r : ins)
+      if (overlaps(o, r)) return SSM_ERR_ALIAS;
+  if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
+  const bool vec = chunk % 4 == 0 && aligned16(dA_cumsum) && aligned16(dt_out);
+  const dim3 grid((unsigned)(batch * m.nc), (unsigned)((heads + kHeads - 1) / kHeads));
+  if (vec)
+    hipLaunchKernelGGL(ssd_cumsum_fwd_kernel<true>, grid, dim3(256), 0, stream, dt, A, dt_bias, dA_cumsum, dt_out,
+                       m);
+  else
+    hipLaunchKernelGGL(ssd_cumsum_fwd_kernel<false>, grid, dim3(256), 0, stream, dt, A, dt_bias, dA_cumsum, dt_out,
+                       m);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+extern "C" size_t ssm_ssd_chunk_cumsum_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                                          int64_t chunk) {
+  if (batch < 1 || seqlen < 1 || heads < 1 || chunk < 1) return 0;
+  const int64_t nc = (seqlen + chunk - 1) / chunk;
+  return 2 * ssm::ws_part_bytes(batch, nc, heads);
+}
+
+extern "C" int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, const float* dt, const float* A,
+                                        const float* dt_bias, float* ddt, float* dA, float* d_dt_bias,
+                                        void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                                        int64_t heads, int64_t chunk, int dt_softplus, float dt_min, float dt_max,
+                                        hipStream_t stream) {
+  using namespace ssm;
+  SsdDims m;
+  const int st = ssd_dims(batch, seqlen, heads, chunk, dt_softplus, dt_min, dt_max, m);
+  if (st != SSM_OK) return st;
+  if (!ddA || !ddt_out || !dt || !A || !ddt || !dA) return SSM_ERR_NULL;
+  const void* all[] = {ddA, ddt_out, dt, A, dt_bias, ddt, dA, d_dt_bias};
+  for (const void* p : all)
+    if (p && !aligned4(p)) return SSM_ERR_ALIGN;
+  const size_t ws_need = ssm_ssd_chunk_cumsum_bwd_workspace_bytes(batch, seqlen, heads, chunk);
+  if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255)) return SSM_ERR_WORKSPACE;
+  const size_t f = 4, nch = (size_t)batch * heads * m.nc * chunk * f, nbl = (size_t)batch * seqlen * heads * f;
+  const Rng ins[] = {span(ddA, nch), span(ddt_out, nch), span(dt, nbl), span(A, heads * f),
+                     span(dt_bias, heads * f)};
+  const Rng outs[] = {span(ddt, nbl), span(dA, heads * f), span(d_dt_bias, heads * f), span(workspace, ws_need)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Rng& r : ins)
+      if (overlaps(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  float* part_a = (float*)workspace;
+  float* part_b = (float*)((char*)workspace + ws_part_bytes(batch, m.nc, heads));
+  const bool vec = chunk % 4 == 0 && aligned16(ddA) && aligned16(ddt_out);
+  const dim3 grid((unsigned)(batch * m.nc), (unsigned)((heads + kHeads - 1) / kHeads));
+  if (vec)
+    hipLaunchKernelGGL(ssd_cumsum_bwd_kernel<true>, grid, dim3(256), 0, stream, ddA, ddt_out, dt, A, dt_bias, ddt,
+                       part_a, part_b, m);
+  else
+    hipLaunchKernelGGL(ssd_cumsum_bwd_kernel<false>, grid, dim3(256), 0, stream, ddA, ddt_out, dt, A, dt_bias, ddt,
+                       part_a, part_b, m);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+  hipLaunchKernelGGL(ssd_param_reduce_kernel, dim3((unsigned)((heads + 63) / 64)), dim3(64), 0, stream, part_a,
+                     part_b, dA, d_dt_bias, (int64_t)(batch * m.nc), (int)heads);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}

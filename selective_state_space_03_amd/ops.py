@@ -36,7 +36,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPOR
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
-           "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd")
+           "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
+           "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd")
 
 
 class ScanOptions(ctypes.Structure):
@@ -100,6 +101,12 @@ def lib():
         L.ssm_mamba3_preprocess_bwd_workspace_bytes.restype = SZ
         L.ssm_mamba3_preprocess_bwd.argtypes = [P] * 13 + [P, SZ] + [I64] * 6 + [F] * 4 + [P]
         L.ssm_mamba3_preprocess_bwd.restype = I
+        L.ssm_ssd_chunk_cumsum_fwd.argtypes = [P] * 5 + [I64] * 4 + [I, F, F, P]
+        L.ssm_ssd_chunk_cumsum_fwd.restype = I
+        L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes.argtypes = [I64] * 4
+        L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes.restype = SZ
+        L.ssm_ssd_chunk_cumsum_bwd.argtypes = [P] * 9 + [SZ] + [I64] * 4 + [I, F, F, P]
+        L.ssm_ssd_chunk_cumsum_bwd.restype = I
         _lib = L
         return L
 
@@ -373,3 +380,66 @@ def mamba3_preprocess_bwd(projected, dt_bias, z_grad, x_grad, b_grad, c_grad, dt
         float(a_floor), _stream())
     _check("ssm_mamba3_preprocess_bwd", st)
     return projected_grad, dt_bias_partial, dbias
+
+
+# ---------------------------------------------------------------- Mamba-2 SSD chunk cumsum
+
+def ssd_chunk_cumsum_fwd(dt, A, chunk, dt_bias=None, dt_softplus=True, dt_min=0.0, dt_max=float("inf"),
+                         dA_cumsum=None, dt_out=None):
+    """Chunk cumsum of the Mamba-2 SSD scan (include/ssm_ssd.h).
+
+    dt [batch, seqlen, heads], A and dt_bias [heads], all fp32 ->
+    (dA_cumsum, dt_out), both [batch, heads, ceil(seqlen / chunk), chunk] fp32."""
+    b, l, h = dt.shape
+    dev, f32 = dt.device, torch.float32
+    nc = (l + chunk - 1) // chunk
+    _req(dt, "dt", (b, l, h), f32, dev)
+    _req(A, "A", (h,), f32, dev)
+    _req(dt_bias, "dt_bias", (h,), f32, dev)
+    if dA_cumsum is None:
+        dA_cumsum = torch.empty((b, h, nc, chunk), dtype=f32, device=dev)
+    if dt_out is None:
+        dt_out = torch.empty((b, h, nc, chunk), dtype=f32, device=dev)
+    _req(dA_cumsum, "dA_cumsum", (b, h, nc, chunk), f32, dev)
+    _req(dt_out, "dt_out", (b, h, nc, chunk), f32, dev)
+    _check("ssm_ssd_chunk_cumsum_fwd", lib().ssm_ssd_chunk_cumsum_fwd(
+        _ptr(dt), _ptr(A), _ptr(dt_bias), _ptr(dA_cumsum), _ptr(dt_out), b, l, h, chunk, 1 if dt_softplus else 0,
+        float(dt_min), float(dt_max), _stream()))
+    return dA_cumsum, dt_out
+
+
+def ssd_chunk_cumsum_bwd_workspace_bytes(batch, seqlen, heads, chunk):
+    return int(lib().ssm_ssd_chunk_cumsum_bwd_workspace_bytes(batch, seqlen, heads, chunk))
+
+
+def ssd_chunk_cumsum_bwd(ddA, ddt_out, dt, A, dt_bias=None, dt_softplus=True, dt_min=0.0, dt_max=float("inf"),
+                         ddt=None, workspace=None, dA=None, d_dt_bias=True):
+    """Backward of the chunk cumsum with ordered dA / d_dt_bias sums (include/ssm_ssd.h).
+
+    Returns {"ddt" [batch, seqlen, heads], "dA" [heads], "d_dt_bias" [heads] or None}."""
+    b, l, h = dt.shape
+    dev, f32 = dt.device, torch.float32
+    nc, chunk = ddA.shape[-2:]
+    _req(ddA, "ddA", (b, h, nc, chunk), f32, dev)
+    _req(ddt_out, "ddt_out", (b, h, nc, chunk), f32, dev)
+    if nc != (l + chunk - 1) // chunk:
+        raise ValueError("ddA: %d chunks of %d do not cover seqlen %d" % (nc, chunk, l))
+    _req(dt, "dt", (b, l, h), f32, dev)
+    _req(A, "A", (h,), f32, dev)
+    _req(dt_bias, "dt_bias", (h,), f32, dev)
+    if ddt is None:
+        ddt = torch.empty((b, l, h), dtype=f32, device=dev)
+    _req(ddt, "ddt", (b, l, h), f32, dev)
+    if dA is None:
+        dA = torch.empty((h,), dtype=f32, device=dev)
+    _req(dA, "dA", (h,), f32, dev)
+    db = (None if dt_bias is None else torch.empty((h,), dtype=f32, device=dev)) if d_dt_bias is True else d_dt_bias
+    _req(db, "d_dt_bias", (h,), f32, dev)
+    if workspace is None:
+        workspace = torch.empty((max(ssd_chunk_cumsum_bwd_workspace_bytes(b, l, h, chunk), 1),),
+                                dtype=torch.uint8, device=dev)
+    _check("ssm_ssd_chunk_cumsum_bwd", lib().ssm_ssd_chunk_cumsum_bwd(
+        _ptr(ddA), _ptr(ddt_out), _ptr(dt), _ptr(A), _ptr(dt_bias), _ptr(ddt), _ptr(dA), _ptr(db), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), b, l, h, chunk, 1 if dt_softplus else 0, float(dt_min),
+        float(dt_max), _stream()))
+    return {"ddt": ddt, "dA": dA, "d_dt_bias": db}

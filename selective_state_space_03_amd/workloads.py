@@ -254,3 +254,63 @@ def make_mamba3_inputs(w: Mamba3Workload, *, rows: Optional[int] = None, inner: 
     return {"rows": r, "inner": inn, "state": st, "heads": hd, "rope_angles": ang, "bc_rows": bc,
             "epsilon": w.epsilon, "dt_min": w.dt_min, "dt_max": w.dt_max, "a_floor": w.a_floor,
             "projected": projected, "dt_bias": dt_bias, "grads": g}
+
+
+# ---------------------------------------------------------------- Mamba-2 SSD chunk cumsum
+
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    """Chunk cumsum of the Mamba-2 SSD scan over [batch, seqlen, heads] step sizes.  The
+    page gives no sizes; the large one is a layer with d_model 2048 (64 heads of 64
+    channels) over 8 x 2048 tokens with 256-step chunks."""
+    name: str
+    batch: int
+    seqlen: int
+    heads: int
+    chunk: int
+    dt_softplus: bool = True
+    dt_min: float = 0.0
+    dt_max: float = float("inf")
+    seed: int = 2200
+
+    @property
+    def kind(self):
+        return "ssd"
+
+    @property
+    def nchunks(self) -> int:
+        return (self.seqlen + self.chunk - 1) // self.chunk
+
+    @property
+    def elements(self) -> int:  # step sizes per launch
+        return self.batch * self.seqlen * self.heads
+
+
+SSD_WORKLOADS = {
+    "ssd_small": SsdWorkload("ssd_small", batch=2, seqlen=300, heads=20, chunk=64, seed=2201),
+    "ssd_b8_l2048_h64_w256": SsdWorkload("ssd_b8_l2048_h64_w256", batch=8, seqlen=2048, heads=64, chunk=256,
+                                         seed=2202),
+}
+
+
+def make_ssd_inputs(w: SsdWorkload, *, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                    heads: Optional[int] = None, chunk: Optional[int] = None, seed: Optional[int] = None) -> dict:
+    """Seeded fp32 inputs of the chunk cumsum and its backward: dt ~ N(0, 1) (raw step
+    sizes before the bias), u ~ U[1e-3, 1e-1] with dt_bias = log(expm1(u)), A = -u'
+    with u' ~ U[1, 16] (Mamba-2's initial decay rates), and the incoming chunk
+    gradients ddA, ddt_out ~ N(0, 1).  Draw order: dt, u, u', ddA, ddt_out."""
+    b = w.batch if batch is None else batch
+    l = w.seqlen if seqlen is None else seqlen
+    h = w.heads if heads is None else heads
+    W = w.chunk if chunk is None else chunk
+    nc = (l + W - 1) // W
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    f = np.float32
+    dt = rng.standard_normal((b, l, h)).astype(f)
+    u = rng.uniform(1e-3, 1e-1, h)
+    dt_bias = np.log(np.expm1(u)).astype(f)
+    A = (-rng.uniform(1.0, 16.0, h)).astype(f)
+    ddA = rng.standard_normal((b, h, nc, W)).astype(f)
+    ddt_out = rng.standard_normal((b, h, nc, W)).astype(f)
+    return {"batch": b, "seqlen": l, "heads": h, "chunk": W, "dt": dt, "dt_bias": dt_bias, "A": A, "ddA": ddA,
+            "ddt_out": ddt_out}

@@ -301,3 +301,39 @@ def test_mamba3_validation():
     assert call(ws=addr(10)) == ALIAS                    # workspace == projected_grad
     assert L.ssm_mamba3_preprocess_bwd_workspace_bytes(130, 64) == 768            # 3 chunks x 64 heads x 4 B
     assert L.ssm_mamba3_preprocess_bwd_workspace_bytes(130, 3) == 256             # rounded up to 256 B
+
+
+@no_gpu_only
+def test_ssd_chunk_cumsum_validation():
+    L = ops.lib()
+    inf = float("inf")
+
+    def fwd(b=2, l=100, h=8, w=64, sp=1, lo=0.0, hi=inf, **over):
+        p = dict(dt=addr(0), A=addr(1), bias=addr(2), cs=addr(3), dto=addr(4))
+        p.update(over)
+        return L.ssm_ssd_chunk_cumsum_fwd(p["dt"], p["A"], p["bias"], p["cs"], p["dto"], b, l, h, w, sp, lo, hi,
+                                          None)
+
+    def bwd(b=2, l=100, h=8, w=64, sp=1, lo=0.0, hi=inf, **over):
+        p = dict(ddA=addr(0), ddo=addr(1), dt=addr(2), A=addr(3), bias=addr(4), ddt=addr(5), dA=addr(6),
+                 db=addr(7), ws=addr(8))
+        p.update(over)
+        wsb = p.get("wsb", L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(b, l, h, w))
+        return L.ssm_ssd_chunk_cumsum_bwd(p["ddA"], p["ddo"], p["dt"], p["A"], p["bias"], p["ddt"], p["dA"],
+                                          p["db"], p["ws"], wsb, b, l, h, w, sp, lo, hi, None)
+    for f in (fwd, bwd):
+        assert f(b=0) == DIM and f(l=0) == DIM and f(h=0) == DIM and f(w=0) == DIM
+        assert f(h=(1 << 20) + 1) == DIM and f(b=1 << 16, l=1 << 16) == DIM
+        assert f(lo=-1.0) == ARG and f(lo=0.5, hi=0.1) == ARG and f(hi=float("nan")) == ARG
+        assert f(A=None) == NULL and f(dt=None) == NULL
+    assert fwd(cs=None) == NULL and fwd(dto=None) == NULL
+    assert fwd(cs=addr(0)) == ALIAS and fwd(dto=addr(3)) == ALIAS and fwd(cs=addr(2)) == ALIAS
+    assert fwd(cs=addr(3, 2)) == ALIGN
+    assert bwd(ddA=None) == NULL and bwd(ddt=None) == NULL and bwd(dA=None) == NULL
+    assert bwd(ws=None) == WS and bwd(wsb=16) == WS and bwd(ws=addr(8, 64)) == WS
+    assert bwd(ddt=addr(2)) == ALIAS and bwd(ws=addr(5)) == ALIAS and bwd(db=addr(6)) == ALIAS
+    assert bwd(ddt=addr(5, 1)) == ALIGN
+    # two [batch, chunks, heads] fp32 partial arrays, each rounded up to 256 bytes
+    assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(2, 100, 8, 64) == 2 * 256
+    assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(8, 2048, 64, 256) == 2 * 8 * 8 * 64 * 4
+    assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(0, 100, 8, 64) == 0
