@@ -82,6 +82,20 @@ def ssd_bwd_bytes(b, l, h, nc, w):
     return 4 * (2 * b * h * nc * w + b * l * h + 2 * h + b * l * h + 2 * h)
 
 
+def ssd_scan_bytes(b, l, h, p, n, nc, w):
+    """SSD scan forward: x read, y written, B and C read once, dt_out and dA_cumsum read,
+    D read (fp32)"""
+    return 4 * (2 * b * l * h * p + 2 * b * l * n + 2 * b * h * nc * w + h)
+
+
+def ssd_scan_flops(b, l, h, p, n, nc, w):
+    """useful multiply-adds of the chunked form, x2: per (batch, head, chunk) the
+    inter-chunk readout C S^T (w n p), the causal C B^T (w (w + 1) / 2 pairs, n each),
+    the causal M X (w (w + 1) / 2 pairs, p each) and the state update X^T B (w p n)"""
+    tri = w * (w + 1) // 2
+    return 2 * b * h * nc * (w * n * p + tri * n + tri * p + w * p * n)
+
+
 def conv_bytes(b, l, d, k, es):
     """depthwise causal conv1d: x read, out written, weight and bias read"""
     return 2 * b * l * d * es + d * k * 4 + d * 4
@@ -364,6 +378,32 @@ def main():
             (label, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
 
+    def ssd_scan_case(name="ssd_scan_b8_l2048_h64_p64_n128"):
+        w = W.SSD_SCAN_WORKLOADS[name]
+        inp = W.make_ssd_scan_inputs(w)
+        args = (w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.nchunks, w.chunk)
+        nb, fl = ssd_scan_bytes(*args), ssd_scan_flops(*args)
+        nsets = max(2, int(np.ceil(1.2e9 / nb)))
+        A, dtb = t32(inp["A"]), t32(inp["dt_bias"])
+        base = {k: t32(inp[k]) for k in ("x", "B", "C")}
+        base["cs"], base["dto"] = ops.ssd_chunk_cumsum_fwd(t32(inp["dt"]), A, w.chunk, dt_bias=dtb)
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        Dv = t32(inp["D"])
+        outs = [(torch.empty_like(base["x"]),
+                 torch.empty((w.batch, w.heads, w.headdim, w.dstate), dtype=torch.float32, device=dev))
+                for _ in range(nsets)]
+
+        def fn(i):
+            s = sets[i]
+            ops.ssd_chunk_scan_fwd(s["x"], s["dto"], s["cs"], s["B"], s["C"], D=Dv, y=outs[i][0], h_final=outs[i][1])
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        tfs = fl / (ev_ms * 1e-3) / 1e12
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f TFLOP/s = %.1f%% of fp32 MFMA 157.3  sets=%d"
+            % (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, tfs, 100 * tfs / 157.3, nsets))
+        return dict(workload=w, bytes=nb, flops=fl, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, tflops=tfs)
+
     def conv_case(name, min_bytes_rotation=1.2e9):
         w = W.CONV_WORKLOADS[name]
         inp = W.make_conv_inputs(w)
@@ -457,6 +497,7 @@ def main():
     if args.only in ("all", "ssd"):
         results["ssd_cumsum_fwd_b8_l2048_h64_w256"] = ssd_case()
         results["ssd_cumsum_bwd_b8_l2048_h64_w256"] = ssd_case(bwd=True)
+        results["ssd_scan_fwd_b8_l2048_h64_p64_n128"] = ssd_scan_case()
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):
@@ -503,6 +544,10 @@ def main():
         secondary[k] = {"gbs": round(v["gbs"], 1), "frac_of_8tbs": round(v["gbs"] / HBM_PEAK_GBS, 4),
                         "us_per_launch": round(v["ev_ms"] * 1e3, 1), "algorithmic_bytes": v["bytes"],
                         "elements_per_s": round(v["workload"].elements / (v["ev_ms"] * 1e-3), 1)}
+        if "tflops" in v:
+            secondary[k]["tflops"] = round(v["tflops"], 2)
+            secondary[k]["frac_of_fp32_mfma"] = round(v["tflops"] / 157.3, 4)
+            secondary[k]["flops"] = v["flops"]
         if v["workload"].kind in ("fwd", "fwdbwd"):
             secondary[k]["state_updates_per_s"] = round(v["workload"].state_updates / (v["ev_ms"] * 1e-3), 1)
 

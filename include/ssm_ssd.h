@@ -43,6 +43,35 @@
  *   SSM_ERR_WORKSPACE (NULL, smaller than ssm_ssd_chunk_cumsum_bwd_workspace_bytes, or
  *   not 256-byte aligned), SSM_ERR_HIP.
  */
+/*
+ * ssm_ssd_chunk_scan_fwd -- the Mamba-2 SSD scan forward over chunks, fed by the chunk
+ * cumsum above.  The layer whose chunked kernels deterministic_backward.py names
+ * (ssd_chunk_state, ssd_state_passing, ssd_chunk_scan) is the selective recurrence
+ * with one scalar decay rate A per head; per (batch b, head h) the state is a
+ * [headdim, d_state] matrix:
+ *   state_t = exp(dt_t A[h]) state_{t-1} + dt_t outer(x[b,t,h,:], B[b,t,:])
+ *   y[b,t,h,:] = state_t C[b,t,:] + D[h] x[b,t,h,:]
+ * with dt_t the clamped step dt_out and A[h] entering only through dA_cumsum (both as
+ * ssm_ssd_chunk_cumsum_fwd writes them).  B and C form one group shared by every head.
+ * Inside a chunk of W steps, with cs = dA_cumsum and dt = dt_out of the chunk:
+ *   y_i   = exp(cs_i) C_i state_in + sum over s <= i of (C_i . B_s) exp(cs_i - cs_s) dt_s x_s
+ *   state_out = exp(cs_{W-1}) state_in + sum over s of exp(cs_{W-1} - cs_s) dt_s outer(x_s, B_s)
+ * which the kernel evaluates as matrix products on the matrix cores, carrying the
+ * state from chunk to chunk.  Equal to the recurrence up to rounding.
+ *
+ * Layout: row-major, last index fastest; all fp32.
+ *   x, y                  : [batch, seqlen, heads, headdim]
+ *   dt_out, dA_cumsum     : [batch, heads, chunks, chunk], chunks = ceil(seqlen / chunk)
+ *                           (steps past the sequence end: dt_out 0, dA_cumsum flat)
+ *   B, C                  : [batch, seqlen, d_state]
+ *   D                     : [heads], may be NULL (no skip term)
+ *   h0, h_final           : [batch, heads, headdim, d_state], may be NULL (zero / not written)
+ * Supported: headdim 64, d_state 64 or 128, chunk 64 (SSM_ERR_UNSUPPORTED otherwise).
+ * Pointers are device pointers, 4-byte aligned.  Outputs must not overlap inputs or
+ * each other.  Nothing is allocated; work goes to `stream`.
+ * Errors: SSM_ERR_NULL, SSM_ERR_DIM (a size < 1, 2^31 elements or more in one tensor,
+ * batch * heads >= 2^31), SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN, SSM_ERR_ALIAS, SSM_ERR_HIP.
+ */
 #ifndef SSM_SSD_H
 #define SSM_SSD_H
 
@@ -62,6 +91,11 @@ int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, const float
                              const float* dt_bias, float* ddt, float* dA, float* d_dt_bias, void* workspace,
                              size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk,
                              int dt_softplus, float dt_min, float dt_max, hipStream_t stream);
+
+int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
+                           const float* C, const float* D, const float* h0, float* y, float* h_final, int64_t batch,
+                           int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t chunk,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

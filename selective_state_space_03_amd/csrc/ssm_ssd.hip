@@ -272,6 +272,188 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
   if (d_dt_bias) d_dt_bias[h] = sb;
 }
 
+
+// ---------------------------------------------------------------------------------
+// SSD scan forward over chunks, on the matrix cores.
+//
+// One workgroup (4 waves) per (batch, head) walks the chunks in order and keeps the
+// [P = 64, N] state in MFMA accumulators: wave w owns the state columns of its N/4
+// range, as 16 x 16 tiles of v_mfma_f32_16x16x4_f32 (lane l, register r of a tile
+// holds row 4 * (l / 16) + r, column l % 16; the A operand of a lane is row l % 16,
+// column l / 16 of the 16 x 4 slice, the B operand row l / 16, column l % 16).
+// Per chunk of W = 64 steps, after staging x, B, C, the state and the chunk's
+// dA_cumsum / dt_out in LDS:
+//   * wave w computes the 16 output rows 16w .. 16w + 15:
+//       Y  = C S^T scaled by exp(cs_i)                     (K = N)
+//       G  = C B^T of its rows and of the step blocks s <= its rows    (K = N)
+//       M  = G exp(cs_i - cs_s) dt_s where s <= i, else 0  (to LDS)
+//       Y += M X                                            (K = 16 (w + 1))
+//       y  = Y + D x, stored;
+//   * then the state: S = exp(cs_last) S + (X exp(cs_last - cs_s) dt_s)^T B (K = W).
+// The sums over s and n have a fixed order: results are deterministic.  LDS rows are
+// padded so that the operand reads of a wavefront fall in distinct banks.
+constexpr int kScanP = 64;  // headdim
+constexpr int kScanW = 64;  // chunk width
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int N>
+__global__ void __launch_bounds__(256)
+ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
+                          const float* __restrict__ dA_cs, const float* __restrict__ Bm,
+                          const float* __restrict__ Cm, const float* __restrict__ Dv,
+                          const float* __restrict__ h0, float* __restrict__ y, float* __restrict__ h_final,
+                          int64_t L, int H, int64_t nc) {
+  constexpr int P = kScanP, W = kScanW;
+  constexpr int SX = P + 16;  // row strides (floats) of the LDS tiles
+  constexpr int SB = N + 4;
+  constexpr int SM = W + 4;
+  constexpr int NTW = N / 64;  // 16-column state tiles per wave
+  __shared__ float Xs[W * SX];
+  __shared__ float Bs[W * SB];
+  __shared__ float Cs[W * SB];
+  __shared__ float Ss[P * SB];
+  __shared__ float Ms[W * SM];
+  __shared__ float cs[W], wd[W];
+
+  const int64_t bh = blockIdx.x;  // (batch, head), head fastest
+  const int64_t b = bh / H;
+  const int h = (int)(bh - b * H);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const float Dh = Dv ? Dv[h] : 0.f;
+
+  // state tiles of this wave: rows pb * 16 .., columns (wave * NTW + j) * 16 ..
+  f32x4 S[4][NTW];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[pb][j][r] = h0 ? h0[((bh * P) + pb * 16 + 4 * lq + r) * N + (wave * NTW + j) * 16 + lr] : 0.f;
+
+  for (int64_t c = 0; c < nc; ++c) {
+    const int64_t t0 = c * W;
+    // ---- stage the chunk: x rows, B and C rows, the state, cumsum and weights
+#pragma unroll
+    for (int k = 0; k < W * P / 256; ++k) {
+      const int i = tid + 256 * k, s = i / P, p = i % P;
+      const int64_t t = t0 + s;
+      Xs[s * SX + p] = t < L ? x[((b * L + t) * H + h) * P + p] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < W * N / 256; ++k) {
+      const int i = tid + 256 * k, s = i / N, n = i % N;
+      const int64_t t = t0 + s;
+      const bool v = t < L;
+      Bs[s * SB + n] = v ? Bm[(b * L + t) * N + n] : 0.f;
+      Cs[s * SB + n] = v ? Cm[(b * L + t) * N + n] : 0.f;
+    }
+    if (tid < W) {
+      const int64_t o = (bh * nc + c) * W;
+      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1];
+      cs[tid] = ci;
+      wd[tid] = exp2_hw((cl - ci) * kLog2e) * dt_out[o + tid];
+    }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ss[(pb * 16 + 4 * lq + r) * SB + (wave * NTW + j) * 16 + lr] = S[pb][j][r];
+    __syncthreads();
+
+    // ---- outputs of rows 16 * wave .. : inter-chunk part and the masked C B^T
+    const int i0 = 16 * wave;
+    f32x4 Y[4];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) Y[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k0 = 0; k0 < N; k0 += 4) {
+      const float a = Cs[(i0 + lr) * SB + k0 + lq];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) Y[pb] = mfma4(a, Ss[(pb * 16 + lr) * SB + k0 + lq], Y[pb]);
+    }
+    float ecs[4], csr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      csr[r] = cs[i0 + 4 * lq + r];
+      ecs[r] = exp2_hw(csr[r] * kLog2e);
+    }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[pb][r] *= ecs[r];
+    for (int sb = 0; sb <= wave; ++sb) {
+      f32x4 G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int k0 = 0; k0 < N; k0 += 4)
+        G = mfma4(Cs[(i0 + lr) * SB + k0 + lq], Bs[(sb * 16 + lr) * SB + k0 + lq], G);
+      const int s = sb * 16 + lr;
+      const float css = cs[s], dts = dt_out[(bh * nc + c) * W + s];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * lq + r;
+        // select, not a product with a mask: exp of a positive exponent may be inf
+        Ms[i * SM + s] = i >= s ? G[r] * exp2_hw((csr[r] - css) * kLog2e) * dts : 0.f;
+      }
+    }
+    __syncthreads();
+    // ---- Y += M X over the step blocks s <= these rows, skip term, store
+    for (int k0 = 0; k0 < 16 * (wave + 1); k0 += 4) {
+      const float a = Ms[(i0 + lr) * SM + k0 + lq];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) Y[pb] = mfma4(a, Xs[(k0 + lq) * SX + pb * 16 + lr], Y[pb]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * lq + r;
+      const int64_t t = t0 + i;
+      if (t < L) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          const int p = pb * 16 + lr;
+          y[((b * L + t) * H + h) * P + p] = fmaf(Dh, Xs[i * SX + p], Y[pb][r]);
+        }
+      }
+    }
+    // ---- state: S = exp(cs_last) S + (X wd)^T B
+    const float el = exp2_hw(cs[W - 1] * kLog2e);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) S[pb][j] *= el;
+#pragma unroll 4
+    for (int k0 = 0; k0 < W; k0 += 4) {
+      const float w = wd[k0 + lq];
+      float bo[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) bo[j] = Bs[(k0 + lq) * SB + (wave * NTW + j) * 16 + lr];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) {
+        const float a = Xs[(k0 + lq) * SX + pb * 16 + lr] * w;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) S[pb][j] = mfma4(a, bo[j], S[pb][j]);
+      }
+    }
+    __syncthreads();  // the next chunk's staging overwrites every tile
+  }
+  if (h_final) {
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          h_final[((bh * P) + pb * 16 + 4 * lq + r) * N + (wave * NTW + j) * 16 + lr] = S[pb][j][r];
+  }
+}
+
 struct Rng {
   uintptr_t lo, hi;
 };
@@ -382,5 +564,41 @@ extern "C" int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, 
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
   hipLaunchKernelGGL(ssd_param_reduce_kernel, dim3((unsigned)((heads + 63) / 64)), dim3(64), 0, stream, part_a,
                      part_b, dA, d_dt_bias, (int64_t)(batch * m.nc), (int)heads);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
+                                      const float* C, const float* D, const float* h0, float* y, float* h_final,
+                                      int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                                      int64_t chunk, hipStream_t stream) {
+  using namespace ssm;
+  if (batch < 1 || seqlen < 1 || heads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return SSM_ERR_DIM;
+  const double lim = (double)((int64_t)1 << 31);
+  const int64_t nc = (seqlen + chunk - 1) / chunk;
+  if ((double)batch * seqlen * heads * headdim >= lim || (double)batch * heads * nc * chunk >= lim ||
+      (double)batch * seqlen * dstate >= lim || (double)batch * heads * headdim * dstate >= lim ||
+      (double)batch * heads >= lim)
+    return SSM_ERR_DIM;
+  if (headdim != kScanP || chunk != kScanW || (dstate != 64 && dstate != 128)) return SSM_ERR_UNSUPPORTED;
+  if (!x || !dt_out || !dA_cumsum || !B || !C || !y) return SSM_ERR_NULL;
+  const void* all[] = {x, dt_out, dA_cumsum, B, C, D, h0, y, h_final};
+  for (const void* p : all)
+    if (p && !aligned4(p)) return SSM_ERR_ALIGN;
+  const size_t f = 4, nx = (size_t)batch * seqlen * heads * headdim * f, nch = (size_t)batch * heads * nc * chunk * f;
+  const size_t nbc = (size_t)batch * seqlen * dstate * f, nst = (size_t)batch * heads * headdim * dstate * f;
+  const Rng ins[] = {span(x, nx), span(dt_out, nch), span(dA_cumsum, nch), span(B, nbc), span(C, nbc),
+                     span(D, heads * f), span(h0, nst)};
+  const Rng outs[] = {span(y, nx), span(h_final, nst)};
+  for (const Rng& o : outs)
+    for (const Rng& r : ins)
+      if (overlaps(o, r)) return SSM_ERR_ALIAS;
+  if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
+  const dim3 grid((unsigned)(batch * heads));
+  if (dstate == 128)
+    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+                       h0, y, h_final, seqlen, (int)heads, nc);
+  else
+    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+                       h0, y, h_final, seqlen, (int)heads, nc);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

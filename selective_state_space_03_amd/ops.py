@@ -37,7 +37,8 @@ EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", 
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
            "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
-           "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd")
+           "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd",
+           "ssm_ssd_chunk_scan_fwd")
 
 
 class ScanOptions(ctypes.Structure):
@@ -107,6 +108,8 @@ def lib():
         L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes.restype = SZ
         L.ssm_ssd_chunk_cumsum_bwd.argtypes = [P] * 9 + [SZ] + [I64] * 4 + [I, F, F, P]
         L.ssm_ssd_chunk_cumsum_bwd.restype = I
+        L.ssm_ssd_chunk_scan_fwd.argtypes = [P] * 9 + [I64] * 6 + [P]
+        L.ssm_ssd_chunk_scan_fwd.restype = I
         _lib = L
         return L
 
@@ -443,3 +446,33 @@ def ssd_chunk_cumsum_bwd(ddA, ddt_out, dt, A, dt_bias=None, dt_softplus=True, dt
         workspace.numel() * workspace.element_size(), b, l, h, chunk, 1 if dt_softplus else 0, float(dt_min),
         float(dt_max), _stream()))
     return {"ddt": ddt, "dA": dA, "d_dt_bias": db}
+
+
+def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_final=True):
+    """SSD scan forward over chunks (include/ssm_ssd.h), fed by ssd_chunk_cumsum_fwd.
+
+    x [batch, seqlen, heads, headdim], dt_out and dA_cumsum [batch, heads, chunks, chunk],
+    B, C [batch, seqlen, dstate], D [heads], h0 [batch, heads, headdim, dstate], all fp32
+    -> (y [batch, seqlen, heads, headdim], h_final [batch, heads, headdim, dstate] or None)."""
+    b, l, h, p = x.shape
+    n = B.shape[-1]
+    nc, chunk = dt_out.shape[-2:]
+    dev, f32 = x.device, torch.float32
+    _req(x, "x", (b, l, h, p), f32, dev)
+    _req(dt_out, "dt_out", (b, h, nc, chunk), f32, dev)
+    _req(dA_cumsum, "dA_cumsum", (b, h, nc, chunk), f32, dev)
+    if nc != (l + chunk - 1) // chunk:
+        raise ValueError("dt_out: %d chunks of %d do not cover seqlen %d" % (nc, chunk, l))
+    _req(B, "B", (b, l, n), f32, dev)
+    _req(C, "C", (b, l, n), f32, dev)
+    _req(D, "D", (h,), f32, dev)
+    _req(h0, "h0", (b, h, p, n), f32, dev)
+    if y is None:
+        y = torch.empty((b, l, h, p), dtype=f32, device=dev)
+    _req(y, "y", (b, l, h, p), f32, dev)
+    hf = torch.empty((b, h, p, n), dtype=f32, device=dev) if h_final is True else h_final
+    _req(hf, "h_final", (b, h, p, n), f32, dev)
+    _check("ssm_ssd_chunk_scan_fwd", lib().ssm_ssd_chunk_scan_fwd(
+        _ptr(x), _ptr(dt_out), _ptr(dA_cumsum), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf), b, l, h, p, n,
+        chunk, _stream()))
+    return y, hf

@@ -314,3 +314,62 @@ def make_ssd_inputs(w: SsdWorkload, *, batch: Optional[int] = None, seqlen: Opti
     ddt_out = rng.standard_normal((b, h, nc, W)).astype(f)
     return {"batch": b, "seqlen": l, "heads": h, "chunk": W, "dt": dt, "dt_bias": dt_bias, "A": A, "ddA": ddA,
             "ddt_out": ddt_out}
+
+
+@dataclasses.dataclass(frozen=True)
+class SsdScanWorkload:
+    """SSD scan forward over [batch, seqlen, heads, headdim] inputs with one B/C group of
+    d_state, in chunks of `chunk` steps.  The page gives no sizes: a d_model-2048 Mamba-2
+    layer (64 heads of 64 channels, d_state 128) over 8 x 2048 tokens."""
+    name: str
+    batch: int
+    seqlen: int
+    heads: int
+    headdim: int
+    dstate: int
+    chunk: int = 64
+    seed: int = 2300
+
+    @property
+    def kind(self):
+        return "ssd_scan"
+
+    @property
+    def nchunks(self) -> int:
+        return (self.seqlen + self.chunk - 1) // self.chunk
+
+    @property
+    def elements(self) -> int:  # outputs y per launch
+        return self.batch * self.seqlen * self.heads * self.headdim
+
+
+SSD_SCAN_WORKLOADS = {
+    "ssd_scan_small": SsdScanWorkload("ssd_scan_small", batch=2, seqlen=150, heads=3, headdim=64, dstate=128, seed=2301),
+    "ssd_scan_b8_l2048_h64_p64_n128": SsdScanWorkload("ssd_scan_b8_l2048_h64_p64_n128", batch=8, seqlen=2048,
+                                                      heads=64, headdim=64, dstate=128, seed=2302),
+}
+
+
+def make_ssd_scan_inputs(w: SsdScanWorkload, *, batch: Optional[int] = None, seqlen: Optional[int] = None,
+                         heads: Optional[int] = None, dstate: Optional[int] = None, h0: bool = False,
+                         seed: Optional[int] = None) -> dict:
+    """Seeded fp32 inputs: x ~ N(0, 1) [batch, seqlen, heads, headdim], raw dt ~ N(0, 1)
+    [batch, seqlen, heads], u ~ U[1e-3, 1e-1] with dt_bias = log(expm1(u)), A = -U[1, 16],
+    B, C ~ N(0, 1) [batch, seqlen, dstate], D = 1, and (when asked) h0 ~ N(0, 1).  Draw
+    order: x, dt, u, A, B, C, h0."""
+    b = w.batch if batch is None else batch
+    l = w.seqlen if seqlen is None else seqlen
+    h = w.heads if heads is None else heads
+    n = w.dstate if dstate is None else dstate
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    f = np.float32
+    x = rng.standard_normal((b, l, h, w.headdim), dtype=np.float32)
+    dt = rng.standard_normal((b, l, h)).astype(f)
+    u = rng.uniform(1e-3, 1e-1, h)
+    dt_bias = np.log(np.expm1(u)).astype(f)
+    A = (-rng.uniform(1.0, 16.0, h)).astype(f)
+    Bm = rng.standard_normal((b, l, n)).astype(f)
+    Cm = rng.standard_normal((b, l, n)).astype(f)
+    h0v = rng.standard_normal((b, h, w.headdim, n)).astype(f) if h0 else None
+    return {"batch": b, "seqlen": l, "heads": h, "headdim": w.headdim, "dstate": n, "chunk": w.chunk, "x": x,
+            "dt": dt, "dt_bias": dt_bias, "A": A, "B": Bm, "C": Cm, "D": np.ones(h, f), "h0": h0v}

@@ -337,3 +337,20 @@ def test_ssd_chunk_cumsum_validation():
     assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(2, 100, 8, 64) == 2 * 256
     assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(8, 2048, 64, 256) == 2 * 8 * 8 * 64 * 4
     assert L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes(0, 100, 8, 64) == 0
+
+
+@no_gpu_only
+def test_ssd_chunk_scan_validation():
+    L = ops.lib()
+
+    def call(b=2, l=100, h=3, p=64, n=128, w=64, **over):
+        a = dict(x=addr(0), dto=addr(1), cs=addr(2), B=addr(3), C=addr(4), D=addr(5), h0=addr(6), y=addr(7),
+                 hf=addr(8))
+        a.update(over)
+        return L.ssm_ssd_chunk_scan_fwd(a["x"], a["dto"], a["cs"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hf"],
+                                        b, l, h, p, n, w, None)
+    assert call(b=0) == DIM and call(l=0) == DIM and call(p=0) == DIM and call(w=0) == DIM
+    assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=128) == UNSUP
+    assert call(x=None) == NULL and call(cs=None) == NULL and call(y=None) == NULL
+    assert call(y=addr(0)) == ALIAS and call(hf=addr(6)) == ALIAS and call(hf=addr(7)) == ALIAS
+    assert call(y=addr(7, 2)) == ALIGN

@@ -1,0 +1,121 @@
+"""GPU parity of the Mamba-2 SSD scan forward (chunk cumsum, then the chunked scan on
+the matrix cores) against the fp64 oracle.
+
+y and the final state are compared element by element at max relative error (RMS
+floor) <= 1e-4, on shapes with a ragged last chunk, one full chunk, a single step,
+d_state 64 and 128, with and without the skip term and an initial state.  The scan is
+checked both as a pipeline (the GPU chunk cumsum feeding it) and alone (fed the
+oracle's dt_out and dA_cumsum rounded to fp32).  On the full workload (8 x 2048, 64
+heads of 64, d_state 128) sampled (batch, head) sequences are compared with the oracle
+run on that sequence alone (sequences are independent).  Repeated runs are
+bit-identical, and unsupported sizes are refused.
+"""
+import numpy as np
+import pytest
+
+from _helpers import RTOL_F32, host, rel_err, say, to_dev32
+from oracle import ssd_cumsum_oracle as CS
+from oracle import ssd_scan_oracle as S
+from selective_state_space_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from selective_state_space_03_amd import ops
+    ops.lib()
+
+
+def oracle_run(inp, bsel=None, hsel=None):
+    """fp64 oracle: chunk cumsum for dt_out, then the sequential SSD recurrence"""
+    l, w = inp["seqlen"], inp["chunk"]
+    dt, A, bias, D, h0 = inp["dt"], inp["A"], inp["dt_bias"], inp["D"], inp["h0"]
+    xs, Bs, Cs = inp["x"], inp["B"], inp["C"]
+    if bsel is not None:  # one (batch, head) sequence
+        hs = slice(hsel, hsel + 1)
+        dt, A, bias = dt[bsel:bsel + 1, :, hs], A[hs], bias[hs]
+        D = None if D is None else D[hs]
+        h0 = None if h0 is None else h0[bsel:bsel + 1, hs]
+        xs, Bs, Cs = xs[bsel:bsel + 1, :, hs], Bs[bsel:bsel + 1], Cs[bsel:bsel + 1]
+    dA, dto = CS.chunk_cumsum_fwd(dt, A, bias, w, True)
+    b, h = dt.shape[0], dt.shape[2]
+    flat = dto.transpose(0, 2, 3, 1).reshape(b, -1, h)[:, :l]  # [b, h, nc, w] -> [b, l, h]
+    ref = S.ssd_scan_fwd(xs, flat, A, Bs, Cs, D, h0)
+    return ref if bsel is not None else (ref, dA, dto)
+
+
+def gpu_run(inp, cs=None, dto=None):
+    from selective_state_space_03_amd import ops
+    if cs is None:
+        cs, dto = ops.ssd_chunk_cumsum_fwd(to_dev32(inp["dt"]), to_dev32(inp["A"]), inp["chunk"],
+                                           dt_bias=to_dev32(inp["dt_bias"]))
+    y, hf = ops.ssd_chunk_scan_fwd(to_dev32(inp["x"]), dto, cs, to_dev32(inp["B"]), to_dev32(inp["C"]),
+                                   D=to_dev32(inp["D"]), h0=to_dev32(inp["h0"]))
+    torch.cuda.synchronize()
+    return host(y), host(hf)
+
+
+CASES = [
+    # (batch, seqlen, heads, dstate, skip, h0)
+    (2, 150, 3, 128, True, True),    # ragged last chunk, initial state
+    (1, 64, 2, 64, False, False),    # one full chunk, no skip term
+    (2, 1, 2, 128, True, True),      # a single step
+    (1, 257, 1, 64, True, False),    # five chunks, the last of one step
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_scan_matches_oracle(case):
+    b, l, h, n, skip, with_h0 = case
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=b, seqlen=l, heads=h, dstate=n, h0=with_h0, seed=w.seed + l + 7 * n)
+    if not skip:
+        inp["D"] = None
+    say("ssd scan b=%d l=%d h=%d n=%d skip=%d h0=%d" % (b, l, h, n, skip, with_h0))
+    ref, rcs, rdto = oracle_run(inp)
+    y, hf = gpu_run(inp)
+    assert rel_err(y, ref["y"]) <= RTOL_F32
+    assert rel_err(hf, ref["h_final"]) <= RTOL_F32
+    # the scan alone, fed the oracle's chunk cumsum (rounded to fp32)
+    y2, hf2 = gpu_run(inp, cs=to_dev32(rcs), dto=to_dev32(rdto))
+    assert rel_err(y2, ref["y"]) <= RTOL_F32
+    assert rel_err(hf2, ref["h_final"]) <= RTOL_F32
+
+
+def test_full_workload_sampled_sequences():
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_b8_l2048_h64_p64_n128"]
+    inp = W.make_ssd_scan_inputs(w)
+    say("ssd scan full workload %s" % w.name)
+    y, hf = gpu_run(inp)
+    for (b, h) in ((0, 0), (5, 37), (7, 63)):
+        ref = oracle_run(inp, b, h)
+        assert rel_err(y[b, :, h], ref["y"][0, :, 0]) <= RTOL_F32
+        assert rel_err(hf[b, h], ref["h_final"][0, 0]) <= RTOL_F32
+
+
+def test_repeat_runs_are_bit_identical():
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, h0=True)
+    runs = [gpu_run(inp) for _ in range(3)]
+    for y, hf in runs[1:]:
+        assert y.tobytes() == runs[0][0].tobytes() and hf.tobytes() == runs[0][1].tobytes()
+
+
+def test_unsupported_sizes_are_refused():
+    from selective_state_space_03_amd import ops
+    dev = "cuda"
+    x = torch.zeros((1, 64, 1, 32), device=dev)           # headdim 32
+    ch = torch.zeros((1, 1, 1, 64), device=dev)
+    bc = torch.zeros((1, 64, 128), device=dev)
+    with pytest.raises(ops.SsmError):
+        ops.ssd_chunk_scan_fwd(x, ch, ch, bc, bc)
+    x = torch.zeros((1, 64, 1, 64), device=dev)
+    with pytest.raises(ops.SsmError):
+        ops.ssd_chunk_scan_fwd(x, ch, ch, torch.zeros((1, 64, 96), device=dev), torch.zeros((1, 64, 96), device=dev))
+    ch32 = torch.zeros((1, 1, 2, 32), device=dev)           # chunk 32
+    with pytest.raises(ops.SsmError):
+        ops.ssd_chunk_scan_fwd(x, ch32, ch32, bc, bc)
