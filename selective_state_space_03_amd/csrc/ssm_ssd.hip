@@ -276,24 +276,25 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
 // ---------------------------------------------------------------------------------
 // SSD scan forward over chunks, on the matrix cores.
 //
-// One workgroup (4 waves) per (batch, head) walks the chunks in order and keeps the
-// [P = 64, N] state in MFMA accumulators: wave w owns the state columns of its N/4
-// range, as 16 x 16 tiles of v_mfma_f32_16x16x4_f32 (lane l, register r of a tile
-// holds row 4 * (l / 16) + r, column l % 16; the A operand of a lane is row l % 16,
-// column l / 16 of the 16 x 4 slice, the B operand row l / 16, column l % 16).
-// Per chunk of W = 64 steps, after staging x, B, C, the state and the chunk's
-// dA_cumsum / dt_out in LDS:
-//   * wave w computes the 16 output rows 16w .. 16w + 15:
-//       Y  = C S^T scaled by exp(cs_i)                     (K = N)
-//       G  = C B^T of its rows and of the step blocks s <= its rows    (K = N)
-//       M  = G exp(cs_i - cs_s) dt_s where s <= i, else 0  (to LDS)
-//       Y += M X                                            (K = 16 (w + 1))
-//       y  = Y + D x, stored;
-//   * then the state: S = exp(cs_last) S + (X exp(cs_last - cs_s) dt_s)^T B (K = W).
-// The sums over s and n have a fixed order: results are deterministic.  LDS rows are
-// padded so that the operand reads of a wavefront fall in distinct banks.
+// One workgroup (8 waves) per (batch, head) walks the chunks in order and keeps the
+// [P = 64, N] state in MFMA accumulators, as 16 x 16 tiles of v_mfma_f32_16x16x4_f32
+// (lane l, register r of a tile holds row 4 * (l / 16) + r, column l % 16; the A
+// operand of a lane is row l % 16, column l / 16 of the 16 x 4 slice, the B operand
+// row l / 16, column l % 16).  Per chunk of W = 64 steps, with x, B, C, the state and
+// the chunk's dA_cumsum / dt_out staged in LDS, wave w = (row block rb = w % 4, column
+// half ph = w / 4) computes the output rows 16 rb .. 16 rb + 15, columns 32 ph ..:
+//   Y  = C S^T scaled by exp(cs_i)                              (K = N)
+//   G  = C B^T of its rows and of the step blocks s <= its rows (split between the two
+//        waves of a row block), M = G exp(cs_i - cs_s) dt_s where s <= i, else 0, to LDS
+//   Y += M X over the step blocks s <= its rows, y = Y + D x, stored;
+// then every wave updates its state tiles: S = exp(cs_last) S + (X exp(cs_last - cs_s)
+// dt_s)^T B (K = W).  The next chunk's x, B and C are loaded into registers while the
+// matrix products run.  Sums over s and n have a fixed order: results are
+// deterministic.  LDS rows are padded so that a wavefront's operand reads fall in
+// distinct banks.
 constexpr int kScanP = 64;  // headdim
 constexpr int kScanW = 64;  // chunk width
+constexpr int kScanThreads = 512;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -302,82 +303,101 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 }
 
 template <int N>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kScanThreads)
 ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
                           const float* __restrict__ Cm, const float* __restrict__ Dv,
                           const float* __restrict__ h0, float* __restrict__ y, float* __restrict__ h_final,
                           int64_t L, int H, int64_t nc) {
-  constexpr int P = kScanP, W = kScanW;
+  constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 16;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
   constexpr int SM = W + 4;
-  constexpr int NTW = N / 64;  // 16-column state tiles per wave
+  constexpr int NT = N / 16;   // 16-column state tiles
+  constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
+  constexpr int XL = W * P / T, BL = W * N / T;  // staged elements per thread
   __shared__ float Xs[W * SX];
   __shared__ float Bs[W * SB];
   __shared__ float Cs[W * SB];
   __shared__ float Ss[P * SB];
   __shared__ float Ms[W * SM];
-  __shared__ float cs[W], wd[W];
+  __shared__ float cs[W], wd[W], dts[W];
 
   const int64_t bh = blockIdx.x;  // (batch, head), head fastest
   const int64_t b = bh / H;
   const int h = (int)(bh - b * H);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
+  const int rb = wave & 3, ph = wave >> 2;
   const float Dh = Dv ? Dv[h] : 0.f;
+  // state tiles of this wave: rows (pb0 + j) * 16 .., columns nbw * 16 ..
+  const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
 
-  // state tiles of this wave: rows pb * 16 .., columns (wave * NTW + j) * 16 ..
-  f32x4 S[4][NTW];
+  f32x4 S[TPW];
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb)
+  for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int r = 0; r < 4; ++r)
+      S[j][r] = h0 ? h0[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] : 0.f;
+
+  // registers of the next chunk's x, B, C (element tid + T * k of each tile)
+  float rx[XL], rbm[BL], rcm[BL];
+  auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * W;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[pb][j][r] = h0 ? h0[((bh * P) + pb * 16 + 4 * lq + r) * N + (wave * NTW + j) * 16 + lr] : 0.f;
+    for (int k = 0; k < XL; ++k) {
+      const int i = tid + T * k, s = i / P, p = i % P;
+      const int64_t t = t0 + s;
+      rx[k] = (c < nc && t < L) ? x[((b * L + t) * H + h) * P + p] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < BL; ++k) {
+      const int i = tid + T * k, s = i / N, n = i % N;
+      const int64_t t = t0 + s;
+      const bool v = c < nc && t < L;
+      rbm[k] = v ? Bm[(b * L + t) * N + n] : 0.f;
+      rcm[k] = v ? Cm[(b * L + t) * N + n] : 0.f;
+    }
+  };
+  load_chunk(0);
 
   for (int64_t c = 0; c < nc; ++c) {
     const int64_t t0 = c * W;
     // ---- stage the chunk: x rows, B and C rows, the state, cumsum and weights
 #pragma unroll
-    for (int k = 0; k < W * P / 256; ++k) {
-      const int i = tid + 256 * k, s = i / P, p = i % P;
-      const int64_t t = t0 + s;
-      Xs[s * SX + p] = t < L ? x[((b * L + t) * H + h) * P + p] : 0.f;
+    for (int k = 0; k < XL; ++k) {
+      const int i = tid + T * k;
+      Xs[(i / P) * SX + i % P] = rx[k];
     }
 #pragma unroll
-    for (int k = 0; k < W * N / 256; ++k) {
-      const int i = tid + 256 * k, s = i / N, n = i % N;
-      const int64_t t = t0 + s;
-      const bool v = t < L;
-      Bs[s * SB + n] = v ? Bm[(b * L + t) * N + n] : 0.f;
-      Cs[s * SB + n] = v ? Cm[(b * L + t) * N + n] : 0.f;
+    for (int k = 0; k < BL; ++k) {
+      const int i = tid + T * k;
+      Bs[(i / N) * SB + i % N] = rbm[k];
+      Cs[(i / N) * SB + i % N] = rcm[k];
     }
     if (tid < W) {
       const int64_t o = (bh * nc + c) * W;
-      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1];
+      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1], dv = dt_out[o + tid];
       cs[tid] = ci;
-      wd[tid] = exp2_hw((cl - ci) * kLog2e) * dt_out[o + tid];
+      dts[tid] = dv;
+      wd[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
     }
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ss[(pb * 16 + 4 * lq + r) * SB + (wave * NTW + j) * 16 + lr] = S[pb][j][r];
+      for (int r = 0; r < 4; ++r) Ss[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = S[j][r];
     __syncthreads();
+    load_chunk(c + 1);  // in flight during the products below (zeros past the end)
 
-    // ---- outputs of rows 16 * wave .. : inter-chunk part and the masked C B^T
-    const int i0 = 16 * wave;
-    f32x4 Y[4];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) Y[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+    // ---- outputs of rows 16 rb .., columns 32 ph ..: inter-chunk part
+    const int i0 = 16 * rb;
+    f32x4 Y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 8
     for (int k0 = 0; k0 < N; k0 += 4) {
       const float a = Cs[(i0 + lr) * SB + k0 + lq];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) Y[pb] = mfma4(a, Ss[(pb * 16 + lr) * SB + k0 + lq], Y[pb]);
+      for (int q = 0; q < 2; ++q) Y[q] = mfma4(a, Ss[((2 * ph + q) * 16 + lr) * SB + k0 + lq], Y[q]);
     }
     float ecs[4], csr[4];
 #pragma unroll
@@ -386,29 +406,42 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       ecs[r] = exp2_hw(csr[r] * kLog2e);
     }
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Y[pb][r] *= ecs[r];
-    for (int sb = 0; sb <= wave; ++sb) {
-      f32x4 G = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) Y[q][r] *= ecs[r];
+    // ---- masked C B^T for step blocks sb = ph, ph + 2 (those <= rb), two accumulators
+    {
+      const bool two = ph + 2 <= rb;  // wave-uniform
+      if (ph <= rb) {
+        f32x4 G0 = {0.f, 0.f, 0.f, 0.f}, G1 = {0.f, 0.f, 0.f, 0.f};
+        const int s0 = ph * 16, s1 = (ph + 2) * 16;
 #pragma unroll 8
-      for (int k0 = 0; k0 < N; k0 += 4)
-        G = mfma4(Cs[(i0 + lr) * SB + k0 + lq], Bs[(sb * 16 + lr) * SB + k0 + lq], G);
-      const int s = sb * 16 + lr;
-      const float css = cs[s], dts = dt_out[(bh * nc + c) * W + s];
+        for (int k0 = 0; k0 < N; k0 += 4) {
+          const float a = Cs[(i0 + lr) * SB + k0 + lq];
+          G0 = mfma4(a, Bs[(s0 + lr) * SB + k0 + lq], G0);
+          if (two) G1 = mfma4(a, Bs[(s1 + lr) * SB + k0 + lq], G1);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * lq + r;
-        // select, not a product with a mask: exp of a positive exponent may be inf
-        Ms[i * SM + s] = i >= s ? G[r] * exp2_hw((csr[r] - css) * kLog2e) * dts : 0.f;
+        for (int u = 0; u < 2; ++u) {
+          if (u == 1 && !two) break;
+          const int s = (u ? s1 : s0) + lr;
+          const float css = cs[s], dv = dts[s];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 4 * lq + r;
+            const float g = u ? G1[r] : G0[r];
+            // select, not a product with a mask: exp of a positive exponent may be inf
+            Ms[i * SM + s] = i >= s ? g * exp2_hw((csr[r] - css) * kLog2e) * dv : 0.f;
+          }
+        }
       }
     }
     __syncthreads();
     // ---- Y += M X over the step blocks s <= these rows, skip term, store
-    for (int k0 = 0; k0 < 16 * (wave + 1); k0 += 4) {
+    for (int k0 = 0; k0 < 16 * (rb + 1); k0 += 4) {
       const float a = Ms[(i0 + lr) * SM + k0 + lq];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) Y[pb] = mfma4(a, Xs[(k0 + lq) * SX + pb * 16 + lr], Y[pb]);
+      for (int q = 0; q < 2; ++q) Y[q] = mfma4(a, Xs[(k0 + lq) * SX + (2 * ph + q) * 16 + lr], Y[q]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -416,41 +449,31 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       const int64_t t = t0 + i;
       if (t < L) {
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const int p = pb * 16 + lr;
-          y[((b * L + t) * H + h) * P + p] = fmaf(Dh, Xs[i * SX + p], Y[pb][r]);
+        for (int q = 0; q < 2; ++q) {
+          const int p = (2 * ph + q) * 16 + lr;
+          y[((b * L + t) * H + h) * P + p] = fmaf(Dh, Xs[i * SX + p], Y[q][r]);
         }
       }
     }
     // ---- state: S = exp(cs_last) S + (X wd)^T B
     const float el = exp2_hw(cs[W - 1] * kLog2e);
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) S[pb][j] *= el;
+    for (int j = 0; j < TPW; ++j) S[j] *= el;
 #pragma unroll 4
     for (int k0 = 0; k0 < W; k0 += 4) {
       const float w = wd[k0 + lq];
-      float bo[NTW];
+      const float bo = Bs[(k0 + lq) * SB + nbw * 16 + lr];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) bo[j] = Bs[(k0 + lq) * SB + (wave * NTW + j) * 16 + lr];
-#pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const float a = Xs[(k0 + lq) * SX + pb * 16 + lr] * w;
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) S[pb][j] = mfma4(a, bo[j], S[pb][j]);
-      }
+      for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[(k0 + lq) * SX + (pb0 + j) * 16 + lr] * w, bo, S[j]);
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
   }
   if (h_final) {
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h_final[((bh * P) + pb * 16 + 4 * lq + r) * N + (wave * NTW + j) * 16 + lr] = S[pb][j][r];
+      for (int r = 0; r < 4; ++r)
+        h_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
   }
 }
 
@@ -595,10 +618,10 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
   if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
   const dim3 grid((unsigned)(batch * heads));
   if (dstate == 128)
-    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
                        h0, y, h_final, seqlen, (int)heads, nc);
   else
-    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
                        h0, y, h_final, seqlen, (int)heads, nc);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
