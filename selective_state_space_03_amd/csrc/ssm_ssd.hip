@@ -316,12 +316,12 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   constexpr int NT = N / 16;   // 16-column state tiles
   constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
   constexpr int XL = W * P / T, BL = W * N / T;  // staged elements per thread
-  __shared__ float Xs[W * SX];
-  __shared__ float Bs[W * SB];
-  __shared__ float Cs[W * SB];
-  __shared__ float Ss[P * SB];
-  __shared__ float Ms[W * SM];
-  __shared__ float cs[W], wd[W], dts[W];
+  __shared__ __attribute__((aligned(16))) float Xs[W * SX];
+  __shared__ __attribute__((aligned(16))) float Bs[W * SB];
+  __shared__ __attribute__((aligned(16))) float Cs[W * SB];
+  __shared__ __attribute__((aligned(16))) float Ss[P * SB];
+  __shared__ __attribute__((aligned(16))) float Ms[W * SM];
+  __shared__ __attribute__((aligned(16))) float cs[W], wd[W], dts[W];
 
   const int64_t bh = blockIdx.x;  // (batch, head), head fastest
   const int64_t b = bh / H;
@@ -329,7 +329,9 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int rb = wave & 3, ph = wave >> 2;
+  // the two waves of a SIMD (w, w + 4) take row blocks r and 3 - r, which evens out
+  // the causal work of the two phases between barriers
+  const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
   const float Dh = Dv ? Dv[h] : 0.f;
   // state tiles of this wave: rows (pb0 + j) * 16 .., columns nbw * 16 ..
   const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
@@ -393,11 +395,18 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     // ---- outputs of rows 16 rb .., columns 32 ph ..: inter-chunk part
     const int i0 = 16 * rb;
     f32x4 Y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-    for (int k0 = 0; k0 < N; k0 += 4) {
-      const float a = Cs[(i0 + lr) * SB + k0 + lq];
+    // Products over n go in 16-wide blocks whose 4 MFMA steps take n = kb + 4 (l / 16)
+    // + m (m = 0..3) on both operands: any assignment of the sum's terms to steps gives
+    // the same sum, and this one lets a lane read its 4 operands as one 16-byte load.
+#pragma unroll 2
+    for (int kb = 0; kb < N; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Cs[(i0 + lr) * SB + kb + 4 * lq];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) Y[q] = mfma4(a, Ss[((2 * ph + q) * 16 + lr) * SB + k0 + lq], Y[q]);
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 bq = *(const f32x4*)&Ss[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Y[q] = mfma4(a[m], bq[m], Y[q]);
+      }
     }
     float ecs[4], csr[4];
 #pragma unroll
@@ -415,11 +424,17 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       if (ph <= rb) {
         f32x4 G0 = {0.f, 0.f, 0.f, 0.f}, G1 = {0.f, 0.f, 0.f, 0.f};
         const int s0 = ph * 16, s1 = (ph + 2) * 16;
-#pragma unroll 8
-        for (int k0 = 0; k0 < N; k0 += 4) {
-          const float a = Cs[(i0 + lr) * SB + k0 + lq];
-          G0 = mfma4(a, Bs[(s0 + lr) * SB + k0 + lq], G0);
-          if (two) G1 = mfma4(a, Bs[(s1 + lr) * SB + k0 + lq], G1);
+#pragma unroll 2
+        for (int kb = 0; kb < N; kb += 16) {
+          const f32x4 a = *(const f32x4*)&Cs[(i0 + lr) * SB + kb + 4 * lq];
+          const f32x4 b0 = *(const f32x4*)&Bs[(s0 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) G0 = mfma4(a[m], b0[m], G0);
+          if (two) {
+            const f32x4 b1 = *(const f32x4*)&Bs[(s1 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) G1 = mfma4(a[m], b1[m], G1);
+          }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -438,10 +453,14 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     }
     __syncthreads();
     // ---- Y += M X over the step blocks s <= these rows, skip term, store
-    for (int k0 = 0; k0 < 16 * (rb + 1); k0 += 4) {
-      const float a = Ms[(i0 + lr) * SM + k0 + lq];
+    for (int kb = 0; kb < 16 * (rb + 1); kb += 16) {
+      const f32x4 a = *(const f32x4*)&Ms[(i0 + lr) * SM + kb + 4 * lq];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) Y[q] = mfma4(a, Xs[(k0 + lq) * SX + (2 * ph + q) * 16 + lr], Y[q]);
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) Y[q] = mfma4(a[m], Xs[k * SX + (2 * ph + q) * 16 + lr], Y[q]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -459,12 +478,16 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     const float el = exp2_hw(cs[W - 1] * kLog2e);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) S[j] *= el;
-#pragma unroll 4
-    for (int k0 = 0; k0 < W; k0 += 4) {
-      const float w = wd[k0 + lq];
-      const float bo = Bs[(k0 + lq) * SB + nbw * 16 + lr];
+#pragma unroll 2
+    for (int kb = 0; kb < W; kb += 16) {
+      const f32x4 w4 = *(const f32x4*)&wd[kb + 4 * lq];
 #pragma unroll
-      for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[(k0 + lq) * SX + (pb0 + j) * 16 + lr] * w, bo, S[j]);
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+        const float bo = Bs[k * SB + nbw * 16 + lr];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[k * SX + (pb0 + j) * 16 + lr] * w4[m], bo, S[j]);
+      }
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
   }
