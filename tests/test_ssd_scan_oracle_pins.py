@@ -7,7 +7,9 @@
   must give the same y and final state;
 * constant inputs: the closed-form geometric sum;
 * brute-force unrolling (products of decays) for L <= 6, with an initial state;
-* composition of two segments through h0 / h_final; zero input gives zero output.
+* composition of two segments through h0 / h_final; zero input gives zero output;
+* backward: fp64 central differences of sum(dy * y) + sum(dh_final * h_final) with
+  respect to every element of x, dt, A, B, C, D and h0.
 """
 import numpy as np
 
@@ -85,3 +87,29 @@ def test_segments_compose_and_zero_input():
     np.testing.assert_allclose(second["h_final"], whole["h_final"], rtol=1e-12, atol=1e-13)
     zero = S.ssd_scan_fwd(np.zeros_like(x), dt, A, Bm, Cm, D)
     assert np.all(zero["y"] == 0) and np.all(zero["h_final"] == 0)
+
+
+def test_backward_matches_central_differences():
+    rng = np.random.default_rng(21)
+    b, L, H, P, N = 1, 5, 2, 2, 3
+    x, dt, A, Bm, Cm, D, h0 = _inputs(rng, b, L, H, P, N)
+    dy = rng.standard_normal((b, L, H, P))
+    dhf = rng.standard_normal((b, H, P, N))
+    args = {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "h0": h0}
+
+    def loss(a):
+        o = S.ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["h0"])
+        return float(np.sum(o["y"] * dy) + np.sum(o["h_final"] * dhf))
+
+    g = S.ssd_scan_bwd(x, dt, A, Bm, Cm, dy, D, h0, dhf)
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+    for k, gk in names.items():
+        num = np.zeros_like(args[k])
+        for idx in np.ndindex(args[k].shape):
+            eps = 1e-6 * max(1.0, abs(args[k][idx]))
+            up = {kk: (v.copy() if kk == k else v) for kk, v in args.items()}
+            dn = {kk: (v.copy() if kk == k else v) for kk, v in args.items()}
+            up[k][idx] += eps
+            dn[k][idx] -= eps
+            num[idx] = (loss(up) - loss(dn)) / (2 * eps)
+        np.testing.assert_allclose(g[gk], num, rtol=1e-6, atol=1e-8, err_msg=k)
