@@ -14,7 +14,9 @@ Printed: ONE JSON line on stdout (everything else goes to stderr) with the
 headline forward GB/s, its roofline (algorithmic bytes per launch / average launch
 time from HIP events on the launch stream, against 8 TB/s), the fp64 CPU oracle
 timed on the host cores, and secondary lines for the bf16 forward, the decode
-step and the backward.  `traffic` comes from the committed rocprofv3 counter
+step, the backward, the conv1d, the Mamba-3 preprocess adjoint and the Mamba-2 SSD
+chunk cumsum and scan (the scan also in TFLOP/s against the fp32 matrix-core
+peak).  `traffic` comes from the committed rocprofv3 counter
 summary for the forward kernel when that summary matches the current kernel
 source, else null.
 """

@@ -17,6 +17,9 @@ Functions mirror the C entry points:
    with the state entering every 16-step chunk, which ssm_scan_bwd then reuses)
 The step-size clamp (dt_min, dt_max) and the state gradients go through the _ex entry
 points and their ssm_scan_options struct; without them the calls are the plain ones.
+Also bound (include/ssm_conv1d.h, ssm_mamba3.h, ssm_ssd.h): conv1d_fwd / conv1d_step /
+conv1d_bwd, mamba3_preprocess_bwd, ssd_chunk_cumsum_fwd / ssd_chunk_cumsum_bwd and
+ssd_chunk_scan_fwd.
 """
 from __future__ import annotations
 
