@@ -345,21 +345,26 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 
   // registers of the next chunk's x, B, C (element tid + T * k of each tile)
   float rx[XL], rbm[BL], rcm[BL];
+  // x of step t0 + s, channel p: row (b, t0 + s, h) of x, stride H * P between steps;
+  // element k of a thread is step tid / P + (T / P) k, channel tid % P.  B and C of a
+  // chunk are one contiguous block of W * N values: element k is tid + T k.
+  const float* const xt = x + ((b * L) * H + h) * P + (int64_t)(tid / P) * H * P + tid % P;
+  const float* const bt = Bm + b * L * N + tid;
+  const float* const ct = Cm + b * L * N + tid;
+  const int64_t xstep = (int64_t)(T / P) * H * P;
   auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W;
+    const int64_t nv = c < nc ? L - t0 : 0;  // valid steps of the chunk (may exceed W)
+    const float* const xc = xt + t0 * H * P;
 #pragma unroll
-    for (int k = 0; k < XL; ++k) {
-      const int i = tid + T * k, s = i / P, p = i % P;
-      const int64_t t = t0 + s;
-      rx[k] = (c < nc && t < L) ? x[((b * L + t) * H + h) * P + p] : 0.f;
-    }
+    for (int k = 0; k < XL; ++k) rx[k] = (tid / P + (T / P) * k < nv) ? xc[k * xstep] : 0.f;
+    const float* const bc = bt + t0 * N;
+    const float* const cc = ct + t0 * N;
 #pragma unroll
     for (int k = 0; k < BL; ++k) {
-      const int i = tid + T * k, s = i / N, n = i % N;
-      const int64_t t = t0 + s;
-      const bool v = c < nc && t < L;
-      rbm[k] = v ? Bm[(b * L + t) * N + n] : 0.f;
-      rcm[k] = v ? Cm[(b * L + t) * N + n] : 0.f;
+      const bool v = (tid + T * k) / N < nv;
+      rbm[k] = v ? bc[T * k] : 0.f;
+      rcm[k] = v ? cc[T * k] : 0.f;
     }
   };
   load_chunk(0);
@@ -474,7 +479,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
         }
       }
     }
-    // ---- state: S = exp(cs_last) S + (X wd)^T B
+    // ---- state: S = exp(cs_last) S + X^T (wd B)  (the step weight scales the B operand,
+    // which all of the wave's tiles share)
     const float el = exp2_hw(cs[W - 1] * kLog2e);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) S[j] *= el;
@@ -484,9 +490,9 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
-        const float bo = Bs[k * SB + nbw * 16 + lr];
+        const float bo = Bs[k * SB + nbw * 16 + lr] * w4[m];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[k * SX + (pb0 + j) * 16 + lr] * w4[m], bo, S[j]);
+        for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[k * SX + (pb0 + j) * 16 + lr], bo, S[j]);
       }
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
