@@ -53,7 +53,7 @@ template <typename T, int K, bool SILU, int V>
 __global__ void __launch_bounds__(64 * kWaves)
 conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
                 T* __restrict__ out, int64_t L, int64_t Dm, int64_t ngroups, int64_t ntg) {
-  constexpr int TL = V == 4 ? kFwdTile / 2 : kFwdTile;
+  constexpr int TL = kFwdTile;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // block -> (b, time group, channel group), channel groups fastest
   const int64_t grp = blockIdx.x % ngroups;
@@ -69,13 +69,19 @@ conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ w, const floa
     for (int k = 0; k < K; ++k) wk[v][k] = w[(d + v) * K + k];
     bs[v] = bias ? bias[d + v] : 0.f;
   }
-  // x[t0-K+1 .. t0+TL-1], zero before t = 0 and past the end
-  float xr[TL + K - 1][V];
+  // x[t0-K+1 .. t0+TL-1], zero before t = 0 and past the end.  Four bf16 channels stay
+  // as their raw 8 bytes until used (half the registers of fp32 values), so a lane can
+  // walk as many steps as in fp32; a K-row window of converted values slides along.
+  constexpr bool RAW = V == 4;
+  float xr[RAW ? 1 : TL + K - 1][V];
+  uint2 xq[RAW ? TL + K - 1 : 1];
 #pragma unroll
   for (int i = 0; i < TL + K - 1; ++i) {
     const int64_t t = t0 - (K - 1) + i;
     const bool in = t >= 0 && t < L;
-    if constexpr (V > 1) {
+    if constexpr (RAW) {
+      xq[i] = in ? *reinterpret_cast<const uint2*>(x + (b * L + t) * Dm + d) : make_uint2(0u, 0u);
+    } else if constexpr (V > 1) {
       if (in) {
         vec_io<T, V>::ld(x, (b * L + t) * Dm + d, xr[i]);
       } else {
@@ -86,6 +92,14 @@ conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ w, const floa
       xr[i][0] = in ? io<T>::ld(x, (b * L + t) * Dm + d) : 0.f;
     }
   }
+  auto row = [&](int i, int v) __attribute__((always_inline)) -> float {
+    if constexpr (RAW) {
+      const uint32_t u = (v < 2) ? xq[i].x : xq[i].y;
+      return __uint_as_float((v & 1) ? (u & 0xffff0000u) : (u << 16));
+    } else {
+      return xr[i][v];
+    }
+  };
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
     float o[V];
@@ -93,7 +107,7 @@ conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ w, const floa
     for (int v = 0; v < V; ++v) {
       float p = bs[v];
 #pragma unroll
-      for (int k = 0; k < K; ++k) p = fmaf(wk[v][k], xr[i + k][v], p);
+      for (int k = 0; k < K; ++k) p = fmaf(wk[v][k], row(i + k, v), p);
       o[v] = SILU ? silu_f(p) : p;
     }
     if (t0 + i < L) {
@@ -230,7 +244,7 @@ conv_reduce_kernel(const float* __restrict__ pdw, const float* __restrict__ pdb,
 
 template <typename T, int K, int V>
 hipError_t fwd_kv(const ConvArgs& a, hipStream_t stream) {
-  constexpr int TL = V == 4 ? kFwdTile / 2 : kFwdTile;
+  constexpr int TL = kFwdTile;
   const int64_t ngroups = (a.dim + 64 * V - 1) / (64 * V);
   const int64_t ntg = (a.seqlen + TL * kWaves - 1) / (TL * kWaves);
   const dim3 grid((unsigned)(ngroups * ntg * a.batch));
