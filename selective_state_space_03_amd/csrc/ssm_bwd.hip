@@ -188,7 +188,7 @@ chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
   float sd = 0.f;
   const int64_t row0 = q.b * L;
   // this wave's rows of a chunk (x, delta_raw, B), loaded one chunk ahead of the prep
-  float lx[EPL], lr[EPL], lb[EPL];
+  uint32_t lx[EPL], lr[EPL], lb[EPL];  // raw element bits
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
@@ -197,9 +197,9 @@ chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
       const int t = q.wave + G * i;
       const bool v = q.dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-      lx[i] = v ? io<T>::ld(x, idx) : 0.f;
-      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
-      lb[i] = (t < tvalid && q.lane < N) ? io<T>::ld(Bm, (row0 + t0 + t) * N + q.lane) : 0.f;
+      lx[i] = v ? ld_bits<T>(x, idx) : 0u;
+      lr[i] = v ? ld_bits<T>(delta_raw, idx) : 0u;
+      lb[i] = (t < tvalid && q.lane < N) ? ld_bits<T>(Bm, (row0 + t0 + t) * N + q.lane) : 0u;
     }
   };
   auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
@@ -209,9 +209,9 @@ chunk_rel_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const float delta = v ? clamp_delta(softplus_f(lr[i] + bias), dt_lo, dt_hi) : 0.f;
-        pd[buf][t * 64 + q.lane] = make_float2(delta, delta * lx[i]);
-        if (q.lane < 16) bs[buf][t * 16 + q.lane] = lb[i];
+        const float delta = v ? clamp_delta(softplus_f(bits_f32<T>(lr[i]) + bias), dt_lo, dt_hi) : 0.f;
+        pd[buf][t * 64 + q.lane] = make_float2(delta, delta * bits_f32<T>(lx[i]));
+        if (q.lane < 16) bs[buf][t * 16 + q.lane] = bits_f32<T>(lb[i]);
       }
     }
   };
@@ -279,7 +279,7 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
   float sd = 0.f;  // sum of Delta over the segment
   const int64_t row0 = q.b * L;
   // this wave's rows of a chunk (delta_raw, dy, z, C), loaded one chunk ahead of the prep
-  float lr[EPL], ly[EPL], lz[EPL], lc[EPL];
+  uint32_t lr[EPL], ly[EPL], lz[EPL], lc[EPL];  // raw element bits
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
     const int tvalid = (int)(L - t0 < TC ? L - t0 : TC);
@@ -288,10 +288,10 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
       const int t = q.wave + G * i;
       const bool v = q.dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + q.d;
-      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
-      ly[i] = v ? io<T>::ld(dy, idx) : 0.f;
-      lz[i] = (GATED && v) ? io<T>::ld(z, idx) : 0.f;
-      lc[i] = (t < tvalid && q.lane < N) ? io<T>::ld(Cm, (row0 + t0 + t) * N + q.lane) : 0.f;
+      lr[i] = v ? ld_bits<T>(delta_raw, idx) : 0u;
+      ly[i] = v ? ld_bits<T>(dy, idx) : 0u;
+      lz[i] = (GATED && v) ? ld_bits<T>(z, idx) : 0u;
+      lc[i] = (t < tvalid && q.lane < N) ? ld_bits<T>(Cm, (row0 + t0 + t) * N + q.lane) : 0u;
     }
   };
   auto prep = [&](int64_t c, int buf) __attribute__((always_inline)) {
@@ -301,11 +301,11 @@ seg_adj_kernel(const T* __restrict__ delta_raw, const T* __restrict__ z,
       const int t = q.wave + G * i;
       if (t < TC) {
         const bool v = q.dvalid && t < tvalid;
-        const float delta = v ? clamp_delta(softplus_f(lr[i] + bias), dt_lo, dt_hi) : 0.f;
-        float g = ly[i];
-        if (GATED) g *= silu_f(lz[i]);
+        const float delta = v ? clamp_delta(softplus_f(bits_f32<T>(lr[i]) + bias), dt_lo, dt_hi) : 0.f;
+        float g = bits_f32<T>(ly[i]);
+        if (GATED) g *= silu_f(bits_f32<T>(lz[i]));
         pa[buf][t * 64 + q.lane] = make_float2(delta, g);
-        if (q.lane < 16) cs[buf][t * 16 + q.lane] = lc[i];
+        if (q.lane < 16) cs[buf][t * 16 + q.lane] = bits_f32<T>(lc[i]);
       }
     }
   };
@@ -428,8 +428,7 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
   const int64_t row0 = b * L;
   // this wave's rows of a chunk (x, delta_raw, dy, z, and B, C for lanes < d_state),
   // loaded one chunk ahead
-  float lx[EPL], lr[EPL], ly[EPL], lz[EPL];
-  float2 lbc[EPL];
+  uint32_t lx[EPL], lr[EPL], ly[EPL], lz[EPL], lbb[EPL], lcc[EPL];  // raw element bits
   float lhr[S], lcd;  // the chunk's relative start state and Delta sum up to it
   auto load = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * TC;
@@ -443,13 +442,14 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
       const int t = wave + G * i;
       const bool v = dvalid && t < tvalid;
       const int64_t idx = (row0 + t0 + t) * Dm + d;
-      lx[i] = v ? io<T>::ld(x, idx) : 0.f;
-      lr[i] = v ? io<T>::ld(delta_raw, idx) : 0.f;
-      ly[i] = v ? io<T>::ld(dy, idx) : 0.f;
-      lz[i] = (GATED && v) ? io<T>::ld(z, idx) : 0.f;
+      lx[i] = v ? ld_bits<T>(x, idx) : 0u;
+      lr[i] = v ? ld_bits<T>(delta_raw, idx) : 0u;
+      ly[i] = v ? ld_bits<T>(dy, idx) : 0u;
+      lz[i] = (GATED && v) ? ld_bits<T>(z, idx) : 0u;
       const bool ok = t < tvalid && lane < N;
       const int64_t o = (row0 + t0 + t) * N + lane;
-      lbc[i] = ok ? make_float2(io<T>::ld(Bm, o), io<T>::ld(Cm, o)) : make_float2(0.f, 0.f);
+      lbb[i] = ok ? ld_bits<T>(Bm, o) : 0u;
+      lcc[i] = ok ? ld_bits<T>(Cm, o) : 0u;
     }
   };
   load(q.c_end - 1);
@@ -463,14 +463,14 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
     for (int i = 0; i < EPL; ++i) {
       const int t = wave + G * i;
       const bool v = dvalid && t < tvalid;
-      const float xv = lx[i];
-      const float r = lr[i] + bias;
-      const float dyv = ly[i];
+      const float xv = bits_f32<T>(lx[i]);
+      const float r = bits_f32<T>(lr[i]) + bias;
+      const float dyv = bits_f32<T>(ly[i]);
       const float sp = softplus_f(r);
       const float delta = v ? clamp_delta(sp, dt_lo, dt_hi) : 0.f;
       float g = dyv, gz = 0.f;
       if (GATED) {
-        const float zv = lz[i];
+        const float zv = bits_f32<T>(lz[i]);
         const float sz = sigmoid_f(zv);
         g = dyv * zv * sz;
         gz = dyv * sz * fmaf(zv, 1.f - sz, 1.f);
@@ -479,7 +479,7 @@ bwd_main_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw,
       ex[i] = xv; edelta[i] = delta; eg[i] = g; esig[i] = sigmoid_f(r) * clamp_mask(sp, dt_lo, dt_hi); egz[i] = gz;
       if (t < TC) {
         pd[t * 64 + lane] = make_float4(delta, delta * xv, g, 0.f);
-        if (lane < 16) bcs[t * 16 + lane] = lbc[i];
+        if (lane < 16) bcs[t * 16 + lane] = make_float2(bits_f32<T>(lbb[i]), bits_f32<T>(lcc[i]));
       }
     }
     // start state of this chunk: relative state + decayed segment entry state

@@ -74,6 +74,20 @@ template <> struct io<bf16_t> {
   __device__ __forceinline__ static void st(bf16_t* __restrict__ p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Raw element bits (fp32 bits, or a bf16 value zero-extended) and their fp32 value.
+// Prefetch registers hold the raw bits and convert at the value's first use, so the
+// wait for a load is not pulled up to the conversion right after it.
+template <typename T> __device__ __forceinline__ uint32_t ld_bits(const T* __restrict__ p, int64_t i);
+template <> __device__ __forceinline__ uint32_t ld_bits<float>(const float* __restrict__ p, int64_t i) {
+  return __float_as_uint(p[i]);
+}
+template <> __device__ __forceinline__ uint32_t ld_bits<bf16_t>(const bf16_t* __restrict__ p, int64_t i) {
+  return (uint32_t)p[i];
+}
+template <typename T> __device__ __forceinline__ float bits_f32(uint32_t u);
+template <> __device__ __forceinline__ float bits_f32<float>(uint32_t u) { return __uint_as_float(u); }
+template <> __device__ __forceinline__ float bits_f32<bf16_t>(uint32_t u) { return __uint_as_float(u << 16); }
+
 // A[d,n] = -exp(A_log[d,n]) folded with log2(e), so that exp(Delta*A) = exp2(Delta*A2)
 // (mamba-rs exp_negate: out = -exp(a_log)).  Computed once per state per kernel with the
 // accurate library exp.
