@@ -139,7 +139,11 @@ def measured_traffic():
 
 
 class Timer:
-    """Per-launch HIP events on the current (launch) stream plus wall time."""
+    """HIP events on the current (launch) stream, which is the stream the library
+    launches on.  The average launch duration is one event pair around the K timed
+    launches, divided by K: the launches queue back to back, so it is the kernels'
+    time plus the gaps between them, with no event record between two launches.  The
+    minimum comes from a few more launches with a pair each, outside that region."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -149,16 +153,23 @@ class Timer:
         for i in range(warmup):
             fn(i % nsets)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        start.record()
         for i in range(steps):
+            fn(i % nsets)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        avg = start.elapsed_time(end) / steps  # ms
+        n_min = min(steps, 10)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_min)]
+        for i in range(n_min):
             evs[i][0].record()
             fn(i % nsets)
             evs[i][1].record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = [a.elapsed_time(b) for a, b in evs]  # ms
-        return wall * 1e3 / steps, sum(per) / len(per), min(per)
+        return wall * 1e3 / steps, avg, min(a.elapsed_time(b) for a, b in evs)
 
 
 def main():
