@@ -356,15 +356,25 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     const int64_t t0 = c * W;
     const int64_t nv = c < nc ? L - t0 : 0;  // valid steps of the chunk (may exceed W)
     const float* const xc = xt + t0 * H * P;
-#pragma unroll
-    for (int k = 0; k < XL; ++k) rx[k] = (tid / P + (T / P) * k < nv) ? xc[k * xstep] : 0.f;
     const float* const bc = bt + t0 * N;
     const float* const cc = ct + t0 * N;
+    if (nv >= W) {  // a whole chunk (uniform): no per-element checks
 #pragma unroll
-    for (int k = 0; k < BL; ++k) {
-      const bool v = (tid + T * k) / N < nv;
-      rbm[k] = v ? bc[T * k] : 0.f;
-      rcm[k] = v ? cc[T * k] : 0.f;
+      for (int k = 0; k < XL; ++k) rx[k] = xc[k * xstep];
+#pragma unroll
+      for (int k = 0; k < BL; ++k) {
+        rbm[k] = bc[T * k];
+        rcm[k] = cc[T * k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < XL; ++k) rx[k] = (tid / P + (T / P) * k < nv) ? xc[k * xstep] : 0.f;
+#pragma unroll
+      for (int k = 0; k < BL; ++k) {
+        const bool v = (tid + T * k) / N < nv;
+        rbm[k] = v ? bc[T * k] : 0.f;
+        rcm[k] = v ? cc[T * k] : 0.f;
+      }
     }
   };
   load_chunk(0);
@@ -467,16 +477,17 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
         for (int q = 0; q < 2; ++q) Y[q] = mfma4(a[m], Xs[k * SX + (2 * ph + q) * 16 + lr], Y[q]);
       }
     }
+    // y[b, t0 + i, h, p] for i = i0 + 4 (l / 16) + r, p = (2 ph + q) 16 + l % 16
+    float* const yrow = y + ((b * L + t0 + i0 + 4 * lq) * H + h) * P + 2 * ph * 16 + lr;
+    const int64_t ystep = (int64_t)H * P;
+    const bool whole = t0 + W <= L;  // uniform
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + 4 * lq + r;
-      const int64_t t = t0 + i;
-      if (t < L) {
+      if (whole || t0 + i < L) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int p = (2 * ph + q) * 16 + lr;
-          y[((b * L + t) * H + h) * P + p] = fmaf(Dh, Xs[i * SX + p], Y[q][r]);
-        }
+        for (int q = 0; q < 2; ++q)
+          yrow[r * ystep + q * 16] = fmaf(Dh, Xs[i * SX + (2 * ph + q) * 16 + lr], Y[q][r]);
       }
     }
     // ---- state: S = exp(cs_last) S + X^T (wd B)  (the step weight scales the B operand,
