@@ -66,7 +66,8 @@
  *   B, C                  : [batch, seqlen, d_state]
  *   D                     : [heads], may be NULL (no skip term)
  *   h0, h_final           : [batch, heads, headdim, d_state], may be NULL (zero / not written)
- * Supported: headdim 64, d_state 64 or 128, chunk 64 (SSM_ERR_UNSUPPORTED otherwise).
+ * Supported: headdim 64, d_state 64 or 128, chunk a multiple of 64 (SSM_ERR_UNSUPPORTED
+ * otherwise); a chunk is walked in blocks of 64 steps.
  * Pointers are device pointers, 4-byte aligned.  Outputs must not overlap inputs or
  * each other.  Nothing is allocated; work goes to `stream`.
  * Errors: SSM_ERR_NULL, SSM_ERR_DIM (a size < 1, 2^31 elements or more in one tensor,

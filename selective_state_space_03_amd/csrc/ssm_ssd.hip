@@ -276,12 +276,14 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
 // ---------------------------------------------------------------------------------
 // SSD scan forward over chunks, on the matrix cores.
 //
-// One workgroup (8 waves) per (batch, head) walks the chunks in order and keeps the
-// [P = 64, N] state in MFMA accumulators, as 16 x 16 tiles of v_mfma_f32_16x16x4_f32
-// (lane l, register r of a tile holds row 4 * (l / 16) + r, column l % 16; the A
-// operand of a lane is row l % 16, column l / 16 of the 16 x 4 slice, the B operand
-// row l / 16, column l % 16).  Per chunk of W = 64 steps, with x, B, C, the state and
-// the chunk's dA_cumsum / dt_out staged in LDS, wave w = (row block rb = w % 4, column
+// One workgroup (8 waves) per (batch, head) walks the sequence in blocks of W = 64
+// steps and keeps the [P = 64, N] state in MFMA accumulators, as 16 x 16 tiles of
+// v_mfma_f32_16x16x4_f32 (lane l, register r of a tile holds row 4 * (l / 16) + r,
+// column l % 16; the A operand of a lane is row l % 16, column l / 16 of the 16 x 4
+// slice, the B operand row l / 16, column l % 16).  A cumsum chunk of 64 k steps is k
+// consecutive blocks; a block's dA_cumsum is taken relative to the step before it
+// (cs below), which leaves every decay between two of its steps unchanged.  Per block,
+// with x, B, C, the state and the block's cs / dt_out staged in LDS, wave w = (row block rb = w % 4, column
 // half ph = w / 4) computes the output rows 16 rb .. 16 rb + 15, columns 32 ph ..:
 //   Y  = C S^T scaled by exp(cs_i)                              (K = N)
 //   G  = C B^T of its rows and of the step blocks s <= its rows (split between the two
@@ -293,7 +295,7 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
 // deterministic.  LDS rows are padded so that a wavefront's operand reads fall in
 // distinct banks.
 constexpr int kScanP = 64;  // headdim
-constexpr int kScanW = 64;  // chunk width
+constexpr int kScanW = 64;  // steps per block (the chunk width is a multiple of it)
 constexpr int kScanThreads = 512;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -308,7 +310,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
                           const float* __restrict__ Cm, const float* __restrict__ Dv,
                           const float* __restrict__ h0, float* __restrict__ y, float* __restrict__ h_final,
-                          int64_t L, int H, int64_t nc) {
+                          int64_t L, int H, int64_t nc, int64_t cw, int64_t nct) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 16;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
@@ -394,8 +396,12 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       Cs[(i / N) * SB + i % N] = rcm[k];
     }
     if (tid < W) {
-      const int64_t o = (bh * nc + c) * W;
-      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1], dv = dt_out[o + tid];
+      // block c is steps [c W, c W + W) of chunk c / (cw / W) of the cumsum; its
+      // exponents are taken relative to the step before the block
+      const int64_t nbc = cw / W, cc = c / nbc, o = (c - cc * nbc) * W;
+      const int64_t base_i = (bh * nct + cc) * cw + o;
+      const float base = o > 0 ? dA_cs[base_i - 1] : 0.f;
+      const float ci = dA_cs[base_i + tid] - base, cl = dA_cs[base_i + W - 1] - base, dv = dt_out[base_i + tid];
       cs[tid] = ci;
       dts[tid] = dv;
       wd[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
@@ -642,7 +648,7 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
       (double)batch * seqlen * dstate >= lim || (double)batch * heads * headdim * dstate >= lim ||
       (double)batch * heads >= lim)
     return SSM_ERR_DIM;
-  if (headdim != kScanP || chunk != kScanW || (dstate != 64 && dstate != 128)) return SSM_ERR_UNSUPPORTED;
+  if (headdim != kScanP || chunk % kScanW != 0 || (dstate != 64 && dstate != 128)) return SSM_ERR_UNSUPPORTED;
   if (!x || !dt_out || !dA_cumsum || !B || !C || !y) return SSM_ERR_NULL;
   const void* all[] = {x, dt_out, dA_cumsum, B, C, D, h0, y, h_final};
   for (const void* p : all)
@@ -657,11 +663,12 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
       if (overlaps(o, r)) return SSM_ERR_ALIAS;
   if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
   const dim3 grid((unsigned)(batch * heads));
+  const int64_t nblk = (seqlen + kScanW - 1) / kScanW;  // 64-step blocks walked by the kernel
   if (dstate == 128)
     hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, seqlen, (int)heads, nc);
+                       h0, y, h_final, seqlen, (int)heads, nblk, chunk, nc);
   else
     hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, seqlen, (int)heads, nc);
+                       h0, y, h_final, seqlen, (int)heads, nblk, chunk, nc);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -350,7 +350,7 @@ def test_ssd_chunk_scan_validation():
         return L.ssm_ssd_chunk_scan_fwd(a["x"], a["dto"], a["cs"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hf"],
                                         b, l, h, p, n, w, None)
     assert call(b=0) == DIM and call(l=0) == DIM and call(p=0) == DIM and call(w=0) == DIM
-    assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=128) == UNSUP
+    assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=96) == UNSUP and call(w=32) == UNSUP
     assert call(x=None) == NULL and call(cs=None) == NULL and call(y=None) == NULL
     assert call(y=addr(0)) == ALIAS and call(hf=addr(6)) == ALIAS and call(hf=addr(7)) == ALIAS
     assert call(y=addr(7, 2)) == ALIGN

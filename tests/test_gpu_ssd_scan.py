@@ -3,7 +3,8 @@ the matrix cores) against the fp64 oracle.
 
 y and the final state are compared element by element at max relative error (RMS
 floor) <= 1e-4, on shapes with a ragged last chunk, one full chunk, a single step,
-d_state 64 and 128, with and without the skip term and an initial state.  The scan is
+d_state 64 and 128, chunks of 64, 128 and 256 steps, with and without the skip term
+and an initial state.  The scan is
 checked both as a pipeline (the GPU chunk cumsum feeding it) and alone (fed the
 oracle's dt_out and dA_cumsum rounded to fp32).  On the full workload (8 x 2048, 64
 heads of 64, d_state 128) sampled (batch, head) sequences are compared with the oracle
@@ -60,22 +61,25 @@ def gpu_run(inp, cs=None, dto=None):
 
 
 CASES = [
-    # (batch, seqlen, heads, dstate, skip, h0)
-    (2, 150, 3, 128, True, True),    # ragged last chunk, initial state
-    (1, 64, 2, 64, False, False),    # one full chunk, no skip term
-    (2, 1, 2, 128, True, True),      # a single step
-    (1, 257, 1, 64, True, False),    # five chunks, the last of one step
+    # (batch, seqlen, heads, dstate, skip, h0, chunk)
+    (2, 150, 3, 128, True, True, 64),     # ragged last chunk, initial state
+    (1, 64, 2, 64, False, False, 64),     # one full chunk, no skip term
+    (2, 1, 2, 128, True, True, 64),       # a single step
+    (1, 257, 1, 64, True, False, 64),     # five chunks, the last of one step
+    (1, 600, 2, 128, True, True, 256),    # 256-step chunks of four blocks, ragged in a middle block
+    (2, 300, 1, 64, True, False, 128),    # 128-step chunks, the last block past the end
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_scan_matches_oracle(case):
-    b, l, h, n, skip, with_h0 = case
+    b, l, h, n, skip, with_h0, chunk = case
     w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
     inp = W.make_ssd_scan_inputs(w, batch=b, seqlen=l, heads=h, dstate=n, h0=with_h0, seed=w.seed + l + 7 * n)
+    inp["chunk"] = chunk
     if not skip:
         inp["D"] = None
-    say("ssd scan b=%d l=%d h=%d n=%d skip=%d h0=%d" % (b, l, h, n, skip, with_h0))
+    say("ssd scan b=%d l=%d h=%d n=%d skip=%d h0=%d chunk=%d" % (b, l, h, n, skip, with_h0, chunk))
     ref, rcs, rdto = oracle_run(inp)
     y, hf = gpu_run(inp)
     assert rel_err(y, ref["y"]) <= RTOL_F32
@@ -119,3 +123,6 @@ def test_unsupported_sizes_are_refused():
     ch32 = torch.zeros((1, 1, 2, 32), device=dev)           # chunk 32
     with pytest.raises(ops.SsmError):
         ops.ssd_chunk_scan_fwd(x, ch32, ch32, bc, bc)
+    ch96 = torch.zeros((1, 1, 1, 96), device=dev)           # chunk 96, not a multiple of 64
+    with pytest.raises(ops.SsmError):
+        ops.ssd_chunk_scan_fwd(x, ch96, ch96, bc, bc)
