@@ -10,9 +10,9 @@
 //
 // Work layout (our own).  dt and ddt are [batch, seqlen, heads] (head fastest) while the
 // chunk tensors are [batch, heads, chunks, chunk] (step fastest), so every workgroup
-// transposes through LDS: one workgroup per (batch, chunk, 16 heads), 4 waves, the
-// chunk walked in sub-tiles of 256 steps.  The [256 steps x 16 heads] slab of dt is
-// read in 64-byte head rows into LDS; then each wave takes 4 heads and handles one
+// transposes through LDS: one workgroup per (batch, chunk, 8 heads), 4 waves, the
+// chunk walked in sub-tiles of 256 steps.  The [256 steps x 8 heads] slab of dt is
+// read in 32-byte head rows into LDS; then each wave takes 2 heads and handles one
 // 256-step row per head with 4 consecutive steps per lane: a sequential 4-term scan in
 // the lane, a 64-lane Hillis-Steele scan of the lane totals, and the carry of the
 // previous sub-tile.  Rows of the chunk tensors move as 16-byte vectors when the chunk
@@ -24,7 +24,8 @@
 namespace ssm {
 namespace {
 
-constexpr int kHeads = 16;   // heads per workgroup
+constexpr int kHeads = 8;    // heads per workgroup
+constexpr int kHPW = kHeads / 4;  // heads per wavefront
 constexpr int kSub = 256;    // steps per sub-tile (64 lanes x 4)
 constexpr int kPad = 4;      // LDS row padding (keeps 16-byte row alignment)
 
@@ -88,7 +89,7 @@ constexpr int kStage = kSub * kHeads / 256;  // slab elements per thread
 // element i of a [256 steps x 16 heads] slab (step i / 16, head i % 16) lies inside the
 // chunk, the sequence and the head range
 __device__ __forceinline__ bool valid(int64_t t0, int n, int h0, int i, const SsdDims& m) {
-  const int r = i >> 4, h = h0 + (i & 15);
+  const int r = i / kHeads, h = h0 + i % kHeads;
   return r < n && t0 + r < m.L && h < m.H;
 }
 
@@ -96,12 +97,12 @@ __device__ __forceinline__ bool valid(int64_t t0, int n, int h0, int i, const Ss
 __device__ __forceinline__ void stage_load(const float* __restrict__ dt, const float* __restrict__ dt_bias, int64_t b,
                                            int64_t t0, int n, int h0, int tid, const SsdDims& m,
                                            float (&raw)[kStage]) {
-  const int h = h0 + (tid & 15);  // the same head for every j (256 is a multiple of 16)
+  const int h = h0 + tid % kHeads;  // the same head for every j (256 is a multiple of kHeads)
   const float bias = (dt_bias && h < m.H) ? dt_bias[h] : 0.f;
 #pragma unroll
   for (int j = 0; j < kStage; ++j) {
     const int i = tid + 256 * j;
-    raw[j] = valid(t0, n, h0, i, m) ? dt[(b * m.L + t0 + (i >> 4)) * m.H + h] : 0.f;
+    raw[j] = valid(t0, n, h0, i, m) ? dt[(b * m.L + t0 + i / kHeads) * m.H + h] : 0.f;
   }
 #pragma unroll
   for (int j = 0; j < kStage; ++j) raw[j] += bias;
@@ -116,7 +117,7 @@ ssd_cumsum_fwd_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   const int64_t b = bc / m.nc, c = bc - b * m.nc;
   const int h0 = blockIdx.y * kHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float carry[4] = {0.f, 0.f, 0.f, 0.f};
+  float carry[kHPW] = {};
   for (int64_t l0 = 0; l0 < m.W; l0 += kSub) {
     const int n = (int)(m.W - l0 < kSub ? m.W - l0 : kSub);
     // stage dt_out of [n steps x 16 heads], read in 64-byte head rows; all of a
@@ -125,13 +126,13 @@ ssd_cumsum_fwd_kernel(const float* __restrict__ dt, const float* __restrict__ A,
     stage_load(dt, dt_bias, b, c * m.W + l0, n, h0, tid, m, raw);
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
-      const int i = tid + 256 * j, r = i >> 4, hh = i & 15;
+      const int i = tid + 256 * j, r = i / kHeads, hh = i % kHeads;
       tile[hh][r] = valid(c * m.W + l0, n, h0, i, m) ? clamp_delta(g_of(raw[j], m.softplus), m.lo, m.hi) : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int hh = wave * 4 + k, h = h0 + hh;
+    for (int k = 0; k < kHPW; ++k) {
+      const int hh = wave * kHPW + k, h = h0 + hh;
       if (h >= m.H) break;  // wave-uniform
       const float a = A[h];
       const float4 q = *reinterpret_cast<const float4*>(&tile[hh][4 * lane]);
@@ -168,7 +169,7 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
   const int64_t b = bc / m.nc, c = bc - b * m.nc;
   const int h0 = blockIdx.y * kHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float carry[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+  float carry[kHPW] = {}, pa[kHPW] = {}, pb[kHPW] = {};
   const int64_t nsub = (m.W + kSub - 1) / kSub;
   for (int64_t s_i = nsub - 1; s_i >= 0; --s_i) {  // sub-tiles from the end of the chunk
     const int64_t l0 = s_i * kSub;
@@ -180,16 +181,16 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
 #pragma unroll
       for (int j = 0; j < kStage; ++j) {
         const int i = tid + 256 * j;
-        tile[i & 15][i >> 4] = raw[j];
+        tile[i % kHeads][i / kHeads] = raw[j];
       }
     }
     __syncthreads();
     // the ddA and ddt_out rows of the wave's 4 heads, all loads issued first
     const int nl = n - 4 * lane;
-    float dA4s[4][4], dO4s[4][4];
+    float dA4s[kHPW][4], dO4s[kHPW][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = h0 + wave * 4 + k;
+    for (int k = 0; k < kHPW; ++k) {
+      const int h = h0 + wave * kHPW + k;
       const int64_t row = ((b * m.H + h) * m.nc + c) * m.W + l0 + 4 * lane;
 #pragma unroll
       for (int q = 0; q < 4; ++q) dA4s[k][q] = dO4s[k][q] = 0.f;
@@ -199,8 +200,8 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int hh = wave * 4 + k, h = h0 + hh;
+    for (int k = 0; k < kHPW; ++k) {
+      const int hh = wave * kHPW + k, h = h0 + hh;
       if (h >= m.H) break;  // wave-uniform
       const float a = A[h];
       const float(&dA4)[4] = dA4s[k];
@@ -239,13 +240,14 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
       const int i = tid + 256 * j;
-      if (valid(c * m.W + l0, n, h0, i, m)) ddt[(b * m.L + c * m.W + l0 + (i >> 4)) * m.H + h0 + (i & 15)] = tile[i & 15][i >> 4];
+      if (valid(c * m.W + l0, n, h0, i, m))
+        ddt[(b * m.L + c * m.W + l0 + i / kHeads) * m.H + h0 + i % kHeads] = tile[i % kHeads][i / kHeads];
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int h = h0 + wave * 4 + k;
+  for (int k = 0; k < kHPW; ++k) {
+    const int h = h0 + wave * kHPW + k;
     if (h >= m.H) break;
     const float sa = wave_sum(pa[k]), sb = wave_sum(pb[k]);
     if (lane == 0) {
