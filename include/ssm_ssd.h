@@ -66,12 +66,36 @@
  *   B, C                  : [batch, seqlen, d_state]
  *   D                     : [heads], may be NULL (no skip term)
  *   h0, h_final           : [batch, heads, headdim, d_state], may be NULL (zero / not written)
+ *   block_states          : [batch, heads, ceil(seqlen / 64), headdim, d_state], may be NULL:
+ *                           the state entering every 64-step block (what the backward
+ *                           below reads instead of recomputing it)
  * Supported: headdim 64, d_state 64 or 128, chunk a multiple of 64 (SSM_ERR_UNSUPPORTED
  * otherwise); a chunk is walked in blocks of 64 steps.
  * Pointers are device pointers, 4-byte aligned.  Outputs must not overlap inputs or
  * each other.  Nothing is allocated; work goes to `stream`.
  * Errors: SSM_ERR_NULL, SSM_ERR_DIM (a size < 1, 2^31 elements or more in one tensor,
  * batch * heads >= 2^31), SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN, SSM_ERR_ALIAS, SSM_ERR_HIP.
+ */
+/*
+ * ssm_ssd_chunk_scan_bwd -- the gradients of ssm_ssd_chunk_scan_fwd for the loss
+ * sum(dy * y) + sum(dh_final * h_final), by the reverse recurrence of the adjoint
+ * state G = dLoss/dstate (G_{t-1} = exp(dt_t A) G_t + outer(dy_{t-1}, C_{t-1})), over
+ * the same chunks on the matrix cores.  It reads the entering state of every chunk
+ * from the forward's block_states instead of recomputing it.  Outputs:
+ *   dx                    : [batch, seqlen, heads, headdim]
+ *   ddA_cumsum, ddt_out   : [batch, heads, chunks, chunk], the gradients of dA_cumsum and
+ *                           dt_out; ssm_ssd_chunk_cumsum_bwd turns them into the
+ *                           gradients of dt, A and dt_bias
+ *   dB, dC                : [batch, seqlen, d_state], summed over heads in ascending
+ *                           head order from per-head values (one writer each, no atomics)
+ *   dD                    : [heads], summed over batch in ascending order (may be NULL)
+ *   dh0                   : [batch, heads, headdim, d_state], dLoss/dh0 (may be NULL)
+ * dh_final may be NULL (zero).  D may be NULL (no skip term; dD is then still the
+ * gradient of a skip weight).  block_states is required.  The workspace holds the
+ * per-head dB, dC and the per-(batch, head) dD: ssm_ssd_chunk_scan_bwd_workspace_bytes,
+ * 256-byte aligned, contents on entry ignored.  Supported: headdim 64, d_state 64 or
+ * 128, chunk 64 (SSM_ERR_UNSUPPORTED otherwise).  Results are bit-identical from run
+ * to run.  Errors as for the forward, plus SSM_ERR_WORKSPACE.
  */
 #ifndef SSM_SSD_H
 #define SSM_SSD_H
@@ -94,7 +118,16 @@ int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, const float
                              int dt_softplus, float dt_min, float dt_max, hipStream_t stream);
 
 int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
-                           const float* C, const float* D, const float* h0, float* y, float* h_final, int64_t batch,
+                           const float* C, const float* D, const float* h0, float* y, float* h_final,
+                           float* block_states, int64_t batch,
+                           int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t chunk,
+                           hipStream_t stream);
+
+size_t ssm_ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t dstate);
+int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
+                           const float* C, const float* D, const float* dy, const float* block_states,
+                           const float* dh_final, float* dx, float* ddA_cumsum, float* ddt_out, float* dB,
+                           float* dC, float* dD, float* dh0, void* workspace, size_t workspace_bytes, int64_t batch,
                            int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t chunk,
                            hipStream_t stream);
 

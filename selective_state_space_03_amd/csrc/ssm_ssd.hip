@@ -312,7 +312,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
                           const float* __restrict__ Cm, const float* __restrict__ Dv,
                           const float* __restrict__ h0, float* __restrict__ y, float* __restrict__ h_final,
-                          int64_t L, int H, int64_t nc, int64_t cw, int64_t nct) {
+                          float* __restrict__ block_states, int64_t L, int H, int64_t nc, int64_t cw,
+                          int64_t nct) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 16;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
@@ -411,7 +412,12 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = S[j][r];
+      for (int r = 0; r < 4; ++r) {
+        Ss[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = S[j][r];
+        // the state entering block c, [batch * heads, blocks, P, N]
+        if (block_states)
+          block_states[((bh * nc + c) * P + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
+      }
     __syncthreads();
     load_chunk(c + 1);  // in flight during the products below (zeros past the end)
 
@@ -522,6 +528,428 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         h_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
+  }
+}
+
+
+// ---------------------------------------------------------------------------------
+// SSD scan backward (64-step chunks), on the matrix cores.
+//
+// The reverse of the forward above, per (batch, head), walking the chunks from the
+// last: G = dLoss/d(state leaving the chunk) is carried in accumulators (the same
+// tile layout as the forward's state), and each chunk's entering state comes from the
+// forward's block_states.  With cs the chunk's dA_cumsum, e_i = exp(cs_i),
+// L_is = exp(cs_i - cs_s) for s <= i, w_s = exp(cs_last - cs_s) dt_s, dY the chunk's
+// dy rows and S the entering state, the chunk's products are
+//   dx_s   = w_s B_s G^T + dt_s sum_{i >= s} K_is dy_i + D dy_s,   K_is = L_is C_i.B_s
+//   dB_s   = w_s x_s G  + sum_{i >= s} V_is C_i,                   V_is = L_is dt_s dy_i.x_s
+//   dC_i   = e_i dy_i S + sum_{s <= i} V_is B_s
+//   ddt_s  = sum_i K_is Z_is + exp(cs_last - cs_s) x_s.(G B_s),     Z_is = dy_i.x_s
+//   dcs_i  = e_i dy_i.(C_i S^T) + sum_s Q_is dt_s - dt_i sum_r Q_ri - w_i x_i.(G B_i)
+//            (+ at the last step: sum_s w_s x_s.(G B_s) + e_last <G, S>),  Q = K Z
+//   G_prev = e_last G + sum_i e_i dy_i (x) C_i,    dD += sum dy x
+// dcs and ddt are the gradients of dA_cumsum and dt_out, which the chunk cumsum
+// backward turns into those of dt, A and dt_bias.  dB and dC are written per head and
+// summed over heads in ascending order by a second kernel (one writer per element, no
+// atomics); every other sum has a fixed order as well.  Wave w owns the 16 rows
+// 16 w .. 16 w + 15 of every [64 x *] product (as rows i or as rows s) and a quarter
+// of the state columns; the [64 x 64] K and V blocks pass between waves through LDS.
+template <int N>
+__global__ void __launch_bounds__(256)
+ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
+                          const float* __restrict__ dA_cs, const float* __restrict__ Bm,
+                          const float* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ dy,
+                          const float* __restrict__ bstates, const float* __restrict__ dh_final,
+                          float* __restrict__ dx, float* __restrict__ ddA, float* __restrict__ ddt,
+                          float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ dDp,
+                          float* __restrict__ dh0, int64_t L, int H, int64_t nc) {
+  constexpr int P = kScanP, W = kScanW;
+  constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
+  constexpr int SB = N + 4;
+  constexpr int SM = W + 4;
+  constexpr int NT = N / 16;   // 16-column tiles of a [*, N] product
+  constexpr int NTW = NT / 4;  // state column tiles per wave
+  __shared__ __attribute__((aligned(16))) float Xs[W * SX];
+  __shared__ __attribute__((aligned(16))) float Ys[W * SX];
+  __shared__ __attribute__((aligned(16))) float Bs[W * SB];
+  __shared__ __attribute__((aligned(16))) float Cs[W * SB];
+  __shared__ __attribute__((aligned(16))) float ST[P * SB];  // G, then the entering state
+  __shared__ __attribute__((aligned(16))) float Ms[W * SM];  // K, then V
+  __shared__ float cs[W], dts[W], ev[W], wv[W];
+  __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
+  __shared__ float rowv[W];     // e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
+  __shared__ float dwv[W];      // x_s.(G B_s)
+  __shared__ float red4[4];     // per-wave sums
+
+  const int64_t bh = blockIdx.x;  // (batch, head), head fastest
+  const int64_t b = bh / H;
+  const int h = (int)(bh - b * H);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int r0 = 16 * w;
+  const float Dh = Dv ? Dv[h] : 0.f;
+
+  // carried adjoint: rows p = pb * 16 + 4 lq + r, columns n = (w NTW + j) 16 + lr
+  f32x4 G[4][NTW];
+#pragma unroll
+  for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        G[pb][j][r] = dh_final ? dh_final[((bh * P) + pb * 16 + 4 * lq + r) * N + (w * NTW + j) * 16 + lr] : 0.f;
+  float dDacc = 0.f;
+
+  for (int64_t c = nc - 1; c >= 0; --c) {
+    const int64_t t0 = c * W;
+    // ---- stage x, dy, B, C rows, the chunk's cumsum and weights, and G
+#pragma unroll 4
+    for (int k = 0; k < W * P / 256; ++k) {
+      const int i = tid + 256 * k, sr = i / P, p = i % P;
+      const int64_t t = t0 + sr;
+      const bool v = t < L;
+      const int64_t o = ((b * L + t) * H + h) * P + p;
+      Xs[sr * SX + p] = v ? x[o] : 0.f;
+      Ys[sr * SX + p] = v ? dy[o] : 0.f;
+    }
+#pragma unroll 4
+    for (int k = 0; k < W * N / 256; ++k) {
+      const int i = tid + 256 * k, sr = i / N, n = i % N;
+      const int64_t t = t0 + sr;
+      const bool v = t < L;
+      Bs[sr * SB + n] = v ? Bm[(b * L + t) * N + n] : 0.f;
+      Cs[sr * SB + n] = v ? Cm[(b * L + t) * N + n] : 0.f;
+    }
+    if (tid < W) {
+      const int64_t o = (bh * nc + c) * W;
+      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1], dv = dt_out[o + tid];
+      cs[tid] = ci;
+      dts[tid] = dv;
+      ev[tid] = exp2_hw(ci * kLog2e);
+      wv[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
+    }
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ST[(pb * 16 + 4 * lq + r) * SB + (w * NTW + j) * 16 + lr] = G[pb][j][r];
+    __syncthreads();
+
+    // ---- with G: B G^T and X G for the rows s of this wave (K = N, then K = P)
+    f32x4 DX[4], DB[NT];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) DX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) DB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < N; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Bs[(r0 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bq = *(const f32x4*)&ST[(q * 16 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) DX[q] = mfma4(a[m], bq[m], DX[q]);
+      }
+    }
+    {
+      float dwp[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dwp[r] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dwp[r] = fmaf(DX[q][r], Xs[(r0 + 4 * lq + r) * SX + q * 16 + lr], dwp[r]);
+#pragma unroll
+        for (int msk = 1; msk < 16; msk <<= 1) dwp[r] += __shfl_xor(dwp[r], msk, 16);
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dwv[r0 + 4 * lq + r] = dwp[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ws = wv[r0 + 4 * lq + r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) DX[q][r] *= ws;
+    }
+#pragma unroll 2
+    for (int kb = 0; kb < P; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Xs[(r0 + lr) * SX + kb + 4 * lq];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) DB[j] = mfma4(a[m], ST[k * SB + j * 16 + lr], DB[j]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ws = wv[r0 + 4 * lq + r];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) DB[j][r] *= ws;
+    }
+    __syncthreads();  // ST now takes the entering state
+#pragma unroll 4
+    for (int k = 0; k < P * N / 256; ++k) {
+      const int i = tid + 256 * k, p = i / N, n = i % N;
+      ST[p * SB + n] = bstates[((bh * nc + c) * P + p) * N + n];
+    }
+    __syncthreads();
+
+    // ---- with S: <G, S>, dY S and C S^T for the rows i of this wave
+    {
+      float gs = 0.f;
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            gs = fmaf(G[pb][j][r], ST[(pb * 16 + 4 * lq + r) * SB + (w * NTW + j) * 16 + lr], gs);
+      gs = wave_sum(gs);
+      if (lane == 0) red4[w] = gs;
+    }
+    f32x4 DC[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) DC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < P; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) DC[j] = mfma4(a[m], ST[k * SB + j * 16 + lr], DC[j]);
+      }
+    }
+    float erow[4], csr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      erow[r] = ev[r0 + 4 * lq + r];
+      csr[r] = cs[r0 + 4 * lq + r];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) DC[j][r] *= erow[r];
+    }
+    float tot[4];
+    {
+      f32x4 P4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) P4[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int kb = 0; kb < N; kb += 16) {
+        const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 bq = *(const f32x4*)&ST[(q * 16 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) P4[q] = mfma4(a[m], bq[m], P4[q]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float rp = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rp = fmaf(P4[q][r], Ys[(r0 + 4 * lq + r) * SX + q * 16 + lr], rp);
+        tot[r] = erow[r] * rp;
+      }
+    }
+
+    // ---- intra-chunk: K and Z blocks of rows i (this wave) and step blocks sb <= w
+    f32x4 VV[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      VV[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sb > w) {
+        if (lq == 0) qcol[w][sb * 16 + lr] = 0.f;
+        continue;
+      }
+      f32x4 KB = {0.f, 0.f, 0.f, 0.f}, ZB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int kb = 0; kb < N; kb += 16) {
+        const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
+        const f32x4 bb = *(const f32x4*)&Bs[(sb * 16 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) KB = mfma4(a[m], bb[m], KB);
+      }
+#pragma unroll 2
+      for (int kb = 0; kb < P; kb += 16) {
+        const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq];
+        const f32x4 bx = *(const f32x4*)&Xs[(sb * 16 + lr) * SX + kb + 4 * lq];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ZB = mfma4(a[m], bx[m], ZB);
+      }
+      const int s = sb * 16 + lr;
+      const float css = cs[s], dvs = dts[s];
+      float colq = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 4 * lq + r;
+        const bool v = s <= i;
+        // select, not a product with a mask: exp of a positive exponent may be inf
+        const float Lis = v ? exp2_hw((csr[r] - css) * kLog2e) : 0.f;
+        const float Kv = KB[r] * Lis;
+        const float Qv = Kv * ZB[r];
+        tot[r] = fmaf(Qv, dvs, tot[r]);
+        colq += Qv;
+        VV[sb][r] = ZB[r] * Lis * dvs;
+        Ms[i * SM + s] = Kv;
+      }
+      colq += __shfl_xor(colq, 16, 64);
+      colq += __shfl_xor(colq, 32, 64);
+      if (lq == 0) qcol[w][s] = colq;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1) tot[r] += __shfl_xor(tot[r], msk, 16);
+    }
+    if (lr == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rowv[r0 + 4 * lq + r] = tot[r];
+    }
+    __syncthreads();  // K of every row block, qcol, rowv, dwv and <G, S> are in LDS
+
+    // ---- dx of the steps s of this wave: += dt_s sum_{i >= s} K_is dy_i
+    {
+      const float dts_l = dts[r0 + lr];
+      for (int kb = r0; kb < W; kb += 16) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int k = kb + 4 * lq + m;
+          const float a = Ms[k * SM + r0 + lr] * dts_l;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) DX[q] = mfma4(a, Ys[k * SX + q * 16 + lr], DX[q]);
+        }
+      }
+    }
+    __syncthreads();  // done with K; Ms takes V
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      if (sb > w) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ms[(r0 + 4 * lq + r) * SM + sb * 16 + lr] = VV[sb][r];
+    }
+    __syncthreads();
+    // dC of rows i += sum_{s <= i} V_is B_s;  dB of steps s += sum_{i >= s} V_is C_i
+    for (int kb = 0; kb < r0 + 16; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Ms[(r0 + lr) * SM + kb + 4 * lq];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) DC[j] = mfma4(a[m], Bs[k * SB + j * 16 + lr], DC[j]);
+      }
+    }
+    for (int kb = r0; kb < W; kb += 16) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+        const float a = Ms[k * SM + r0 + lr];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) DB[j] = mfma4(a, Cs[k * SB + j * 16 + lr], DB[j]);
+      }
+    }
+
+    // ---- outputs of the rows of this wave
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sr = r0 + 4 * lq + r;
+      const int64_t t = t0 + sr;
+      if (t < L) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = q * 16 + lr;
+          const float yv = Ys[sr * SX + p];
+          dx[((b * L + t) * H + h) * P + p] = fmaf(Dh, yv, DX[q][r]);
+          dDacc = fmaf(yv, Xs[sr * SX + p], dDacc);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          dBh[(bh * L + t) * N + j * 16 + lr] = DB[j][r];
+          dCh[(bh * L + t) * N + j * 16 + lr] = DC[j][r];
+        }
+      }
+    }
+    // gradients of dA_cumsum and dt_out, one thread per step, fixed-order sums
+    if (tid < W) {
+      const int sp = tid;
+      const float qc = ((qcol[0][sp] + qcol[1][sp]) + qcol[2][sp]) + qcol[3][sp];
+      const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dwv[sp], qc);
+      float g_cs = rowv[sp] - dts[sp] * qc - wv[sp] * dwv[sp];
+      if (sp == W - 1) {
+        float tw = 0.f;
+        for (int k = 0; k < W; ++k) tw = fmaf(wv[k], dwv[k], tw);
+        g_cs += tw + ev[W - 1] * (((red4[0] + red4[1]) + red4[2]) + red4[3]);
+      }
+      const int64_t o = (bh * nc + c) * W + sp;
+      ddA[o] = g_cs;
+      ddt[o] = g_dt;
+    }
+
+    // ---- carry: G = e_last G + sum_i e_i dy_i (x) C_i  (K = W)
+    const float el = ev[W - 1];
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) G[pb][j] *= el;
+#pragma unroll 2
+    for (int kb = 0; kb < W; kb += 16) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+        const float ek = ev[k];
+        float bo[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bo[j] = Cs[k * SB + (w * NTW + j) * 16 + lr];
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          const float a = Ys[k * SX + pb * 16 + lr] * ek;
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) G[pb][j] = mfma4(a, bo[j], G[pb][j]);
+        }
+      }
+    }
+    __syncthreads();  // the next chunk's staging overwrites every tile
+  }
+  if (dh0) {
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dh0[((bh * P) + pb * 16 + 4 * lq + r) * N + (w * NTW + j) * 16 + lr] = G[pb][j][r];
+  }
+  dDacc = wave_sum(dDacc);
+  if (lane == 0) red4[w] = dDacc;
+  __syncthreads();
+  if (tid == 0) dDp[bh] = ((red4[0] + red4[1]) + red4[2]) + red4[3];
+}
+
+// dB, dC [batch, seqlen, N]: the per-head values summed in ascending head order;
+// dD [heads]: the per-(batch, head) values summed in ascending batch order
+__global__ void __launch_bounds__(256)
+ssd_bwd_reduce_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh, const float* __restrict__ dDp,
+                      float* __restrict__ dB, float* __restrict__ dC, float* __restrict__ dD, int64_t batch,
+                      int64_t LN, int H) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < batch * LN) {
+    const int64_t b = i / LN, tn = i - b * LN;
+    float sB = 0.f, sC = 0.f;
+    for (int h = 0; h < H; ++h) {
+      const int64_t o = ((b * H + h) * LN) + tn;
+      sB += dBh[o];
+      sC += dCh[o];
+    }
+    dB[i] = sB;
+    dC[i] = sC;
+  }
+  if (dD && i < H) {
+    float sD = 0.f;
+    for (int64_t bb = 0; bb < batch; ++bb) sD += dDp[bb * H + i];
+    dD[i] = sD;
   }
 }
 
@@ -640,7 +1068,7 @@ extern "C" int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, 
 
 extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
                                       const float* C, const float* D, const float* h0, float* y, float* h_final,
-                                      int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                                      float* block_states, int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
                                       int64_t chunk, hipStream_t stream) {
   using namespace ssm;
   if (batch < 1 || seqlen < 1 || heads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return SSM_ERR_DIM;
@@ -652,25 +1080,93 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
     return SSM_ERR_DIM;
   if (headdim != kScanP || chunk % kScanW != 0 || (dstate != 64 && dstate != 128)) return SSM_ERR_UNSUPPORTED;
   if (!x || !dt_out || !dA_cumsum || !B || !C || !y) return SSM_ERR_NULL;
-  const void* all[] = {x, dt_out, dA_cumsum, B, C, D, h0, y, h_final};
+  const void* all[] = {x, dt_out, dA_cumsum, B, C, D, h0, y, h_final, block_states};
   for (const void* p : all)
     if (p && !aligned4(p)) return SSM_ERR_ALIGN;
+  const int64_t nblk = (seqlen + kScanW - 1) / kScanW;  // 64-step blocks walked by the kernel
+  if ((double)batch * heads * nblk * headdim * dstate >= lim) return SSM_ERR_DIM;
   const size_t f = 4, nx = (size_t)batch * seqlen * heads * headdim * f, nch = (size_t)batch * heads * nc * chunk * f;
   const size_t nbc = (size_t)batch * seqlen * dstate * f, nst = (size_t)batch * heads * headdim * dstate * f;
   const Rng ins[] = {span(x, nx), span(dt_out, nch), span(dA_cumsum, nch), span(B, nbc), span(C, nbc),
                      span(D, heads * f), span(h0, nst)};
-  const Rng outs[] = {span(y, nx), span(h_final, nst)};
-  for (const Rng& o : outs)
+  const Rng outs[] = {span(y, nx), span(h_final, nst), span(block_states, nst * nblk)};
+  for (int i = 0; i < 3; ++i) {
     for (const Rng& r : ins)
-      if (overlaps(o, r)) return SSM_ERR_ALIAS;
-  if (overlaps(outs[0], outs[1])) return SSM_ERR_ALIAS;
+      if (overlaps(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
   const dim3 grid((unsigned)(batch * heads));
-  const int64_t nblk = (seqlen + kScanW - 1) / kScanW;  // 64-step blocks walked by the kernel
   if (dstate == 128)
     hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, seqlen, (int)heads, nblk, chunk, nc);
+                       h0, y, h_final, block_states, seqlen, (int)heads, nblk, chunk, nc);
   else
     hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, seqlen, (int)heads, nblk, chunk, nc);
+                       h0, y, h_final, block_states, seqlen, (int)heads, nblk, chunk, nc);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+extern "C" size_t ssm_ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                                        int64_t dstate) {
+  if (batch < 1 || seqlen < 1 || heads < 1 || dstate < 1) return 0;
+  const size_t part = ((size_t)batch * heads * seqlen * dstate * 4 + 255) & ~(size_t)255;
+  return 2 * part + (((size_t)batch * heads * 4 + 255) & ~(size_t)255);
+}
+
+extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
+                                      const float* C, const float* D, const float* dy, const float* block_states,
+                                      const float* dh_final, float* dx, float* ddA_cumsum, float* ddt_out, float* dB,
+                                      float* dC, float* dD, float* dh0, void* workspace, size_t workspace_bytes,
+                                      int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                                      int64_t chunk, hipStream_t stream) {
+  using namespace ssm;
+  if (batch < 1 || seqlen < 1 || heads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return SSM_ERR_DIM;
+  const double lim = (double)((int64_t)1 << 31);
+  const int64_t nc = (seqlen + chunk - 1) / chunk;
+  if ((double)batch * seqlen * heads * headdim >= lim || (double)batch * heads * nc * chunk >= lim ||
+      (double)batch * seqlen * dstate * heads >= lim || (double)batch * heads * nc * headdim * dstate >= lim ||
+      (double)batch * heads >= lim)
+    return SSM_ERR_DIM;
+  if (headdim != kScanP || chunk != kScanW || (dstate != 64 && dstate != 128)) return SSM_ERR_UNSUPPORTED;
+  if (!x || !dt_out || !dA_cumsum || !B || !C || !dy || !block_states || !dx || !ddA_cumsum || !ddt_out || !dB ||
+      !dC)
+    return SSM_ERR_NULL;
+  const void* all[] = {x, dt_out, dA_cumsum, B, C, D, dy, block_states, dh_final, dx, ddA_cumsum, ddt_out,
+                       dB, dC, dD, dh0};
+  for (const void* p : all)
+    if (p && !aligned4(p)) return SSM_ERR_ALIGN;
+  const size_t ws_need = ssm_ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, heads, dstate);
+  if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255)) return SSM_ERR_WORKSPACE;
+  const size_t f = 4, nx = (size_t)batch * seqlen * heads * headdim * f, nch = (size_t)batch * heads * nc * chunk * f;
+  const size_t nbc = (size_t)batch * seqlen * dstate * f, nst = (size_t)batch * heads * headdim * dstate * f;
+  const Rng ins[] = {span(x, nx), span(dt_out, nch), span(dA_cumsum, nch), span(B, nbc), span(C, nbc),
+                     span(D, heads * f), span(dy, nx), span(block_states, nst * nc), span(dh_final, nst)};
+  const Rng outs[] = {span(dx, nx), span(ddA_cumsum, nch), span(ddt_out, nch), span(dB, nbc), span(dC, nbc),
+                      span(dD, heads * f), span(dh0, nst), span(workspace, ws_need)};
+  constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < NO; ++i) {
+    for (const Rng& r : ins)
+      if (overlaps(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < NO; ++j)
+      if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  const size_t part = ((size_t)batch * heads * seqlen * dstate * 4 + 255) & ~(size_t)255;
+  float* dBh = (float*)workspace;
+  float* dCh = (float*)((char*)workspace + part);
+  float* dDp = (float*)((char*)workspace + 2 * part);
+  const dim3 grid((unsigned)(batch * heads));
+  if (dstate == 128)
+    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<128>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+                       dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
+                       nc);
+  else
+    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<64>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+                       dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
+                       nc);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+  const int64_t LN = seqlen * dstate;
+  const int64_t nthr = batch * LN > heads ? batch * LN : heads;
+  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, dBh, dCh,
+                     dDp, dB, dC, dD, batch, LN, (int)heads);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -41,7 +41,7 @@ EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", 
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
            "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
            "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd",
-           "ssm_ssd_chunk_scan_fwd")
+           "ssm_ssd_chunk_scan_fwd", "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd")
 
 
 class ScanOptions(ctypes.Structure):
@@ -111,8 +111,12 @@ def lib():
         L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes.restype = SZ
         L.ssm_ssd_chunk_cumsum_bwd.argtypes = [P] * 9 + [SZ] + [I64] * 4 + [I, F, F, P]
         L.ssm_ssd_chunk_cumsum_bwd.restype = I
-        L.ssm_ssd_chunk_scan_fwd.argtypes = [P] * 9 + [I64] * 6 + [P]
+        L.ssm_ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I64] * 6 + [P]
         L.ssm_ssd_chunk_scan_fwd.restype = I
+        L.ssm_ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 4
+        L.ssm_ssd_chunk_scan_bwd_workspace_bytes.restype = SZ
+        L.ssm_ssd_chunk_scan_bwd.argtypes = [P] * 17 + [SZ] + [I64] * 6 + [P]
+        L.ssm_ssd_chunk_scan_bwd.restype = I
         _lib = L
         return L
 
@@ -451,7 +455,12 @@ def ssd_chunk_cumsum_bwd(ddA, ddt_out, dt, A, dt_bias=None, dt_softplus=True, dt
     return {"ddt": ddt, "dA": dA, "d_dt_bias": db}
 
 
-def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_final=True):
+def ssd_block_states_shape(batch, seqlen, heads, headdim, dstate):
+    """shape of the saved states: the state entering every 64-step block"""
+    return (batch, heads, (seqlen + 63) // 64, headdim, dstate)
+
+
+def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_final=True, block_states=None):
     """SSD scan forward over chunks (include/ssm_ssd.h), fed by ssd_chunk_cumsum_fwd.
 
     x [batch, seqlen, heads, headdim], dt_out and dA_cumsum [batch, heads, chunks, chunk],
@@ -475,7 +484,50 @@ def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_fi
     _req(y, "y", (b, l, h, p), f32, dev)
     hf = torch.empty((b, h, p, n), dtype=f32, device=dev) if h_final is True else h_final
     _req(hf, "h_final", (b, h, p, n), f32, dev)
+    _req(block_states, "block_states", ssd_block_states_shape(b, l, h, p, n), f32, dev)
     _check("ssm_ssd_chunk_scan_fwd", lib().ssm_ssd_chunk_scan_fwd(
-        _ptr(x), _ptr(dt_out), _ptr(dA_cumsum), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf), b, l, h, p, n,
-        chunk, _stream()))
+        _ptr(x), _ptr(dt_out), _ptr(dA_cumsum), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf),
+        _ptr(block_states), b, l, h, p, n, chunk, _stream()))
     return y, hf
+
+
+def ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, heads, dstate):
+    return int(lib().ssm_ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, heads, dstate))
+
+
+def ssd_chunk_scan_bwd(x, dt_out, dA_cumsum, B, C, dy, block_states, D=None, dh_final=None, return_dh0=False,
+                       workspace=None, out=None):
+    """Backward of ssd_chunk_scan_fwd (include/ssm_ssd.h), from the forward's block_states.
+
+    Returns {"dx", "ddA_cumsum", "ddt_out", "dB", "dC", "dD", "dh0" (or None)}; pass
+    ddA_cumsum and ddt_out to ssd_chunk_cumsum_bwd for the gradients of dt, A, dt_bias."""
+    b, l, h, p = x.shape
+    n = B.shape[-1]
+    nc, chunk = dt_out.shape[-2:]
+    dev, f32 = x.device, torch.float32
+    _req(x, "x", (b, l, h, p), f32, dev)
+    _req(dy, "dy", (b, l, h, p), f32, dev)
+    _req(dt_out, "dt_out", (b, h, nc, chunk), f32, dev)
+    _req(dA_cumsum, "dA_cumsum", (b, h, nc, chunk), f32, dev)
+    _req(B, "B", (b, l, n), f32, dev)
+    _req(C, "C", (b, l, n), f32, dev)
+    _req(D, "D", (h,), f32, dev)
+    _req(block_states, "block_states", ssd_block_states_shape(b, l, h, p, n), f32, dev)
+    _req(dh_final, "dh_final", (b, h, p, n), f32, dev)
+    o = dict(out or {})
+    o.setdefault("dx", torch.empty_like(x))
+    o.setdefault("ddA_cumsum", torch.empty_like(dA_cumsum))
+    o.setdefault("ddt_out", torch.empty_like(dt_out))
+    o.setdefault("dB", torch.empty((b, l, n), dtype=f32, device=dev))
+    o.setdefault("dC", torch.empty((b, l, n), dtype=f32, device=dev))
+    o.setdefault("dD", torch.empty((h,), dtype=f32, device=dev))
+    o.setdefault("dh0", torch.empty((b, h, p, n), dtype=f32, device=dev) if return_dh0 else None)
+    if workspace is None:
+        workspace = torch.empty((max(ssd_chunk_scan_bwd_workspace_bytes(b, l, h, n), 1),), dtype=torch.uint8,
+                                device=dev)
+    _check("ssm_ssd_chunk_scan_bwd", lib().ssm_ssd_chunk_scan_bwd(
+        _ptr(x), _ptr(dt_out), _ptr(dA_cumsum), _ptr(B), _ptr(C), _ptr(D), _ptr(dy), _ptr(block_states),
+        _ptr(dh_final), _ptr(o["dx"]), _ptr(o["ddA_cumsum"]), _ptr(o["ddt_out"]), _ptr(o["dB"]), _ptr(o["dC"]),
+        _ptr(o["dD"]), _ptr(o["dh0"]), _ptr(workspace), workspace.numel() * workspace.element_size(), b, l, h, p, n,
+        chunk, _stream()))
+    return o

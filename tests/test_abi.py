@@ -345,12 +345,36 @@ def test_ssd_chunk_scan_validation():
 
     def call(b=2, l=100, h=3, p=64, n=128, w=64, **over):
         a = dict(x=addr(0), dto=addr(1), cs=addr(2), B=addr(3), C=addr(4), D=addr(5), h0=addr(6), y=addr(7),
-                 hf=addr(8))
+                 hf=addr(8), bs=addr(9))
         a.update(over)
         return L.ssm_ssd_chunk_scan_fwd(a["x"], a["dto"], a["cs"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hf"],
-                                        b, l, h, p, n, w, None)
+                                        a["bs"], b, l, h, p, n, w, None)
     assert call(b=0) == DIM and call(l=0) == DIM and call(p=0) == DIM and call(w=0) == DIM
     assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=96) == UNSUP and call(w=32) == UNSUP
     assert call(x=None) == NULL and call(cs=None) == NULL and call(y=None) == NULL
     assert call(y=addr(0)) == ALIAS and call(hf=addr(6)) == ALIAS and call(hf=addr(7)) == ALIAS
-    assert call(y=addr(7, 2)) == ALIGN
+    assert call(y=addr(7, 2)) == ALIGN and call(bs=addr(9, 2)) == ALIGN
+    assert call(bs=addr(0)) == ALIAS and call(bs=addr(8)) == ALIAS
+
+
+@no_gpu_only
+def test_ssd_chunk_scan_bwd_validation():
+    L = ops.lib()
+
+    def call(b=2, l=100, h=3, p=64, n=128, w=64, **over):
+        a = dict(x=addr(0), dto=addr(1), cs=addr(2), B=addr(3), C=addr(4), D=addr(5), dy=addr(6), bs=addr(7),
+                 dhf=addr(8), dx=addr(9), dcs=addr(10), ddt=addr(11), dB=addr(12), dC=addr(13), dD=addr(14),
+                 dh0=addr(15), ws=addr(16))
+        a.update(over)
+        wsb = a.get("wsb", L.ssm_ssd_chunk_scan_bwd_workspace_bytes(b, l, h, n))
+        return L.ssm_ssd_chunk_scan_bwd(a["x"], a["dto"], a["cs"], a["B"], a["C"], a["D"], a["dy"], a["bs"], a["dhf"],
+                                        a["dx"], a["dcs"], a["ddt"], a["dB"], a["dC"], a["dD"], a["dh0"], a["ws"], wsb,
+                                        b, l, h, p, n, w, None)
+    assert call(b=0) == DIM and call(l=0) == DIM and call(n=0) == DIM
+    assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=128) == UNSUP
+    assert call(bs=None) == NULL and call(dy=None) == NULL and call(dB=None) == NULL and call(ddt=None) == NULL
+    assert call(dx=addr(0)) == ALIAS and call(dB=addr(13)) == ALIAS and call(ws=addr(9)) == ALIAS
+    assert call(dx=addr(9, 2)) == ALIGN
+    assert call(ws=None) == WS and call(wsb=16) == WS and call(ws=addr(16, 64)) == WS
+    # per-head dB and dC ([batch, heads, seqlen, N] fp32 each) and the per-(batch, head) dD
+    assert L.ssm_ssd_chunk_scan_bwd_workspace_bytes(2, 100, 3, 128) == 2 * 307200 + 256

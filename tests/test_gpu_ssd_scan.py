@@ -126,3 +126,80 @@ def test_unsupported_sizes_are_refused():
     ch96 = torch.zeros((1, 1, 1, 96), device=dev)           # chunk 96, not a multiple of 64
     with pytest.raises(ops.SsmError):
         ops.ssd_chunk_scan_fwd(x, ch96, ch96, bc, bc)
+
+
+# ------------------------------------------------------------------ backward
+
+def oracle_bwd(inp, dy, dhf):
+    """fp64 oracle of the whole pipeline's gradients: the sequential adjoint of the scan
+    with respect to dt_out, then through softplus to the raw dt (no clamp binds)"""
+    from oracle import ssd_cumsum_oracle as CSo
+    l, w = inp["seqlen"], inp["chunk"]
+    _, dto = CSo.chunk_cumsum_fwd(inp["dt"], inp["A"], inp["dt_bias"], w, True)
+    b, h = inp["dt"].shape[0], inp["dt"].shape[2]
+    flat = dto.transpose(0, 2, 3, 1).reshape(b, -1, h)[:, :l]
+    g = S.ssd_scan_bwd(inp["x"], flat, inp["A"], inp["B"], inp["C"], dy, inp["D"], inp["h0"], dhf)
+    raw = inp["dt"].astype(np.float64) + inp["dt_bias"].astype(np.float64)[None, None]
+    g["ddt_raw"] = g["ddt"] * CSo._g_prime(raw, True)
+    g["d_dt_bias"] = g["ddt_raw"].sum(axis=(0, 1))
+    return g
+
+
+def gpu_bwd(inp, dy, dhf):
+    from selective_state_space_03_amd import ops
+    dt, A, bias = to_dev32(inp["dt"]), to_dev32(inp["A"]), to_dev32(inp["dt_bias"])
+    cs, dto = ops.ssd_chunk_cumsum_fwd(dt, A, inp["chunk"], dt_bias=bias)
+    b, l, h, p = inp["x"].shape
+    n = inp["B"].shape[-1]
+    bs = torch.empty(ops.ssd_block_states_shape(b, l, h, p, n), dtype=torch.float32, device="cuda")
+    x, Bm, Cm, D = to_dev32(inp["x"]), to_dev32(inp["B"]), to_dev32(inp["C"]), to_dev32(inp["D"])
+    ops.ssd_chunk_scan_fwd(x, dto, cs, Bm, Cm, D=D, h0=to_dev32(inp["h0"]), block_states=bs)
+    g = ops.ssd_chunk_scan_bwd(x, dto, cs, Bm, Cm, to_dev32(dy), bs, D=D, dh_final=to_dev32(dhf), return_dh0=True)
+    gc = ops.ssd_chunk_cumsum_bwd(g["ddA_cumsum"], g["ddt_out"], dt, A, dt_bias=bias)
+    torch.cuda.synchronize()
+    out = {k: (None if v is None else host(v)) for k, v in g.items()}
+    out.update(ddt_raw=host(gc["ddt"]), dA=host(gc["dA"]), d_dt_bias=host(gc["d_dt_bias"]))
+    return out
+
+
+BWD_CASES = [
+    # (batch, seqlen, heads, dstate, skip, h0, dh_final)
+    (2, 150, 3, 128, True, True, True),    # ragged last chunk, initial state and final-state gradient
+    (1, 64, 2, 64, False, False, False),   # one full chunk, no skip term
+    (2, 1, 2, 128, True, True, False),     # a single step
+    (1, 257, 1, 64, True, False, True),    # five chunks, the last of one step
+    (2, 512, 4, 128, True, True, True),    # eight chunks
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(i) for i in range(len(BWD_CASES))])
+def test_scan_backward_matches_oracle(case):
+    b, l, h, n, skip, with_h0, with_dhf = case
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=b, seqlen=l, heads=h, dstate=n, h0=with_h0, seed=w.seed + 3 * l + n)
+    if not skip:
+        inp["D"] = None
+    rng = np.random.default_rng(w.seed + l)
+    dy = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    dhf = rng.standard_normal((b, h, 64, n)).astype(np.float32) if with_dhf else None
+    say("ssd scan bwd b=%d l=%d h=%d n=%d skip=%d h0=%d dhf=%d" % (b, l, h, n, skip, with_h0, with_dhf))
+    g = gpu_bwd(inp, dy, dhf)
+    r = oracle_bwd(inp, dy, dhf)
+    bad = {}
+    for k_gpu, k_ref in (("dx", "dx"), ("dB", "dB"), ("dC", "dC"), ("dD", "dD"), ("dh0", "dh0"),
+                         ("ddt_raw", "ddt_raw"), ("dA", "dA"), ("d_dt_bias", "d_dt_bias")):
+        e = rel_err(g[k_gpu], r[k_ref])
+        if not e <= RTOL_F32:
+            bad[k_gpu] = e
+    assert not bad, bad
+
+
+def test_scan_backward_is_bit_identical_across_runs():
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, h0=True)
+    dy = np.random.default_rng(5).standard_normal(inp["x"].shape).astype(np.float32)
+    runs = [gpu_bwd(inp, dy, None) for _ in range(3)]
+    for r in runs[1:]:
+        for k, v in r.items():
+            if v is not None:
+                assert v.tobytes() == runs[0][k].tobytes(), k
