@@ -98,6 +98,21 @@ def ssd_scan_flops(b, l, h, p, n, nc, w):
     return 2 * b * h * nc * (w * n * p + tri * n + tri * p + w * p * n)
 
 
+def ssd_scan_bwd_bytes(b, l, h, p, n, nc, w):
+    """SSD scan backward: x, dy read and dx written, B and C read once and dB, dC written,
+    dt_out and dA_cumsum read and their gradients written, the saved block states read,
+    dh0 written (fp32)"""
+    return 4 * (3 * b * l * h * p + 4 * b * l * n + 4 * b * h * nc * w + b * h * nc * p * n + b * h * p * n)
+
+
+def ssd_scan_bwd_flops(b, l, h, p, n, nc, w):
+    """useful multiply-adds of the chunked backward, x2: per (batch, head, chunk) five
+    full products of w p n (B G^T, X G, dY S, C S^T and the carry update) and the causal
+    C B^T, dY X^T, K^T dY, V B and V^T C (w (w + 1) / 2 pairs each, of length n, p, p, n, n)"""
+    tri = w * (w + 1) // 2
+    return 2 * b * h * nc * (5 * w * p * n + tri * (3 * n + 2 * p))
+
+
 def conv_bytes(b, l, d, k, es):
     """depthwise causal conv1d: x read, out written, weight and bias read"""
     return 2 * b * l * d * es + d * k * 4 + d * 4
@@ -417,6 +432,45 @@ def main():
             % (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, tfs, 100 * tfs / 157.3, nsets))
         return dict(workload=w, bytes=nb, flops=fl, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, tflops=tfs)
 
+    def ssd_scan_bwd_case(name="ssd_scan_b8_l2048_h64_p64_n128"):
+        w = W.SSD_SCAN_WORKLOADS[name]
+        inp = W.make_ssd_scan_inputs(w)
+        args = (w.batch, w.seqlen, w.heads, w.headdim, w.dstate, w.nchunks, w.chunk)
+        nb, fl = ssd_scan_bwd_bytes(*args), ssd_scan_bwd_flops(*args)
+        nsets = 2
+        A, dtb, Dv = t32(inp["A"]), t32(inp["dt_bias"]), t32(inp["D"])
+        dy = np.random.default_rng(w.seed).standard_normal(inp["x"].shape, dtype=np.float32)
+        base = {k: t32(inp[k]) for k in ("x", "B", "C")}
+        base["dy"] = t32(dy)
+        base["cs"], base["dto"] = ops.ssd_chunk_cumsum_fwd(t32(inp["dt"]), A, w.chunk, dt_bias=dtb)
+        base["bs"] = torch.empty(ops.ssd_block_states_shape(w.batch, w.seqlen, w.heads, w.headdim, w.dstate),
+                                 dtype=torch.float32, device=dev)
+        ops.ssd_chunk_scan_fwd(base["x"], base["dto"], base["cs"], base["B"], base["C"], D=Dv,
+                               block_states=base["bs"])
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        wsb = ops.ssd_chunk_scan_bwd_workspace_bytes(w.batch, w.seqlen, w.heads, w.dstate)
+        f = torch.float32
+        outs = [{"dx": torch.empty_like(base["x"]), "ddA_cumsum": torch.empty_like(base["cs"]),
+                 "ddt_out": torch.empty_like(base["dto"]),
+                 "dB": torch.empty((w.batch, w.seqlen, w.dstate), dtype=f, device=dev),
+                 "dC": torch.empty((w.batch, w.seqlen, w.dstate), dtype=f, device=dev),
+                 "dD": torch.empty((w.heads,), dtype=f, device=dev),
+                 "dh0": torch.empty((w.batch, w.heads, w.headdim, w.dstate), dtype=f, device=dev),
+                 "ws": torch.empty((wsb,), dtype=torch.uint8, device=dev)} for _ in range(nsets)]
+
+        def fn(i):
+            s, o = sets[i], outs[i]
+            ops.ssd_chunk_scan_bwd(s["x"], s["dto"], s["cs"], s["B"], s["C"], s["dy"], s["bs"], D=Dv,
+                                   return_dh0=True, workspace=o["ws"], out={k: v for k, v in o.items() if k != "ws"})
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        tfs = fl / (ev_ms * 1e-3) / 1e12
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f TFLOP/s = %.1f%% of fp32 MFMA 157.3  "
+            "workspace %.0f MB" % (name + "_bwd", ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, tfs, 100 * tfs / 157.3,
+                                   wsb / 1e6))
+        return dict(workload=w, bytes=nb, flops=fl, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs, tflops=tfs)
+
     def conv_case(name, min_bytes_rotation=1.2e9):
         w = W.CONV_WORKLOADS[name]
         inp = W.make_conv_inputs(w)
@@ -511,6 +565,7 @@ def main():
         results["ssd_cumsum_fwd_b8_l2048_h64_w256"] = ssd_case()
         results["ssd_cumsum_bwd_b8_l2048_h64_w256"] = ssd_case(bwd=True)
         results["ssd_scan_fwd_b8_l2048_h64_p64_n128"] = ssd_scan_case()
+        results["ssd_scan_bwd_b8_l2048_h64_p64_n128"] = ssd_scan_bwd_case()
     if args.only in ("all", "conv"):
         results["conv_b8_l2048_d1536_k4"] = conv_case("conv_b8_l2048_d1536_k4")
     if args.only in ("all", "conv_bf16"):

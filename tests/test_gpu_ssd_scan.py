@@ -203,3 +203,19 @@ def test_scan_backward_is_bit_identical_across_runs():
         for k, v in r.items():
             if v is not None:
                 assert v.tobytes() == runs[0][k].tobytes(), k
+
+
+def test_scan_backward_full_workload_sampled_sequences():
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_b8_l2048_h64_p64_n128"]
+    inp = W.make_ssd_scan_inputs(w)
+    dy = np.random.default_rng(w.seed).standard_normal(inp["x"].shape, dtype=np.float32)
+    say("ssd scan bwd full workload %s" % w.name)
+    g = gpu_bwd(inp, dy, None)
+    for (b, h) in ((0, 0), (6, 41)):
+        one = {"seqlen": inp["seqlen"], "chunk": inp["chunk"], "dt": inp["dt"][b:b + 1, :, h:h + 1],
+               "A": inp["A"][h:h + 1], "dt_bias": inp["dt_bias"][h:h + 1], "x": inp["x"][b:b + 1, :, h:h + 1],
+               "B": inp["B"][b:b + 1], "C": inp["C"][b:b + 1], "D": inp["D"][h:h + 1], "h0": None}
+        r = oracle_bwd(one, dy[b:b + 1, :, h:h + 1], None)
+        assert rel_err(g["dx"][b, :, h], r["dx"][0, :, 0]) <= RTOL_F32
+        assert rel_err(g["dh0"][b, h], r["dh0"][0, 0]) <= RTOL_F32
+        assert rel_err(g["ddt_raw"][b, :, h], r["ddt_raw"][0, :, 0]) <= RTOL_F32
