@@ -306,7 +306,7 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int N>
+template <int N, bool SAVE>
 __global__ void __launch_bounds__(kScanThreads)
 ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
@@ -415,7 +415,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int r = 0; r < 4; ++r) {
         Ss[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = S[j][r];
         // the state entering block c, [batch * heads, blocks, P, N]
-        if (block_states)
+        if (SAVE)
           block_states[((bh * nc + c) * P + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
       }
     __syncthreads();
@@ -1097,12 +1097,11 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
       if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
   }
   const dim3 grid((unsigned)(batch * heads));
-  if (dstate == 128)
-    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, block_states, seqlen, (int)heads, nblk, chunk, nc);
-  else
-    hipLaunchKernelGGL(ssd_chunk_scan_fwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       h0, y, h_final, block_states, seqlen, (int)heads, nblk, chunk, nc);
+  // (saving the block states is a separate instantiation: the plain forward stays as lean)
+  auto kern = dstate == 128 ? (block_states ? ssd_chunk_scan_fwd_kernel<128, true> : ssd_chunk_scan_fwd_kernel<128, false>)
+                            : (block_states ? ssd_chunk_scan_fwd_kernel<64, true> : ssd_chunk_scan_fwd_kernel<64, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D, h0, y, h_final,
+                     block_states, seqlen, (int)heads, nblk, chunk, nc);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
