@@ -551,11 +551,15 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 // dcs and ddt are the gradients of dA_cumsum and dt_out, which the chunk cumsum
 // backward turns into those of dt, A and dt_bias.  dB and dC are written per head and
 // summed over heads in ascending order by a second kernel (one writer per element, no
-// atomics); every other sum has a fixed order as well.  Wave w owns the 16 rows
-// 16 w .. 16 w + 15 of every [64 x *] product (as rows i or as rows s) and a quarter
-// of the state columns; the [64 x 64] K and V blocks pass between waves through LDS.
+// atomics); every other sum has a fixed order as well.  Eight waves: wave (rb, ph)
+// owns the 16 rows 16 rb .. of every [64 x *] product (as rows i or as steps s) and
+// half of its columns (ph), as in the forward (the two waves of a SIMD take row
+// blocks r and 3 - r); the causal K and Z blocks of a row block are split between its
+// two waves.  The [64 x 64] K and V blocks pass between waves through LDS, and the
+// row and column sums that two or four waves share go through small LDS arrays added
+// in a fixed order.
 template <int N>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kScanThreads)
 ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
                           const float* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ dy,
@@ -563,12 +567,13 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
                           float* __restrict__ dx, float* __restrict__ ddA, float* __restrict__ ddt,
                           float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ dDp,
                           float* __restrict__ dh0, int64_t L, int H, int64_t nc) {
-  constexpr int P = kScanP, W = kScanW;
+  constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
   constexpr int SM = W + 4;
   constexpr int NT = N / 16;   // 16-column tiles of a [*, N] product
-  constexpr int NTW = NT / 4;  // state column tiles per wave
+  constexpr int NH = NT / 2;   // ... per half
+  constexpr int TPW = NT / 2;  // carried-state tiles per wave (32 or 16 tiles over 8 waves)
   __shared__ __attribute__((aligned(16))) float Xs[W * SX];
   __shared__ __attribute__((aligned(16))) float Ys[W * SX];
   __shared__ __attribute__((aligned(16))) float Bs[W * SB];
@@ -577,36 +582,36 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
   __shared__ __attribute__((aligned(16))) float Ms[W * SM];  // K, then V
   __shared__ float cs[W], dts[W], ev[W], wv[W];
   __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
-  __shared__ float rowv[W];     // e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
-  __shared__ float dwv[W];      // x_s.(G B_s)
-  __shared__ float red4[4];     // per-wave sums
+  __shared__ float rowp[2][W];  // per half: e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
+  __shared__ float dwp[2][W];   // per half: x_s.(G B_s)
+  __shared__ float red8[8];     // per-wave sums
 
   const int64_t bh = blockIdx.x;  // (batch, head), head fastest
   const int64_t b = bh / H;
   const int h = (int)(bh - b * H);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int r0 = 16 * w;
+  const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
+  const int r0 = 16 * rb;
   const float Dh = Dv ? Dv[h] : 0.f;
+  // carried adjoint tiles of this wave: rows p = (pb0 + j) 16 + 4 lq + r, columns n = nbw 16 + lr
+  const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
 
-  // carried adjoint: rows p = pb * 16 + 4 lq + r, columns n = (w NTW + j) 16 + lr
-  f32x4 G[4][NTW];
+  f32x4 G[TPW];
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb)
+  for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        G[pb][j][r] = dh_final ? dh_final[((bh * P) + pb * 16 + 4 * lq + r) * N + (w * NTW + j) * 16 + lr] : 0.f;
+    for (int r = 0; r < 4; ++r)
+      G[j][r] = dh_final ? dh_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] : 0.f;
   float dDacc = 0.f;
 
   for (int64_t c = nc - 1; c >= 0; --c) {
     const int64_t t0 = c * W;
     // ---- stage x, dy, B, C rows, the chunk's cumsum and weights, and G
 #pragma unroll 4
-    for (int k = 0; k < W * P / 256; ++k) {
-      const int i = tid + 256 * k, sr = i / P, p = i % P;
+    for (int k = 0; k < W * P / T; ++k) {
+      const int i = tid + T * k, sr = i / P, p = i % P;
       const int64_t t = t0 + sr;
       const bool v = t < L;
       const int64_t o = ((b * L + t) * H + h) * P + p;
@@ -614,8 +619,8 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       Ys[sr * SX + p] = v ? dy[o] : 0.f;
     }
 #pragma unroll 4
-    for (int k = 0; k < W * N / 256; ++k) {
-      const int i = tid + 256 * k, sr = i / N, n = i % N;
+    for (int k = 0; k < W * N / T; ++k) {
+      const int i = tid + T * k, sr = i / N, n = i % N;
       const int64_t t = t0 + sr;
       const bool v = t < L;
       Bs[sr * SB + n] = v ? Bm[(b * L + t) * N + n] : 0.f;
@@ -630,49 +635,48 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       wv[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
     }
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ST[(pb * 16 + 4 * lq + r) * SB + (w * NTW + j) * 16 + lr] = G[pb][j][r];
+      for (int r = 0; r < 4; ++r) ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = G[j][r];
     __syncthreads();
 
-    // ---- with G: B G^T and X G for the rows s of this wave (K = N, then K = P)
-    f32x4 DX[4], DB[NT];
+    // ---- with G: B G^T (columns of half ph) and X G (column tiles of half ph), rows s
+    f32x4 DX[2], DB[NH];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) DX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 2; ++q) DX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NT; ++j) DB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NH; ++j) DB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int kb = 0; kb < N; kb += 16) {
       const f32x4 a = *(const f32x4*)&Bs[(r0 + lr) * SB + kb + 4 * lq];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 bq = *(const f32x4*)&ST[(q * 16 + lr) * SB + kb + 4 * lq];
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 bq = *(const f32x4*)&ST[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
 #pragma unroll
         for (int m = 0; m < 4; ++m) DX[q] = mfma4(a[m], bq[m], DX[q]);
       }
     }
     {
-      float dwp[4];
+      float dwq[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        dwp[r] = 0.f;
+        dwq[r] = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dwp[r] = fmaf(DX[q][r], Xs[(r0 + 4 * lq + r) * SX + q * 16 + lr], dwp[r]);
+        for (int q = 0; q < 2; ++q)
+          dwq[r] = fmaf(DX[q][r], Xs[(r0 + 4 * lq + r) * SX + (2 * ph + q) * 16 + lr], dwq[r]);
 #pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) dwp[r] += __shfl_xor(dwp[r], msk, 16);
+        for (int msk = 1; msk < 16; msk <<= 1) dwq[r] += __shfl_xor(dwq[r], msk, 16);
       }
       if (lr == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dwv[r0 + 4 * lq + r] = dwp[r];
+        for (int r = 0; r < 4; ++r) dwp[ph][r0 + 4 * lq + r] = dwq[r];
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float ws = wv[r0 + 4 * lq + r];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) DX[q][r] *= ws;
+      for (int q = 0; q < 2; ++q) DX[q][r] *= ws;
     }
 #pragma unroll 2
     for (int kb = 0; kb < P; kb += 16) {
@@ -681,39 +685,36 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) DB[j] = mfma4(a[m], ST[k * SB + j * 16 + lr], DB[j]);
+        for (int j = 0; j < NH; ++j) DB[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float ws = wv[r0 + 4 * lq + r];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) DB[j][r] *= ws;
+      for (int j = 0; j < NH; ++j) DB[j][r] *= ws;
     }
     __syncthreads();  // ST now takes the entering state
 #pragma unroll 4
-    for (int k = 0; k < P * N / 256; ++k) {
-      const int i = tid + 256 * k, p = i / N, n = i % N;
+    for (int k = 0; k < P * N / T; ++k) {
+      const int i = tid + T * k, p = i / N, n = i % N;
       ST[p * SB + n] = bstates[((bh * nc + c) * P + p) * N + n];
     }
     __syncthreads();
 
-    // ---- with S: <G, S>, dY S and C S^T for the rows i of this wave
+    // ---- with S: <G, S>, dY S (column tiles of half ph) and C S^T (columns of half ph)
     {
       float gs = 0.f;
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
+      for (int j = 0; j < TPW; ++j)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            gs = fmaf(G[pb][j][r], ST[(pb * 16 + 4 * lq + r) * SB + (w * NTW + j) * 16 + lr], gs);
+        for (int r = 0; r < 4; ++r) gs = fmaf(G[j][r], ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr], gs);
       gs = wave_sum(gs);
-      if (lane == 0) red4[w] = gs;
+      if (lane == 0) red8[wave] = gs;
     }
-    f32x4 DC[NT];
+    f32x4 DC[NH];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) DC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NH; ++j) DC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int kb = 0; kb < P; kb += 16) {
       const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq];
@@ -721,7 +722,7 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) DC[j] = mfma4(a[m], ST[k * SB + j * 16 + lr], DC[j]);
+        for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
       }
     }
     float erow[4], csr[4];
@@ -730,19 +731,17 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       erow[r] = ev[r0 + 4 * lq + r];
       csr[r] = cs[r0 + 4 * lq + r];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) DC[j][r] *= erow[r];
+      for (int j = 0; j < NH; ++j) DC[j][r] *= erow[r];
     }
     float tot[4];
     {
-      f32x4 P4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) P4[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 P4[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
       for (int kb = 0; kb < N; kb += 16) {
         const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 bq = *(const f32x4*)&ST[(q * 16 + lr) * SB + kb + 4 * lq];
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 bq = *(const f32x4*)&ST[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
 #pragma unroll
           for (int m = 0; m < 4; ++m) P4[q] = mfma4(a[m], bq[m], P4[q]);
         }
@@ -751,18 +750,21 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int r = 0; r < 4; ++r) {
         float rp = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rp = fmaf(P4[q][r], Ys[(r0 + 4 * lq + r) * SX + q * 16 + lr], rp);
+        for (int q = 0; q < 2; ++q)
+          rp = fmaf(P4[q][r], Ys[(r0 + 4 * lq + r) * SX + (2 * ph + q) * 16 + lr], rp);
         tot[r] = erow[r] * rp;
       }
     }
 
-    // ---- intra-chunk: K and Z blocks of rows i (this wave) and step blocks sb <= w
-    f32x4 VV[4];
+    // ---- intra-chunk: K and Z blocks of rows i (this row block) and step blocks
+    // sb = ph, ph + 2 (those <= rb); the other wave of the row block takes the rest
+    f32x4 VV[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      VV[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (sb > w) {
-        if (lq == 0) qcol[w][sb * 16 + lr] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int sb = ph + 2 * u;
+      VV[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sb > rb) {
+        if (lq == 0) qcol[rb][sb * 16 + lr] = 0.f;
         continue;
       }
       f32x4 KB = {0.f, 0.f, 0.f, 0.f}, ZB = {0.f, 0.f, 0.f, 0.f};
@@ -793,12 +795,12 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
         const float Qv = Kv * ZB[r];
         tot[r] = fmaf(Qv, dvs, tot[r]);
         colq += Qv;
-        VV[sb][r] = ZB[r] * Lis * dvs;
+        VV[u][r] = ZB[r] * Lis * dvs;
         Ms[i * SM + s] = Kv;
       }
       colq += __shfl_xor(colq, 16, 64);
       colq += __shfl_xor(colq, 32, 64);
-      if (lq == 0) qcol[w][s] = colq;
+      if (lq == 0) qcol[rb][s] = colq;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -807,11 +809,11 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
     }
     if (lr == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rowv[r0 + 4 * lq + r] = tot[r];
+      for (int r = 0; r < 4; ++r) rowp[ph][r0 + 4 * lq + r] = tot[r];
     }
-    __syncthreads();  // K of every row block, qcol, rowv, dwv and <G, S> are in LDS
+    __syncthreads();  // K of every row block, qcol, rowp, dwp and <G, S> are in LDS
 
-    // ---- dx of the steps s of this wave: += dt_s sum_{i >= s} K_is dy_i
+    // ---- dx of the steps s of this row block (columns of half ph): += dt_s sum_{i >= s} K_is dy_i
     {
       const float dts_l = dts[r0 + lr];
       for (int kb = r0; kb < W; kb += 16) {
@@ -820,16 +822,17 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
           const int k = kb + 4 * lq + m;
           const float a = Ms[k * SM + r0 + lr] * dts_l;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) DX[q] = mfma4(a, Ys[k * SX + q * 16 + lr], DX[q]);
+          for (int q = 0; q < 2; ++q) DX[q] = mfma4(a, Ys[k * SX + (2 * ph + q) * 16 + lr], DX[q]);
         }
       }
     }
     __syncthreads();  // done with K; Ms takes V
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      if (sb > w) break;
+    for (int u = 0; u < 2; ++u) {
+      const int sb = ph + 2 * u;
+      if (sb > rb) break;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ms[(r0 + 4 * lq + r) * SM + sb * 16 + lr] = VV[sb][r];
+      for (int r = 0; r < 4; ++r) Ms[(r0 + 4 * lq + r) * SM + sb * 16 + lr] = VV[u][r];
     }
     __syncthreads();
     // dC of rows i += sum_{s <= i} V_is B_s;  dB of steps s += sum_{i >= s} V_is C_i
@@ -839,7 +842,7 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) DC[j] = mfma4(a[m], Bs[k * SB + j * 16 + lr], DC[j]);
+        for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], Bs[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
       }
     }
     for (int kb = r0; kb < W; kb += 16) {
@@ -848,27 +851,27 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
         const int k = kb + 4 * lq + m;
         const float a = Ms[k * SM + r0 + lr];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) DB[j] = mfma4(a, Cs[k * SB + j * 16 + lr], DB[j]);
+        for (int j = 0; j < NH; ++j) DB[j] = mfma4(a, Cs[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
       }
     }
 
-    // ---- outputs of the rows of this wave
+    // ---- outputs of the rows and columns of this wave
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int sr = r0 + 4 * lq + r;
       const int64_t t = t0 + sr;
       if (t < L) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int p = q * 16 + lr;
+        for (int q = 0; q < 2; ++q) {
+          const int p = (2 * ph + q) * 16 + lr;
           const float yv = Ys[sr * SX + p];
           dx[((b * L + t) * H + h) * P + p] = fmaf(Dh, yv, DX[q][r]);
           dDacc = fmaf(yv, Xs[sr * SX + p], dDacc);
         }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          dBh[(bh * L + t) * N + j * 16 + lr] = DB[j][r];
-          dCh[(bh * L + t) * N + j * 16 + lr] = DC[j][r];
+        for (int j = 0; j < NH; ++j) {
+          dBh[(bh * L + t) * N + (ph * NH + j) * 16 + lr] = DB[j][r];
+          dCh[(bh * L + t) * N + (ph * NH + j) * 16 + lr] = DC[j][r];
         }
       }
     }
@@ -876,56 +879,52 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
     if (tid < W) {
       const int sp = tid;
       const float qc = ((qcol[0][sp] + qcol[1][sp]) + qcol[2][sp]) + qcol[3][sp];
-      const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dwv[sp], qc);
-      float g_cs = rowv[sp] - dts[sp] * qc - wv[sp] * dwv[sp];
+      const float dw = dwp[0][sp] + dwp[1][sp];
+      const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dw, qc);
+      float g_cs = (rowp[0][sp] + rowp[1][sp]) - dts[sp] * qc - wv[sp] * dw;
       if (sp == W - 1) {
         float tw = 0.f;
-        for (int k = 0; k < W; ++k) tw = fmaf(wv[k], dwv[k], tw);
-        g_cs += tw + ev[W - 1] * (((red4[0] + red4[1]) + red4[2]) + red4[3]);
+        for (int k = 0; k < W; ++k) tw = fmaf(wv[k], dwp[0][k] + dwp[1][k], tw);
+        float gsum = 0.f;
+        for (int k = 0; k < 8; ++k) gsum += red8[k];
+        g_cs += tw + ev[W - 1] * gsum;
       }
       const int64_t o = (bh * nc + c) * W + sp;
       ddA[o] = g_cs;
       ddt[o] = g_dt;
     }
 
-    // ---- carry: G = e_last G + sum_i e_i dy_i (x) C_i  (K = W)
+    // ---- carry: G = e_last G + sum_i dy_i (x) (e_i C_i)  (K = W; e scales the shared B operand)
     const float el = ev[W - 1];
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) G[pb][j] *= el;
+    for (int j = 0; j < TPW; ++j) G[j] *= el;
 #pragma unroll 2
     for (int kb = 0; kb < W; kb += 16) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
-        const float ek = ev[k];
-        float bo[NTW];
+        const float bo = Cs[k * SB + nbw * 16 + lr] * ev[k];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) bo[j] = Cs[k * SB + (w * NTW + j) * 16 + lr];
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-          const float a = Ys[k * SX + pb * 16 + lr] * ek;
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) G[pb][j] = mfma4(a, bo[j], G[pb][j]);
-        }
+        for (int j = 0; j < TPW; ++j) G[j] = mfma4(Ys[k * SX + (pb0 + j) * 16 + lr], bo, G[j]);
       }
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
   }
   if (dh0) {
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dh0[((bh * P) + pb * 16 + 4 * lq + r) * N + (w * NTW + j) * 16 + lr] = G[pb][j][r];
+      for (int r = 0; r < 4; ++r)
+        dh0[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = G[j][r];
   }
   dDacc = wave_sum(dDacc);
-  if (lane == 0) red4[w] = dDacc;
+  if (lane == 0) red8[wave] = dDacc;
   __syncthreads();
-  if (tid == 0) dDp[bh] = ((red4[0] + red4[1]) + red4[2]) + red4[3];
+  if (tid == 0) {
+    float sD = 0.f;
+    for (int k = 0; k < 8; ++k) sD += red8[k];
+    dDp[bh] = sD;
+  }
 }
 
 // dB, dC [batch, seqlen, N]: the per-head values summed in ascending head order;
@@ -1155,11 +1154,11 @@ extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const
   float* dDp = (float*)((char*)workspace + 2 * part);
   const dim3 grid((unsigned)(batch * heads));
   if (dstate == 128)
-    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<128>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
                        dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
                        nc);
   else
-    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<64>, grid, dim3(256), 0, stream, x, dt_out, dA_cumsum, B, C, D,
+    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
                        dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
                        nc);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
