@@ -598,6 +598,14 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
   // carried adjoint tiles of this wave: rows p = (pb0 + j) 16 + 4 lq + r, columns n = nbw 16 + lr
   const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
 
+  // per-thread bases of the staged rows: x and dy of step tid / P + (T / P) k, channel
+  // tid % P; B and C of a chunk are one contiguous block (element tid + T k); the block
+  // states of a chunk likewise
+  const int64_t xoff = ((b * L) * H + h) * P + (int64_t)(tid / P) * H * P + tid % P;
+  const int64_t xstep = (int64_t)(T / P) * H * P;
+  const float* const bt = Bm + b * L * N + tid;
+  const float* const ct = Cm + b * L * N + tid;
+
   f32x4 G[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j)
@@ -609,22 +617,26 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
   for (int64_t c = nc - 1; c >= 0; --c) {
     const int64_t t0 = c * W;
     // ---- stage x, dy, B, C rows, the chunk's cumsum and weights, and G
-#pragma unroll 4
-    for (int k = 0; k < W * P / T; ++k) {
-      const int i = tid + T * k, sr = i / P, p = i % P;
-      const int64_t t = t0 + sr;
-      const bool v = t < L;
-      const int64_t o = ((b * L + t) * H + h) * P + p;
-      Xs[sr * SX + p] = v ? x[o] : 0.f;
-      Ys[sr * SX + p] = v ? dy[o] : 0.f;
-    }
-#pragma unroll 4
-    for (int k = 0; k < W * N / T; ++k) {
-      const int i = tid + T * k, sr = i / N, n = i % N;
-      const int64_t t = t0 + sr;
-      const bool v = t < L;
-      Bs[sr * SB + n] = v ? Bm[(b * L + t) * N + n] : 0.f;
-      Cs[sr * SB + n] = v ? Cm[(b * L + t) * N + n] : 0.f;
+    const int64_t nv = L - t0;  // valid steps of the chunk (may exceed W)
+    {
+      const float* const xc = x + xoff + t0 * H * P;
+      const float* const yc = dy + xoff + t0 * H * P;
+#pragma unroll 2
+      for (int k = 0; k < W * P / T; ++k) {
+        const int sr = tid / P + (T / P) * k, p = tid % P;
+        const bool v = sr < nv;
+        Xs[sr * SX + p] = v ? xc[k * xstep] : 0.f;
+        Ys[sr * SX + p] = v ? yc[k * xstep] : 0.f;
+      }
+      const float* const bc = bt + t0 * N;
+      const float* const cc = ct + t0 * N;
+#pragma unroll 2
+      for (int k = 0; k < W * N / T; ++k) {
+        const int i = tid + T * k, sr = i / N, n = i % N;
+        const bool v = sr < nv;
+        Bs[sr * SB + n] = v ? bc[T * k] : 0.f;
+        Cs[sr * SB + n] = v ? cc[T * k] : 0.f;
+      }
     }
     if (tid < W) {
       const int64_t o = (bh * nc + c) * W;
@@ -695,10 +707,13 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int j = 0; j < NH; ++j) DB[j][r] *= ws;
     }
     __syncthreads();  // ST now takes the entering state
-#pragma unroll 4
-    for (int k = 0; k < P * N / T; ++k) {
-      const int i = tid + T * k, p = i / N, n = i % N;
-      ST[p * SB + n] = bstates[((bh * nc + c) * P + p) * N + n];
+    {
+      const float* const sc = bstates + (bh * nc + c) * P * N + tid;
+#pragma unroll 2
+      for (int k = 0; k < P * N / T; ++k) {
+        const int i = tid + T * k;
+        ST[(i / N) * SB + i % N] = sc[T * k];
+      }
     }
     __syncthreads();
 
