@@ -1,4 +1,4 @@
-"""fp64 oracle of the Mamba-2 SSD scan forward -- TEST INFRASTRUCTURE ONLY.
+"""fp64 oracle of the Mamba-2 SSD scan, forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module.  It shares no code with the HIP library.
@@ -15,7 +15,8 @@ with dt_t = dt_out[b, t, h] (the discretised, clamped step of the chunk cumsum),
 x_t = x[b, t, h, :], and B_t, C_t = B[b, t, :], C[b, t, :] shared by every head (one
 B/C group).  The readout uses the updated state, as in the Mamba selective scan.
 This is the plain definition, walked sequentially in t; the chunked form that the
-GPU computes reaches the same values up to rounding.
+GPU computes reaches the same values up to rounding.  The backward is the reverse
+(adjoint) recurrence of the same definition, pinned by central differences.
 """
 from __future__ import annotations
 
