@@ -315,7 +315,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
                           float* __restrict__ block_states, int64_t L, int H, int64_t nc, int64_t cw,
                           int64_t nct) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
-  constexpr int SX = P + 16;  // row strides (floats) of the LDS tiles
+  constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
   constexpr int SM = W + 4;
   constexpr int NT = N / 16;   // 16-column state tiles
