@@ -113,3 +113,15 @@ def test_bwd_is_bit_identical_across_runs():
     for r in runs[1:]:
         for k in GRADS:
             assert np.array_equal(r[k], runs[0][k]), k
+
+
+def test_bwd_full_size_workload_bf16():
+    """The backward workload's sizes (B=4, L=2048, d_inner=2048, N=16, gated) with bf16
+    I/O: every gradient against the oracle run on the same bf16-representable inputs."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["fwdbwd_b4_l2048_d2048"], io="bf16")
+    inp = W.make_inputs(w)
+    say("bwd full bf16 B=4 L=2048 D=2048 N=16")
+    g = gpu_bwd(inp)
+    say("bwd full bf16: oracle")
+    check(g, oracle_bwd(inp), tol("bf16"))

@@ -219,3 +219,24 @@ def test_scan_backward_full_workload_sampled_sequences():
         assert rel_err(g["dx"][b, :, h], r["dx"][0, :, 0]) <= RTOL_F32
         assert rel_err(g["dh0"][b, h], r["dh0"][0, 0]) <= RTOL_F32
         assert rel_err(g["ddt_raw"][b, :, h], r["ddt_raw"][0, :, 0]) <= RTOL_F32
+
+
+def test_scan_backward_full_length_all_heads_one_batch_element():
+    """Every output of the backward at the workload's per-sequence size (L = 2048,
+    64 heads of 64, d_state 128, one batch element), including the sums over heads
+    (dB, dC: the single-writer per-head values of deterministic_backward.py's
+    single_writer_kernels, added in a fixed head order) and over time (dD, dA,
+    d_dt_bias), against the sequential fp64 adjoint."""
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_b8_l2048_h64_p64_n128"]
+    inp = W.make_ssd_scan_inputs(w, batch=1)
+    dy = np.random.default_rng(w.seed + 11).standard_normal(inp["x"].shape, dtype=np.float32)
+    say("ssd scan bwd b=1 l=%d h=%d n=%d (all outputs)" % (inp["seqlen"], inp["heads"], inp["dstate"]))
+    g = gpu_bwd(inp, dy, None)
+    say("ssd scan bwd b=1: oracle")
+    r = oracle_bwd(inp, dy, None)
+    bad = {}
+    for k in ("dx", "dB", "dC", "dD", "dh0", "ddt_raw", "dA", "d_dt_bias"):
+        e = rel_err(g[k], r[k])
+        if not e <= RTOL_F32:
+            bad[k] = e
+    assert not bad, bad

@@ -77,16 +77,13 @@ FWD_CLAMP = [
     ("lanes_fp32", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=300, dim=130, random_h0=True), None),
     ("lanes_bf16", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=200, dim=96, random_h0=True), None),
     ("lanes_n12", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=77, dim=50, dstate=12), None),
-    ("one_state_per_wave", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=150, dim=70), "1"),
-    ("all_states_in_a_lane", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=150, dim=70), "16"),
+    ("one_state_per_wave_n8", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=150, dim=70, dstate=8), None),
     ("n4", "fwd_b8_l2048_d1536", dict(batch=2, seqlen=90, dim=40, dstate=4), None),
 ]
 
 
 @pytest.mark.parametrize("name,wl,over,layout", FWD_CLAMP, ids=[c[0] for c in FWD_CLAMP])
-def test_fwd_clamp_parity(name, wl, over, layout, monkeypatch):
-    if layout is not None:
-        monkeypatch.setenv("SSM_FWD_STATES_PER_WAVE", layout)
+def test_fwd_clamp_parity(name, wl, over, layout):
     inp = W.make_inputs(W.WORKLOADS[wl], **over)
     lo, hi = clamp_bounds(inp)
     say("fwd clamp %s [%.4g, %.4g] B=%d L=%d D=%d N=%d io=%s" % (name, lo, hi, inp["batch"], inp["seqlen"],
