@@ -63,6 +63,25 @@ int ssm_conv1d_bwd(const void* x, const float* weight, const float* bias, const 
                    int64_t seqlen, int64_t dim, int64_t width, int activation, int io_dtype,
                    hipStream_t stream);
 
+/* ssm_conv1d_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as ssm_conv1d_bwd; the weight and
+ * bias partials go to a fixed scratch array inside the library instead:
+ *   - SSM_CONV1D_SCRATCH_BYTES (16 MiB) per GPU, held by every GPU the library runs on
+ *     until the process ends.  Sizes whose ssm_conv1d_bwd_workspace_bytes() exceeds it
+ *     return SSM_ERR_SCRATCH, checked before anything is enqueued.
+ *   - The array's device address is looked up (hipGetSymbolAddress) on the first call
+ *     on each device; no call allocates, frees or calls an allocating routine.
+ *   - Every call on one GPU uses that GPU's one array, so calls that may overlap in
+ *     time on one GPU (different streams without ordering, several host threads) race
+ *     and give undefined results: order them on one stream or synchronise.  Nothing
+ *     needs to start at zero; every partial the reduction reads is written first. */
+#define SSM_CONV1D_SCRATCH_BYTES ((size_t)16 << 20)
+int ssm_conv1d_bwd_noalloc(const void* x, const float* weight, const float* bias, const void* dout,
+                           void* dx, float* dweight, float* dbias, int64_t batch, int64_t seqlen,
+                           int64_t dim, int64_t width, int activation, int io_dtype,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

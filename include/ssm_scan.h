@@ -31,7 +31,8 @@
  *   `state` of ssm_scan_step, which is read and written in place.
  *   Ownership: the caller allocates and frees every buffer, including any
  *   workspace; the library allocates no device memory and keeps no pointer
- *   after a call returns.
+ *   after a call returns.  (The one exception is the fixed scratch array of
+ *   ssm_conv1d_bwd_noalloc in ssm_conv1d.h, part of the loaded code object.)
  *   Asynchrony: work is enqueued on `stream` (NULL = the default stream) and the
  *   call returns without waiting.  Faults inside a kernel surface at the
  *   caller's next synchronisation.
@@ -64,7 +65,9 @@ typedef enum {
   SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input                         */
   SSM_ERR_HIP = 7,         /* the HIP runtime reported an error at launch         */
-  SSM_ERR_ARG = 8          /* an option value is out of range                     */
+  SSM_ERR_ARG = 8,         /* an option value is out of range                     */
+  SSM_ERR_SCRATCH = 9      /* a no-allocation entry point would need more scratch
+                              than the library's fixed array holds                */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;

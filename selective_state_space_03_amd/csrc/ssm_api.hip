@@ -65,6 +65,47 @@ bool chunk_states_fit(int64_t seqlen, int64_t d_inner, int64_t d_state) {
   return (uint64_t)state_chunks(seqlen) * (uint64_t)d_state * (uint64_t)d_inner * 4 < ((uint64_t)1 << 31);
 }
 
+// The conv1d backward with a caller workspace, or (use_scratch) with the library's
+// fixed per-device scratch, which must hold the workspace the sizes need.  Every check
+// runs before the scratch address is looked up or anything is launched.
+int conv1d_bwd_common(const void* x, const float* weight, const float* bias, const void* dout, void* dx,
+                      float* dweight, float* dbias, void* workspace, size_t workspace_bytes, bool use_scratch,
+                      int64_t batch, int64_t seqlen, int64_t dim, int64_t width, int activation, int io_dtype,
+                      hipStream_t stream) {
+  if (!x || !weight || !dout || !dx) return SSM_ERR_NULL;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!conv_dims_ok(batch, seqlen, dim, width)) return SSM_ERR_DIM;
+  if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
+  const ssm::ConvBwdLayout l = ssm::conv_bwd_layout(batch, seqlen, dim, width);
+  if (use_scratch) {
+    if (l.total > ssm::kConvScratchBytes) return SSM_ERR_SCRATCH;
+  } else {
+    if (!workspace) return SSM_ERR_WORKSPACE;
+    if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
+  }
+  const void* all[] = {x, weight, bias, dout, dx, dweight, dbias};
+  for (const void* p : all)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * seqlen * dim, W = (size_t)dim * width;
+  const Range ins[] = {rng(x, E * 4), rng(weight, W * 4), rng(bias, bias ? dim * 4 : 0), rng(dout, E * 4)};
+  const Range outs[] = {rng(dx, E * 4), rng(dweight, dweight ? W * 4 : 0), rng(dbias, dbias ? dim * 4 : 0),
+                        rng(workspace, use_scratch ? 0 : l.total)};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+  if (use_scratch && ssm::conv_scratch(&workspace) != hipSuccess) return SSM_ERR_HIP;
+  ssm::ConvArgs a{};
+  a.x = x; a.w = weight; a.bias = bias; a.dout = dout; a.dx = dx; a.dw = dweight; a.dbias = dbias;
+  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.width = (int)width;
+  a.silu = activation == SSM_ACT_SILU; a.bf16 = false;
+  return ssm::launch_conv_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +121,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported an error";
     case SSM_ERR_ARG: return "SSM_ERR_ARG: an option value is out of range";
+    case SSM_ERR_SCRATCH: return "SSM_ERR_SCRATCH: the sizes need more than the library's fixed scratch";
     default: return "unknown ssm_status";
   }
 }
@@ -330,33 +372,15 @@ int ssm_conv1d_bwd(const void* x, const float* weight, const float* bias, const 
                    float* dweight, float* dbias, void* workspace, size_t workspace_bytes, int64_t batch,
                    int64_t seqlen, int64_t dim, int64_t width, int activation, int io_dtype,
                    hipStream_t stream) {
-  if (!x || !weight || !dout || !dx) return SSM_ERR_NULL;
-  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
-  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
-  if (!conv_dims_ok(batch, seqlen, dim, width)) return SSM_ERR_DIM;
-  if (io_dtype != SSM_F32) return SSM_ERR_UNSUPPORTED;
-  if (!workspace) return SSM_ERR_WORKSPACE;
-  const ssm::ConvBwdLayout l = ssm::conv_bwd_layout(batch, seqlen, dim, width);
-  if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
-  const void* all[] = {x, weight, bias, dout, dx, dweight, dbias};
-  for (const void* p : all)
-    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
-  const size_t E = (size_t)batch * seqlen * dim, W = (size_t)dim * width;
-  const Range ins[] = {rng(x, E * 4), rng(weight, W * 4), rng(bias, bias ? dim * 4 : 0), rng(dout, E * 4)};
-  const Range outs[] = {rng(dx, E * 4), rng(dweight, dweight ? W * 4 : 0), rng(dbias, dbias ? dim * 4 : 0),
-                        rng(workspace, l.total)};
-  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
-  for (int i = 0; i < nout; ++i) {
-    for (const Range& r : ins)
-      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
-    for (int j = i + 1; j < nout; ++j)
-      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
-  }
-  ssm::ConvArgs a{};
-  a.x = x; a.w = weight; a.bias = bias; a.dout = dout; a.dx = dx; a.dw = dweight; a.dbias = dbias;
-  a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.width = (int)width;
-  a.silu = activation == SSM_ACT_SILU; a.bf16 = false;
-  return ssm::launch_conv_bwd(a, workspace, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  return conv1d_bwd_common(x, weight, bias, dout, dx, dweight, dbias, workspace, workspace_bytes, false, batch,
+                           seqlen, dim, width, activation, io_dtype, stream);
+}
+
+int ssm_conv1d_bwd_noalloc(const void* x, const float* weight, const float* bias, const void* dout, void* dx,
+                           float* dweight, float* dbias, int64_t batch, int64_t seqlen, int64_t dim,
+                           int64_t width, int activation, int io_dtype, hipStream_t stream) {
+  return conv1d_bwd_common(x, weight, bias, dout, dx, dweight, dbias, nullptr, 0, true, batch, seqlen, dim, width,
+                           activation, io_dtype, stream);
 }
 
 }  // extern "C"

@@ -14,11 +14,23 @@
 // and each lane walks a tile of TL time steps keeping the K-tap window in registers
 // (the halo of K-1 rows per tile is the only re-read).  All loads of a tile are
 // issued before any arithmetic.
+#include <atomic>
+
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+// Fixed scratch of the no-allocation backward (ssm_conv1d_bwd_noalloc): the per-(batch,
+// segment) weight and bias partials live here instead of in a caller workspace.  Every
+// GPU the library runs on holds its own copy for the life of the process.  In host code
+// the name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns, cached per device by ssm::conv_scratch() below.
+static __device__ __align__(256) unsigned char scratch[ssm::kConvScratchBytes];
+
 namespace ssm {
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
 
 constexpr int kFwdTile = 32;  // time steps per lane in the forward
 constexpr int kBwdTile = 16;  // time steps per lane in the backward
@@ -354,6 +366,24 @@ hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t s) {
 hipError_t launch_conv_step(const ConvArgs& a, hipStream_t s) {
   return a.bf16 ? step_t<bf16_t>(a, s) : step_t<float>(a, s);
 }
+// Device address of this device's scratch array: resolved with hipGetSymbolAddress
+// (current device) on the first call on each device, then reused.
+hipError_t conv_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // same value from any racing thread
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 hipError_t launch_conv_bwd(const ConvArgs& a, void* ws, hipStream_t s) {
   switch (a.width) {
     case 1: return bwd_k<1>(a, ws, s);

@@ -109,6 +109,10 @@ ConvBwdLayout conv_bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_
 hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_conv_step(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_conv_bwd(const ConvArgs& a, void* workspace, hipStream_t stream);
+// the no-allocation backward's fixed scratch: its size, and its device address on the
+// current device (resolved once per device)
+constexpr size_t kConvScratchBytes = (size_t)16 << 20;
+hipError_t conv_scratch(void** out);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);

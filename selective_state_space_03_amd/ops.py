@@ -35,11 +35,11 @@ LIB_PATH = os.path.join(HERE, "lib", "libssmscan.so")
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_DIM", 3: "SSM_ERR_UNSUPPORTED",
           4: "SSM_ERR_ALIGN", 5: "SSM_ERR_WORKSPACE", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_HIP",
-          8: "SSM_ERR_ARG"}
+          8: "SSM_ERR_ARG", 9: "SSM_ERR_SCRATCH"}
 EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_step",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_fwd_ex", "ssm_scan_step_ex",
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
-           "ssm_conv1d_bwd", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
+           "ssm_conv1d_bwd", "ssm_conv1d_bwd_noalloc", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
            "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd",
            "ssm_ssd_chunk_scan_fwd", "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd")
 
@@ -100,6 +100,8 @@ def lib():
         L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
         L.ssm_conv1d_bwd.argtypes = [P] * 7 + [P, SZ] + [I64] * 4 + [I, I, P]
         L.ssm_conv1d_bwd.restype = I
+        L.ssm_conv1d_bwd_noalloc.argtypes = [P] * 7 + [I64] * 4 + [I, I, P]
+        L.ssm_conv1d_bwd_noalloc.restype = I
         F = ctypes.c_float
         L.ssm_mamba3_preprocess_bwd_workspace_bytes.argtypes = [I64, I64]
         L.ssm_mamba3_preprocess_bwd_workspace_bytes.restype = SZ
@@ -346,6 +348,35 @@ def conv1d_bwd(x, weight, dout, bias=None, silu=True, workspace=None, dx=None, d
     _check("ssm_conv1d_bwd", lib().ssm_conv1d_bwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(dout), _ptr(dx),
                                                   _ptr(dweight), _ptr(dbias), _ptr(workspace), ws_bytes, b, l, d,
                                                   k, SSM_ACT_SILU if silu else SSM_ACT_NONE, SSM_F32, _stream()))
+    return {"dx": dx, "dweight": dweight, "dbias": dbias}
+
+
+CONV1D_SCRATCH_BYTES = 16 << 20  # SSM_CONV1D_SCRATCH_BYTES of include/ssm_conv1d.h
+
+
+def conv1d_bwd_noalloc(x, weight, dout, bias=None, silu=True, dx=None, dweight=None, dbias=None,
+                       want_params=True):
+    """conv1d_bwd through ssm_conv1d_bwd_noalloc: no workspace; the library's fixed
+    per-GPU scratch holds the partials (sizes that need more raise SSM_ERR_SCRATCH).
+    Outputs are allocated here unless passed in."""
+    b, l, d = x.shape
+    k = weight.shape[1]
+    dev = x.device
+    f = torch.float32
+    _req(x, "x", (b, l, d), f, dev)
+    _req(weight, "weight", (d, k), f, dev)
+    _req(bias, "bias", (d,), f, dev)
+    _req(dout, "dout", (b, l, d), f, dev)
+    if dx is None:
+        dx = torch.empty((b, l, d), dtype=f, device=dev)
+    if want_params and dweight is None:
+        dweight = torch.empty((d, k), dtype=f, device=dev)
+    if want_params and dbias is None:
+        dbias = torch.empty((d,), dtype=f, device=dev)
+    _check("ssm_conv1d_bwd_noalloc",
+           lib().ssm_conv1d_bwd_noalloc(_ptr(x), _ptr(weight), _ptr(bias), _ptr(dout), _ptr(dx), _ptr(dweight),
+                                        _ptr(dbias), b, l, d, k, SSM_ACT_SILU if silu else SSM_ACT_NONE, SSM_F32,
+                                        _stream()))
     return {"dx": dx, "dweight": dweight, "dbias": dbias}
 
 

@@ -202,6 +202,27 @@ def test_conv_step_and_bwd_validation():
                             0, None) == ALIAS
 
 
+@no_gpu_only
+def test_conv_bwd_noalloc_validation():
+    """The no-allocation backward checks like ssm_conv1d_bwd, and refuses sizes whose
+    workspace exceeds its fixed scratch with SSM_ERR_SCRATCH, before any HIP call."""
+    L = ops.lib()
+    SCRATCH = 9
+    assert L.ssm_conv1d_bwd_noalloc(None, addr(5), None, addr(1), addr(9), None, None, 2, 64, 32, 4, 1, 0,
+                                    None) == NULL
+    assert L.ssm_conv1d_bwd_noalloc(addr(0), addr(5), None, addr(1), addr(9), None, None, 2, 64, 32, 4, 1, 1,
+                                    None) == UNSUP
+    assert L.ssm_conv1d_bwd_noalloc(addr(0), addr(5), None, addr(1), addr(0), None, None, 2, 64, 32, 4, 1, 0,
+                                    None) == ALIAS
+    # many short sequences: one partial per batch element, 128 MB of partials
+    big = (100000, 16, 64, 4)
+    assert L.ssm_conv1d_bwd_workspace_bytes(*big, 0) > ops.CONV1D_SCRATCH_BYTES
+    assert L.ssm_conv1d_bwd_noalloc(addr(0), addr(5), None, addr(1), addr(9), None, None, *big, 1, 0,
+                                    None) == SCRATCH
+    # the benchmark's conv shape fits
+    assert L.ssm_conv1d_bwd_workspace_bytes(8, 2048, 1536, 4, 0) <= ops.CONV1D_SCRATCH_BYTES
+
+
 # ------------------------------------------------ options of the _ex entry points
 
 def _opts(dt_min=0.0, dt_max=0.0, dh_final=None, dh0=None):
