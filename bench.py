@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|step|fwd5|bwd|bwd_bf16|train|mamba3|ssd|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|long|step|fwd5|bwd|bwd_bf16|train|mamba3|ssd|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -193,7 +193,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "bf16", "step", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                    choices=["all", "fwd", "bf16", "long", "step", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
                              "ssd", "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -254,11 +254,14 @@ def main():
         hfs = [torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in range(nsets)]
         css = [torch.empty(ops.chunk_states_shape(w.batch, w.seqlen, w.dim, w.dstate), dtype=torch.float32,
                            device=dev) if save else None for _ in range(nsets)]
+        # the time-split path (long sequences of few channels) takes a workspace
+        wsb = ops.fwd_workspace_bytes(w.batch, w.seqlen, w.dim, w.dstate, ops.SSM_BF16 if io == "bf16" else ops.SSM_F32)
+        wss = [torch.empty((wsb,), dtype=torch.uint8, device=dev) if wsb else None for _ in range(nsets)]
 
         def fn(i):
             s = sets[i]
             ops.ssm_scan_fwd(s["x"], s["dr"], s["B"], s["C"], A_log, D_skip=Dsk, dt_bias=dtb, z=s["z"],
-                             y=ys[i], h_final=hfs[i], chunk_states=css[i])
+                             y=ys[i], h_final=hfs[i], chunk_states=css[i], workspace=wss[i])
 
         wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
         gbs = nb / (ev_ms * 1e-3) / 1e9
@@ -549,6 +552,8 @@ def main():
         results["fwd_bf16_b4_l4096_d4096"] = fwd_case("fwd_bf16_b4_l4096_d4096")
     if args.only in ("all", "fwd5"):
         results["fwd_b4_l2048_d2048"] = fwd_case("fwdbwd_b4_l2048_d2048")
+    if args.only in ("all", "long"):
+        results["fwd_long_b1_l65536_d1536"] = fwd_case("fwd_long_b1_l65536_d1536")
     if args.only in ("all", "step"):
         results["step_b256_d5120"] = step_case()
     if args.only in ("all", "bwd"):

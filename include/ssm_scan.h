@@ -82,10 +82,15 @@ const char* ssm_status_string(int status);
  *            h0 (fp32) optional: NULL means a zero initial state.
  *   Outputs: y (io_dtype) required; h_final (fp32) optional (NULL: not written),
  *            the state after the last step.
- *   workspace: optional scratch for the time-split path that long sequences of
- *            few channels use; ssm_scan_fwd_workspace_bytes() gives the size that
- *            enables it (0 when it is never used).  NULL or a smaller buffer is
- *            not an error: the scan then runs unsplit.
+ *   workspace: scratch of the time-split path (mamba-rs kernels.rs, MambaKernels
+ *            ssm_parallel_fwd: the parallel-prefix forward of long sequences).  When
+ *            batch * ceil(d_inner / 4) is below 1024 and seqlen is at least 1024, the
+ *            sequence is cut into segments scanned in parallel and joined by a scan of
+ *            their (decay, increment) pairs; ssm_scan_fwd_workspace_bytes() gives the bytes
+ *            that path needs, 0 for sizes that run unsplit.  The choice depends on the
+ *            sizes alone; when the size is > 0 the workspace is required (256-byte
+ *            aligned, not overlapping any argument; SSM_ERR_WORKSPACE otherwise), and
+ *            it is ignored when the size is 0.  Contents on entry are ignored.
  *   io_dtype: SSM_F32 or SSM_BF16.
  *   Limits: one batch element's slice, seqlen * max(d_inner, d_state) elements of
  *   io_dtype, must be below 2^31 bytes (SSM_ERR_UNSUPPORTED otherwise); d_inner

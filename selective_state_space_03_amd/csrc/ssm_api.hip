@@ -133,8 +133,10 @@ size_t ssm_scan_chunk_states_bytes(int64_t batch, int64_t seqlen, int64_t d_inne
 
 size_t ssm_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                                     int io_dtype) {
-  (void)batch; (void)seqlen; (void)d_inner; (void)d_state; (void)io_dtype;
-  return 0;  // this build always runs the scan unsplit
+  (void)io_dtype;
+  if (!dims_ok(batch, seqlen, d_inner, d_state)) return 0;
+  const ssm::FwdSplit sp = ssm::fwd_split(batch, seqlen, d_inner, (int)d_state);
+  return sp.nseg > 1 ? sp.total : 0;
 }
 
 int ssm_scan_fwd(const void* x, const void* delta_raw, const void* z, const void* B, const void* C,
@@ -150,7 +152,6 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
                     float* h_final, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                     int io_dtype, void* workspace, size_t workspace_bytes, const ssm_scan_options* options,
                     hipStream_t stream) {
-  (void)workspace; (void)workspace_bytes;
   if (!x || !delta_raw || !B || !C || !A_log || !y) return SSM_ERR_NULL;
   float dt_lo, dt_hi;
   if (!options_ok(options, false, &dt_lo, &dt_hi)) return SSM_ERR_ARG;
@@ -174,6 +175,11 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
   for (const void* p : f_in)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   if (!aligned(y, es)) return SSM_ERR_ALIGN;
+  // the time-split path (long sequences of few channels) needs the workspace; whether
+  // it is taken depends on the sizes alone
+  const ssm::FwdSplit sp = ssm::fwd_split(batch, seqlen, d_inner, (int)d_state);
+  const size_t ws_used = sp.nseg > 1 ? sp.total : 0;
+  if (ws_used && (!workspace || workspace_bytes < ws_used || !aligned(workspace, 256))) return SSM_ERR_WORKSPACE;
   const size_t E = (size_t)batch * seqlen * d_inner, S = (size_t)batch * seqlen * d_state;
   const size_t H = (size_t)batch * d_inner * d_state;
   const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
@@ -181,7 +187,8 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
                        rng(D_skip, D_skip ? d_inner * 4 : 0), rng(dt_bias, dt_bias ? d_inner * 4 : 0),
                        rng(h0, h0 ? H * 4 : 0)};
   const Range outs[] = {rng(y, E * es), rng(h_final, h_final ? H * 4 : 0),
-                        rng(chunk_states, chunk_states ? ssm_scan_chunk_states_bytes(batch, seqlen, d_inner, d_state) : 0)};
+                        rng(chunk_states, chunk_states ? ssm_scan_chunk_states_bytes(batch, seqlen, d_inner, d_state) : 0),
+                        rng(workspace, ws_used)};
   const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
   for (int i = 0; i < nout; ++i) {
     for (const Range& r : ins)
@@ -196,6 +203,7 @@ int ssm_scan_fwd_ex(const void* x, const void* delta_raw, const void* z, const v
   a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = (int)d_state;
   a.bf16 = io_dtype == SSM_BF16;
   a.dt_lo = dt_lo; a.dt_hi = dt_hi; a.chunk_states = chunk_states;
+  a.workspace = ws_used ? workspace : nullptr;
   return ssm::launch_fwd(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -637,6 +637,340 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Time-split forward for long sequences of few channels (mamba-rs kernels.rs,
+// MambaKernels ssm_parallel_fwd / ssm_parallel_fwd_nosave: a parallel-prefix scan
+// forward for long sequences).  When batch x channels alone cannot fill the chip, the
+// sequence is cut into S segments of SEG steps (a multiple of 16) and three launches
+// follow:
+//  1. fwd_seg_kernel<.., OUT = false>: every segment but the last, from a zero state:
+//     its end state E_j[n] (the increment) and its step sum, whose decay over the
+//     segment is exp2(A2[n] * sum Delta);
+//  2. fwd_seg_carry_kernel: per (batch, state, channel), the (decay, increment) pairs
+//     of the segments are combined by an inclusive wavefront-64 scan with DPP (lane =
+//     segment), blocks of 64 segments chained through a carry in LDS; it writes the
+//     state entering every segment (h0 for the first);
+//  3. fwd_seg_kernel<.., OUT = true>: every segment again from its entering state, with
+//     the readout, the gate, the stores of y (and of the saved chunk states, h_final).
+// Layout of the segment kernels: lane = channel, and all 16 states of a channel in
+// VGPRs of one lane, so Delta and Delta*x need no exchange and the readout sum over
+// states stays in the lane (the states-across-lanes kernel needs both exchanges, but
+// has 16 times the wavefronts).  B and C of a time tile are staged in LDS by the
+// workgroup and read with same-address 16-byte reads.  Segments give the wavefronts.
+constexpr int kSegTT = 4;     // steps per tile of the segment kernels
+constexpr int kSegWaves = 4;  // waves per workgroup (256 channels)
+
+// inclusive scan over the 64 lanes (lane order = segment order) of the pairs
+// (a, b) -> state a * h + b, under composition: the earlier pair (a1, b1) followed by
+// the later (a2, b2) is (a1 a2, a2 b1 + b2).  Hillis-Steele with DPP: shifts 1, 2, 4,
+// 8 inside each row, then the last lane of row 0 (2) into row 1 (3), then lane 31 into
+// rows 2 and 3.  Lanes without a source take the identity (1, 0).
+__device__ __forceinline__ void scan64_pairs(float& a, float& b) {
+#define SSM_SCAN_STEP(CTRL, ROWS)                                                    \
+  {                                                                                  \
+    const float ap = __builtin_amdgcn_update_dpp(1.0f, a, CTRL, ROWS, 0xf, false);    \
+    const float bp = __builtin_amdgcn_update_dpp(0.0f, b, CTRL, ROWS, 0xf, false);    \
+    b = fmaf(a, bp, b);                                                              \
+    a = ap * a;                                                                      \
+  }
+  SSM_SCAN_STEP(0x111, 0xf)  // row_shr:1
+  SSM_SCAN_STEP(0x112, 0xf)  // row_shr:2
+  SSM_SCAN_STEP(0x114, 0xf)  // row_shr:4
+  SSM_SCAN_STEP(0x118, 0xf)  // row_shr:8
+  SSM_SCAN_STEP(0x142, 0xa)  // row_bcast:15 into rows 1 and 3
+  SSM_SCAN_STEP(0x143, 0xc)  // row_bcast:31 into rows 2 and 3
+#undef SSM_SCAN_STEP
+}
+
+template <typename T, bool GATED, bool OUT, bool SAVE, bool CLAMP>
+__global__ void __launch_bounds__(64 * kSegWaves)
+fwd_seg_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
+               const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
+               const float* __restrict__ D_skip, const float* __restrict__ dt_bias, float* __restrict__ carry,
+               float* __restrict__ sumd, T* __restrict__ y, float* __restrict__ h_final,
+               float* __restrict__ chunk_states, int L, int Dm, int N, int S, int nseg_grid, int seglen,
+               int ngroups, int nblocks, float dt_lo, float dt_hi) {
+  constexpr int TT = kSegTT;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int R = 4;               // activation ring: tile k + 3 is loaded while tile k is scanned
+  constexpr int U = 4;               // loop unroll: ring slots and LDS buffers are constants
+  constexpr int NBC = OUT ? 32 : 16;  // B, and C for the readout, per step
+  constexpr int PER = TT * NBC / 64;  // B/C elements each lane stages per tile
+  static_assert(PER >= 1 && TT * NBC % 64 == 0, "whole B/C elements per lane");
+  // Each wave stages the B (0..15) and C (16..31) of every step of a tile in its own
+  // LDS buffer (tile k in k & 1) and reads them with same-address reads: nothing is
+  // shared between waves, so the loop has no barrier (a wave's LDS accesses complete
+  // in program order).
+  __shared__ __attribute__((aligned(16))) float bc[kSegWaves][2][TT][NBC];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the channel groups of one (batch, segment) read the same B/C rows: blocks are
+  // dispatched to the 8 XCDs round robin, so give the blocks of one XCD consecutive ids
+  const int xcd = blockIdx.x & 7, per = nblocks >> 3, rem = nblocks & 7;
+  const int lb = xcd * per + (xcd < rem ? xcd : rem) + (int)(blockIdx.x >> 3);
+  const int g = lb % ngroups;
+  const int rr = lb / ngroups;
+  const int j = rr % nseg_grid;
+  const int b = rr / nseg_grid;
+  const int d = g * 64 * kSegWaves + wave * 64 + lane;
+  const bool dvalid = d < Dm;
+  const int t0 = j * seglen;
+  const int t1 = (L - t0 < seglen) ? L : t0 + seglen;
+  const int nfull = (t1 - t0) / TT;  // whole tiles; a shorter last tile only ends the sequence
+
+  float A2[16], h[16];
+  const int64_t cbase = ((int64_t)b * S + j) * N * Dm + d;  // carry[b][j][n][d] at n = 0
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const bool nv = dvalid && n < N;
+    A2[n] = nv ? a2_from_alog(A_log[(int64_t)d * N + n]) : 0.f;
+    h[n] = (OUT && nv) ? carry[cbase + (int64_t)n * Dm] : 0.f;
+  }
+  const float bias = (dvalid && dt_bias) ? dt_bias[d] : 0.f;
+  const float dsk = (dvalid && D_skip) ? D_skip[d] : 0.f;
+
+  const int64_t row0 = (int64_t)b * L;
+  const int64_t slice = (int64_t)L * Dm * ES;
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rr_ = tile_rsrc(delta_raw + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t rz = tile_rsrc(GATED ? z + row0 * Dm : x + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t ry = tile_rsrc(OUT ? (const void*)(y + row0 * Dm) : (const void*)x, OUT ? slice : 0);
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(Bm + row0 * N, (int64_t)L * N * ES);
+  const __amdgpu_buffer_rsrc_t rc = tile_rsrc(Cm + row0 * N, (int64_t)L * N * ES);
+  const uint32_t dl_off = dvalid ? (uint32_t)(d * ES) : kOutside;  // lane offset inside a row
+  const uint32_t row_bytes = (uint32_t)(Dm * ES);
+  const int64_t nch = (L + kStateChunk - 1) / kStateChunk;
+
+  auto delta_of = [&](uint32_t rbits) __attribute__((always_inline)) {
+    const float sp = softplus_f(raw_f32<T>(rbits) + bias);
+    return CLAMP ? clamp_delta(sp, dt_lo, dt_hi) : sp;
+  };
+  auto save_state = [&](int t) __attribute__((always_inline)) {
+    if (SAVE && (t & (kStateChunk - 1)) == 0 && dvalid) {
+      float* cs = chunk_states + ((int64_t)b * nch + t / kStateChunk) * N * Dm + d;
+#pragma unroll
+      for (int n = 0; n < 16; ++n)
+        if (n < N) cs[(int64_t)n * Dm] = h[n];
+    }
+  };
+  // one step from Delta, x (and z), B and C of the step
+  float sd = 0.f;
+  auto step = [&](float dl, float xv, uint32_t zbits, const float (&bv)[16], const float (&cv)[16], int t)
+      __attribute__((always_inline)) {
+    const float dlx = dl * xv;
+    // the readout in four interleaved partial sums (states n = 4i + q in sum q), so its
+    // dependent chain is 4 deep, not 16
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const float a = exp2_hw(dl * A2[n]);
+      h[n] = fmaf(a, h[n], dlx * bv[n]);
+      if (OUT) acc4[n & 3] = fmaf(cv[n], h[n], acc4[n & 3]);
+    }
+    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    if (OUT) {
+      const float gate = GATED ? silu_f(raw_f32<T>(zbits)) : 1.f;
+      buf_st<T>(fmaf(dsk, xv, acc) * gate, ry, off_add(dl_off, (uint32_t)t * row_bytes));
+    } else {
+      sd += dl;
+    }
+  };
+
+  // ---- whole tiles: activations through a ring of registers, B/C through LDS
+  auto tile_t = [&](int k) __attribute__((always_inline)) {  // loads past the last whole tile re-read it
+    return t0 + (k < nfull ? k : (nfull > 0 ? nfull - 1 : 0)) * TT;
+  };
+  uint32_t qx[R][TT], qr[R][TT], qz[R][TT], qbc[2][PER];
+  auto load_act = [&](int k, int slot) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)tile_t(k) * row_bytes;
+#pragma unroll
+    for (int s2 = 0; s2 < TT; ++s2) {
+      const uint32_t o = off_add(dl_off, base + (uint32_t)s2 * row_bytes);
+      qx[slot][s2] = buf_ld_raw<T>(rx, o);
+      qr[slot][s2] = buf_ld_raw<T>(rr_, o);
+      qz[slot][s2] = GATED && OUT ? buf_ld_raw<T>(rz, o) : 0u;
+    }
+  };
+  // lane element e = lane + 64 i of a tile: step e / NBC, B (k < 16) or C (k >= 16),
+  // state k & 15, k = e % NBC
+  auto load_bc = [&](int k, int slot) __attribute__((always_inline)) {
+    const int tb = tile_t(k);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i, kk = e % NBC, n = kk & 15, t = tb + e / NBC;
+      const uint32_t o = (n < N) ? (uint32_t)((t * N + n) * ES) : kOutside;
+      qbc[slot][i] = kk >= 16 ? buf_ld_raw<T>(rc, o) : buf_ld_raw<T>(rb, o);
+    }
+  };
+  auto stage_bc = [&](int slot, int buf) __attribute__((always_inline)) {
+    float* dst = &bc[wave][buf][0][0];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[lane + 64 * i] = raw_f32<T>(qbc[slot][i]);
+  };
+
+  if (nfull > 0) {
+    load_bc(0, 0);
+    load_bc(1, 1);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) load_act(k, k);
+    stage_bc(0, 0);
+  }
+  for (int kk = 0; kk < nfull; kk += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kk + u;
+      if (k >= nfull) break;
+      const int slot = u % R, buf = u & 1;
+      load_act(k + R - 1, (u + R - 1) % R);
+      stage_bc((u + 1) & 1, buf ^ 1);  // tile k + 1 (loaded one iteration ago)
+      load_bc(k + 2, u & 1);           // its slot held tile k, staged one iteration ago
+      const int tk = t0 + k * TT;
+      save_state(tk);
+#pragma unroll
+      for (int s2 = 0; s2 < TT; ++s2) {
+        float bv[16], cv[16];
+        const float4* pbc = reinterpret_cast<const float4*>(&bc[wave][buf][s2][0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 vb = pbc[q];
+          bv[4 * q] = vb.x; bv[4 * q + 1] = vb.y; bv[4 * q + 2] = vb.z; bv[4 * q + 3] = vb.w;
+          if (OUT) {
+            const float4 vc = pbc[4 + q];
+            cv[4 * q] = vc.x; cv[4 * q + 1] = vc.y; cv[4 * q + 2] = vc.z; cv[4 * q + 3] = vc.w;
+          } else {
+            cv[4 * q] = cv[4 * q + 1] = cv[4 * q + 2] = cv[4 * q + 3] = 0.f;
+          }
+        }
+        step(delta_of(qr[slot][s2]), raw_f32<T>(qx[slot][s2]), qz[slot][s2], bv, cv, tk + s2);
+      }
+    }
+  }
+  // ---- the steps after the last whole tile (end of the sequence only): plain loads
+  for (int t = t0 + nfull * TT; t < t1; ++t) {
+    save_state(t);
+    const uint32_t o = off_add(dl_off, (uint32_t)t * row_bytes);
+    float bv[16], cv[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const uint32_t ob = n < N ? (uint32_t)((t * N + n) * ES) : kOutside;
+      bv[n] = raw_f32<T>(buf_ld_raw<T>(rb, ob));
+      cv[n] = OUT ? raw_f32<T>(buf_ld_raw<T>(rc, ob)) : 0.f;
+    }
+    step(delta_of(buf_ld_raw<T>(rr_, o)), raw_f32<T>(buf_ld_raw<T>(rx, o)),
+         GATED && OUT ? buf_ld_raw<T>(rz, o) : 0u, bv, cv, t);
+  }
+
+  if (!OUT && dvalid) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      if (n < N) carry[cbase + (int64_t)n * Dm] = h[n];
+    sumd[((int64_t)b * S + j) * Dm + d] = sd;
+  }
+  if (OUT && h_final && dvalid && j == S - 1) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      if (n < N) h_final[((int64_t)b * Dm + d) * N + n] = h[n];
+  }
+}
+
+// Per (batch, state n, tile of 16 channels): the state entering every segment, from
+// the segments' (decay, increment) pairs, in place over the increments.  Blocks of 64
+// segments: thread (row r, channel c) loads segments r, r + 16, ... of channel c; then
+// wave w scans channels 4w .. 4w + 3 in turn (lane = segment), and the state after the
+// block carries into the next one through LDS.
+constexpr int kCarryCh = 16;
+__global__ void __launch_bounds__(256)
+fwd_seg_carry_kernel(const float* __restrict__ A_log, const float* __restrict__ h0, float* __restrict__ carry,
+                     const float* __restrict__ sumd, int Dm, int N, int S, int ndt) {
+  __shared__ float pa[64][kCarryCh + 1], pb[64][kCarryCh + 1], co[64][kCarryCh + 1];
+  __shared__ float cb[kCarryCh];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int dtile = blockIdx.x % ndt;
+  const int n = (blockIdx.x / ndt) % N;
+  const int b = blockIdx.x / (ndt * N);
+  const int c = threadIdx.x % kCarryCh, r = threadIdx.x / kCarryCh;  // load / store phases
+  const int d = dtile * kCarryCh + c;
+  const bool dv = d < Dm;
+  const float A2 = dv ? a2_from_alog(A_log[(int64_t)d * N + n]) : 0.f;
+  if (threadIdx.x < kCarryCh) cb[c] = (dv && h0) ? h0[((int64_t)b * Dm + d) * N + n] : 0.f;
+  for (int j0 = 0; j0 < S; j0 += 64) {
+    // pairs of segments j0 .. j0 + 63 (the last segment and those past it: identity)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sgi = r + 16 * i, seg = j0 + sgi;
+      float a = 1.f, inc = 0.f;
+      if (dv && seg < S - 1) {
+        a = exp2_hw(A2 * sumd[((int64_t)b * S + seg) * Dm + d]);
+        inc = carry[(((int64_t)b * S + seg) * N + n) * Dm + d];
+      }
+      pa[sgi][c] = a;
+      pb[sgi][c] = inc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kCarryCh / 4; ++q) {
+      const int cc = wave * (kCarryCh / 4) + q;
+      float a = pa[lane][cc], bb = pb[lane][cc];
+      scan64_pairs(a, bb);
+      pa[lane][cc] = a;
+      pb[lane][cc] = bb;
+      const float cin = cb[cc];
+      const float ap = lane ? pa[lane - 1][cc] : 1.f;
+      const float bp = lane ? pb[lane - 1][cc] : 0.f;
+      co[lane][cc] = fmaf(ap, cin, bp);           // the state entering segment j0 + lane
+      if (lane == 63) cb[cc] = fmaf(a, cin, bb);  // ... and the one after this block
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sgi = r + 16 * i, seg = j0 + sgi;
+      if (dv && seg < S) carry[(((int64_t)b * S + seg) * N + n) * Dm + d] = co[sgi][c];
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, bool GATED, bool CLAMP>
+hipError_t launch_split_c(const FwdArgs& a, const FwdSplit& sp, hipStream_t stream) {
+  float* carry = (float*)a.workspace;
+  float* sumd = (float*)((char*)a.workspace + sp.off_sumd);
+  const int S = (int)sp.nseg, seglen = (int)sp.seglen;
+  const int ngroups = (int)((a.dim + 64 * kSegWaves - 1) / (64 * kSegWaves));
+  const int L = (int)a.seqlen, Dm = (int)a.dim, N = a.dstate;
+  const T* x = (const T*)a.x;
+  const T* r = (const T*)a.delta_raw;
+  const T* z = (const T*)a.z;
+  const T* Bm = (const T*)a.B;
+  const T* Cm = (const T*)a.C;
+  if (S > 1) {
+    const int nb = (int)(a.batch * (S - 1) * ngroups);
+    hipLaunchKernelGGL((fwd_seg_kernel<T, GATED, false, false, CLAMP>), dim3(nb), dim3(64 * kSegWaves), 0, stream,
+                       x, r, z, Bm, Cm, a.A_log, a.D_skip, a.dt_bias, carry, sumd, (T*)nullptr, (float*)nullptr,
+                       (float*)nullptr, L, Dm, N, S, S - 1, seglen, ngroups, nb, a.dt_lo, a.dt_hi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int ndt = (Dm + kCarryCh - 1) / kCarryCh;
+  hipLaunchKernelGGL(fwd_seg_carry_kernel, dim3((unsigned)(a.batch * N * ndt)), dim3(256), 0, stream, a.A_log, a.h0,
+                     carry, sumd, Dm, N, S, ndt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb = (int)(a.batch * S * ngroups);
+  auto kern = a.chunk_states ? fwd_seg_kernel<T, GATED, true, true, CLAMP> : fwd_seg_kernel<T, GATED, true, false, CLAMP>;
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(64 * kSegWaves), 0, stream, x, r, z, Bm, Cm, a.A_log, a.D_skip, a.dt_bias,
+                     carry, sumd, (T*)a.y, a.h_final, a.chunk_states, L, Dm, N, S, S, seglen, ngroups, nb, a.dt_lo,
+                     a.dt_hi);
+  return hipGetLastError();
+}
+
+template <typename T, bool GATED>
+hipError_t launch_split(const FwdArgs& a, const FwdSplit& sp, hipStream_t stream) {
+  // no clamp (the default: dt_min = 0, no upper bound) skips the clamp's compares
+  const bool clamp = a.dt_lo > 0.f || a.dt_hi < __builtin_inff();
+  return clamp ? launch_split_c<T, GATED, true>(a, sp, stream) : launch_split_c<T, GATED, false>(a, sp, stream);
+}
+
 // Kernel choice, a function of d_state only (so results never depend on anything but
 // the sizes): d_state 9..16 runs the states-across-lanes kernel with 4 waves per
 // group; smaller states run one state per wave over 64-channel tiles.  Measured at
@@ -645,12 +979,42 @@ hipError_t launch_cfg(const FwdArgs& a, hipStream_t stream) {
 // the lanes kernel 190 us.
 template <typename T, bool GATED>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+  const FwdSplit sp = fwd_split(a.batch, a.seqlen, a.dim, a.dstate);
+  if (sp.nseg > 1) return launch_split<T, GATED>(a, sp, stream);
   if (a.dstate > 8) return launch_lanes_w<T, 4, GATED>(a, stream);
   if (a.dstate > 4) return launch_cfg<T, 1, 8, GATED>(a, stream);
   return launch_cfg<T, 1, 4, GATED>(a, stream);
 }
 
 }  // namespace
+
+// The split is taken when the states-across-lanes kernel would have fewer than 1024
+// wavefronts (one per SIMD; it has one per 4 channels of a batch element) and the
+// sequence is at least 1024 steps: then segments of at least 128 steps give the
+// segment kernels about 3072 wavefronts (one per 64 channels of a segment).  The
+// split costs a second pass over the sequence.  Measured (fp32, gated, N = 16), split
+// against unsplit: 1 x 8192 x 2048 (512 wavefronts unsplit) 171 against 282 us;
+// 2 x 8192 x 2048 (1024) 313 against 320; 1 x 4096 x 4096 (1024) 163 against 152;
+// 4 x 8192 x 1536 (1536) 437 against 360.
+FwdSplit fwd_split(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
+  FwdSplit sp{1, seqlen, 0, 0};
+  const int64_t lanes_waves = batch * ((dim + 3) / 4);
+  if (lanes_waves >= 1024 || seqlen < 1024) return sp;
+  const int64_t seg_waves = batch * ((dim + 63) / 64);
+  int64_t want = (3072 + seg_waves - 1) / seg_waves;
+  const int64_t most = seqlen / 128;
+  if (want > most) want = most;
+  if (want < 2) return sp;
+  int64_t seglen = (seqlen + want - 1) / want;
+  seglen = (seglen + kStateChunk - 1) / kStateChunk * kStateChunk;
+  sp.seglen = seglen;
+  sp.nseg = (seqlen + seglen - 1) / seglen;
+  if (sp.nseg < 2) return FwdSplit{1, seqlen, 0, 0};
+  const size_t carry_bytes = (size_t)batch * sp.nseg * dstate * dim * 4;
+  sp.off_sumd = (carry_bytes + 255) & ~(size_t)255;
+  sp.total = (sp.off_sumd + (size_t)batch * sp.nseg * dim * 4 + 255) & ~(size_t)255;
+  return sp;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   if (a.bf16) return a.z ? launch_t<bf16_t, true>(a, stream) : launch_t<bf16_t, false>(a, stream);

@@ -25,8 +25,19 @@ struct FwdArgs {
   int bf16;  // io dtype is bf16
   float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
   float* chunk_states = nullptr;  // [B, ceil(L/16), N, D]: state entering each 16-step chunk
+  void* workspace = nullptr;      // the time-split path's workspace (FwdSplit::total bytes)
 };
 constexpr int kStateChunk = 16;  // steps per saved chunk state (forward tile = backward chunk)
+
+// Time split of the forward: sequences too long for the channels alone to fill the chip
+// are cut into nseg segments of seglen steps (a multiple of 16).  nseg == 1: unsplit,
+// no workspace.  Workspace: the state entering each segment [B, nseg, N, D] fp32 (first
+// the local end states), then the segments' step sums [B, nseg, D] fp32.
+struct FwdSplit {
+  int64_t nseg, seglen;
+  size_t off_sumd, total;
+};
+FwdSplit fwd_split(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
 
 struct StepArgs {
   float* state;

@@ -204,6 +204,10 @@ def ssm_scan_fwd(x, delta_raw, B, C, A_log, D_skip=None, dt_bias=None, z=None, h
     if h_final is None and return_final_state:
         h_final = torch.empty((b, d, n), dtype=f32, device=dev)
     _req(h_final, "h_final", (b, d, n), f32, dev)
+    if workspace is None:
+        need = fwd_workspace_bytes(b, l, d, n, io)
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C), _ptr(A_log),
                                _ptr(D_skip), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),

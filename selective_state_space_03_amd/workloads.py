@@ -47,13 +47,16 @@ class Workload:
         return self.elements * self.dstate
 
 
-# The five workloads the build is measured and checked on.
+# The five workloads the build is measured and checked on, and the long-sequence one.
 WORKLOADS = {
     "fwd_small": Workload("fwd_small", "fwd", 1, 64, 16, 4, "f32", False, "zero", 1001),
     "fwd_b8_l2048_d1536": Workload("fwd_b8_l2048_d1536", "fwd", 8, 2048, 1536, 16, "f32", True, "mamba", 1002),
     "fwd_bf16_b4_l4096_d4096": Workload("fwd_bf16_b4_l4096_d4096", "fwd", 4, 4096, 4096, 16, "bf16", True, "mamba", 1003),
     "step_b256_d5120": Workload("step_b256_d5120", "step", 256, 1, 5120, 16, "f32", True, "mamba", 1004),
     "fwdbwd_b4_l2048_d2048": Workload("fwdbwd_b4_l2048_d2048", "fwdbwd", 4, 2048, 2048, 16, "f32", True, "mamba", 1005),
+    # one long sequence of few channels: the time-split forward
+    "fwd_long_b1_l65536_d1536": Workload("fwd_long_b1_l65536_d1536", "fwd", 1, 65536, 1536, 16, "f32", True, "mamba",
+                                         1006),
 }
 
 
