@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIBDIR, "libssmscan.so")
-SOURCES = ["ssm_api.hip", "ssm_fwd.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_conv1d.hip", "ssm_mamba3.hip", "ssm_ssd.hip"]
+SOURCES = ["ssm_api.hip", "ssm_fwd.hip", "ssm_step.hip", "ssm_bwd.hip", "ssm_bwd_fused.hip", "ssm_conv1d.hip", "ssm_mamba3.hip", "ssm_ssd.hip"]
 ARCH = "gfx950"
 
 

@@ -105,6 +105,25 @@ int waves_for(int dstate) { return dstate <= 2 ? 1 : (dstate <= 4 ? 2 : (dstate 
 
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
   BwdLayout l;
+  l.fused = batch * ((dim + 3) / 4) >= 1024 || seqlen < 1024;
+  if (l.fused) {
+    // chunk states, then per-workgroup dB/dC partials, then the per-batch-element
+    // parameter partials (dA [B, N, D], dD [B, D], d_dt_bias [B, D])
+    const size_t f = sizeof(float), N = (size_t)dstate;
+    l.chunk = kStateChunk;
+    l.nchunks = (seqlen + kStateChunk - 1) / kStateChunk;
+    l.ngroups = bwd_fused_groups(dim);
+    l.segc = l.nchunks;
+    l.nseg = 1;
+    size_t off = 0;
+    l.off_cs = off;     off = align256(off + (size_t)batch * l.nchunks * N * dim * f);
+    l.off_dbc = off;    off = align256(off + 2 * (size_t)batch * l.ngroups * seqlen * N * f);
+    l.off_dparam = off; off = align256(off + ((size_t)batch * dim * N + 2 * (size_t)batch * dim) * f);
+    l.off_hrel = l.off_cumd = l.off_hseg = l.off_sdseg = l.off_gseg = l.off_hin = l.off_gin = 0;
+    l.total = off;
+    return l;
+  }
+  l.off_cs = 0;
   l.chunk = kChunk;
   l.nchunks = (seqlen + kChunk - 1) / kChunk;
   l.ngroups = (dim + 63) / 64;
@@ -619,11 +638,27 @@ reduce_bc_kernel(const float* __restrict__ pdB, const float* __restrict__ pdC, f
   const int64_t per_b = L * N;
   if (i >= batch * per_b) return;
   const int64_t b = i / per_b, tn = i % per_b;
+  const float* pb = pdB + b * ngroups * per_b + tn;
+  const float* pc = pdC + b * ngroups * per_b + tn;
   float sB = 0.f, sC = 0.f;
-  for (int64_t g = 0; g < ngroups; ++g) {
-    const int64_t o = (b * ngroups + g) * per_b + tn;
-    sB += pdB[o];
-    sC += pdC[o];
+  int64_t g = 0;
+  // eight tiles' loads in flight at a time, added in ascending tile order
+  for (; g + 8 <= ngroups; g += 8) {
+    float vb[8], vc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      vb[k] = pb[(g + k) * per_b];
+      vc[k] = pc[(g + k) * per_b];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sB += vb[k];
+      sC += vc[k];
+    }
+  }
+  for (; g < ngroups; ++g) {
+    sB += pb[g * per_b];
+    sC += pc[g * per_b];
   }
   dB[i] = sB;
   dC[i] = sC;
@@ -720,6 +755,32 @@ hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
   const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate);
   char* ws = (char*)workspace;
   hipError_t e;
+  if (l.fused) {
+    const float* cs = a.chunk_states;
+    if (!cs) {  // the forward did not save its chunk states: a states-only forward writes them
+      FwdArgs f;
+      f.x = a.x; f.delta_raw = a.delta_raw; f.z = nullptr; f.B = a.B; f.C = a.C; f.A_log = a.A_log;
+      f.D_skip = nullptr; f.dt_bias = a.dt_bias; f.h0 = a.h0; f.y = nullptr; f.h_final = nullptr;
+      f.batch = a.batch; f.seqlen = a.seqlen; f.dim = a.dim; f.dstate = a.dstate; f.bf16 = a.bf16;
+      f.dt_lo = a.dt_lo; f.dt_hi = a.dt_hi; f.chunk_states = (float*)(ws + l.off_cs);
+      if ((e = launch_fwd_states(f, stream)) != hipSuccess) return e;
+      cs = f.chunk_states;
+    }
+    float* pdB = (float*)(ws + l.off_dbc);
+    float* pdC = pdB + (size_t)a.batch * l.ngroups * a.seqlen * a.dstate;
+    float* pdA = (float*)(ws + l.off_dparam);
+    float* pdD = pdA + (size_t)a.batch * a.dim * a.dstate;
+    float* pdb = pdD + (size_t)a.batch * a.dim;
+    if ((e = launch_bwd_fused(a, cs, pdB, pdC, pdA, pdD, pdb, stream)) != hipSuccess) return e;
+    const int64_t n = a.batch * a.seqlen * a.dstate;
+    hipLaunchKernelGGL(reduce_bc_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pdB, pdC,
+                       a.dB, a.dC, a.batch, a.seqlen, a.dstate, l.ngroups);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t np = a.dim * a.dstate > a.dim ? a.dim * a.dstate : a.dim;
+    hipLaunchKernelGGL(reduce_params_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, stream, pdA, pdD,
+                       pdb, a.A_log, a.dA_log, a.dD, a.d_dt_bias, a.batch, a.dim, a.dstate);
+    return hipGetLastError();
+  }
   switch (waves_for(a.dstate)) {
     case 1: e = a.bf16 ? launch_segments<bf16_t, 1>(a, l, ws, stream) : launch_segments<float, 1>(a, l, ws, stream); break;
     case 2: e = a.bf16 ? launch_segments<bf16_t, 2>(a, l, ws, stream) : launch_segments<float, 2>(a, l, ws, stream); break;

@@ -38,49 +38,6 @@
 namespace ssm {
 namespace {
 
-// Raw buffer access: a per-tile buffer resource whose range ends at the end of the
-// sequence (or is empty), so loads outside it return 0 and stores outside it are
-// dropped by the hardware.  Lanes of padding channels use an offset >= 2^31, which is
-// always outside.  This keeps every load and store of the loop unconditional.
-constexpr uint32_t kBufWord3 = 0x00020000;  // gfx9-family raw buffer descriptor, word 3
-constexpr uint32_t kOutside = 0x80000000u;
-
-// lane offset + tile offset; either one outside makes the sum outside (no wrap-around)
-__device__ __forceinline__ uint32_t off_add(uint32_t a, uint32_t b) {
-  return ((a | b) & kOutside) ? kOutside : a + b;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t bytes) {
-  const int nr = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kBufWord3);
-}
-template <typename T> __device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off);
-template <> __device__ __forceinline__ float buf_ld<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));  // bits, not a value cast
-}
-template <> __device__ __forceinline__ float buf_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-}
-// raw element bits (zero-extended), converted to fp32 only where the value is used, so
-// that a load's wait is not pulled up to the load
-template <typename T> __device__ __forceinline__ uint32_t buf_ld_raw(__amdgpu_buffer_rsrc_t r, uint32_t off);
-template <> __device__ __forceinline__ uint32_t buf_ld_raw<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-template <> __device__ __forceinline__ uint32_t buf_ld_raw<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-template <typename T> __device__ __forceinline__ float raw_f32(uint32_t v) {
-  return std::is_same<T, float>::value ? __uint_as_float(v) : __uint_as_float(v << 16);
-}
-template <typename T> __device__ __forceinline__ void buf_st(float v, __amdgpu_buffer_rsrc_t r, uint32_t off);
-template <> __device__ __forceinline__ void buf_st<float>(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);  // bits, not a value cast
-}
-template <> __device__ __forceinline__ void buf_st<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
-}
-
 template <typename T, int S, int G, int TT, int R, bool GATED, bool MASKED>
 __global__ void __launch_bounds__(64 * G)
 fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
@@ -334,90 +291,23 @@ fwd_scan_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const 
 // Nothing is shared between waves, so the loop has no barrier.  The sums are taken in
 // a fixed order: results are deterministic.
 
-// Halving exchanges of the in-row transpose-reduce, written as DPP adds whose bank
-// masks make each instruction write only half of the row, so one register holds both
-// halves' results.  One s_nop covers the DPP read-after-VALU-write wait for the whole
-// block (its sources are not written inside it).
-// Stage 1: partner lane i^8 (rows rotate by 8); lanes 0-7 of a row keep p[j] + partner's
-// p[j], lanes 8-15 p[j+8] + partner's p[j+8] (j < 8).
-__device__ __forceinline__ void row_halve_ror8(const float (&p)[16], float (&q)[8]) {
-  asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
-      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
-      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc"
-      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(p[8]),
-        "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
-}
-// Stage 2: partner = the mirror lane inside each half row (lane i^7); lanes with bit 2
-// clear (banks 0 and 2) keep q[j] + partner's q[j], the others q[j+4] + partner's (j < 4).
-__device__ __forceinline__ void row_halve_mirror8(const float (&q)[8], float (&r)[4]) {
-  asm("s_nop 1\n\t"
-      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
-      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
-      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
-      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
-}
-template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_amdgcn_update_dpp(0.f, v, CTRL, 0xf, 0xf, false);
-}
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppRowBcast0 = 0x150;  // row_newbcast:0 (+t: every lane of a row reads its lane t)
-
-// p[j] in every lane of a 16-lane row -> lane i of the row returns sum over the row of
-// p[i].  Exchanges halve the values held at lane distances 8, 7, 2, 1; lane i keeps
-// the half that its bit 3, 2, 1, 0 selects, so the index it ends with is i itself.
-__device__ __forceinline__ float row_transpose_sum16(const float (&p)[16], int lane) {
-  float q[8], r[4], s[2];
-  row_halve_ror8(p, q);
-  row_halve_mirror8(q, r);
-  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float send = b1 ? r[j] : r[j + 2];
-    const float keep = b1 ? r[j + 2] : r[j];
-    s[j] = keep + dpp_f<kDppQuadXor2>(send);
-  }
-  const float send = b0 ? s[0] : s[1];
-  const float keep = b0 ? s[1] : s[0];
-  return keep + dpp_f<kDppQuadXor1>(send);
-}
-
 // one step of the recurrence in a state lane: Delta and Delta*x of step T come from
 // lane T of the row
-template <int T>
+template <int T, bool OUTY>
 __device__ __forceinline__ void lane_step(float& h, float dl, float dlx, float A2, float b, float& c) {
   const float a = exp2_hw(dpp_f<kDppRowBcast0 + T>(dl) * A2);
   h = fmaf(a, h, dpp_f<kDppRowBcast0 + T>(dlx) * b);
-  c *= h;  // C[t][n] h_t[n], summed over the row by the readout
+  if (OUTY) c *= h;  // C[t][n] h_t[n], summed over the row by the readout
 }
-template <int... I>
+template <bool OUTY, int... I>
 __device__ __forceinline__ void lane_scan16(std::integer_sequence<int, I...>, float& h, float dl, float dlx,
                                             float A2, const float (&bv)[16], float (&cv)[16]) {
-  (lane_step<I>(h, dl, dlx, A2, bv[I], cv[I]), ...);
+  (lane_step<I, OUTY>(h, dl, dlx, A2, bv[I], cv[I]), ...);
 }
 
-template <typename T, int W, bool GATED, bool SAVE>
+// OUTY = false: the states only (the backward's pass that writes the chunk states when
+// the forward did not): no readout, no gate, no y.
+template <typename T, int W, bool GATED, bool SAVE, bool OUTY = true>
 __global__ void __launch_bounds__(64 * W)
 fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
                  const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ A_log,
@@ -476,7 +366,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t rr = tile_rsrc(delta_raw + row0 * Dm, slice);
   const __amdgpu_buffer_rsrc_t rz = tile_rsrc(GATED ? z + row0 * Dm : x + row0 * Dm, slice);
-  const __amdgpu_buffer_rsrc_t ry = tile_rsrc(y + row0 * Dm, slice);
+  const __amdgpu_buffer_rsrc_t ry = tile_rsrc(OUTY ? (const void*)(y + row0 * Dm) : (const void*)x, OUTY ? slice : 0);
   const __amdgpu_buffer_rsrc_t rb = tile_rsrc(Bm + row0 * N, (int64_t)L * N * ES);
   const __amdgpu_buffer_rsrc_t rc = tile_rsrc(Cm + row0 * N, (int64_t)L * N * ES);
   const uint32_t tile_bytes = (uint32_t)(TT * Dm * ES);  // j * tile_bytes < 2^31 for j < ntiles
@@ -499,17 +389,17 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     const uint32_t ob = boff + (uint32_t)jc * btile_bytes;
     qx[slot] = buf_ld_raw<T>(rx, o);
     qr[slot] = buf_ld_raw<T>(rr, o);
-    qz[slot] = GATED ? buf_ld_raw<T>(rz, o) : 0u;
+    qz[slot] = GATED && OUTY ? buf_ld_raw<T>(rz, o) : 0u;
     qb[slot] = buf_ld_raw<T>(rb, ob);
-    qcv[slot] = buf_ld_raw<T>(rc, ob);
+    qcv[slot] = OUTY ? buf_ld_raw<T>(rc, ob) : 0u;
   };
   auto stage_tile = [&](int slot, int buf) __attribute__((always_inline)) {
     act[buf][0][qt * SA + qc] = raw_f32<T>(qx[slot]);
     act[buf][1][qt * SA + qc] = raw_f32<T>(qr[slot]);
-    if (GATED) act[buf][2][qt * SA + qc] = raw_f32<T>(qz[slot]);
+    if (GATED && OUTY) act[buf][2][qt * SA + qc] = raw_f32<T>(qz[slot]);
     if (bl) {
       bct[buf][0][li * SP + bqt] = raw_f32<T>(qb[slot]);
-      bct[buf][1][li * SP + bqt] = raw_f32<T>(qcv[slot]);
+      if (OUTY) bct[buf][1][li * SP + bqt] = raw_f32<T>(qcv[slot]);
     }
   };
   // B[t][li] and C[t][li] of the 16 steps of the tile in buffer buf (state lane)
@@ -538,7 +428,7 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   };
   // y of tile j from LDS, stored as 64-byte rows (rows past the end and k < 0 outside)
   auto store_y = [&](int j, int ybuf) __attribute__((always_inline)) {
-    if (j >= 0) buf_st<T>(yb[ybuf][qt * SA + qc], ry, aoff + (uint32_t)j * tile_bytes);
+    if (OUTY && j >= 0) buf_st<T>(yb[ybuf][qt * SA + qc], ry, aoff + (uint32_t)j * tile_bytes);
   };
   // chunk states of this batch element: tile j at rows [j*N, j*N + N) of [*, Dm]; this
   // lane stores state row qt (when qt < N) of channel g0 + qc
@@ -586,11 +476,13 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
         hsv[u & 1][li * SA + wave * 4 + row] = h;  // the state entering tile k
       }
       __builtin_amdgcn_s_setprio(1);
-      lane_scan16(std::make_integer_sequence<int, 16>(), h, dl, dlx, A2, bv, cv);
+      lane_scan16<OUTY>(std::make_integer_sequence<int, 16>(), h, dl, dlx, A2, bv, cv);
       // readout of tile k in the prep lane of step li
-      const float s = row_transpose_sum16(cv, lane);
-      const float gate = GATED ? silu_f(zk) : 1.f;
-      yb[u & 1][pcol] = fmaf(dsk, xk, s) * gate;
+      if (OUTY) {
+        const float s = row_transpose_sum16(cv, lane);
+        const float gate = GATED ? silu_f(zk) : 1.f;
+        yb[u & 1][pcol] = fmaf(dsk, xk, s) * gate;
+      }
       dl = dln;
       dlx = dlxn;
       xk = xkn;
@@ -600,6 +492,20 @@ fwd_lanes_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   store_y(ntiles - 1, (ntiles - 1) & 1);
   store_state(ntiles - 1);
   if (h_final && nvalid) h_final[hb] = h;
+}
+
+// the states-only pass: chunk states written, nothing else (y, h_final unused)
+template <typename T>
+hipError_t launch_states(const FwdArgs& a, hipStream_t stream) {
+  constexpr int W = 4;
+  const int ngroups = (int)((a.dim + 4 * W - 1) / (4 * W));
+  const int64_t nblocks = (int64_t)ngroups * a.batch;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_lanes_kernel<T, W, false, true, false>), dim3((unsigned)nblocks), dim3(64 * W), 0, stream,
+                     (const T*)a.x, (const T*)a.delta_raw, (const T*)nullptr, (const T*)a.B, (const T*)a.C, a.A_log,
+                     a.D_skip, a.dt_bias, a.h0, (T*)nullptr, (float*)nullptr, (int)a.seqlen, (int)a.dim, a.dstate,
+                     ngroups, (int)nblocks, a.dt_lo, a.dt_hi, a.chunk_states);
+  return hipGetLastError();
 }
 
 template <typename T, int W, bool GATED>
@@ -1014,6 +920,10 @@ FwdSplit fwd_split(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
   sp.off_sumd = (carry_bytes + 255) & ~(size_t)255;
   sp.total = (sp.off_sumd + (size_t)batch * sp.nseg * dim * 4 + 255) & ~(size_t)255;
   return sp;
+}
+
+hipError_t launch_fwd_states(const FwdArgs& a, hipStream_t stream) {
+  return a.bf16 ? launch_states<bf16_t>(a, stream) : launch_states<float>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {

@@ -84,8 +84,14 @@ struct BwdArgs {
   float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
 };
 
-// Workspace layout of the backward (byte offsets into one caller buffer).
+// Workspace layout of the backward (byte offsets into one caller buffer).  Two paths,
+// chosen by the sizes: "fused" (each wavefront walks its channels' whole sequence; the
+// chunk states come from the forward or from a states-only forward pass into off_cs)
+// when batch x ceil(dim / 4) >= 1024 or seqlen < 1024, else "segments" (time cut into
+// segments processed in parallel, as the time-split forward does).
 struct BwdLayout {
+  bool fused;
+  size_t off_cs;     // fused: chunk states [B, nchunks, N, D] when the forward did not save them
   int chunk;         // time steps per chunk (the recompute window)
   int64_t nchunks;   // ceil(seqlen / chunk)
   int64_t ngroups;   // ceil(dim / 64) channel groups
@@ -126,6 +132,13 @@ constexpr size_t kConvScratchBytes = (size_t)16 << 20;
 hipError_t conv_scratch(void** out);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// the states-only forward: writes a.chunk_states and nothing else (y, h_final unused)
+hipError_t launch_fwd_states(const FwdArgs& a, hipStream_t stream);
+// the fused backward (ssm_bwd_fused.hip): per-workgroup dB/dC partials
+// [B, bwd_fused_groups(D), L, N], dA partials [B, N, D], dD and d_dt_bias partials [B, D]
+int64_t bwd_fused_groups(int64_t dim);
+hipError_t launch_bwd_fused(const BwdArgs& a, const float* chunk_states, float* pdB, float* pdC, float* pdA,
+                            float* pdD, float* pdb, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
