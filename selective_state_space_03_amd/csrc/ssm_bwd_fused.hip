@@ -227,6 +227,32 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     }
   };
 
+  // The results of chunk jr (after the barrier that ends its iteration): dB / dC partials
+  // (the waves' sums added in wave order) and the activation gradients as 128-byte
+  // rows.  Done at the start of the next chunk's iteration, so that these LDS reads
+  // overlap that chunk's arithmetic.
+  auto results = [&](int jr) __attribute__((always_inline)) {
+    const int pr = jr & 1;
+#pragma unroll
+    for (int i = 0; i < 512 / kFThr; ++i) {
+      const int e2 = tid + kFThr * i;
+      const int e = e2 & 255;  // (step, state) = (e / 16, e % 16)
+      const int which = e2 >> 8;
+      float acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < kFWaves; ++v) acc += red[pr][v][which][e];
+      const int tt = jr * kFT + (e >> 4), nn = e & 15;
+      if (tt < L && nn < N) {
+        float* dst = which ? pdC : pdB;
+        dst[(((int64_t)b * ngroups + grp) * L + tt) * N + nn] = acc;
+      }
+    }
+    const uint32_t o = off_add(aoff, (uint32_t)jr * kFT * row_bytes);  // past the end: dropped
+    buf_st<T>(outs[pr][0][ls][lc], rdx, o);
+    buf_st<T>(outs[pr][1][ls][lc], rddr, o);
+    if (GATED) buf_st<T>(outs[pr][2][ls][lc], rdz, o);
+  };
+
   // carried over the whole sequence
   float Gc = (nvalid && dh_final) ? dh_final[((int64_t)b * Dm + d) * N + li] : 0.f;  // a_{t+1} G_{t+1}
   float dA = 0.f;                 // state lane: sum of Delta G a h_prev
@@ -248,6 +274,7 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     // stage the next chunk (loaded one iteration ago) and load the one after it
     if (j > 0) stage_chunk(u ^ 1, u ^ 1);
     load_chunk(j - 2, u);
+    if (k > 0) results(j + 1);  // the previous chunk's, written before the last barrier
     // ---- per-element values of step li of channel cw (prep lane)
     const int t = j * kFT + li;
     const bool tv = dvalid && t < L;
@@ -316,30 +343,10 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     }
     __syncthreads();
 
-    // ---- the chunk's results: dB / dC partials (sum over waves in wave order) and
-    // the activation gradients as 128-byte rows
-    {
-#pragma unroll
-      for (int i = 0; i < 512 / kFThr; ++i) {
-        const int e2 = tid + kFThr * i;
-        const int e = e2 & 255;  // (step, state) = (e / 16, e % 16)
-        const int which = e2 >> 8;
-        float acc = 0.f;
-#pragma unroll
-        for (int v = 0; v < kFWaves; ++v) acc += red[par][v][which][e];
-        const int tt = j * kFT + (e >> 4), nn = e & 15;
-        if (tt < L && nn < N) {
-          float* dst = which ? pdC : pdB;
-          dst[(((int64_t)b * ngroups + grp) * L + tt) * N + nn] = acc;
-        }
-      }
-      const uint32_t o = off_add(aoff, (uint32_t)j * kFT * row_bytes);  // past the end: dropped
-      buf_st<T>(outs[par][0][ls][lc], rdx, o);
-      buf_st<T>(outs[par][1][ls][lc], rddr, o);
-      if (GATED) buf_st<T>(outs[par][2][ls][lc], rdz, o);
-    }
   }
   }
+  __syncthreads();
+  results(0);
 
   // ---- per-sequence results
   if (dh0 && nvalid) dh0[((int64_t)b * Dm + d) * N + li] = Gc;  // a_0 G_0
