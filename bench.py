@@ -153,6 +153,78 @@ def measured_traffic():
     return c.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """the host CPU's model name (lscpu), or None"""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
+def cpu_baseline(head):
+    """The fp64 oracle timed on the host, on the same synthetic inputs as the GPU lines:
+    every forward workload, the decode step and the backward on the oracle's thread pool
+    (the machine's CPU share, at most 16 threads), plus the small and the benchmark forward
+    on one thread.  Whole passes are timed; the benchmark forward is repeated until about
+    10 s are spent on it.  The headline value is the benchmark forward's GB/s."""
+    import oracle
+    from selective_state_space_03_amd import workloads as W
+    nthreads = oracle.default_threads()
+    per = {}
+
+    def timed(fn, min_s=0.0):
+        passes, t0 = 0, time.perf_counter()
+        while passes == 0 or time.perf_counter() - t0 < min_s:
+            fn()
+            passes += 1
+        return (time.perf_counter() - t0) / passes, passes
+
+    def fwd_of(inp, nt):
+        return lambda: oracle.fwd(inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"], D=inp["D"],
+                                  dt_bias=inp["dt_bias"], z=inp["z"], nthreads=nt)
+
+    for name in ("fwd_small", "fwd_b8_l2048_d1536", "fwd_bf16_b4_l4096_d4096", "fwdbwd_b4_l2048_d2048"):
+        w = W.WORKLOADS[name]
+        inp = head["inp"] if name == "fwd_b8_l2048_d1536" else W.make_inputs(w, with_dy=False)
+        es = 2 if w.io == "bf16" else 4
+        nb = fwd_bytes(w.batch, w.seqlen, w.dim, w.dstate, es, w.gated)
+        dt, passes = timed(fwd_of(inp, nthreads), 10.0 if name == "fwd_b8_l2048_d1536" else 0.0)
+        per["fwd_" + name] = {"seconds_per_pass": round(dt, 5), "passes": passes, "threads": nthreads,
+                              "gbs": round(nb / dt / 1e9, 4), "elements_per_s": round(w.elements / dt, 1)}
+        if name in ("fwd_small", "fwd_b8_l2048_d1536"):
+            dt1, p1 = timed(fwd_of(inp, 1))
+            per["fwd_" + name + "_1thread"] = {"seconds_per_pass": round(dt1, 5), "passes": p1, "threads": 1,
+                                               "gbs": round(nb / dt1 / 1e9, 4)}
+        log("cpu oracle fwd %-24s %.4f s per pass on %d threads" % (name, dt, nthreads))
+    w = W.WORKLOADS["step_b256_d5120"]
+    inp = W.make_inputs(w)
+    dt, passes = timed(lambda: oracle.step(inp["state"], inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"],
+                                           D=inp["D"], dt_bias=inp["dt_bias"], z=inp["z"], nthreads=nthreads), 1.0)
+    per["step_b256_d5120"] = {"seconds_per_pass": round(dt, 5), "passes": passes, "threads": nthreads,
+                              "gbs": round(step_bytes(w.batch, w.dim, w.dstate, 4, w.gated) / dt / 1e9, 4)}
+    w = W.WORKLOADS["fwdbwd_b4_l2048_d2048"]
+    inp = W.make_inputs(w)
+    dt, passes = timed(lambda: oracle.bwd(inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"], inp["dy"],
+                                          D=inp["D"], dt_bias=inp["dt_bias"], z=inp["z"], nthreads=nthreads))
+    per["bwd_b4_l2048_d2048"] = {"seconds_per_pass": round(dt, 5), "passes": passes, "threads": nthreads,
+                                 "gbs": round(bwd_bytes(w.batch, w.seqlen, w.dim, w.dstate, w.gated) / dt / 1e9, 4)}
+    log("cpu oracle step %.4f s, bwd %.4f s per pass" % (per["step_b256_d5120"]["seconds_per_pass"], dt))
+    hb = per["fwd_fwd_b8_l2048_d1536"]
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"value": hb["gbs"], "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": "the fp64 oracle on the same inputs: %d whole passes of the benchmark forward (B=8 L=2048 "
+                      "d_inner=1536 N=16), one pass of each other forward workload, the decode step and the backward "
+                      "on %d threads, and the small and benchmark forwards on 1 thread" % (hb["passes"], nthreads),
+            "seconds_per_pass": hb["seconds_per_pass"], "gpu_speedup": round(hb["seconds_per_pass"] / (head["ev_ms"] * 1e-3), 1),
+            "threads": nthreads, "host_cpu_count": os.cpu_count(), "host_affinity_cpus": aff, "host_cpu_model": cpu_model(),
+            "per_workload": per}
+
+
 class Timer:
     """HIP events on the current (launch) stream, which is the stream the library
     launches on.  The average launch duration is one event pair around the K timed
@@ -596,22 +668,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        import oracle
-        inp = head["inp"]
-        nthreads = oracle.default_threads()
-        # whole passes of the oracle over the same inputs until about 10 s of CPU time is spent
-        passes, t0 = 0, time.perf_counter()
-        while passes == 0 or time.perf_counter() - t0 < 10.0:
-            oracle.fwd(inp["x"], inp["delta_raw"], inp["B"], inp["C"], inp["A_log"], D=inp["D"],
-                       dt_bias=inp["dt_bias"], z=inp["z"], nthreads=nthreads)
-            passes += 1
-        dt = (time.perf_counter() - t0) / passes
-        cpu = {"value": round(head["bytes"] / dt / 1e9, 3), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-               "sample": "%d passes over the whole forward workload B=8 L=2048 d_inner=1536 N=16 (fp64), "
-                         "%.3f s per pass" % (passes, dt),
-               "seconds_per_pass": round(dt, 4), "gpu_speedup": round(dt / (head["ev_ms"] * 1e-3), 1)}
-        log("cpu oracle: %.3f s per pass (%d passes) on %d threads (%.2f GB/s)" % (dt, passes, nthreads, cpu["value"]))
-
+        cpu = cpu_baseline(head)
     secondary = {}
     for k, v in results.items():
         secondary[k] = {"gbs": round(v["gbs"], 1), "frac_of_8tbs": round(v["gbs"] / HBM_PEAK_GBS, 4),

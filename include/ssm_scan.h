@@ -130,6 +130,8 @@ int ssm_scan_step(float* state, const void* x, const void* delta_raw, const void
  *   deterministic_backward.py (ordered_cumsum: partials added in lexical
  *   (batch, chunk) order) and the deterministic row partial of
  *   mamba3_preprocess_backward.slang (dt_bias_partial).
+ *   Limits: as the forward, one batch element's slice, seqlen * max(d_inner, d_state)
+ *   elements of io_dtype, must be below 2^31 bytes (SSM_ERR_UNSUPPORTED otherwise).
  *   io_dtype SSM_F32 or SSM_BF16: x, delta_raw, z, B, C, dy are read and dx, ddelta_raw,
  *   dz written in io_dtype (bf16 rounded to nearest even); dB, dC and the parameter
  *   gradients are fp32 in both cases, as are the state and all arithmetic. */

@@ -281,6 +281,11 @@ int ssm_scan_bwd_ex(const void* x, const void* delta_raw, const void* z, const v
   const float* chunk_states = options ? options->chunk_states : nullptr;
   if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (!dims_ok(batch, seqlen, d_inner, d_state)) return SSM_ERR_DIM;
+  // the backward addresses one batch element's [seqlen, d_inner] slice and its chunk
+  // states with 31-bit offsets
+  if ((uint64_t)seqlen * (uint64_t)(d_inner > d_state ? d_inner : d_state) * esize(io_dtype) >= ((uint64_t)1 << 31) ||
+      !chunk_states_fit(seqlen, d_inner, d_state))
+    return SSM_ERR_UNSUPPORTED;
   if (!workspace) return SSM_ERR_WORKSPACE;
   const ssm::BwdLayout l = ssm::bwd_layout(batch, seqlen, d_inner, (int)d_state);
   if (workspace_bytes < l.total || !aligned(workspace, 256)) return SSM_ERR_WORKSPACE;
