@@ -108,9 +108,11 @@ def ssd_scan_bwd_bytes(b, l, h, p, n, nc, w):
 def ssd_scan_bwd_flops(b, l, h, p, n, nc, w):
     """useful multiply-adds of the chunked backward, x2: per (batch, head, chunk) five
     full products of w p n (B G^T, X G, dY S, C S^T and the carry update) and the causal
-    C B^T, dY X^T, K^T dY, V B and V^T C (w (w + 1) / 2 pairs each, of length n, p, p, n, n)"""
+    dY X^T and K^T dY (w (w + 1) / 2 pairs each, of length p); per (batch, chunk), since
+    B and C are shared by the heads, the causal C B^T once and the V terms V B and V^T C
+    once on V summed over the heads (w (w + 1) / 2 pairs each, of length n)"""
     tri = w * (w + 1) // 2
-    return 2 * b * h * nc * (5 * w * p * n + tri * (3 * n + 2 * p))
+    return 2 * b * h * nc * (5 * w * p * n + tri * 2 * p) + 2 * b * nc * tri * 3 * n
 
 
 def conv_bytes(b, l, d, k, es):

@@ -535,56 +535,55 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 // ---------------------------------------------------------------------------------
 // SSD scan backward (64-step chunks), on the matrix cores.
 //
-// The reverse of the forward above, per (batch, head), walking the chunks from the
-// last: G = dLoss/d(state leaving the chunk) is carried in accumulators (the same
-// tile layout as the forward's state), and each chunk's entering state comes from the
-// forward's block_states.  With cs the chunk's dA_cumsum, e_i = exp(cs_i),
-// L_is = exp(cs_i - cs_s) for s <= i, w_s = exp(cs_last - cs_s) dt_s, dY the chunk's
-// dy rows and S the entering state, the chunk's products are
-//   dx_s   = w_s B_s G^T + dt_s sum_{i >= s} K_is dy_i + D dy_s,   K_is = L_is C_i.B_s
-//   dB_s   = w_s x_s G  + sum_{i >= s} V_is C_i,                   V_is = L_is dt_s dy_i.x_s
+// The reverse of the forward above.  With G = dLoss/d(state leaving a chunk), S the
+// state entering it (the forward's block_states), cs the chunk's dA_cumsum,
+// e_i = exp(cs_i), L_is = exp(cs_i - cs_s) for s <= i, w_s = exp(cs_last - cs_s) dt_s,
+// dY the chunk's dy rows, K_is = L_is C_i.B_s, Z_is = dy_i.x_s, Q = K o Z and
+// V_is = L_is dt_s Z_is (s <= i), one head's share of a chunk is
+//   dx_s   = w_s B_s G^T + dt_s sum_{i >= s} K_is dy_i + D dy_s
+//   dB_s   = w_s x_s G  + sum_{i >= s} V_is C_i
 //   dC_i   = e_i dy_i S + sum_{s <= i} V_is B_s
-//   ddt_s  = sum_i K_is Z_is + exp(cs_last - cs_s) x_s.(G B_s),     Z_is = dy_i.x_s
+//   ddt_s  = sum_i Q_is + exp(cs_last - cs_s) x_s.(G B_s)
 //   dcs_i  = e_i dy_i.(C_i S^T) + sum_s Q_is dt_s - dt_i sum_r Q_ri - w_i x_i.(G B_i)
-//            (+ at the last step: sum_s w_s x_s.(G B_s) + e_last <G, S>),  Q = K Z
+//            (+ at the last step: sum_s w_s x_s.(G B_s) + e_last <G, S>)
 //   G_prev = e_last G + sum_i e_i dy_i (x) C_i,    dD += sum dy x
 // dcs and ddt are the gradients of dA_cumsum and dt_out, which the chunk cumsum
-// backward turns into those of dt, A and dt_bias.  dB and dC are written per head and
-// summed over heads in ascending order by a second kernel (one writer per element, no
-// atomics); every other sum has a fixed order as well.  Eight waves: wave (rb, ph)
-// owns the 16 rows 16 rb .. of every [64 x *] product (as rows i or as steps s) and
-// half of its columns (ph), as in the forward (the two waves of a SIMD take row
-// blocks r and 3 - r); the causal K and Z blocks of a row block are split between its
-// two waves.  The [64 x 64] K and V blocks pass between waves through LDS, and the
-// row and column sums that two or four waves share go through small LDS arrays added
-// in a fixed order.
+// backward turns into those of dt, A and dt_bias.
+//
+// Two kernels.  The carry kernel, one workgroup per (batch, head), runs only the G
+// recurrence from the last chunk and stores the G of every chunk in a workspace, in
+// the order of its accumulator fragments.  The chunk kernel, one workgroup per
+// (batch, chunk, group of heads), walks its heads in ascending order: B and C are the
+// same for every head, so C_i.B_s is computed once per chunk, dB and dC stay in
+// accumulators across the heads (the per-head weights w and e scale the X and dY
+// operands), and the V terms are summed over the heads first and multiplied by B and
+// C once at the end.  dB and dC have one writer per element and no per-head copies;
+// when a chunk's heads are split over several workgroups (few chunks), the groups'
+// values are added in ascending group order by a second kernel, which also adds dD
+// over (batch, chunk) in ascending order.  No atomics; every sum has a fixed order.
+//
+// Work layout of the chunk kernel (eight waves, as in the forward): wave (rb, ph) owns
+// the 16 rows 16 rb .. of every [64 x *] product (as rows i or as steps s) and half of
+// its columns (ph); the two waves of a SIMD take row blocks r and 3 - r.  The causal
+// Z blocks of a row block are split between its two waves (step blocks ph, ph + 2).
+// The row and column sums that two or four waves share go through small LDS arrays
+// added in a fixed order.  G and then S pass through one LDS tile.
+
+// the carry kernel: G of every chunk into Gbuf, dLoss/dh0 into dh0 (if given)
 template <int N>
-__global__ void __launch_bounds__(kScanThreads)
-ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
-                          const float* __restrict__ dA_cs, const float* __restrict__ Bm,
-                          const float* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ dy,
-                          const float* __restrict__ bstates, const float* __restrict__ dh_final,
-                          float* __restrict__ dx, float* __restrict__ ddA, float* __restrict__ ddt,
-                          float* __restrict__ dBh, float* __restrict__ dCh, float* __restrict__ dDp,
-                          float* __restrict__ dh0, int64_t L, int H, int64_t nc) {
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)))
+ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ Cm, const float* __restrict__ dy,
+                     const float* __restrict__ dh_final, float* __restrict__ Gbuf, float* __restrict__ dh0,
+                     int64_t L, int H, int64_t nc) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
-  constexpr int SM = W + 4;
-  constexpr int NT = N / 16;   // 16-column tiles of a [*, N] product
-  constexpr int NH = NT / 2;   // ... per half
-  constexpr int TPW = NT / 2;  // carried-state tiles per wave (32 or 16 tiles over 8 waves)
-  __shared__ __attribute__((aligned(16))) float Xs[W * SX];
+  constexpr int NT = N / 16;   // 16-column tiles of the state
+  constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
+  constexpr int YL = W * P / T, CL = W * N / T;  // staged elements per thread
   __shared__ __attribute__((aligned(16))) float Ys[W * SX];
-  __shared__ __attribute__((aligned(16))) float Bs[W * SB];
   __shared__ __attribute__((aligned(16))) float Cs[W * SB];
-  __shared__ __attribute__((aligned(16))) float ST[P * SB];  // G, then the entering state
-  __shared__ __attribute__((aligned(16))) float Ms[W * SM];  // K, then V
-  __shared__ float cs[W], dts[W], ev[W], wv[W];
-  __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
-  __shared__ float rowp[2][W];  // per half: e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
-  __shared__ float dwp[2][W];   // per half: x_s.(G B_s)
-  __shared__ float red8[8];     // per-wave sums
+  __shared__ float ev[W];
 
   const int64_t bh = blockIdx.x;  // (batch, head), head fastest
   const int64_t b = bh / H;
@@ -592,19 +591,8 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
-  const int r0 = 16 * rb;
-  const float Dh = Dv ? Dv[h] : 0.f;
-  // carried adjoint tiles of this wave: rows p = (pb0 + j) 16 + 4 lq + r, columns n = nbw 16 + lr
+  // state tiles of this wave: rows (pb0 + j) 16 + 4 lq + r, columns nbw 16 + lr
   const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
-
-  // per-thread bases of the staged rows: x and dy of step tid / P + (T / P) k, channel
-  // tid % P; B and C of a chunk are one contiguous block (element tid + T k); the block
-  // states of a chunk likewise
-  const int64_t xoff = ((b * L) * H + h) * P + (int64_t)(tid / P) * H * P + tid % P;
-  const int64_t xstep = (int64_t)(T / P) * H * P;
-  const float* const bt = Bm + b * L * N + tid;
-  const float* const ct = Cm + b * L * N + tid;
 
   f32x4 G[TPW];
 #pragma unroll
@@ -612,52 +600,238 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       G[j][r] = dh_final ? dh_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] : 0.f;
-  float dDacc = 0.f;
+
+  // element k of a thread: dy of step tid / P + (T / P) k, channel tid % P; C element
+  // tid + T k of the chunk's contiguous [W, N] block
+  // (32-bit offsets from uniform bases: the sequence of one (batch, head) holds fewer
+  // than 2^31 elements, which the entry point checks)
+  const float* const yb = dy + ((b * L) * H + h) * P;
+  const float* const cb = Cm + b * L * N;
+  const unsigned yoff = (unsigned)((tid / P) * H * P + tid % P);
+  const unsigned ystep = (unsigned)((T / P) * H * P);
+  float ry[YL], rc[CL], rcs = 0.f;
+  auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t t0 = c * W, nv = L - t0;  // valid steps (at least 1, may exceed W)
+    const unsigned y0 = (unsigned)(t0 * H * P) + yoff, c0 = (unsigned)(t0 * N) + (unsigned)tid;
+    if (nv >= W) {  // a whole chunk (uniform): no per-element checks
+#pragma unroll
+      for (int k = 0; k < YL; ++k) ry[k] = yb[y0 + k * ystep];
+#pragma unroll
+      for (int k = 0; k < CL; ++k) rc[k] = cb[c0 + T * k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < YL; ++k) ry[k] = (tid / P + (T / P) * k < nv) ? yb[y0 + k * ystep] : 0.f;
+#pragma unroll
+      for (int k = 0; k < CL; ++k) rc[k] = ((tid + T * k) / N < nv) ? cb[c0 + T * k] : 0.f;
+    }
+    if (tid < W) rcs = dA_cs[(bh * nc + c) * W + tid];
+  };
+  load_chunk(nc - 1);
+  // fragment order: ((wave TPW + j) 4 + r) 64 + lane, P N floats per (batch, head, chunk)
+  float* const gfrag = Gbuf + (int64_t)wave * TPW * 256 + lane;
 
   for (int64_t c = nc - 1; c >= 0; --c) {
-    const int64_t t0 = c * W;
-    // ---- stage x, dy, B, C rows, the chunk's cumsum and weights, and G
-    const int64_t nv = L - t0;  // valid steps of the chunk (may exceed W)
-    {
-      const float* const xc = x + xoff + t0 * H * P;
-      const float* const yc = dy + xoff + t0 * H * P;
-#pragma unroll 2
-      for (int k = 0; k < W * P / T; ++k) {
-        const int sr = tid / P + (T / P) * k, p = tid % P;
-        const bool v = sr < nv;
-        Xs[sr * SX + p] = v ? xc[k * xstep] : 0.f;
-        Ys[sr * SX + p] = v ? yc[k * xstep] : 0.f;
-      }
-      const float* const bc = bt + t0 * N;
-      const float* const cc = ct + t0 * N;
-#pragma unroll 2
-      for (int k = 0; k < W * N / T; ++k) {
-        const int i = tid + T * k, sr = i / N, n = i % N;
-        const bool v = sr < nv;
-        Bs[sr * SB + n] = v ? bc[T * k] : 0.f;
-        Cs[sr * SB + n] = v ? cc[T * k] : 0.f;
+    float* const gc = gfrag + (bh * nc + c) * (int64_t)(P * N);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gc[(j * 4 + r) * 64] = G[j][r];
+#pragma unroll
+    for (int k = 0; k < YL; ++k) {
+      const int i = tid + T * k;
+      Ys[(i / P) * SX + i % P] = ry[k];
+    }
+#pragma unroll
+    for (int k = 0; k < CL; ++k) {
+      const int i = tid + T * k;
+      Cs[(i / N) * SB + i % N] = rc[k];
+    }
+    if (tid < W) ev[tid] = exp2_hw(rcs * kLog2e);
+    __syncthreads();
+    if (c > 0) load_chunk(c - 1);  // in flight during the products below
+
+    // G = e_last G + sum_i dy_i (x) (e_i C_i)  (K = W; e scales the shared B operand)
+    const float el = ev[W - 1];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) G[j] *= el;
+#pragma unroll 1
+    for (int kb = 0; kb < W; kb += 16) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = kb + 4 * lq + m;
+        const float bo = Cs[k * SB + nbw * 16 + lr] * ev[k];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) G[j] = mfma4(Ys[k * SX + (pb0 + j) * 16 + lr], bo, G[j]);
       }
     }
+    __syncthreads();  // the next chunk's staging overwrites both tiles
+  }
+  if (dh0) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dh0[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = G[j][r];
+  }
+}
+
+// the chunk kernel: dx, ddA_cumsum, ddt_out of its heads, dB and dC of its chunk summed
+// over its heads (at dBo / dCo + grp * gstride), dD of each head and chunk into dDp
+template <int N>
+__global__ void __launch_bounds__(kScanThreads)
+ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
+                     const float* __restrict__ dA_cs, const float* __restrict__ Bm,
+                     const float* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ dy,
+                     const float* __restrict__ bstates, const float* __restrict__ Gbuf,
+                     float* __restrict__ dx, float* __restrict__ ddA, float* __restrict__ ddt,
+                     float* __restrict__ dBo, float* __restrict__ dCo, float* __restrict__ dDp, int64_t L, int H,
+                     int64_t nc, int hpg, int ngrp, int64_t gstride) {
+  constexpr int P = kScanP, W = kScanW, T = kScanThreads;
+  constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
+  constexpr int SB = N + 4;
+  constexpr int SM = W + 4;
+  constexpr int NT = N / 16;   // 16-column tiles of a [*, N] product
+  constexpr int NH = NT / 2;   // ... per half
+  constexpr int TPW = NT / 2;  // G fragment tiles per wave
+  constexpr int XL = W * P / T, BL = W * N / T, SL = P * N / T;  // staged elements per thread
+  static_assert(W == 64, "one lane per step of a chunk in the last phase");
+  __shared__ __attribute__((aligned(16))) float Xs[W * SX];
+  __shared__ __attribute__((aligned(16))) float Ys[W * SX];
+  __shared__ __attribute__((aligned(16))) float Bs[W * SB];
+  __shared__ __attribute__((aligned(16))) float Cs[W * SB];
+  __shared__ __attribute__((aligned(16))) float ST[P * SB];  // G, then the entering state
+  __shared__ __attribute__((aligned(16))) float Ms[W * SM];  // C_i.B_s (s <= i), at the end V
+  __shared__ float cs[W], dts[W], ev[W], wv[W];
+  __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
+  __shared__ float rowp[2][W];  // per half: e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
+  __shared__ float dwp[2][W];   // per half: x_s.(G B_s)
+  __shared__ float red8[8];     // per-wave <G, S>
+  __shared__ float redD[8];     // per-wave dy.x
+
+  const int64_t blk = blockIdx.x;  // ((batch, chunk), head group), group fastest
+  const int64_t bcn = blk / ngrp;
+  const int grp = (int)(blk - bcn * ngrp);
+  const int64_t b = bcn / nc, c = bcn - b * nc;
+  const int hlo = grp * hpg, hhi = hlo + hpg < H ? hlo + hpg : H;
+  const int64_t t0 = c * W, nv = L - t0;  // valid steps of the chunk (at least 1, may exceed W)
+  const int nvw = nv < W ? (int)nv : W;   // ... within the chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
+  const int r0 = 16 * rb;
+  const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
+
+  // ---- B and C rows of the chunk (shared by every head), then C_i.B_s of this wave's
+  // causal blocks into Ms (zero where s > i; blocks above the diagonal are never read)
+  {
+    const float* const bp = Bm + (b * L + t0) * N + tid;
+    const float* const cp = Cm + (b * L + t0) * N + tid;
+#pragma unroll 4
+    for (int k = 0; k < BL; ++k) {
+      const int i = tid + T * k;
+      const bool v = i / N < nv;
+      Bs[(i / N) * SB + i % N] = v ? bp[T * k] : 0.f;
+      Cs[(i / N) * SB + i % N] = v ? cp[T * k] : 0.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sb = ph + 2 * u;
+    if (sb > rb) break;  // wave-uniform
+    f32x4 KB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < N; kb += 16) {
+      const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
+      const f32x4 bb = *(const f32x4*)&Bs[(sb * 16 + lr) * SB + kb + 4 * lq];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) KB = mfma4(a[m], bb[m], KB);
+    }
+    const int s = sb * 16 + lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * lq + r;
+      Ms[i * SM + s] = s <= i ? KB[r] : 0.f;
+    }
+  }
+
+  f32x4 DB[NH], DC[NH], VS[2];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) DB[j] = DC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  VS[0] = VS[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // x and dy of head h: element k of a thread is step tid / P + (T / P) k, channel tid % P
+  const int64_t xstep = (int64_t)(T / P) * H * P;
+  const int64_t xrow0 = ((b * L + t0) * H) * P + (int64_t)(tid / P) * H * P + tid % P;
+
+  // the next head's x and dy rows, G fragment and step values, loaded one head ahead
+  float px[XL], py[XL], pc0 = 0.f, pcl = 0.f, pdt = 0.f;
+  f32x4 pG[TPW];
+  auto load_head = [&](int hn) __attribute__((always_inline)) {
+    const int64_t bhn = b * H + hn;
+    const float* const xc = x + xrow0 + (int64_t)hn * P;
+    const float* const yc = dy + xrow0 + (int64_t)hn * P;
+    if (nv >= W) {  // a whole chunk (uniform): no per-element checks
+#pragma unroll
+      for (int k = 0; k < XL; ++k) {
+        px[k] = xc[k * xstep];
+        py[k] = yc[k * xstep];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < XL; ++k) {
+        const bool v = tid / P + (T / P) * k < nv;
+        px[k] = v ? xc[k * xstep] : 0.f;
+        py[k] = v ? yc[k * xstep] : 0.f;
+      }
+    }
+    const float* const gc = Gbuf + (bhn * nc + c) * (int64_t)(P * N) + (int64_t)wave * TPW * 256 + lane;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pG[j][r] = gc[(j * 4 + r) * 64];
     if (tid < W) {
-      const int64_t o = (bh * nc + c) * W;
-      const float ci = dA_cs[o + tid], cl = dA_cs[o + W - 1], dv = dt_out[o + tid];
-      cs[tid] = ci;
-      dts[tid] = dv;
-      ev[tid] = exp2_hw(ci * kLog2e);
-      wv[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
+      const int64_t o = (bhn * nc + c) * W;
+      pc0 = dA_cs[o + tid];
+      pcl = dA_cs[o + W - 1];
+      pdt = dt_out[o + tid];
+    }
+  };
+  if (hlo < hhi) load_head(hlo);
+
+  for (int h = hlo; h < hhi; ++h) {
+    const int64_t bh = b * H + h;
+    // ---- (a) stage x and dy rows, G, the chunk's cumsum and weights
+    if (tid < W) {
+      cs[tid] = pc0;
+      dts[tid] = pdt;
+      ev[tid] = exp2_hw(pc0 * kLog2e);
+      wv[tid] = exp2_hw((pcl - pc0) * kLog2e) * pdt;
+    }
+#pragma unroll
+    for (int k = 0; k < XL; ++k) {
+      const int i = tid + T * k;
+      Xs[(i / P) * SX + i % P] = px[k];
+      Ys[(i / P) * SX + i % P] = py[k];
     }
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = G[j][r];
+      for (int r = 0; r < 4; ++r) ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = pG[j][r];
     __syncthreads();
 
-    // ---- with G: B G^T (columns of half ph) and X G (column tiles of half ph), rows s
-    f32x4 DX[2], DB[NH];
+    // the entering state, loaded now and staged after the G products
+    float rs[SL];
+    {
+      const float* const sc = bstates + (bh * nc + c) * (int64_t)(P * N) + tid;
+#pragma unroll
+      for (int k = 0; k < SL; ++k) rs[k] = sc[T * k];
+    }
+
+    // ---- (b) with G: B G^T (columns of half ph) and diag(w) X G (column tiles of half ph)
+    f32x4 DX[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) DX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NH; ++j) DB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int kb = 0; kb < N; kb += 16) {
       const f32x4 a = *(const f32x4*)&Bs[(r0 + lr) * SB + kb + 4 * lq];
@@ -690,65 +864,52 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
       for (int q = 0; q < 2; ++q) DX[q][r] *= ws;
     }
+    {
+      const float wl = wv[r0 + lr];  // the weight of the A operand's row s = r0 + lr
 #pragma unroll 2
-    for (int kb = 0; kb < P; kb += 16) {
-      const f32x4 a = *(const f32x4*)&Xs[(r0 + lr) * SX + kb + 4 * lq];
+      for (int kb = 0; kb < P; kb += 16) {
+        const f32x4 a = *(const f32x4*)&Xs[(r0 + lr) * SX + kb + 4 * lq] * wl;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
+        for (int m = 0; m < 4; ++m) {
+          const int k = kb + 4 * lq + m;
 #pragma unroll
-        for (int j = 0; j < NH; ++j) DB[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
+          for (int j = 0; j < NH; ++j) DB[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
+        }
       }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ws = wv[r0 + 4 * lq + r];
-#pragma unroll
-      for (int j = 0; j < NH; ++j) DB[j][r] *= ws;
     }
     __syncthreads();  // ST now takes the entering state
-    {
-      const float* const sc = bstates + (bh * nc + c) * P * N + tid;
-#pragma unroll 2
-      for (int k = 0; k < P * N / T; ++k) {
-        const int i = tid + T * k;
-        ST[(i / N) * SB + i % N] = sc[T * k];
-      }
-    }
-    __syncthreads();
 
-    // ---- with S: <G, S>, dY S (column tiles of half ph) and C S^T (columns of half ph)
+    // ---- (c) stage S; each thread also forms its part of <G, S> from the G it replaces
     {
       float gs = 0.f;
 #pragma unroll
-      for (int j = 0; j < TPW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gs = fmaf(G[j][r], ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr], gs);
+      for (int k = 0; k < SL; ++k) {
+        const int i = tid + T * k;
+        float* const pst = &ST[(i / N) * SB + i % N];
+        gs = fmaf(*pst, rs[k], gs);
+        *pst = rs[k];
+      }
       gs = wave_sum(gs);
       if (lane == 0) red8[wave] = gs;
     }
-    f32x4 DC[NH];
-#pragma unroll
-    for (int j = 0; j < NH; ++j) DC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    if (h + 1 < hhi) load_head(h + 1);  // in flight during the products below
+
+    // ---- (d) with S: diag(e) dY S (column tiles of half ph) and C S^T (columns of half ph)
+    {
+      const float el = ev[r0 + lr];  // the weight of the A operand's row i = r0 + lr
 #pragma unroll 2
-    for (int kb = 0; kb < P; kb += 16) {
-      const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq];
+      for (int kb = 0; kb < P; kb += 16) {
+        const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq] * el;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
+        for (int m = 0; m < 4; ++m) {
+          const int k = kb + 4 * lq + m;
 #pragma unroll
-        for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
+          for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
+        }
       }
     }
-    float erow[4], csr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      erow[r] = ev[r0 + 4 * lq + r];
-      csr[r] = cs[r0 + 4 * lq + r];
-#pragma unroll
-      for (int j = 0; j < NH; ++j) DC[j][r] *= erow[r];
-    }
-    float tot[4];
+    float csr[4], tot[4];
     {
       f32x4 P4[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
@@ -763,33 +924,23 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        csr[r] = cs[r0 + 4 * lq + r];
         float rp = 0.f;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           rp = fmaf(P4[q][r], Ys[(r0 + 4 * lq + r) * SX + (2 * ph + q) * 16 + lr], rp);
-        tot[r] = erow[r] * rp;
+        tot[r] = ev[r0 + 4 * lq + r] * rp;
       }
     }
-
-    // ---- intra-chunk: K and Z blocks of rows i (this row block) and step blocks
-    // sb = ph, ph + 2 (those <= rb); the other wave of the row block takes the rest
-    f32x4 VV[2];
+    // Z blocks of rows i (this row block) and step blocks sb = ph, ph + 2 (those <= rb)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int sb = ph + 2 * u;
-      VV[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (sb > rb) {
         if (lq == 0) qcol[rb][sb * 16 + lr] = 0.f;
         continue;
       }
-      f32x4 KB = {0.f, 0.f, 0.f, 0.f}, ZB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int kb = 0; kb < N; kb += 16) {
-        const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
-        const f32x4 bb = *(const f32x4*)&Bs[(sb * 16 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) KB = mfma4(a[m], bb[m], KB);
-      }
+      f32x4 ZB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
       for (int kb = 0; kb < P; kb += 16) {
         const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq];
@@ -803,15 +954,13 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = r0 + 4 * lq + r;
-        const bool v = s <= i;
         // select, not a product with a mask: exp of a positive exponent may be inf
-        const float Lis = v ? exp2_hw((csr[r] - css) * kLog2e) : 0.f;
-        const float Kv = KB[r] * Lis;
+        const float Lis = s <= i ? exp2_hw((csr[r] - css) * kLog2e) : 0.f;
+        const float Kv = Ms[i * SM + s] * Lis;
         const float Qv = Kv * ZB[r];
         tot[r] = fmaf(Qv, dvs, tot[r]);
         colq += Qv;
-        VV[u][r] = ZB[r] * Lis * dvs;
-        Ms[i * SM + s] = Kv;
+        VS[u][r] = fmaf(ZB[r] * Lis, dvs, VS[u][r]);
       }
       colq += __shfl_xor(colq, 16, 64);
       colq += __shfl_xor(colq, 32, 64);
@@ -826,80 +975,54 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) rowp[ph][r0 + 4 * lq + r] = tot[r];
     }
-    __syncthreads();  // K of every row block, qcol, rowp, dwp and <G, S> are in LDS
 
-    // ---- dx of the steps s of this row block (columns of half ph): += dt_s sum_{i >= s} K_is dy_i
+    // ---- (e) dx of the steps s of this row block (columns of half ph):
+    // += dt_s sum_{i >= s} K_is dy_i, with K from C_i.B_s in Ms and the decays here
     {
-      const float dts_l = dts[r0 + lr];
+      const int s = r0 + lr;
+      const float css = cs[s], dts_l = dts[s];
       for (int kb = r0; kb < W; kb += 16) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int k = kb + 4 * lq + m;
-          const float a = Ms[k * SM + r0 + lr] * dts_l;
+          const float lk = k >= s ? exp2_hw((cs[k] - css) * kLog2e) : 0.f;
+          const float a = Ms[k * SM + s] * lk * dts_l;
 #pragma unroll
           for (int q = 0; q < 2; ++q) DX[q] = mfma4(a, Ys[k * SX + (2 * ph + q) * 16 + lr], DX[q]);
         }
       }
     }
-    __syncthreads();  // done with K; Ms takes V
+    {
+      const float Dh = Dv ? Dv[h] : 0.f;
+      float dD = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int sb = ph + 2 * u;
-      if (sb > rb) break;
+      for (int r = 0; r < 4; ++r) {
+        const int sr = r0 + 4 * lq + r;
+        if (sr < nvw) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ms[(r0 + 4 * lq + r) * SM + sb * 16 + lr] = VV[u][r];
-    }
-    __syncthreads();
-    // dC of rows i += sum_{s <= i} V_is B_s;  dB of steps s += sum_{i >= s} V_is C_i
-    for (int kb = 0; kb < r0 + 16; kb += 16) {
-      const f32x4 a = *(const f32x4*)&Ms[(r0 + lr) * SM + kb + 4 * lq];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-#pragma unroll
-        for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], Bs[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
+          for (int q = 0; q < 2; ++q) {
+            const int p = (2 * ph + q) * 16 + lr;
+            const float yv = Ys[sr * SX + p];
+            dx[((b * L + t0 + sr) * H + h) * P + p] = fmaf(Dh, yv, DX[q][r]);
+            dD = fmaf(yv, Xs[sr * SX + p], dD);
+          }
+        }
       }
+      dD = wave_sum(dD);
+      if (lane == 0) redD[wave] = dD;
     }
-    for (int kb = r0; kb < W; kb += 16) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-        const float a = Ms[k * SM + r0 + lr];
-#pragma unroll
-        for (int j = 0; j < NH; ++j) DB[j] = mfma4(a, Cs[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
-      }
-    }
+    __syncthreads();  // qcol, rowp, dwp, <G, S> and dD partials are in LDS; tiles free
 
-    // ---- outputs of the rows and columns of this wave
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int sr = r0 + 4 * lq + r;
-      const int64_t t = t0 + sr;
-      if (t < L) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int p = (2 * ph + q) * 16 + lr;
-          const float yv = Ys[sr * SX + p];
-          dx[((b * L + t) * H + h) * P + p] = fmaf(Dh, yv, DX[q][r]);
-          dDacc = fmaf(yv, Xs[sr * SX + p], dDacc);
-        }
-#pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          dBh[(bh * L + t) * N + (ph * NH + j) * 16 + lr] = DB[j][r];
-          dCh[(bh * L + t) * N + (ph * NH + j) * 16 + lr] = DC[j][r];
-        }
-      }
-    }
-    // gradients of dA_cumsum and dt_out, one thread per step, fixed-order sums
-    if (tid < W) {
-      const int sp = tid;
+    // ---- (f) gradients of dA_cumsum and dt_out, one thread per step, fixed-order sums
+    // (wave 0: lane = step, W = 64; the sums over steps are butterflies of fixed order)
+    if (wave == 0) {
+      const int sp = lane;
       const float qc = ((qcol[0][sp] + qcol[1][sp]) + qcol[2][sp]) + qcol[3][sp];
       const float dw = dwp[0][sp] + dwp[1][sp];
       const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dw, qc);
       float g_cs = (rowp[0][sp] + rowp[1][sp]) - dts[sp] * qc - wv[sp] * dw;
+      const float tw = wave_sum(wv[sp] * dw);  // sum_s w_s x_s.(G B_s)
       if (sp == W - 1) {
-        float tw = 0.f;
-        for (int k = 0; k < W; ++k) tw = fmaf(wv[k], dwp[0][k] + dwp[1][k], tw);
         float gsum = 0.f;
         for (int k = 0; k < 8; ++k) gsum += red8[k];
         g_cs += tw + ev[W - 1] * gsum;
@@ -907,64 +1030,84 @@ ssd_chunk_scan_bwd_kernel(const float* __restrict__ x, const float* __restrict__
       const int64_t o = (bh * nc + c) * W + sp;
       ddA[o] = g_cs;
       ddt[o] = g_dt;
-    }
-
-    // ---- carry: G = e_last G + sum_i dy_i (x) (e_i C_i)  (K = W; e scales the shared B operand)
-    const float el = ev[W - 1];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) G[j] *= el;
-#pragma unroll 2
-    for (int kb = 0; kb < W; kb += 16) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-        const float bo = Cs[k * SB + nbw * 16 + lr] * ev[k];
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) G[j] = mfma4(Ys[k * SX + (pb0 + j) * 16 + lr], bo, G[j]);
+      if (sp == 0) {
+        float sD = 0.f;
+        for (int k = 0; k < 8; ++k) sD += redD[k];
+        dDp[bcn * H + h] = sD;
       }
     }
-    __syncthreads();  // the next chunk's staging overwrites every tile
+    // (the next head's staging may start: every wave is past the barrier above, and
+    // wave 0 finishes these reads before it writes the next head's cs, dts, ev, wv)
   }
-  if (dh0) {
+
+  // ---- the V terms summed over the heads: dC_i += sum_{s <= i} V_is B_s and
+  // dB_s += sum_{i >= s} V_is C_i (Ms is free: every wave passed the last barrier)
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+  for (int u = 0; u < 2; ++u) {
+    const int sb = ph + 2 * u;
+    if (sb > rb) break;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dh0[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = G[j][r];
+    for (int r = 0; r < 4; ++r) Ms[(r0 + 4 * lq + r) * SM + sb * 16 + lr] = VS[u][r];
   }
-  dDacc = wave_sum(dDacc);
-  if (lane == 0) red8[wave] = dDacc;
   __syncthreads();
-  if (tid == 0) {
-    float sD = 0.f;
-    for (int k = 0; k < 8; ++k) sD += red8[k];
-    dDp[bh] = sD;
+  for (int kb = 0; kb < r0 + 16; kb += 16) {
+    const f32x4 a = *(const f32x4*)&Ms[(r0 + lr) * SM + kb + 4 * lq];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int k = kb + 4 * lq + m;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], Bs[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
+    }
+  }
+  for (int kb = r0; kb < W; kb += 16) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int k = kb + 4 * lq + m;
+      const float a = Ms[k * SM + r0 + lr];
+#pragma unroll
+      for (int j = 0; j < NH; ++j) DB[j] = mfma4(a, Cs[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
+    }
+  }
+  float* const dBg = dBo + grp * gstride;
+  float* const dCg = dCo + grp * gstride;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int sr = r0 + 4 * lq + r;
+    if (sr < nvw) {
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        dBg[(b * L + t0 + sr) * N + (ph * NH + j) * 16 + lr] = DB[j][r];
+        dCg[(b * L + t0 + sr) * N + (ph * NH + j) * 16 + lr] = DC[j][r];
+      }
+    }
   }
 }
 
-// dB, dC [batch, seqlen, N]: the per-head values summed in ascending head order;
-// dD [heads]: the per-(batch, head) values summed in ascending batch order
+// dB, dC [batch, seqlen, N]: the head groups' values added in ascending group order
+// (only when a chunk's heads were split over several workgroups)
 __global__ void __launch_bounds__(256)
-ssd_bwd_reduce_kernel(const float* __restrict__ dBh, const float* __restrict__ dCh, const float* __restrict__ dDp,
-                      float* __restrict__ dB, float* __restrict__ dC, float* __restrict__ dD, int64_t batch,
-                      int64_t LN, int H) {
+ssd_bwd_group_sum_kernel(const float* __restrict__ dBp, const float* __restrict__ dCp, float* __restrict__ dB,
+                         float* __restrict__ dC, int64_t nbln, int ngrp) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < batch * LN) {
-    const int64_t b = i / LN, tn = i - b * LN;
-    float sB = 0.f, sC = 0.f;
-    for (int h = 0; h < H; ++h) {
-      const int64_t o = ((b * H + h) * LN) + tn;
-      sB += dBh[o];
-      sC += dCh[o];
-    }
-    dB[i] = sB;
-    dC[i] = sC;
+  if (i >= nbln) return;
+  float sB = 0.f, sC = 0.f;
+  for (int g = 0; g < ngrp; ++g) {
+    sB += dBp[g * nbln + i];
+    sC += dCp[g * nbln + i];
   }
-  if (dD && i < H) {
-    float sD = 0.f;
-    for (int64_t bb = 0; bb < batch; ++bb) sD += dDp[bb * H + i];
-    dD[i] = sD;
-  }
+  dB[i] = sB;
+  dC[i] = sC;
+}
+
+// dD [heads]: one wave per head; lane l adds the per-(batch, chunk) values l, l + 64, ..
+// in ascending order, then the lanes are added by a butterfly of fixed order
+__global__ void __launch_bounds__(64)
+ssd_bwd_dD_kernel(const float* __restrict__ dDp, float* __restrict__ dD, int64_t nbc, int H) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  float s = 0.f;
+  for (int64_t k = lane; k < nbc; k += 64) s += dDp[k * H + h];
+  s = wave_sum(s);
+  if (lane == 0) dD[h] = s;
 }
 
 struct Rng {
@@ -998,6 +1141,38 @@ int ssd_dims(int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk, int so
 
 size_t ws_part_bytes(int64_t batch, int64_t nc, int64_t heads) {
   return ((size_t)batch * (size_t)nc * (size_t)heads * 4 + 255) & ~(size_t)255;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// heads per workgroup of the backward's chunk kernel: all of them unless there are
+// fewer than 128 (batch, chunk) pairs, then split so that about 256 workgroups run
+struct SsdBwdSplit {
+  int hpg, ngrp;
+};
+SsdBwdSplit ssd_bwd_split(int64_t batch, int64_t nc, int64_t heads) {
+  const int64_t bc = batch * nc;
+  int64_t want = bc >= 256 ? 1 : 256 / bc;
+  if (want > heads) want = heads;
+  if (want < 1) want = 1;
+  const int64_t hpg = (heads + want - 1) / want;
+  return SsdBwdSplit{(int)hpg, (int)((heads + hpg - 1) / hpg)};
+}
+
+// the backward's workspace: G of every (batch, head, chunk) [P N floats each], dD per
+// (batch, chunk, head), and the head groups' dB and dC when a chunk's heads are split
+struct SsdBwdLayout {
+  size_t g_bytes, d_bytes, p_bytes, total;
+};
+SsdBwdLayout ssd_bwd_layout(int64_t batch, int64_t seqlen, int64_t heads, int64_t dstate) {
+  const int64_t nc = (seqlen + kScanW - 1) / kScanW;
+  const SsdBwdSplit sp = ssd_bwd_split(batch, nc, heads);
+  SsdBwdLayout l;
+  l.g_bytes = align256((size_t)batch * heads * nc * kScanP * dstate * 4);
+  l.d_bytes = align256((size_t)batch * nc * heads * 4);
+  l.p_bytes = sp.ngrp > 1 ? align256((size_t)sp.ngrp * batch * seqlen * dstate * 4) : 0;
+  l.total = l.g_bytes + l.d_bytes + 2 * l.p_bytes;
+  return l;
 }
 
 }  // namespace
@@ -1122,8 +1297,7 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
 extern "C" size_t ssm_ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                                         int64_t dstate) {
   if (batch < 1 || seqlen < 1 || heads < 1 || dstate < 1) return 0;
-  const size_t part = ((size_t)batch * heads * seqlen * dstate * 4 + 255) & ~(size_t)255;
-  return 2 * part + (((size_t)batch * heads * 4 + 255) & ~(size_t)255);
+  return ssm::ssd_bwd_layout(batch, seqlen, heads, dstate).total;
 }
 
 extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
@@ -1163,23 +1337,30 @@ extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const
     for (int j = i + 1; j < NO; ++j)
       if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
   }
-  const size_t part = ((size_t)batch * heads * seqlen * dstate * 4 + 255) & ~(size_t)255;
-  float* dBh = (float*)workspace;
-  float* dCh = (float*)((char*)workspace + part);
-  float* dDp = (float*)((char*)workspace + 2 * part);
-  const dim3 grid((unsigned)(batch * heads));
-  if (dstate == 128)
-    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<128>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
-                       nc);
-  else
-    hipLaunchKernelGGL(ssd_chunk_scan_bwd_kernel<64>, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D,
-                       dy, block_states, dh_final, dx, ddA_cumsum, ddt_out, dBh, dCh, dDp, dh0, seqlen, (int)heads,
-                       nc);
+  const SsdBwdLayout lay = ssd_bwd_layout(batch, seqlen, heads, dstate);
+  const SsdBwdSplit sp = ssd_bwd_split(batch, nc, heads);
+  float* const Gbuf = (float*)workspace;
+  float* const dDp = (float*)((char*)workspace + lay.g_bytes);
+  float* const dBp = sp.ngrp > 1 ? (float*)((char*)workspace + lay.g_bytes + lay.d_bytes) : dB;
+  float* const dCp = sp.ngrp > 1 ? (float*)((char*)workspace + lay.g_bytes + lay.d_bytes + lay.p_bytes) : dC;
+  const int64_t gstride = sp.ngrp > 1 ? batch * seqlen * dstate : 0;
+  auto carry = dstate == 128 ? ssd_bwd_carry_kernel<128> : ssd_bwd_carry_kernel<64>;
+  hipLaunchKernelGGL(carry, dim3((unsigned)(batch * heads)), dim3(kScanThreads), 0, stream, dA_cumsum, C, dy,
+                     dh_final, Gbuf, dh0, seqlen, (int)heads, nc);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
-  const int64_t LN = seqlen * dstate;
-  const int64_t nthr = batch * LN > heads ? batch * LN : heads;
-  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream, dBh, dCh,
-                     dDp, dB, dC, dD, batch, LN, (int)heads);
+  auto chunk_k = dstate == 128 ? ssd_bwd_chunk_kernel<128> : ssd_bwd_chunk_kernel<64>;
+  hipLaunchKernelGGL(chunk_k, dim3((unsigned)(batch * nc * sp.ngrp)), dim3(kScanThreads), 0, stream, x, dt_out,
+                     dA_cumsum, B, C, D, dy, block_states, Gbuf, dx, ddA_cumsum, ddt_out, dBp, dCp, dDp, seqlen,
+                     (int)heads, nc, sp.hpg, sp.ngrp, gstride);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+  const int64_t nbln = batch * seqlen * dstate;
+  if (sp.ngrp > 1) {
+    hipLaunchKernelGGL(ssd_bwd_group_sum_kernel, dim3((unsigned)((nbln + 255) / 256)), dim3(256), 0, stream, dBp,
+                       dCp, dB, dC, nbln, sp.ngrp);
+    if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
+  }
+  if (dD)
+    hipLaunchKernelGGL(ssd_bwd_dD_kernel, dim3((unsigned)heads), dim3(64), 0, stream, dDp, dD, batch * nc,
+                       (int)heads);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

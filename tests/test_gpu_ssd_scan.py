@@ -169,6 +169,8 @@ BWD_CASES = [
     (2, 1, 2, 128, True, True, False),     # a single step
     (1, 257, 1, 64, True, False, True),    # five chunks, the last of one step
     (2, 512, 4, 128, True, True, True),    # eight chunks
+    (3, 1300, 11, 64, True, True, True),   # heads of a chunk in uneven groups (3, 3, 3, 2), ragged chunk
+    (4, 4096, 2, 64, False, True, True),   # 256 (batch, chunk) pairs: every head in one group
 ]
 
 
@@ -224,8 +226,8 @@ def test_scan_backward_full_workload_sampled_sequences():
 def test_scan_backward_full_length_all_heads_one_batch_element():
     """Every output of the backward at the workload's per-sequence size (L = 2048,
     64 heads of 64, d_state 128, one batch element), including the sums over heads
-    (dB, dC: the single-writer per-head values of deterministic_backward.py's
-    single_writer_kernels, added in a fixed head order) and over time (dD, dA,
+    (dB, dC: one writer per element, as in deterministic_backward.py's
+    single_writer_kernels, the heads added in a fixed order) and over time (dD, dA,
     d_dt_bias), against the sequential fp64 adjoint."""
     w = W.SSD_SCAN_WORKLOADS["ssd_scan_b8_l2048_h64_p64_n128"]
     inp = W.make_ssd_scan_inputs(w, batch=1)
