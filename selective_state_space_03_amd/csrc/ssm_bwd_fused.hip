@@ -122,15 +122,6 @@ __device__ __forceinline__ void rows_sum16(float (&v)[kFT], float (&o)[4]) {
   }
 }
 
-// sum over the 16 lanes of a row, the same in every lane of the row (fixed butterfly)
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dpp_f<kDppQuadXor1>(v);
-  v += dpp_f<kDppQuadXor2>(v);
-  v += dpp_f<0x141>(v);  // row_half_mirror: lane i <-> 7 - i of its half row
-  v += dpp_f<0x140>(v);  // row_mirror: lane i <-> 15 - i
-  return v;
-}
-
 template <typename T, bool GATED, bool CLAMP>
 __global__ void __launch_bounds__(kFThr)
 bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,

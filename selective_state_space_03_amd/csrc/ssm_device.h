@@ -191,6 +191,26 @@ constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppRowBcast0 = 0x150;  // row_newbcast:0 (+t: every lane of a row reads its lane t)
 
+// sum over the 16 lanes of a row, the same value in every lane of the row (a fixed
+// butterfly: quad neighbours, quads, half rows)
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane i <-> 7 - i of its half row
+  v += dpp_f<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
+}
+// sum over the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48), the same value in each:
+// permlane swaps of the halves, then of even and odd rows, ((r0 + r2) + (r1 + r3))
+__device__ __forceinline__ float rows_sum4(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// sum over the 64 lanes of a wave, the same value in every lane, without LDS
+__device__ __forceinline__ float wave_sum64(float v) { return rows_sum4(row_sum16(v)); }
+
 // p[j] in every lane of a 16-lane row -> lane i of the row returns sum over the row of
 // p[i].  Exchanges halve the values held at lane distances 8, 7, 2, 1; lane i keeps
 // the half that its bit 3, 2, 1, 0 selects, so the index it ends with is i itself.

@@ -569,6 +569,66 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 // The row and column sums that two or four waves share go through small LDS arrays
 // added in a fixed order.  G and then S pass through one LDS tile.
 
+
+// Matrix-core product loops of the backward's chunk kernel, with the LDS reads of the
+// next 16-wide reduction step issued before the products of the current one (the
+// reads of a step are independent, so one wait covers them).
+//
+// acc[j] += A T over k = 0 .. 63 for the 16 rows of A at arow (a row of 64 floats,
+// scaled by `scale`) and the column tiles j of T at tcol: step kb takes k = kb + 4 lq + m
+// (m = 0..3) on both operands, so A comes as one 16-byte read and T as 16 b32 reads.
+// arow = the lane's row of A (row lr of the block), tcol = &T[4 lq][first column + lr].
+template <int NJ, int ST_>
+__device__ __forceinline__ void mm_k64(f32x4 (&acc)[NJ], const float* arow, float scale, const float* tcol, int lq) {
+  f32x4 a[2];
+  float bv[2][4][NJ];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if (st == 0) {
+      a[0] = *(const f32x4*)&arow[4 * lq] * scale;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bv[0][m][j] = tcol[m * ST_ + 16 * j];
+    }
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st < 3) {
+      const int kb = 16 * (st + 1);
+      a[nxt] = *(const f32x4*)&arow[kb + 4 * lq] * scale;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bv[nxt][m][j] = tcol[(kb + m) * ST_ + 16 * j];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma4(a[cur][m], bv[cur][m][j], acc[j]);
+  }
+}
+// acc[q] += A B^T over the KN columns of two row-major tiles (both operands 16-byte reads):
+// arow = the lane's row of A + 4 lq, brow[q] = the lane's row of B for column tile q + 4 lq
+template <int KN>
+__device__ __forceinline__ void mm_nt(f32x4 (&acc)[2], const float* arow, const float* brow0, const float* brow1) {
+  f32x4 a[2], b0[2], b1[2];
+  a[0] = *(const f32x4*)&arow[0];
+  b0[0] = *(const f32x4*)&brow0[0];
+  b1[0] = *(const f32x4*)&brow1[0];
+#pragma unroll
+  for (int st = 0; st < KN / 16; ++st) {
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st + 1 < KN / 16) {
+      a[nxt] = *(const f32x4*)&arow[16 * (st + 1)];
+      b0[nxt] = *(const f32x4*)&brow0[16 * (st + 1)];
+      b1[nxt] = *(const f32x4*)&brow1[16 * (st + 1)];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[0] = mfma4(a[cur][m], b0[cur][m], acc[0]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[1] = mfma4(a[cur][m], b1[cur][m], acc[1]);
+  }
+}
+
 // the carry kernel: G of every chunk into Gbuf, dLoss/dh0 into dh0 (if given)
 template <int N>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -832,16 +892,8 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     f32x4 DX[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) DX[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int kb = 0; kb < N; kb += 16) {
-      const f32x4 a = *(const f32x4*)&Bs[(r0 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f32x4 bq = *(const f32x4*)&ST[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) DX[q] = mfma4(a[m], bq[m], DX[q]);
-      }
-    }
+    mm_nt<N>(DX, &Bs[(r0 + lr) * SB + 4 * lq], &ST[(2 * ph * 16 + lr) * SB + 4 * lq],
+             &ST[((2 * ph + 1) * 16 + lr) * SB + 4 * lq]);
     {
       float dwq[4];
 #pragma unroll
@@ -850,8 +902,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           dwq[r] = fmaf(DX[q][r], Xs[(r0 + 4 * lq + r) * SX + (2 * ph + q) * 16 + lr], dwq[r]);
-#pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) dwq[r] += __shfl_xor(dwq[r], msk, 16);
+        dwq[r] = row_sum16(dwq[r]);
       }
       if (lr == 0) {
 #pragma unroll
@@ -866,16 +917,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     }
     {
       const float wl = wv[r0 + lr];  // the weight of the A operand's row s = r0 + lr
-#pragma unroll 2
-      for (int kb = 0; kb < P; kb += 16) {
-        const f32x4 a = *(const f32x4*)&Xs[(r0 + lr) * SX + kb + 4 * lq] * wl;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int k = kb + 4 * lq + m;
-#pragma unroll
-          for (int j = 0; j < NH; ++j) DB[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DB[j]);
-        }
-      }
+      mm_k64<NH, SB>(DB, &Xs[(r0 + lr) * SX], wl, &ST[(4 * lq) * SB + ph * NH * 16 + lr], lq);
     }
     __syncthreads();  // ST now takes the entering state
 
@@ -889,7 +931,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
         gs = fmaf(*pst, rs[k], gs);
         *pst = rs[k];
       }
-      gs = wave_sum(gs);
+      gs = wave_sum64(gs);
       if (lane == 0) red8[wave] = gs;
     }
     __syncthreads();
@@ -898,30 +940,13 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     // ---- (d) with S: diag(e) dY S (column tiles of half ph) and C S^T (columns of half ph)
     {
       const float el = ev[r0 + lr];  // the weight of the A operand's row i = r0 + lr
-#pragma unroll 2
-      for (int kb = 0; kb < P; kb += 16) {
-        const f32x4 a = *(const f32x4*)&Ys[(r0 + lr) * SX + kb + 4 * lq] * el;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int k = kb + 4 * lq + m;
-#pragma unroll
-          for (int j = 0; j < NH; ++j) DC[j] = mfma4(a[m], ST[k * SB + (ph * NH + j) * 16 + lr], DC[j]);
-        }
-      }
+      mm_k64<NH, SB>(DC, &Ys[(r0 + lr) * SX], el, &ST[(4 * lq) * SB + ph * NH * 16 + lr], lq);
     }
     float csr[4], tot[4];
     {
       f32x4 P4[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 2
-      for (int kb = 0; kb < N; kb += 16) {
-        const f32x4 a = *(const f32x4*)&Cs[(r0 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const f32x4 bq = *(const f32x4*)&ST[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) P4[q] = mfma4(a[m], bq[m], P4[q]);
-        }
-      }
+      mm_nt<N>(P4, &Cs[(r0 + lr) * SB + 4 * lq], &ST[(2 * ph * 16 + lr) * SB + 4 * lq],
+               &ST[((2 * ph + 1) * 16 + lr) * SB + 4 * lq]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         csr[r] = cs[r0 + 4 * lq + r];
@@ -962,14 +987,12 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
         colq += Qv;
         VS[u][r] = fmaf(ZB[r] * Lis, dvs, VS[u][r]);
       }
-      colq += __shfl_xor(colq, 16, 64);
-      colq += __shfl_xor(colq, 32, 64);
+      colq = rows_sum4(colq);
       if (lq == 0) qcol[rb][s] = colq;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) tot[r] += __shfl_xor(tot[r], msk, 16);
+      tot[r] = row_sum16(tot[r]);
     }
     if (lr == 0) {
 #pragma unroll
@@ -1008,7 +1031,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
           }
         }
       }
-      dD = wave_sum(dD);
+      dD = wave_sum64(dD);
       if (lane == 0) redD[wave] = dD;
     }
     __syncthreads();  // qcol, rowp, dwp, <G, S> and dD partials are in LDS; tiles free
@@ -1021,7 +1044,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
       const float dw = dwp[0][sp] + dwp[1][sp];
       const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dw, qc);
       float g_cs = (rowp[0][sp] + rowp[1][sp]) - dts[sp] * qc - wv[sp] * dw;
-      const float tw = wave_sum(wv[sp] * dw);  // sum_s w_s x_s.(G B_s)
+      const float tw = wave_sum64(wv[sp] * dw);  // sum_s w_s x_s.(G B_s)
       if (sp == W - 1) {
         float gsum = 0.f;
         for (int k = 0; k < 8; ++k) gsum += red8[k];
