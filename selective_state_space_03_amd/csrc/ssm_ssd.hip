@@ -572,7 +572,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 
 // Matrix-core product loops of the backward's chunk kernel, with the LDS reads of the
 // next 16-wide reduction step issued before the products of the current one (the
-// reads of a step are independent, so one wait covers them).
+// reads of a step are independent, so one wait covers them).  Scheduling barriers keep
+// the compiler from moving the reads back next to their products.
 //
 // acc[j] += A T over k = 0 .. 63 for the 16 rows of A at arow (a row of 64 floats,
 // scaled by `scale`) and the column tiles j of T at tcol: step kb takes k = kb + 4 lq + m
@@ -604,6 +605,9 @@ __device__ __forceinline__ void mm_k64(f32x4 (&acc)[NJ], const float* arow, floa
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j] = mfma4(a[cur][m], bv[cur][m][j], acc[j]);
+    // the next step's LDS reads go out before this step's products
+    if (st < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1 + 2 * NJ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ, 0);
   }
 }
 // acc[q] += A B^T over the KN columns of two row-major tiles (both operands 16-byte reads):
@@ -626,6 +630,9 @@ __device__ __forceinline__ void mm_nt(f32x4 (&acc)[2], const float* arow, const 
     for (int m = 0; m < 4; ++m) acc[0] = mfma4(a[cur][m], b0[cur][m], acc[0]);
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[1] = mfma4(a[cur][m], b1[cur][m], acc[1]);
+    // the next step's LDS reads go out before this step's products
+    if (st + 1 < KN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
 }
 
@@ -760,7 +767,10 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   __shared__ __attribute__((aligned(16))) float Bs[W * SB];
   __shared__ __attribute__((aligned(16))) float Cs[W * SB];
   __shared__ __attribute__((aligned(16))) float ST[P * SB];  // G, then the entering state
-  __shared__ __attribute__((aligned(16))) float Ms[W * SM];  // C_i.B_s (s <= i), at the end V
+  // Ms: below the diagonal C_i.B_s (s < i, the same for every head); on and above it the
+  // head's K transposed, Ms[s][i] = K_is (s <= i); at the end the V sums.  cbd: C_i.B_i.
+  __shared__ __attribute__((aligned(16))) float Ms[W * SM];
+  __shared__ float cbd[W];
   __shared__ float cs[W], dts[W], ev[W], wv[W];
   __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
   __shared__ float rowp[2][W];  // per half: e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
@@ -783,7 +793,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
 
   // ---- B and C rows of the chunk (shared by every head), then C_i.B_s of this wave's
-  // causal blocks into Ms (zero where s > i; blocks above the diagonal are never read)
+  // causal blocks into Ms below the diagonal and cbd on it
   {
     const float* const bp = Bm + (b * L + t0) * N + tid;
     const float* const cp = Cm + (b * L + t0) * N + tid;
@@ -812,7 +822,8 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r0 + 4 * lq + r;
-      Ms[i * SM + s] = s <= i ? KB[r] : 0.f;
+      if (s < i) Ms[i * SM + s] = KB[r];
+      if (s == i) cbd[i] = KB[r];
     }
   }
 
@@ -981,11 +992,13 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
         const int i = r0 + 4 * lq + r;
         // select, not a product with a mask: exp of a positive exponent may be inf
         const float Lis = s <= i ? exp2_hw((csr[r] - css) * kLog2e) : 0.f;
-        const float Kv = Ms[i * SM + s] * Lis;
+        const float cb = s < i ? Ms[i * SM + s] : (s == i ? cbd[i] : 0.f);
+        const float Kv = cb * Lis;
         const float Qv = Kv * ZB[r];
         tot[r] = fmaf(Qv, dvs, tot[r]);
         colq += Qv;
         VS[u][r] = fmaf(ZB[r] * Lis, dvs, VS[u][r]);
+        if (s <= i) Ms[s * SM + i] = Kv;  // K transposed, for the dx products below
       }
       colq = rows_sum4(colq);
       if (lq == 0) qcol[rb][s] = colq;
@@ -999,19 +1012,30 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
       for (int r = 0; r < 4; ++r) rowp[ph][r0 + 4 * lq + r] = tot[r];
     }
 
+    __syncthreads();  // K of every causal block is in Ms
+
     // ---- (e) dx of the steps s of this row block (columns of half ph):
-    // += dt_s sum_{i >= s} K_is dy_i, with K from C_i.B_s in Ms and the decays here
+    // += dt_s sum_{i >= s} K_is dy_i, K^T rows from Ms (16-byte reads)
     {
       const int s = r0 + lr;
-      const float css = cs[s], dts_l = dts[s];
-      for (int kb = r0; kb < W; kb += 16) {
+      const float dts_l = dts[s];
+#pragma unroll
+      for (int kbi = 0; kbi < 4; ++kbi) {
+        if (kbi >= 4 - rb) break;  // wave-uniform: blocks rb .. 3
+        const int kb = r0 + 16 * kbi;
+        f32x4 a = *(const f32x4*)&Ms[s * SM + kb + 4 * lq];
+        float yv[4][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) yv[m][q] = Ys[(kb + 4 * lq + m) * SX + (2 * ph + q) * 16 + lr];
+        __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const int k = kb + 4 * lq + m;
-          const float lk = k >= s ? exp2_hw((cs[k] - css) * kLog2e) : 0.f;
-          const float a = Ms[k * SM + s] * lk * dts_l;
+          // below the diagonal of the first block Ms holds C.B, not K: those terms are 0
+          const float am = (kbi > 0 || kb + 4 * lq + m >= s) ? a[m] * dts_l : 0.f;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) DX[q] = mfma4(a, Ys[k * SX + (2 * ph + q) * 16 + lr], DX[q]);
+          for (int q = 0; q < 2; ++q) DX[q] = mfma4(am, yv[m][q], DX[q]);
         }
       }
     }
