@@ -643,14 +643,15 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
                      const float* __restrict__ dh_final, float* __restrict__ Gbuf, float* __restrict__ dh0,
                      int64_t L, int H, int64_t nc) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
-  constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
-  constexpr int SB = N + 4;
+  constexpr int SW = W + 4;    // row stride (floats) of the transposed LDS tiles
   constexpr int NT = N / 16;   // 16-column tiles of the state
   constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
   constexpr int YL = W * P / T, CL = W * N / T;  // staged elements per thread
-  __shared__ __attribute__((aligned(16))) float Ys[W * SX];
-  __shared__ __attribute__((aligned(16))) float Cs[W * SB];
-  __shared__ float ev[W];
+  // dy and C of the chunk transposed ([channel][step], [state][step]): both operands of
+  // the update are then 16-byte reads along the steps
+  __shared__ __attribute__((aligned(16))) float YT[P * SW];
+  __shared__ __attribute__((aligned(16))) float CT[N * SW];
+  __shared__ __attribute__((aligned(16))) float ev[W];
 
   const int64_t bh = blockIdx.x;  // (batch, head), head fastest
   const int64_t b = bh / H;
@@ -670,27 +671,20 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
 
   // element k of a thread: dy of step tid / P + (T / P) k, channel tid % P; C element
   // tid + T k of the chunk's contiguous [W, N] block
-  // (32-bit offsets from uniform bases: the sequence of one (batch, head) holds fewer
-  // than 2^31 elements, which the entry point checks)
-  const float* const yb = dy + ((b * L) * H + h) * P;
-  const float* const cb = Cm + b * L * N;
-  const unsigned yoff = (unsigned)((tid / P) * H * P + tid % P);
-  const unsigned ystep = (unsigned)((T / P) * H * P);
+  // Loads go through buffer resources with uniform bases and 32-bit lane offsets; a
+  // chunk's range ends after its last valid step, so rows past the end read 0.
+  const unsigned yoff = (unsigned)((tid / P) * H * P + tid % P) * 4u;
+  const unsigned ystep4 = (unsigned)((T / P) * H * P) * 4u;
   float ry[YL], rc[CL], rcs = 0.f;
   auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W, nv = L - t0;  // valid steps (at least 1, may exceed W)
-    const unsigned y0 = (unsigned)(t0 * H * P) + yoff, c0 = (unsigned)(t0 * N) + (unsigned)tid;
-    if (nv >= W) {  // a whole chunk (uniform): no per-element checks
+    const int nvw = nv < W ? (int)nv : W;
+    const auto rdy = tile_rsrc(dy + ((b * L + t0) * H + h) * P, ((int64_t)(nvw - 1) * H * P + P) * 4);
+    const auto rcm = tile_rsrc(Cm + (b * L + t0) * N, (int64_t)nvw * N * 4);
 #pragma unroll
-      for (int k = 0; k < YL; ++k) ry[k] = yb[y0 + k * ystep];
+    for (int k = 0; k < YL; ++k) ry[k] = buf_ld<float>(rdy, yoff + k * ystep4);
 #pragma unroll
-      for (int k = 0; k < CL; ++k) rc[k] = cb[c0 + T * k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < YL; ++k) ry[k] = (tid / P + (T / P) * k < nv) ? yb[y0 + k * ystep] : 0.f;
-#pragma unroll
-      for (int k = 0; k < CL; ++k) rc[k] = ((tid + T * k) / N < nv) ? cb[c0 + T * k] : 0.f;
-    }
+    for (int k = 0; k < CL; ++k) rc[k] = buf_ld<float>(rcm, (unsigned)(tid + T * k) * 4u);
     if (tid < W) rcs = dA_cs[(bh * nc + c) * W + tid];
   };
   load_chunk(nc - 1);
@@ -706,12 +700,12 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
 #pragma unroll
     for (int k = 0; k < YL; ++k) {
       const int i = tid + T * k;
-      Ys[(i / P) * SX + i % P] = ry[k];
+      YT[(i % P) * SW + i / P] = ry[k];
     }
 #pragma unroll
     for (int k = 0; k < CL; ++k) {
       const int i = tid + T * k;
-      Cs[(i / N) * SB + i % N] = rc[k];
+      CT[(i % N) * SW + i / N] = rc[k];
     }
     if (tid < W) ev[tid] = exp2_hw(rcs * kLog2e);
     __syncthreads();
@@ -721,15 +715,18 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
     const float el = ev[W - 1];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) G[j] *= el;
+    // steps k = kb + 4 lq + m (m = 0..3) of both operands from one 16-byte read each
 #pragma unroll 1
     for (int kb = 0; kb < W; kb += 16) {
+      const f32x4 bo = *(const f32x4*)&CT[(nbw * 16 + lr) * SW + kb + 4 * lq] *
+                       *(const f32x4*)&ev[kb + 4 * lq];
+      f32x4 ao[TPW];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-        const float bo = Cs[k * SB + nbw * 16 + lr] * ev[k];
+      for (int j = 0; j < TPW; ++j) ao[j] = *(const f32x4*)&YT[((pb0 + j) * 16 + lr) * SW + kb + 4 * lq];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) G[j] = mfma4(Ys[k * SX + (pb0 + j) * 16 + lr], bo, G[j]);
-      }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) G[j] = mfma4(ao[j][m], bo[m], G[j]);
     }
     __syncthreads();  // the next chunk's staging overwrites both tiles
   }
