@@ -86,14 +86,17 @@
  *   ddA_cumsum, ddt_out   : [batch, heads, chunks, chunk], the gradients of dA_cumsum and
  *                           dt_out; ssm_ssd_chunk_cumsum_bwd turns them into the
  *                           gradients of dt, A and dt_bias
- *   dB, dC                : [batch, seqlen, d_state], summed over heads in ascending
- *                           head order from per-head values (one writer each, no atomics)
- *   dD                    : [heads], summed over batch in ascending order (may be NULL)
+ *   dB, dC                : [batch, seqlen, d_state], summed over the heads in a fixed
+ *                           order inside the workgroup of each (batch, chunk) (one writer
+ *                           each, no atomics)
+ *   dD                    : [heads], summed over (batch, chunk) in ascending order (may be NULL)
  *   dh0                   : [batch, heads, headdim, d_state], dLoss/dh0 (may be NULL)
  * dh_final may be NULL (zero).  D may be NULL (no skip term; dD is then still the
  * gradient of a skip weight).  block_states is required.  The workspace holds the
- * per-head dB, dC and the per-(batch, head) dD: ssm_ssd_chunk_scan_bwd_workspace_bytes,
- * 256-byte aligned, contents on entry ignored.  Supported: headdim 64, d_state 64 or
+ * state adjoint G of every (batch, head, chunk) ([headdim, d_state] fp32 each), dD per
+ * (batch, chunk, head), and, when there are fewer than 128 (batch, chunk) pairs and the
+ * heads of a chunk are split over several workgroups, each group's dB and dC:
+ * ssm_ssd_chunk_scan_bwd_workspace_bytes, 256-byte aligned, contents on entry ignored.  Supported: headdim 64, d_state 64 or
  * 128, chunk 64 (SSM_ERR_UNSUPPORTED otherwise).  Results are bit-identical from run
  * to run.  Errors as for the forward, plus SSM_ERR_WORKSPACE.
  */
