@@ -321,7 +321,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   constexpr int NT = N / 16;   // 16-column state tiles
   constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
   constexpr int XL = W * P / T, BL = W * N / T;  // staged elements per thread
-  __shared__ __attribute__((aligned(16))) float Xs[W * SX];
+  __shared__ __attribute__((aligned(16))) float XT[P * SM];  // x transposed: [channel][step]
   __shared__ __attribute__((aligned(16))) float Bs[W * SB];
   __shared__ __attribute__((aligned(16))) float Cs[W * SB];
   __shared__ __attribute__((aligned(16))) float Ss[P * SB];
@@ -390,7 +390,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll
     for (int k = 0; k < XL; ++k) {
       const int i = tid + T * k;
-      Xs[(i / P) * SX + i % P] = rx[k];
+      XT[(i % P) * SM + i / P] = rx[k];
     }
 #pragma unroll
     for (int k = 0; k < BL; ++k) {
@@ -482,13 +482,15 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     }
     __syncthreads();
     // ---- Y += M X over the step blocks s <= these rows, skip term, store
+    // (both operands along the steps: 16-byte reads of M's rows and of x transposed)
     for (int kb = 0; kb < 16 * (rb + 1); kb += 16) {
       const f32x4 a = *(const f32x4*)&Ms[(i0 + lr) * SM + kb + 4 * lq];
+      const f32x4 x0 = *(const f32x4*)&XT[(2 * ph * 16 + lr) * SM + kb + 4 * lq];
+      const f32x4 x1 = *(const f32x4*)&XT[((2 * ph + 1) * 16 + lr) * SM + kb + 4 * lq];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) Y[q] = mfma4(a[m], Xs[k * SX + (2 * ph + q) * 16 + lr], Y[q]);
+        Y[0] = mfma4(a[m], x0[m], Y[0]);
+        Y[1] = mfma4(a[m], x1[m], Y[1]);
       }
     }
     // y[b, t0 + i, h, p] for i = i0 + 4 (l / 16) + r, p = (2 ph + q) 16 + l % 16
@@ -501,7 +503,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       if (whole || t0 + i < L) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          yrow[r * ystep + q * 16] = fmaf(Dh, Xs[i * SX + (2 * ph + q) * 16 + lr], Y[q][r]);
+          yrow[r * ystep + q * 16] = fmaf(Dh, XT[((2 * ph + q) * 16 + lr) * SM + i], Y[q][r]);
       }
     }
     // ---- state: S = exp(cs_last) S + X^T (wd B)  (the step weight scales the B operand,
@@ -512,12 +514,15 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 #pragma unroll 2
     for (int kb = 0; kb < W; kb += 16) {
       const f32x4 w4 = *(const f32x4*)&wd[kb + 4 * lq];
+      f32x4 xa[TPW];
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) xa[j] = *(const f32x4*)&XT[((pb0 + j) * 16 + lr) * SM + kb + 4 * lq];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int k = kb + 4 * lq + m;
         const float bo = Bs[k * SB + nbw * 16 + lr] * w4[m];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) S[j] = mfma4(Xs[k * SX + (pb0 + j) * 16 + lr], bo, S[j]);
+        for (int j = 0; j < TPW; ++j) S[j] = mfma4(xa[j][m], bo, S[j]);
       }
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
