@@ -306,6 +306,92 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Matrix-core product loops of the scan kernels, with the LDS reads of the
+// next 16-wide reduction step issued before the products of the current one (the
+// reads of a step are independent, so one wait covers them).  Scheduling barriers keep
+// the compiler from moving the reads back next to their products.
+//
+// acc[j] += A T over k = 0 .. 63 for the 16 rows of A at arow (a row of 64 floats,
+// scaled by `scale`) and the column tiles j of T at tcol: step kb takes k = kb + 4 lq + m
+// (m = 0..3) on both operands, so A comes as one 16-byte read and T as 16 b32 reads.
+// arow = the lane's row of A (row lr of the block), tcol = &T[4 lq][first column + lr].
+template <int NJ, int ST_>
+__device__ __forceinline__ void mm_k64(f32x4 (&acc)[NJ], const float* arow, float scale, const float* tcol, int lq) {
+  f32x4 a[2];
+  float bv[2][4][NJ];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if (st == 0) {
+      a[0] = *(const f32x4*)&arow[4 * lq] * scale;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bv[0][m][j] = tcol[m * ST_ + 16 * j];
+    }
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st < 3) {
+      const int kb = 16 * (st + 1);
+      a[nxt] = *(const f32x4*)&arow[kb + 4 * lq] * scale;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bv[nxt][m][j] = tcol[(kb + m) * ST_ + 16 * j];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma4(a[cur][m], bv[cur][m][j], acc[j]);
+    // the next step's LDS reads go out before this step's products
+    if (st < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1 + 2 * NJ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ, 0);
+  }
+}
+// acc[q] += A B^T over the KN columns of two row-major tiles (both operands 16-byte reads):
+// arow = the lane's row of A + 4 lq, brow[q] = the lane's row of B for column tile q + 4 lq
+template <int KN>
+__device__ __forceinline__ void mm_nt(f32x4 (&acc)[2], const float* arow, const float* brow0, const float* brow1) {
+  f32x4 a[2], b0[2], b1[2];
+  a[0] = *(const f32x4*)&arow[0];
+  b0[0] = *(const f32x4*)&brow0[0];
+  b1[0] = *(const f32x4*)&brow1[0];
+#pragma unroll
+  for (int st = 0; st < KN / 16; ++st) {
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st + 1 < KN / 16) {
+      a[nxt] = *(const f32x4*)&arow[16 * (st + 1)];
+      b0[nxt] = *(const f32x4*)&brow0[16 * (st + 1)];
+      b1[nxt] = *(const f32x4*)&brow1[16 * (st + 1)];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[0] = mfma4(a[cur][m], b0[cur][m], acc[0]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[1] = mfma4(a[cur][m], b1[cur][m], acc[1]);
+    // the next step's LDS reads go out before this step's products
+    if (st + 1 < KN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+}
+
+// acc += A B^T over KN columns for one B tile (as mm_nt)
+template <int KN>
+__device__ __forceinline__ void mm_nt1(f32x4& acc, const float* arow, const float* brow) {
+  f32x4 a[2], b0[2];
+  a[0] = *(const f32x4*)&arow[0];
+  b0[0] = *(const f32x4*)&brow[0];
+#pragma unroll
+  for (int st = 0; st < KN / 16; ++st) {
+    const int cur = st & 1, nxt = cur ^ 1;
+    if (st + 1 < KN / 16) {
+      a[nxt] = *(const f32x4*)&arow[16 * (st + 1)];
+      b0[nxt] = *(const f32x4*)&brow[16 * (st + 1)];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = mfma4(a[cur][m], b0[cur][m], acc);
+    if (st + 1 < KN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+}
+
 template <int N, bool SAVE>
 __global__ void __launch_bounds__(kScanThreads)
 ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
@@ -427,16 +513,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     // Products over n go in 16-wide blocks whose 4 MFMA steps take n = kb + 4 (l / 16)
     // + m (m = 0..3) on both operands: any assignment of the sum's terms to steps gives
     // the same sum, and this one lets a lane read its 4 operands as one 16-byte load.
-#pragma unroll 2
-    for (int kb = 0; kb < N; kb += 16) {
-      const f32x4 a = *(const f32x4*)&Cs[(i0 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f32x4 bq = *(const f32x4*)&Ss[((2 * ph + q) * 16 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) Y[q] = mfma4(a[m], bq[m], Y[q]);
-      }
-    }
+    mm_nt<N>(Y, &Cs[(i0 + lr) * SB + 4 * lq], &Ss[(2 * ph * 16 + lr) * SB + 4 * lq],
+             &Ss[((2 * ph + 1) * 16 + lr) * SB + 4 * lq]);
     float ecs[4], csr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -451,20 +529,13 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     {
       const bool two = ph + 2 <= rb;  // wave-uniform
       if (ph <= rb) {
-        f32x4 G0 = {0.f, 0.f, 0.f, 0.f}, G1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 GG[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         const int s0 = ph * 16, s1 = (ph + 2) * 16;
-#pragma unroll 2
-        for (int kb = 0; kb < N; kb += 16) {
-          const f32x4 a = *(const f32x4*)&Cs[(i0 + lr) * SB + kb + 4 * lq];
-          const f32x4 b0 = *(const f32x4*)&Bs[(s0 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) G0 = mfma4(a[m], b0[m], G0);
-          if (two) {
-            const f32x4 b1 = *(const f32x4*)&Bs[(s1 + lr) * SB + kb + 4 * lq];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) G1 = mfma4(a[m], b1[m], G1);
-          }
-        }
+        if (two)
+          mm_nt<N>(GG, &Cs[(i0 + lr) * SB + 4 * lq], &Bs[(s0 + lr) * SB + 4 * lq], &Bs[(s1 + lr) * SB + 4 * lq]);
+        else
+          mm_nt1<N>(GG[0], &Cs[(i0 + lr) * SB + 4 * lq], &Bs[(s0 + lr) * SB + 4 * lq]);
+        const f32x4 G0 = GG[0], G1 = GG[1];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           if (u == 1 && !two) break;
@@ -574,72 +645,6 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
 // The row and column sums that two or four waves share go through small LDS arrays
 // added in a fixed order.  G and then S pass through one LDS tile.
 
-
-// Matrix-core product loops of the backward's chunk kernel, with the LDS reads of the
-// next 16-wide reduction step issued before the products of the current one (the
-// reads of a step are independent, so one wait covers them).  Scheduling barriers keep
-// the compiler from moving the reads back next to their products.
-//
-// acc[j] += A T over k = 0 .. 63 for the 16 rows of A at arow (a row of 64 floats,
-// scaled by `scale`) and the column tiles j of T at tcol: step kb takes k = kb + 4 lq + m
-// (m = 0..3) on both operands, so A comes as one 16-byte read and T as 16 b32 reads.
-// arow = the lane's row of A (row lr of the block), tcol = &T[4 lq][first column + lr].
-template <int NJ, int ST_>
-__device__ __forceinline__ void mm_k64(f32x4 (&acc)[NJ], const float* arow, float scale, const float* tcol, int lq) {
-  f32x4 a[2];
-  float bv[2][4][NJ];
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    if (st == 0) {
-      a[0] = *(const f32x4*)&arow[4 * lq] * scale;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) bv[0][m][j] = tcol[m * ST_ + 16 * j];
-    }
-    const int cur = st & 1, nxt = cur ^ 1;
-    if (st < 3) {
-      const int kb = 16 * (st + 1);
-      a[nxt] = *(const f32x4*)&arow[kb + 4 * lq] * scale;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) bv[nxt][m][j] = tcol[(kb + m) * ST_ + 16 * j];
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] = mfma4(a[cur][m], bv[cur][m][j], acc[j]);
-    // the next step's LDS reads go out before this step's products
-    if (st < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1 + 2 * NJ, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ, 0);
-  }
-}
-// acc[q] += A B^T over the KN columns of two row-major tiles (both operands 16-byte reads):
-// arow = the lane's row of A + 4 lq, brow[q] = the lane's row of B for column tile q + 4 lq
-template <int KN>
-__device__ __forceinline__ void mm_nt(f32x4 (&acc)[2], const float* arow, const float* brow0, const float* brow1) {
-  f32x4 a[2], b0[2], b1[2];
-  a[0] = *(const f32x4*)&arow[0];
-  b0[0] = *(const f32x4*)&brow0[0];
-  b1[0] = *(const f32x4*)&brow1[0];
-#pragma unroll
-  for (int st = 0; st < KN / 16; ++st) {
-    const int cur = st & 1, nxt = cur ^ 1;
-    if (st + 1 < KN / 16) {
-      a[nxt] = *(const f32x4*)&arow[16 * (st + 1)];
-      b0[nxt] = *(const f32x4*)&brow0[16 * (st + 1)];
-      b1[nxt] = *(const f32x4*)&brow1[16 * (st + 1)];
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[0] = mfma4(a[cur][m], b0[cur][m], acc[0]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[1] = mfma4(a[cur][m], b1[cur][m], acc[1]);
-    // the next step's LDS reads go out before this step's products
-    if (st + 1 < KN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  }
-}
 
 // the carry kernel: G of every chunk into Gbuf, dLoss/dh0 into dh0 (if given)
 template <int N>
