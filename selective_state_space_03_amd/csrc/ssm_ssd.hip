@@ -582,16 +582,19 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     const float el = exp2_hw(cs[W - 1] * kLog2e);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) S[j] *= el;
-#pragma unroll 2
+#pragma unroll
     for (int kb = 0; kb < W; kb += 16) {
       const f32x4 w4 = *(const f32x4*)&wd[kb + 4 * lq];
       f32x4 xa[TPW];
+      float bv[4];
 #pragma unroll
       for (int j = 0; j < TPW; ++j) xa[j] = *(const f32x4*)&XT[((pb0 + j) * 16 + lr) * SM + kb + 4 * lq];
 #pragma unroll
+      for (int m = 0; m < 4; ++m) bv[m] = Bs[(kb + 4 * lq + m) * SB + nbw * 16 + lr];
+      __builtin_amdgcn_sched_group_barrier(0x100, TPW + 5, 0);  // this step's reads together
+#pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int k = kb + 4 * lq + m;
-        const float bo = Bs[k * SB + nbw * 16 + lr] * w4[m];
+        const float bo = bv[m] * w4[m];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) S[j] = mfma4(xa[j][m], bo, S[j]);
       }
