@@ -92,10 +92,11 @@ def ssd_scan_bytes(b, l, h, p, n, nc, w):
 
 def ssd_scan_flops(b, l, h, p, n, nc, w):
     """useful multiply-adds of the chunked form, x2: per (batch, head, chunk) the
-    inter-chunk readout C S^T (w n p), the causal C B^T (w (w + 1) / 2 pairs, n each),
-    the causal M X (w (w + 1) / 2 pairs, p each) and the state update X^T B (w p n)"""
+    inter-chunk readout C S^T (w n p), the causal M X (w (w + 1) / 2 pairs, p each) and
+    the state update X^T B (w p n); per (batch, chunk) the causal C B^T (w (w + 1) / 2
+    pairs, n each), which the heads share (one B, C group)"""
     tri = w * (w + 1) // 2
-    return 2 * b * h * nc * (w * n * p + tri * n + tri * p + w * p * n)
+    return 2 * b * h * nc * (w * n * p + tri * p + w * p * n) + 2 * b * nc * tri * n
 
 
 def ssd_scan_bwd_bytes(b, l, h, p, n, nc, w):
@@ -494,13 +495,16 @@ def main():
         base["cs"], base["dto"] = ops.ssd_chunk_cumsum_fwd(t32(inp["dt"]), A, w.chunk, dt_bias=dtb)
         sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
         Dv = t32(inp["D"])
+        wsb = ops.ssd_chunk_scan_fwd_workspace_bytes(w.batch, w.seqlen, w.dstate)
         outs = [(torch.empty_like(base["x"]),
-                 torch.empty((w.batch, w.heads, w.headdim, w.dstate), dtype=torch.float32, device=dev))
+                 torch.empty((w.batch, w.heads, w.headdim, w.dstate), dtype=torch.float32, device=dev),
+                 torch.empty((wsb,), dtype=torch.uint8, device=dev))
                 for _ in range(nsets)]
 
         def fn(i):
             s = sets[i]
-            ops.ssd_chunk_scan_fwd(s["x"], s["dto"], s["cs"], s["B"], s["C"], D=Dv, y=outs[i][0], h_final=outs[i][1])
+            ops.ssd_chunk_scan_fwd(s["x"], s["dto"], s["cs"], s["B"], s["C"], D=Dv, y=outs[i][0], h_final=outs[i][1],
+                                   workspace=outs[i][2])
 
         wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
         gbs = nb / (ev_ms * 1e-3) / 1e9

@@ -71,10 +71,15 @@
  *                           below reads instead of recomputing it)
  * Supported: headdim 64, d_state 64 or 128, chunk a multiple of 64 (SSM_ERR_UNSUPPORTED
  * otherwise); a chunk is walked in blocks of 64 steps.
+ * workspace             : ssm_ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, d_state)
+ *                           bytes, 256-byte aligned, contents on entry ignored: the
+ *                           products C_i.B_s of every 64-step block, [batch, blocks, 64,
+ *                           64] fp32, computed once and shared by all heads
  * Pointers are device pointers, 4-byte aligned.  Outputs must not overlap inputs or
  * each other.  Nothing is allocated; work goes to `stream`.
  * Errors: SSM_ERR_NULL, SSM_ERR_DIM (a size < 1, 2^31 elements or more in one tensor,
- * batch * heads >= 2^31), SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN, SSM_ERR_ALIAS, SSM_ERR_HIP.
+ * batch * heads >= 2^31), SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN, SSM_ERR_ALIAS,
+ * SSM_ERR_WORKSPACE (NULL, smaller than the size above or misaligned), SSM_ERR_HIP.
  */
 /*
  * ssm_ssd_chunk_scan_bwd -- the gradients of ssm_ssd_chunk_scan_fwd for the loss
@@ -120,9 +125,10 @@ int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, const float
                              size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t heads, int64_t chunk,
                              int dt_softplus, float dt_min, float dt_max, hipStream_t stream);
 
+size_t ssm_ssd_chunk_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dstate);
 int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
                            const float* C, const float* D, const float* h0, float* y, float* h_final,
-                           float* block_states, int64_t batch,
+                           float* block_states, void* workspace, size_t workspace_bytes, int64_t batch,
                            int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t chunk,
                            hipStream_t stream);
 

@@ -372,23 +372,47 @@ __device__ __forceinline__ void mm_nt(f32x4 (&acc)[2], const float* arow, const 
   }
 }
 
-// acc += A B^T over KN columns for one B tile (as mm_nt)
-template <int KN>
-__device__ __forceinline__ void mm_nt1(f32x4& acc, const float* arow, const float* brow) {
-  f32x4 a[2], b0[2];
-  a[0] = *(const f32x4*)&arow[0];
-  b0[0] = *(const f32x4*)&brow[0];
+// C_i.B_s of every 64-step block, which all heads share (one B, C group): CB[b, blk, i, s]
+// for s <= i (entries above the diagonal are not written and never read).  One
+// workgroup of 8 waves per (batch, block); wave (rb, ph) takes the causal 16 x 16 blocks
+// (rb, ph) and (rb, ph + 2), both operands as 16-byte reads of B and C rows straight
+// from memory (rows past the end of the sequence read 0).
+template <int N>
+__global__ void __launch_bounds__(kScanThreads)
+ssd_cb_kernel(const float* __restrict__ Bm, const float* __restrict__ Cm, float* __restrict__ CB, int64_t L,
+              int64_t nblk) {
+  constexpr int W = kScanW;
+  const int64_t bb = blockIdx.x;  // (batch, block), block fastest
+  const int64_t b = bb / nblk, blk = bb - b * nblk;
+  const int64_t t0 = blk * W, nv = L - t0;
+  const int nvw = nv < W ? (int)nv : W;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
+  const auto rbm = tile_rsrc(Bm + (b * L + t0) * N, (int64_t)nvw * N * 4);
+  const auto rcm = tile_rsrc(Cm + (b * L + t0) * N, (int64_t)nvw * N * 4);
+  float* const cbo = CB + bb * (W * W);
 #pragma unroll
-  for (int st = 0; st < KN / 16; ++st) {
-    const int cur = st & 1, nxt = cur ^ 1;
-    if (st + 1 < KN / 16) {
-      a[nxt] = *(const f32x4*)&arow[16 * (st + 1)];
-      b0[nxt] = *(const f32x4*)&brow[16 * (st + 1)];
+  for (int u = 0; u < 2; ++u) {
+    const int sb = ph + 2 * u;
+    if (sb > rb) break;  // wave-uniform
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const unsigned ao = (unsigned)((16 * rb + lr) * N + 4 * lq) * 4u;
+    const unsigned bo = (unsigned)((16 * sb + lr) * N + 4 * lq) * 4u;
+#pragma unroll
+    for (int kb = 0; kb < N; kb += 16) {
+      f32x4 a, bv;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        a[m] = buf_ld<float>(rcm, ao + (unsigned)(kb + m) * 4u);
+        bv[m] = buf_ld<float>(rbm, bo + (unsigned)(kb + m) * 4u);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma4(a[m], bv[m], acc);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc = mfma4(a[cur][m], b0[cur][m], acc);
-    if (st + 1 < KN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    for (int r = 0; r < 4; ++r) cbo[(16 * rb + 4 * lq + r) * W + 16 * sb + lr] = acc[r];
   }
 }
 
@@ -398,8 +422,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
                           const float* __restrict__ dA_cs, const float* __restrict__ Bm,
                           const float* __restrict__ Cm, const float* __restrict__ Dv,
                           const float* __restrict__ h0, float* __restrict__ y, float* __restrict__ h_final,
-                          float* __restrict__ block_states, int64_t L, int H, int64_t nc, int64_t cw,
-                          int64_t nct) {
+                          float* __restrict__ block_states, const float* __restrict__ CBw, int64_t L, int H,
+                          int64_t nc, int64_t cw, int64_t nct) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
   constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
   constexpr int SB = N + 4;
@@ -529,13 +553,16 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
     {
       const bool two = ph + 2 <= rb;  // wave-uniform
       if (ph <= rb) {
-        f32x4 GG[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        // C_i.B_s of this block from the shared table (the same for every head)
         const int s0 = ph * 16, s1 = (ph + 2) * 16;
-        if (two)
-          mm_nt<N>(GG, &Cs[(i0 + lr) * SB + 4 * lq], &Bs[(s0 + lr) * SB + 4 * lq], &Bs[(s1 + lr) * SB + 4 * lq]);
-        else
-          mm_nt1<N>(GG[0], &Cs[(i0 + lr) * SB + 4 * lq], &Bs[(s0 + lr) * SB + 4 * lq]);
-        const f32x4 G0 = GG[0], G1 = GG[1];
+        const float* const cbt = CBw + ((b * nc + c) * W + i0 + 4 * lq) * W + lr;
+        f32x4 G0, G1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G0[r] = cbt[r * W + s0];
+        if (two) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) G1[r] = cbt[r * W + s1];
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           if (u == 1 && !two) break;
@@ -1312,10 +1339,17 @@ extern "C" int ssm_ssd_chunk_cumsum_bwd(const float* ddA, const float* ddt_out, 
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+extern "C" size_t ssm_ssd_chunk_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dstate) {
+  if (batch < 1 || seqlen < 1 || dstate < 1) return 0;
+  const int64_t nblk = (seqlen + ssm::kScanW - 1) / ssm::kScanW;
+  return ssm::align256((size_t)batch * nblk * ssm::kScanW * ssm::kScanW * 4);
+}
+
 extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const float* dA_cumsum, const float* B,
                                       const float* C, const float* D, const float* h0, float* y, float* h_final,
-                                      float* block_states, int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
-                                      int64_t chunk, hipStream_t stream) {
+                                      float* block_states, void* workspace, size_t workspace_bytes, int64_t batch,
+                                      int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate, int64_t chunk,
+                                      hipStream_t stream) {
   using namespace ssm;
   if (batch < 1 || seqlen < 1 || heads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return SSM_ERR_DIM;
   const double lim = (double)((int64_t)1 << 31);
@@ -1331,23 +1365,29 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
     if (p && !aligned4(p)) return SSM_ERR_ALIGN;
   const int64_t nblk = (seqlen + kScanW - 1) / kScanW;  // 64-step blocks walked by the kernel
   if ((double)batch * heads * nblk * headdim * dstate >= lim) return SSM_ERR_DIM;
+  const size_t ws_need = ssm_ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, dstate);
+  if (!workspace || workspace_bytes < ws_need || ((uintptr_t)workspace & 255)) return SSM_ERR_WORKSPACE;
   const size_t f = 4, nx = (size_t)batch * seqlen * heads * headdim * f, nch = (size_t)batch * heads * nc * chunk * f;
   const size_t nbc = (size_t)batch * seqlen * dstate * f, nst = (size_t)batch * heads * headdim * dstate * f;
   const Rng ins[] = {span(x, nx), span(dt_out, nch), span(dA_cumsum, nch), span(B, nbc), span(C, nbc),
                      span(D, heads * f), span(h0, nst)};
-  const Rng outs[] = {span(y, nx), span(h_final, nst), span(block_states, nst * nblk)};
-  for (int i = 0; i < 3; ++i) {
+  const Rng outs[] = {span(y, nx), span(h_final, nst), span(block_states, nst * nblk), span(workspace, ws_need)};
+  for (int i = 0; i < 4; ++i) {
     for (const Rng& r : ins)
       if (overlaps(outs[i], r)) return SSM_ERR_ALIAS;
-    for (int j = i + 1; j < 3; ++j)
+    for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], outs[j])) return SSM_ERR_ALIAS;
   }
+  float* const CBw = (float*)workspace;
+  auto cbk = dstate == 128 ? ssd_cb_kernel<128> : ssd_cb_kernel<64>;
+  hipLaunchKernelGGL(cbk, dim3((unsigned)(batch * nblk)), dim3(kScanThreads), 0, stream, B, C, CBw, seqlen, nblk);
+  if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
   const dim3 grid((unsigned)(batch * heads));
   // (saving the block states is a separate instantiation: the plain forward stays as lean)
   auto kern = dstate == 128 ? (block_states ? ssd_chunk_scan_fwd_kernel<128, true> : ssd_chunk_scan_fwd_kernel<128, false>)
                             : (block_states ? ssd_chunk_scan_fwd_kernel<64, true> : ssd_chunk_scan_fwd_kernel<64, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), 0, stream, x, dt_out, dA_cumsum, B, C, D, h0, y, h_final,
-                     block_states, seqlen, (int)heads, nblk, chunk, nc);
+                     block_states, CBw, seqlen, (int)heads, nblk, chunk, nc);
   return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

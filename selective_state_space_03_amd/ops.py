@@ -41,7 +41,8 @@ EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", 
            "ssm_scan_bwd_ex", "ssm_scan_chunk_states_bytes", "ssm_conv1d_fwd", "ssm_conv1d_step", "ssm_conv1d_bwd_workspace_bytes",
            "ssm_conv1d_bwd", "ssm_conv1d_bwd_noalloc", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
            "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd",
-           "ssm_ssd_chunk_scan_fwd", "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd")
+           "ssm_ssd_chunk_scan_fwd_workspace_bytes", "ssm_ssd_chunk_scan_fwd",
+           "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd")
 
 
 class ScanOptions(ctypes.Structure):
@@ -113,7 +114,9 @@ def lib():
         L.ssm_ssd_chunk_cumsum_bwd_workspace_bytes.restype = SZ
         L.ssm_ssd_chunk_cumsum_bwd.argtypes = [P] * 9 + [SZ] + [I64] * 4 + [I, F, F, P]
         L.ssm_ssd_chunk_cumsum_bwd.restype = I
-        L.ssm_ssd_chunk_scan_fwd.argtypes = [P] * 10 + [I64] * 6 + [P]
+        L.ssm_ssd_chunk_scan_fwd_workspace_bytes.argtypes = [I64] * 3
+        L.ssm_ssd_chunk_scan_fwd_workspace_bytes.restype = SZ
+        L.ssm_ssd_chunk_scan_fwd.argtypes = [P] * 11 + [SZ] + [I64] * 6 + [P]
         L.ssm_ssd_chunk_scan_fwd.restype = I
         L.ssm_ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 4
         L.ssm_ssd_chunk_scan_bwd_workspace_bytes.restype = SZ
@@ -495,12 +498,19 @@ def ssd_block_states_shape(batch, seqlen, heads, headdim, dstate):
     return (batch, heads, (seqlen + 63) // 64, headdim, dstate)
 
 
-def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_final=True, block_states=None):
+def ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, dstate):
+    return int(lib().ssm_ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, dstate))
+
+
+def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_final=True, block_states=None,
+                       workspace=None):
     """SSD scan forward over chunks (include/ssm_ssd.h), fed by ssd_chunk_cumsum_fwd.
 
     x [batch, seqlen, heads, headdim], dt_out and dA_cumsum [batch, heads, chunks, chunk],
     B, C [batch, seqlen, dstate], D [heads], h0 [batch, heads, headdim, dstate], all fp32
-    -> (y [batch, seqlen, heads, headdim], h_final [batch, heads, headdim, dstate] or None)."""
+    -> (y [batch, seqlen, heads, headdim], h_final [batch, heads, headdim, dstate] or None).
+    workspace: a uint8 device tensor of ssd_chunk_scan_fwd_workspace_bytes (allocated here
+    when not given)."""
     b, l, h, p = x.shape
     n = B.shape[-1]
     nc, chunk = dt_out.shape[-2:]
@@ -520,9 +530,13 @@ def ssd_chunk_scan_fwd(x, dt_out, dA_cumsum, B, C, D=None, h0=None, y=None, h_fi
     hf = torch.empty((b, h, p, n), dtype=f32, device=dev) if h_final is True else h_final
     _req(hf, "h_final", (b, h, p, n), f32, dev)
     _req(block_states, "block_states", ssd_block_states_shape(b, l, h, p, n), f32, dev)
+    wsb = ssd_chunk_scan_fwd_workspace_bytes(b, l, n)
+    if workspace is None:
+        workspace = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
     _check("ssm_ssd_chunk_scan_fwd", lib().ssm_ssd_chunk_scan_fwd(
         _ptr(x), _ptr(dt_out), _ptr(dA_cumsum), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf),
-        _ptr(block_states), b, l, h, p, n, chunk, _stream()))
+        _ptr(block_states), _ptr(workspace), workspace.numel() * workspace.element_size(), b, l, h, p, n, chunk,
+        _stream()))
     return y, hf
 
 

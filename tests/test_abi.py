@@ -366,16 +366,22 @@ def test_ssd_chunk_scan_validation():
 
     def call(b=2, l=100, h=3, p=64, n=128, w=64, **over):
         a = dict(x=addr(0), dto=addr(1), cs=addr(2), B=addr(3), C=addr(4), D=addr(5), h0=addr(6), y=addr(7),
-                 hf=addr(8), bs=addr(9))
+                 hf=addr(8), bs=addr(9), ws=addr(10))
         a.update(over)
+        wsb = a.get("wsb", L.ssm_ssd_chunk_scan_fwd_workspace_bytes(b, l, n))
         return L.ssm_ssd_chunk_scan_fwd(a["x"], a["dto"], a["cs"], a["B"], a["C"], a["D"], a["h0"], a["y"], a["hf"],
-                                        a["bs"], b, l, h, p, n, w, None)
+                                        a["bs"], a["ws"], wsb, b, l, h, p, n, w, None)
     assert call(b=0) == DIM and call(l=0) == DIM and call(p=0) == DIM and call(w=0) == DIM
     assert call(p=32) == UNSUP and call(n=96) == UNSUP and call(w=96) == UNSUP and call(w=32) == UNSUP
     assert call(x=None) == NULL and call(cs=None) == NULL and call(y=None) == NULL
     assert call(y=addr(0)) == ALIAS and call(hf=addr(6)) == ALIAS and call(hf=addr(7)) == ALIAS
     assert call(y=addr(7, 2)) == ALIGN and call(bs=addr(9, 2)) == ALIGN
     assert call(bs=addr(0)) == ALIAS and call(bs=addr(8)) == ALIAS
+    assert call(ws=None) == WS and call(wsb=16) == WS and call(ws=addr(10, 64)) == WS
+    assert call(ws=addr(3)) == ALIAS and call(ws=addr(7)) == ALIAS
+    # C_i.B_s of every 64-step block: [batch, blocks, 64, 64] fp32 (2 x 2 x 16 KB)
+    assert L.ssm_ssd_chunk_scan_fwd_workspace_bytes(2, 100, 128) == 2 * 2 * 64 * 64 * 4
+    assert L.ssm_ssd_chunk_scan_fwd_workspace_bytes(0, 100, 128) == 0
 
 
 @no_gpu_only
