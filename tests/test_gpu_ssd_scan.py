@@ -171,6 +171,7 @@ BWD_CASES = [
     (2, 512, 4, 128, True, True, True),    # eight chunks
     (3, 1300, 11, 64, True, True, True),   # heads of a chunk in uneven groups (3, 3, 3, 2), ragged chunk
     (4, 4096, 2, 64, False, True, True),   # 256 (batch, chunk) pairs: every head in one group
+    (4, 4050, 2, 128, True, False, True),  # one group, d_state 128, a ragged last chunk of 18 steps
 ]
 
 
