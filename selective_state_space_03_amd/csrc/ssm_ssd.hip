@@ -709,12 +709,15 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
     for (int r = 0; r < 4; ++r)
       G[j][r] = dh_final ? dh_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] : 0.f;
 
-  // element k of a thread: dy of step tid / P + (T / P) k, channel tid % P; C element
-  // tid + T k of the chunk's contiguous [W, N] block
+  // Thread (wave w, lane l) moves steps 8 w .. 8 w + 7 of channel l of dy and of states
+  // l, l + 64 of C: each of its loads is one contiguous 256-byte row across the wave, and
+  // its 8 steps go to the transposed tiles as two 16-byte writes (no bank conflicts).
   // Loads go through buffer resources with uniform bases and 32-bit lane offsets; a
   // chunk's range ends after its last valid step, so rows past the end read 0.
-  const unsigned yoff = (unsigned)((tid / P) * H * P + tid % P) * 4u;
-  const unsigned ystep4 = (unsigned)((T / P) * H * P) * 4u;
+  static_assert(W == 8 * (T / 64) && YL == 8 && CL == 8 * (N / 64), "8 steps per thread");
+  const unsigned yoff = (unsigned)((8 * wave) * H * P + lane) * 4u;
+  const unsigned ystep4 = (unsigned)(H * P) * 4u;
+  const unsigned coff = (unsigned)((8 * wave) * N + lane) * 4u;
   float ry[YL], rc[CL], rcs = 0.f;
   auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W, nv = L - t0;  // valid steps (at least 1, may exceed W)
@@ -722,9 +725,11 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
     const auto rdy = tile_rsrc(dy + ((b * L + t0) * H + h) * P, ((int64_t)(nvw - 1) * H * P + P) * 4);
     const auto rcm = tile_rsrc(Cm + (b * L + t0) * N, (int64_t)nvw * N * 4);
 #pragma unroll
-    for (int k = 0; k < YL; ++k) ry[k] = buf_ld<float>(rdy, yoff + k * ystep4);
+    for (int k = 0; k < 8; ++k) ry[k] = buf_ld<float>(rdy, yoff + k * ystep4);
 #pragma unroll
-    for (int k = 0; k < CL; ++k) rc[k] = buf_ld<float>(rcm, (unsigned)(tid + T * k) * 4u);
+    for (int q = 0; q < N / 64; ++q)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rc[8 * q + k] = buf_ld<float>(rcm, coff + (unsigned)(k * N + 64 * q) * 4u);
     if (tid < W) rcs = dA_cs[(bh * nc + c) * W + tid];
   };
   load_chunk(nc - 1);
@@ -738,15 +743,14 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) gc[(j * 4 + r) * 64] = G[j][r];
 #pragma unroll
-    for (int k = 0; k < YL; ++k) {
-      const int i = tid + T * k;
-      YT[(i % P) * SW + i / P] = ry[k];
-    }
+    for (int k = 0; k < 8; k += 4)
+      *(f32x4*)&YT[lane * SW + 8 * wave + k] = f32x4{ry[k], ry[k + 1], ry[k + 2], ry[k + 3]};
 #pragma unroll
-    for (int k = 0; k < CL; ++k) {
-      const int i = tid + T * k;
-      CT[(i % N) * SW + i / N] = rc[k];
-    }
+    for (int q = 0; q < N / 64; ++q)
+#pragma unroll
+      for (int k = 0; k < 8; k += 4)
+        *(f32x4*)&CT[(lane + 64 * q) * SW + 8 * wave + k] =
+            f32x4{rc[8 * q + k], rc[8 * q + k + 1], rc[8 * q + k + 2], rc[8 * q + k + 3]};
     if (tid < W) ev[tid] = exp2_hw(rcs * kLog2e);
     __syncthreads();
     if (c > 0) load_chunk(c - 1);  // in flight during the products below
