@@ -70,7 +70,9 @@
  *                           the state entering every 64-step block (what the backward
  *                           below reads instead of recomputing it)
  * Supported: headdim 64, d_state 64 or 128, chunk a multiple of 64 (SSM_ERR_UNSUPPORTED
- * otherwise); a chunk is walked in blocks of 64 steps.
+ * otherwise); a chunk is walked in blocks of 64 steps.  Inputs are expected finite: the
+ * in-block products are dense matrix products, so a NaN or Inf in a 64-step block can
+ * reach the outputs of every step of that block (and, through the state, later ones).
  * workspace             : ssm_ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, d_state)
  *                           bytes, 256-byte aligned, contents on entry ignored: the
  *                           products C_i.B_s of every 64-step block, [batch, blocks, 64,
