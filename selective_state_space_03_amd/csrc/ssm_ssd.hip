@@ -812,10 +812,12 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   // head's K transposed, Ms[s][i] = K_is (s <= i); at the end the V sums.  cbd: C_i.B_i.
   __shared__ __attribute__((aligned(16))) float Ms[W * SM];
   __shared__ float cbd[W];
-  __shared__ float cs[W], dts[W], ev[W], wv[W];
+  // per-head step values and x.(G B) partials, by head parity: the gradients of dA_cumsum
+  // and dt_out of a head are formed while the next head's products run
+  __shared__ float cs[2][W], dts[2][W], ev[2][W], wv[2][W];
   __shared__ float qcol[4][W];  // column sums of Q over the rows of each row block
   __shared__ float rowp[2][W];  // per half: e_i dy_i.(C_i S^T) + sum_s Q_is dt_s
-  __shared__ float dwp[2][W];   // per half: x_s.(G B_s)
+  __shared__ float dwp[2][2][W];  // [parity][half]: x_s.(G B_s)
   __shared__ float red8[8];     // per-wave <G, S>
   __shared__ float redD[8];     // per-wave dy.x
 
@@ -911,14 +913,43 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   };
   if (hlo < hhi) load_head(hlo);
 
+  // ---- (f) for head hp (parity pp): gradients of dA_cumsum and dt_out, one lane per
+  // step of wave 0 (W = 64), fixed-order sums (the sums over steps are butterflies).
+  // Run by wave 0 after the next head's first barrier (or after the last head): the
+  // next head's staging and products write the other parity's arrays, and its qcol,
+  // rowp, <G, S> and dD partials only after barriers that wave 0 reaches after this.
+  auto finish_head = [&](int hp, int pp) __attribute__((always_inline)) {
+    const int64_t bhp = b * H + hp;
+    const int sp = lane;
+    const float qc = ((qcol[0][sp] + qcol[1][sp]) + qcol[2][sp]) + qcol[3][sp];
+    const float dw = dwp[pp][0][sp] + dwp[pp][1][sp];
+    const float g_dt = fmaf(exp2_hw((cs[pp][W - 1] - cs[pp][sp]) * kLog2e), dw, qc);
+    float g_cs = (rowp[0][sp] + rowp[1][sp]) - dts[pp][sp] * qc - wv[pp][sp] * dw;
+    const float tw = wave_sum64(wv[pp][sp] * dw);  // sum_s w_s x_s.(G B_s)
+    if (sp == W - 1) {
+      float gsum = 0.f;
+      for (int kk = 0; kk < 8; ++kk) gsum += red8[kk];
+      g_cs += tw + ev[pp][W - 1] * gsum;
+    }
+    const int64_t o = (bhp * nc + c) * W + sp;
+    ddA[o] = g_cs;
+    ddt[o] = g_dt;
+    if (sp == 0) {
+      float sD = 0.f;
+      for (int kk = 0; kk < 8; ++kk) sD += redD[kk];
+      dDp[bcn * H + hp] = sD;
+    }
+  };
+
   for (int h = hlo; h < hhi; ++h) {
     const int64_t bh = b * H + h;
+    const int par = (h - hlo) & 1;
     // ---- (a) stage x and dy rows, G, the chunk's cumsum and weights
     if (tid < W) {
-      cs[tid] = pc0;
-      dts[tid] = pdt;
-      ev[tid] = exp2_hw(pc0 * kLog2e);
-      wv[tid] = exp2_hw((pcl - pc0) * kLog2e) * pdt;
+      cs[par][tid] = pc0;
+      dts[par][tid] = pdt;
+      ev[par][tid] = exp2_hw(pc0 * kLog2e);
+      wv[par][tid] = exp2_hw((pcl - pc0) * kLog2e) * pdt;
     }
 #pragma unroll
     for (int k = 0; k < XL; ++k) {
@@ -931,6 +962,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
 #pragma unroll
       for (int r = 0; r < 4; ++r) ST[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = pG[j][r];
     __syncthreads();
+    if (wave == 0 && h > hlo) finish_head(h - 1, par ^ 1);  // the previous head's
 
     // the entering state, loaded now and staged after the G products
     float rs[SL];
@@ -958,17 +990,17 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
       }
       if (lr == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dwp[ph][r0 + 4 * lq + r] = dwq[r];
+        for (int r = 0; r < 4; ++r) dwp[par][ph][r0 + 4 * lq + r] = dwq[r];
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float ws = wv[r0 + 4 * lq + r];
+      const float ws = wv[par][r0 + 4 * lq + r];
 #pragma unroll
       for (int q = 0; q < 2; ++q) DX[q][r] *= ws;
     }
     {
-      const float wl = wv[r0 + lr];  // the weight of the A operand's row s = r0 + lr
+      const float wl = wv[par][r0 + lr];  // the weight of the A operand's row s = r0 + lr
       mm_k64<NH, SB>(DB, &Xs[(r0 + lr) * SX], wl, &ST[(4 * lq) * SB + ph * NH * 16 + lr], lq);
     }
     __syncthreads();  // ST now takes the entering state
@@ -991,7 +1023,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
 
     // ---- (d) with S: diag(e) dY S (column tiles of half ph) and C S^T (columns of half ph)
     {
-      const float el = ev[r0 + lr];  // the weight of the A operand's row i = r0 + lr
+      const float el = ev[par][r0 + lr];  // the weight of the A operand's row i = r0 + lr
       mm_k64<NH, SB>(DC, &Ys[(r0 + lr) * SX], el, &ST[(4 * lq) * SB + ph * NH * 16 + lr], lq);
     }
     float csr[4], tot[4];
@@ -1001,12 +1033,12 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
                &ST[((2 * ph + 1) * 16 + lr) * SB + 4 * lq]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        csr[r] = cs[r0 + 4 * lq + r];
+        csr[r] = cs[par][r0 + 4 * lq + r];
         float rp = 0.f;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           rp = fmaf(P4[q][r], Ys[(r0 + 4 * lq + r) * SX + (2 * ph + q) * 16 + lr], rp);
-        tot[r] = ev[r0 + 4 * lq + r] * rp;
+        tot[r] = ev[par][r0 + 4 * lq + r] * rp;
       }
     }
     // Z blocks of rows i (this row block) and step blocks sb = ph, ph + 2 (those <= rb)
@@ -1026,7 +1058,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
         for (int m = 0; m < 4; ++m) ZB = mfma4(a[m], bx[m], ZB);
       }
       const int s = sb * 16 + lr;
-      const float css = cs[s], dvs = dts[s];
+      const float css = cs[par][s], dvs = dts[par][s];
       float colq = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1059,7 +1091,7 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     // += dt_s sum_{i >= s} K_is dy_i, K^T rows from Ms (16-byte reads)
     {
       const int s = r0 + lr;
-      const float dts_l = dts[s];
+      const float dts_l = dts[par][s];
 #pragma unroll
       for (int kbi = 0; kbi < 4; ++kbi) {
         if (kbi >= 4 - rb) break;  // wave-uniform: blocks rb .. 3
@@ -1101,32 +1133,8 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     }
     __syncthreads();  // qcol, rowp, dwp, <G, S> and dD partials are in LDS; tiles free
 
-    // ---- (f) gradients of dA_cumsum and dt_out, one thread per step, fixed-order sums
-    // (wave 0: lane = step, W = 64; the sums over steps are butterflies of fixed order)
-    if (wave == 0) {
-      const int sp = lane;
-      const float qc = ((qcol[0][sp] + qcol[1][sp]) + qcol[2][sp]) + qcol[3][sp];
-      const float dw = dwp[0][sp] + dwp[1][sp];
-      const float g_dt = fmaf(exp2_hw((cs[W - 1] - cs[sp]) * kLog2e), dw, qc);
-      float g_cs = (rowp[0][sp] + rowp[1][sp]) - dts[sp] * qc - wv[sp] * dw;
-      const float tw = wave_sum64(wv[sp] * dw);  // sum_s w_s x_s.(G B_s)
-      if (sp == W - 1) {
-        float gsum = 0.f;
-        for (int k = 0; k < 8; ++k) gsum += red8[k];
-        g_cs += tw + ev[W - 1] * gsum;
-      }
-      const int64_t o = (bh * nc + c) * W + sp;
-      ddA[o] = g_cs;
-      ddt[o] = g_dt;
-      if (sp == 0) {
-        float sD = 0.f;
-        for (int k = 0; k < 8; ++k) sD += redD[k];
-        dDp[bcn * H + h] = sD;
-      }
-    }
-    // (the next head's staging may start: every wave is past the barrier above, and
-    // wave 0 finishes these reads before it writes the next head's cs, dts, ev, wv)
   }
+  if (wave == 0 && hhi > hlo) finish_head(hhi - 1, (hhi - 1 - hlo) & 1);  // the last head's
 
   // ---- the V terms summed over the heads: dC_i += sum_{s <= i} V_is B_s and
   // dB_s += sum_{i >= s} V_is C_i (Ms is free: every wave passed the last barrier)
