@@ -101,7 +101,7 @@
  * dh_final may be NULL (zero).  D may be NULL (no skip term; dD is then still the
  * gradient of a skip weight).  block_states is required.  The workspace holds the
  * state adjoint G of every (batch, head, chunk) ([headdim, d_state] fp32 each), dD per
- * (batch, chunk, head), and, when there are fewer than 128 (batch, chunk) pairs and the
+ * (batch, chunk, head), and, when there are at most 128 (batch, chunk) pairs and the
  * heads of a chunk are split over several workgroups, each group's dB and dC:
  * ssm_ssd_chunk_scan_bwd_workspace_bytes, 256-byte aligned, contents on entry ignored.  Supported: headdim 64, d_state 64 or
  * 128, chunk 64 (SSM_ERR_UNSUPPORTED otherwise).  Results are bit-identical from run

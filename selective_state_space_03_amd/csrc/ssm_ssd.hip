@@ -1242,7 +1242,7 @@ size_t ws_part_bytes(int64_t batch, int64_t nc, int64_t heads) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // heads per workgroup of the backward's chunk kernel: all of them unless there are
-// fewer than 128 (batch, chunk) pairs, then split so that about 256 workgroups run
+// at most 128 (batch, chunk) pairs, then split so that about 256 workgroups run
 struct SsdBwdSplit {
   int hpg, ngrp;
 };

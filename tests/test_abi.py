@@ -404,7 +404,7 @@ def test_ssd_chunk_scan_bwd_validation():
     assert call(dx=addr(9, 2)) == ALIGN
     assert call(ws=None) == WS and call(wsb=16) == WS and call(ws=addr(16, 64)) == WS
     # G of every (batch, head, 64-step chunk), [64, N] fp32; dD per (batch, chunk, head);
-    # with fewer than 128 (batch, chunk) pairs the heads are split into groups (here 3
+    # with at most 128 (batch, chunk) pairs the heads are split into groups (here 3
     # groups of 1) and each group's dB and dC ([batch, seqlen, N] fp32) is kept
     assert L.ssm_ssd_chunk_scan_bwd_workspace_bytes(2, 100, 3, 128) == 2 * 3 * 2 * 64 * 128 * 4 + 256 + 2 * 307200
     # 256 (batch, chunk) pairs: one group, dB and dC written in place
