@@ -24,10 +24,12 @@
 // sequence from the last.  (4-wave workgroups, two per CU, measured the same and
 // double the dB / dC partials.)  Per chunk:
 //   * the workgroup stages the chunk's activation rows (x, delta_raw, z, dy; 128-byte
-//     rows of its 32 channels), B and C, and the chunk's start states through LDS;
+//     rows of its 32 channels), B and C, and the chunk's start states through LDS (in
+//     fp32 with 16 states and whole channel groups, as 16-byte pieces);
 //   * lane 16 c + t computes the per-element values of step t of channel c once
 //     (Delta, Delta x, g, the gate terms, sigmoid(r)); the state lanes get them with
-//     DPP row broadcasts, one per value and step;
+//     DPP row broadcasts, each folded into the multiply that uses it (the reverse
+//     broadcasts again rather than keeping 32 broadcast registers);
 //   * the chunk's forward is recomputed into VGPRs (a_t and h_t of 16 steps per lane),
 //     the readout s_t is summed over the row by a transpose-reduce (lane 16 c + t ends
 //     with s_t), then the reverse recurrence runs over the 16 steps;
@@ -64,46 +66,51 @@ template <int T> __device__ __forceinline__ float bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppRowBcast0 + T, 0xf, 0xf, true));
 }
 
-// forward step T of the chunk in a state lane; keeps the broadcast Delta and Delta x of
-// step T for the reverse
+// forward step T of the chunk in a state lane (each broadcast has one use, so it folds
+// into the multiply as a DPP operand)
 template <int T>
-__device__ __forceinline__ void fstep(float (&a)[kFT], float (&h)[kFT], float (&dlb)[kFT], float (&xb)[kFT],
-                                      float& hp, float dl, float dlx, float A2, const float (&bv)[kFT]) {
-  dlb[T] = bcast<T>(dl);
-  xb[T] = bcast<T>(dlx);
-  a[T] = exp2_hw(dlb[T] * A2);
-  h[T] = fmaf(a[T], hp, xb[T] * bv[T]);
+__device__ __forceinline__ void fstep(float (&a)[kFT], float (&h)[kFT], float& hp, float dl, float dlx, float A2,
+                                      const float (&bv)[kFT]) {
+  a[T] = exp2_hw(bcast<T>(dl) * A2);
+  h[T] = fmaf(a[T], hp, bcast<T>(dlx) * bv[T]);
   hp = h[T];
 }
 template <int... I>
-__device__ __forceinline__ void fwd16(std::integer_sequence<int, I...>, float (&a)[kFT], float (&h)[kFT],
-                                      float (&dlb)[kFT], float (&xb)[kFT], float& hp, float dl, float dlx, float A2,
-                                      const float (&bv)[kFT]) {
-  (fstep<I>(a, h, dlb, xb, hp, dl, dlx, A2, bv), ...);
+__device__ __forceinline__ void fwd16(std::integer_sequence<int, I...>, float (&a)[kFT], float (&h)[kFT], float& hp,
+                                      float dl, float dlx, float A2, const float (&bv)[kFT]) {
+  (fstep<I>(a, h, hp, dl, dlx, A2, bv), ...);
 }
 
-// reverse step T (T = 15 .. 0): Gc enters as a_{T+1} G_{T+1} and leaves as a_T G_T
+// A copy of v that the compiler cannot identify with v, so that a broadcast of it is not
+// merged with a broadcast of v (a merged broadcast has two uses and is not folded).
+__device__ __forceinline__ float fresh(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// reverse step T (T = 15 .. 0): Gc enters as a_{T+1} G_{T+1} and leaves as a_T G_T.
+// dl, dlx, g, g2 are the prep lane's values (g2 a fresh copy of g): every broadcast
+// below has one use.
 template <int T>
 __device__ __forceinline__ void rstep(float& Gc, float& dA, const float (&a)[kFT], const float (&h)[kFT],
-                                      const float (&dlb)[kFT], const float (&xb)[kFT], float h0c, float g, float A,
+                                      float dl, float dlx, float h0c, float g, float g2, float A,
                                       const float (&bv)[kFT], const float (&cv)[kFT], float (&r1)[kFT],
                                       float (&w)[kFT], float (&pb)[kFT], float (&pc)[kFT]) {
-  const float gb = bcast<T>(g);
-  const float G = fmaf(gb, cv[T], Gc);  // dLoss/dh_T
-  pc[T] = gb * h[T];                    // dC: g_T h_T
-  Gc = a[T] * G;                        // a_T G_T, carried to step T - 1
+  const float G = fmaf(bcast<T>(g), cv[T], Gc);  // dLoss/dh_T
+  pc[T] = bcast<T>(g2) * h[T];                   // dC: g_T h_T
+  Gc = a[T] * G;                                 // a_T G_T, carried to step T - 1
   const float t1 = Gc * (T == 0 ? h0c : h[T > 0 ? T - 1 : 0]);  // G_T a_T h_{T-1}
-  dA = fmaf(dlb[T], t1, dA);            // Delta_T G_T a_T h_{T-1}
+  dA = fmaf(bcast<T>(dl), t1, dA);               // Delta_T G_T a_T h_{T-1}
   r1[T] = A * t1;
   w[T] = G * bv[T];
-  pb[T] = G * xb[T];                    // dB: G_T Delta_T x_T
+  pb[T] = bcast<T>(dlx) * G;                     // dB: G_T Delta_T x_T
 }
 template <int... I>
 __device__ __forceinline__ void rev16(std::integer_sequence<int, I...>, float& Gc, float& dA, const float (&a)[kFT],
-                                      const float (&h)[kFT], const float (&dlb)[kFT], const float (&xb)[kFT],
-                                      float h0c, float g, float A, const float (&bv)[kFT], const float (&cv)[kFT],
-                                      float (&r1)[kFT], float (&w)[kFT], float (&pb)[kFT], float (&pc)[kFT]) {
-  (rstep<15 - I>(Gc, dA, a, h, dlb, xb, h0c, g, A, bv, cv, r1, w, pb, pc), ...);
+                                      const float (&h)[kFT], float dl, float dlx, float h0c, float g, float g2,
+                                      float A, const float (&bv)[kFT], const float (&cv)[kFT], float (&r1)[kFT],
+                                      float (&w)[kFT], float (&pb)[kFT], float (&pc)[kFT]) {
+  (rstep<15 - I>(Gc, dA, a, h, dl, dlx, h0c, g, g2, A, bv, cv, r1, w, pb, pc), ...);
 }
 
 // v[t] of every lane 16 r + n summed over the four rows r (channels): permlane swaps
@@ -122,7 +129,22 @@ __device__ __forceinline__ void rows_sum16(float (&v)[kFT], float (&o)[4]) {
   }
 }
 
-template <typename T, bool GATED, bool CLAMP>
+// 16-byte buffer loads and stores (range-checked like the 4-byte ones: a 16-byte piece
+// lies wholly inside or wholly outside the ranges used here)
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// VEC: fp32 with 16 states and whole 32-channel groups, where every row piece the
+// workgroup moves is 16 bytes: thread tid moves 4 consecutive channels (or states) of one
+// row, so a wavefront issues at most two loads and one store per chunk instead of seven
+// loads and four stores (the address units serve a 16-byte access of 64 lanes in about
+// the time of a 4-byte one).
+template <typename T, bool GATED, bool CLAMP, bool VEC>
 __global__ void __launch_bounds__(kFThr)
 bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
                  const T* __restrict__ Bm, const T* __restrict__ Cm, const T* __restrict__ dy,
@@ -137,7 +159,7 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   __shared__ float hsm[2][16][kFA];                                       // chunk start states [state][channel]
   // results of a chunk (buffer by chunk parity)
   __shared__ float outs[2][3][kFT][kFA];                                  // dx, ddelta_raw, dz
-  __shared__ float red[2][kFWaves][2][kFT * 16];                          // per-wave dB, dC sums
+  __shared__ __attribute__((aligned(16))) float red[2][kFWaves][2][kFT * 16];  // per-wave dB, dC sums
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,7 +213,42 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     boff[i] = bn < N ? (uint32_t)(bs * N + bn) * ES : kOutside;  // + chunk * 16 N
   }
   uint32_t q[2][5 + kFBCPer];  // ring of two chunks: x, delta_raw, z, dy, start state, B / C
+  // VEC: thread tid moves row vs, channels (or states) vc .. vc + 3 of piece vq: the
+  // activation rows x, delta_raw, z, dy (vq = 0 .. 3), then the start states (vq = 0) or
+  // B and C (vq = 1: threads 128-191 B, 192-255 C, step vm / 4, states 4 (vm % 4) ..)
+  const int vm = tid & 127, vq = wave >> 1;
+  const int vs = vm >> 3, vc = 4 * (vm & 7);
+  const int bsv = (vm & 63) >> 2, bnv = 4 * (vm & 3);
+  const uint32_t voff = (uint32_t)(vs * Dm + g0 + vc) * 4;  // + chunk * 16 rows (activations), + chunk * N D (states)
+  const uint32_t vboff = (uint32_t)(bsv * 16 + bnv) * 4;     // + chunk * 16 N
+  u32x4 q4[2][2];
+  auto load_chunk4 = [&](int j, int slot) __attribute__((always_inline)) {
+    if (j < 0) return;
+    const uint32_t o = voff + (uint32_t)j * kFT * row_bytes;
+    if (vq == 0) q4[slot][0] = buf_ld4(rx, o);
+    if (vq == 1) q4[slot][0] = buf_ld4(rr, o);
+    if (GATED && vq == 2) q4[slot][0] = buf_ld4(rz, o);
+    if (vq == 3) q4[slot][0] = buf_ld4(rdy, o);
+    if (vq == 0) q4[slot][1] = buf_ld4(rcs, voff + (uint32_t)(j * N * Dm * 4));
+    if (wave == 2) q4[slot][1] = buf_ld4(rb, vboff + (uint32_t)(j * kFT * N * 4));
+    if (wave == 3) q4[slot][1] = buf_ld4(rc, vboff + (uint32_t)(j * kFT * N * 4));
+  };
+  auto stage_chunk4 = [&](int slot, int buf) __attribute__((always_inline)) {
+    if (vq != 2 || GATED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) act[buf][vq][vs][vc + i] = __uint_as_float(q4[slot][0][i]);
+    }
+    if (vq == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hsm[buf][vs][vc + i] = __uint_as_float(q4[slot][1][i]);
+    }
+    if (vq == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bcT[buf][wave - 2][bnv + i][bsv] = __uint_as_float(q4[slot][1][i]);
+    }
+  };
   auto load_chunk = [&](int j, int slot) __attribute__((always_inline)) {
+    if (VEC) return load_chunk4(j, slot);
     if (j < 0) return;
     const uint32_t o = off_add(aoff, (uint32_t)j * kFT * row_bytes);
     q[slot][0] = buf_ld_raw<T>(rx, o);
@@ -206,6 +263,7 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     }
   };
   auto stage_chunk = [&](int slot, int buf) __attribute__((always_inline)) {
+    if (VEC) return stage_chunk4(slot, buf);
     act[buf][0][ls][lc] = raw_f32<T>(q[slot][0]);
     act[buf][1][ls][lc] = raw_f32<T>(q[slot][1]);
     act[buf][2][ls][lc] = raw_f32<T>(q[slot][2]);
@@ -222,7 +280,36 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   // (the waves' sums added in wave order) and the activation gradients as 128-byte
   // rows.  Done at the start of the next chunk's iteration, so that these LDS reads
   // overlap that chunk's arithmetic.
+  auto results4 = [&](int jr) __attribute__((always_inline)) {
+    const int pr = jr & 1;
+    if (vq < 3) {  // dx, ddelta_raw, dz rows
+      if (vq == 2 && !GATED) return;
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(outs[pr][vq][vs][vc + i]);
+      const uint32_t o = voff + (uint32_t)jr * kFT * row_bytes;  // past the end: dropped
+      if (vq == 0) buf_st4(v, rdx, o);
+      if (vq == 1) buf_st4(v, rddr, o);
+      if (GATED && vq == 2) buf_st4(v, rdz, o);
+    } else {  // dB (threads 384-447), dC (448-511): 4 states of one step
+      const int which = wave - 6, e = 4 * (vm & 63);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kFWaves; ++v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += red[pr][v][which][e + i];
+      }
+      const int tt = jr * kFT + (e >> 4);
+      if (tt < L) {
+        const int64_t o = (((int64_t)b * ngroups + grp) * L + tt) * 16 + (e & 15);
+        const float4 v4 = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (which == 0) *(float4*)(pdB + o) = v4;
+        else *(float4*)(pdC + o) = v4;
+      }
+    }
+  };
   auto results = [&](int jr) __attribute__((always_inline)) {
+    if (VEC) return results4(jr);
     const int pr = jr & 1;
 #pragma unroll
     for (int i = 0; i < 512 / kFThr; ++i) {
@@ -298,9 +385,9 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     const float hstart = hsm[buf][li][cw];
 
     // ---- forward of the chunk: a_t and h_t of its 16 steps
-    float a[kFT], h[kFT], dlb[kFT], xb[kFT];
+    float a[kFT], h[kFT];
     float hp = hstart;
-    fwd16(std::make_integer_sequence<int, kFT>(), a, h, dlb, xb, hp, dl, dlx, A2, bv);
+    fwd16(std::make_integer_sequence<int, kFT>(), a, h, hp, dl, dlx, A2, bv);
     // readout s_t (lane 16 c + t), then dz
     float p[kFT];
 #pragma unroll
@@ -310,7 +397,8 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
 
     // ---- reverse over the chunk
     float r1[kFT], w[kFT], pbv[kFT], pcv[kFT];
-    rev16(std::make_integer_sequence<int, kFT>(), Gc, dA, a, h, dlb, xb, hstart, g, A, bv, cv, r1, w, pbv, pcv);
+    rev16(std::make_integer_sequence<int, kFT>(), Gc, dA, a, h, fresh(dl), fresh(dlx), hstart, g, fresh(g), A, bv, cv,
+          r1, w, pbv, pcv);
     const float sw = row_transpose_sum16(w, lane);   // sum_n G_t B_t   (lane 16 c + t)
     const float sa = row_transpose_sum16(r1, lane);  // sum_n A G_t a_t h_{t-1}
     const float dxv = fmaf(dsk, g, dl * sw);
@@ -349,12 +437,22 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   }
 }
 
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 template <typename T, bool GATED>
 hipError_t launch_t(const BwdArgs& a, const float* cstates, float* pdB, float* pdC, float* pdA, float* pdD,
                     float* pdb, int ngroups, hipStream_t stream) {
   const bool clamp = a.dt_lo > 0.f || a.dt_hi < __builtin_inff();
   const dim3 grid((unsigned)(a.batch * ngroups)), blk(kFThr);
-  auto kern = clamp ? bwd_fused_kernel<T, GATED, true> : bwd_fused_kernel<T, GATED, false>;
+  // the 16-byte path: fp32, 16 states, whole channel groups, 16-byte aligned arrays
+  bool vec = sizeof(T) == 4 && a.dstate == 16 && a.dim % kFCh == 0;
+  for (const void* p : {a.x, a.delta_raw, a.z, a.dy, (const void*)a.dx, (const void*)a.ddelta_raw, (const void*)a.dz,
+                        (const void*)a.B, (const void*)a.C, (const void*)cstates, (const void*)pdB, (const void*)pdC})
+    vec = vec && aligned16(p);
+  auto kern = clamp ? bwd_fused_kernel<T, GATED, true, false> : bwd_fused_kernel<T, GATED, false, false>;
+  if constexpr (sizeof(T) == 4) {
+    if (vec) kern = clamp ? bwd_fused_kernel<T, GATED, true, true> : bwd_fused_kernel<T, GATED, false, true>;
+  }
   hipLaunchKernelGGL(kern, grid, blk, 0, stream, (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B,
                      (const T*)a.C, (const T*)a.dy, a.A_log, a.D_skip, a.dt_bias, cstates, a.dh_final, a.dh0,
                      (T*)a.dx, (T*)a.ddelta_raw, (T*)a.dz, pdB, pdC, pdA, pdD, pdb, (int)a.seqlen, (int)a.dim,
