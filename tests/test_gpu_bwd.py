@@ -75,6 +75,9 @@ BWD_CASES = [
     ("seqlen_one", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=1, dim=65, random_h0=True)),
     ("ungated", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=90, dim=80, gated=False)),
     ("long_sequence", "fwdbwd_b4_l2048_d2048", dict(batch=1, seqlen=3000, dim=64)),
+    # 16 states and whole 32-channel groups: the fused kernel's 16-byte load / store path
+    ("wide_rows_ragged_gated_h0", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=301, dim=96, random_h0=True)),
+    ("wide_rows_ungated", "fwdbwd_b4_l2048_d2048", dict(batch=3, seqlen=64, dim=64, gated=False)),
     ("bf16_gated_h0", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=300, dim=130, random_h0=True, with_dy=True)),
     ("bf16_ragged_n7_ungated", "fwd_bf16_b4_l4096_d4096",
      dict(batch=3, seqlen=77, dim=65, dstate=7, gated=False, with_dy=True)),
@@ -104,6 +107,35 @@ def test_bwd_full_size_workload():
     g = gpu_bwd(inp)
     say("bwd full: oracle")
     check(g, oracle_bwd(inp))
+
+
+def test_bwd_16_byte_and_4_byte_paths_agree_bit_for_bit():
+    """With 16 states and whole channel groups the fused backward moves 16-byte pieces;
+    an input that is not 16-byte aligned sends the same call down the 4-byte path.  The
+    arithmetic and every sum order are the same, so all gradients must be bit-identical."""
+    from selective_state_space_03_amd import ops
+    inp = W.make_inputs(W.WORKLOADS["fwdbwd_b4_l2048_d2048"], batch=2, seqlen=203, dim=64, random_h0=True)
+    say("bwd 16-byte vs 4-byte path B=2 L=203 D=64")
+
+    def run(shift):
+        def dev(a):
+            if shift == 0:
+                return to_dev(a, "fp32")
+            buf = torch.zeros(a.size + shift, dtype=torch.float32, device="cuda")
+            v = buf[shift:].view(a.shape)  # contiguous, 4 bytes past a 16-byte boundary
+            v.copy_(torch.from_numpy(np.ascontiguousarray(a, np.float32)))
+            return v
+        g = ops.ssm_scan_bwd(dev(inp["x"]), to_dev(inp["delta_raw"], "fp32"), to_dev(inp["B"], "fp32"),
+                             to_dev(inp["C"], "fp32"), to_dev32(inp["A_log"]), to_dev(inp["dy"], "fp32"),
+                             D_skip=to_dev32(inp["D"]), dt_bias=to_dev32(inp["dt_bias"]),
+                             z=to_dev(inp["z"], "fp32"), h0=to_dev32(inp["h0"]))
+        torch.cuda.synchronize()
+        return {k: host(v) for k, v in g.items() if v is not None}
+
+    a16, a4 = run(0), run(1)
+    for k in GRADS:
+        assert np.array_equal(a16[k], a4[k]), k
+    check(a16, oracle_bwd(inp))
 
 
 def test_bwd_is_bit_identical_across_runs():

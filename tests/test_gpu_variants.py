@@ -148,6 +148,7 @@ BWD_VARIANTS = [
     ("many_segments", dict(batch=1, seqlen=3000, dim=64, random_h0=True), True, True),
     ("n5_ungated", dict(batch=2, seqlen=90, dim=70, dstate=5, gated=False), True, True),
     ("seqlen_one", dict(batch=2, seqlen=1, dim=65, random_h0=True), True, True),
+    ("wide_rows", dict(batch=2, seqlen=130, dim=64, random_h0=True), True, True),  # 16-byte path
 ]
 
 
@@ -251,6 +252,7 @@ BWD_SAVED = [
      True, True),
     ("bf16", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=150, dim=96, random_h0=True, with_dy=True),
      False, True),
+    ("wide_rows", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=200, dim=64, random_h0=True), True, True),
 ]
 
 
