@@ -139,11 +139,45 @@ __device__ __forceinline__ void buf_st4(u32x4 v, __amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
-// VEC: fp32 with 16 states and whole 32-channel groups, where every row piece the
-// workgroup moves is 16 bytes: thread tid moves 4 consecutive channels (or states) of one
-// row, so a wavefront issues at most two loads and one store per chunk instead of seven
-// loads and four stores (the address units serve a 16-byte access of 64 lanes in about
-// the time of a 4-byte one).
+// 4 consecutive elements of T as one buffer access: 16 bytes of fp32 or 8 of bf16
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
+template <typename T> struct Piece;
+template <> struct Piece<float> {
+  using type = u32x4;
+  __device__ __forceinline__ static type ld(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_ld4(r, off); }
+  __device__ __forceinline__ static void st(type v, __amdgpu_buffer_rsrc_t r, uint32_t off) { buf_st4(v, r, off); }
+  __device__ __forceinline__ static float get(type v, int i) { return __uint_as_float(v[i]); }
+  __device__ __forceinline__ static type make(const float (&f)[4]) {
+    type v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+template <> struct Piece<bf16_t> {
+  using type = u32x2;
+  __device__ __forceinline__ static type ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
+  __device__ __forceinline__ static void st(type v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  }
+  __device__ __forceinline__ static float get(type v, int i) {  // element i: the low half first
+    const uint32_t w = v[i >> 1];
+    return bf16_to_f32((bf16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  __device__ __forceinline__ static type make(const float (&f)[4]) {
+    type v;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    return v;
+  }
+};
+
+// VEC: 16 states and whole 32-channel groups: thread tid moves 4 consecutive channels (or
+// states) of one row as one access (16 bytes of fp32, 8 of bf16), so a wavefront issues
+// at most two loads and one store per chunk instead of seven loads and four stores (the
+// address units serve a wide access of 64 lanes in about the time of a 4-byte one).
 template <typename T, bool GATED, bool CLAMP, bool VEC>
 __global__ void __launch_bounds__(kFThr)
 bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const T* __restrict__ z,
@@ -219,32 +253,36 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
   const int vm = tid & 127, vq = wave >> 1;
   const int vs = vm >> 3, vc = 4 * (vm & 7);
   const int bsv = (vm & 63) >> 2, bnv = 4 * (vm & 3);
-  const uint32_t voff = (uint32_t)(vs * Dm + g0 + vc) * 4;  // + chunk * 16 rows (activations), + chunk * N D (states)
-  const uint32_t vboff = (uint32_t)(bsv * 16 + bnv) * 4;     // + chunk * 16 N
-  u32x4 q4[2][2];
+  using PT = Piece<T>;
+  const uint32_t vidx = (uint32_t)(vs * Dm + g0 + vc);
+  const uint32_t voff = vidx * ES;                           // + chunk * 16 rows (activations)
+  const uint32_t vsoff = vidx * 4;                           // + chunk * N D (fp32 states)
+  const uint32_t vboff = (uint32_t)(bsv * 16 + bnv) * ES;    // + chunk * 16 N
+  typename PT::type qa[2], qb[2];  // activation piece; B or C piece (waves 2, 3)
+  u32x4 qs[2];                     // start-state piece (waves 0, 1)
   auto load_chunk4 = [&](int j, int slot) __attribute__((always_inline)) {
     if (j < 0) return;
     const uint32_t o = voff + (uint32_t)j * kFT * row_bytes;
-    if (vq == 0) q4[slot][0] = buf_ld4(rx, o);
-    if (vq == 1) q4[slot][0] = buf_ld4(rr, o);
-    if (GATED && vq == 2) q4[slot][0] = buf_ld4(rz, o);
-    if (vq == 3) q4[slot][0] = buf_ld4(rdy, o);
-    if (vq == 0) q4[slot][1] = buf_ld4(rcs, voff + (uint32_t)(j * N * Dm * 4));
-    if (wave == 2) q4[slot][1] = buf_ld4(rb, vboff + (uint32_t)(j * kFT * N * 4));
-    if (wave == 3) q4[slot][1] = buf_ld4(rc, vboff + (uint32_t)(j * kFT * N * 4));
+    if (vq == 0) qa[slot] = PT::ld(rx, o);
+    if (vq == 1) qa[slot] = PT::ld(rr, o);
+    if (GATED && vq == 2) qa[slot] = PT::ld(rz, o);
+    if (vq == 3) qa[slot] = PT::ld(rdy, o);
+    if (vq == 0) qs[slot] = buf_ld4(rcs, vsoff + (uint32_t)(j * N * Dm * 4));
+    if (wave == 2) qb[slot] = PT::ld(rb, vboff + (uint32_t)(j * kFT * N * ES));
+    if (wave == 3) qb[slot] = PT::ld(rc, vboff + (uint32_t)(j * kFT * N * ES));
   };
   auto stage_chunk4 = [&](int slot, int buf) __attribute__((always_inline)) {
     if (vq != 2 || GATED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) act[buf][vq][vs][vc + i] = __uint_as_float(q4[slot][0][i]);
+      for (int i = 0; i < 4; ++i) act[buf][vq][vs][vc + i] = PT::get(qa[slot], i);
     }
     if (vq == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hsm[buf][vs][vc + i] = __uint_as_float(q4[slot][1][i]);
+      for (int i = 0; i < 4; ++i) hsm[buf][vs][vc + i] = __uint_as_float(qs[slot][i]);
     }
     if (vq == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bcT[buf][wave - 2][bnv + i][bsv] = __uint_as_float(q4[slot][1][i]);
+      for (int i = 0; i < 4; ++i) bcT[buf][wave - 2][bnv + i][bsv] = PT::get(qb[slot], i);
     }
   };
   auto load_chunk = [&](int j, int slot) __attribute__((always_inline)) {
@@ -284,13 +322,14 @@ bwd_fused_kernel(const T* __restrict__ x, const T* __restrict__ delta_raw, const
     const int pr = jr & 1;
     if (vq < 3) {  // dx, ddelta_raw, dz rows
       if (vq == 2 && !GATED) return;
-      u32x4 v;
+      float f[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(outs[pr][vq][vs][vc + i]);
+      for (int i = 0; i < 4; ++i) f[i] = outs[pr][vq][vs][vc + i];
+      const typename PT::type v = PT::make(f);
       const uint32_t o = voff + (uint32_t)jr * kFT * row_bytes;  // past the end: dropped
-      if (vq == 0) buf_st4(v, rdx, o);
-      if (vq == 1) buf_st4(v, rddr, o);
-      if (GATED && vq == 2) buf_st4(v, rdz, o);
+      if (vq == 0) PT::st(v, rdx, o);
+      if (vq == 1) PT::st(v, rddr, o);
+      if (GATED && vq == 2) PT::st(v, rdz, o);
     } else {  // dB (threads 384-447), dC (448-511): 4 states of one step
       const int which = wave - 6, e = 4 * (vm & 63);
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -448,15 +487,13 @@ hipError_t launch_t(const BwdArgs& a, const float* cstates, float* pdB, float* p
                     float* pdb, int ngroups, hipStream_t stream) {
   const bool clamp = a.dt_lo > 0.f || a.dt_hi < __builtin_inff();
   const dim3 grid((unsigned)(a.batch * ngroups)), blk(kFThr);
-  // the 16-byte path: fp32, 16 states, whole channel groups, 16-byte aligned arrays
-  bool vec = sizeof(T) == 4 && a.dstate == 16 && a.dim % kFCh == 0;
+  // the wide path: 16 states, whole channel groups, 16-byte aligned arrays
+  bool vec = a.dstate == 16 && a.dim % kFCh == 0;
   for (const void* p : {a.x, a.delta_raw, a.z, a.dy, (const void*)a.dx, (const void*)a.ddelta_raw, (const void*)a.dz,
                         (const void*)a.B, (const void*)a.C, (const void*)cstates, (const void*)pdB, (const void*)pdC})
     vec = vec && aligned16(p);
   auto kern = clamp ? bwd_fused_kernel<T, GATED, true, false> : bwd_fused_kernel<T, GATED, false, false>;
-  if constexpr (sizeof(T) == 4) {
-    if (vec) kern = clamp ? bwd_fused_kernel<T, GATED, true, true> : bwd_fused_kernel<T, GATED, false, true>;
-  }
+  if (vec) kern = clamp ? bwd_fused_kernel<T, GATED, true, true> : bwd_fused_kernel<T, GATED, false, true>;
   hipLaunchKernelGGL(kern, grid, blk, 0, stream, (const T*)a.x, (const T*)a.delta_raw, (const T*)a.z, (const T*)a.B,
                      (const T*)a.C, (const T*)a.dy, a.A_log, a.D_skip, a.dt_bias, cstates, a.dh_final, a.dh0,
                      (T*)a.dx, (T*)a.ddelta_raw, (T*)a.dz, pdB, pdC, pdA, pdD, pdb, (int)a.seqlen, (int)a.dim,

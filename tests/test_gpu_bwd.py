@@ -78,6 +78,7 @@ BWD_CASES = [
     # 16 states and whole 32-channel groups: the fused kernel's 16-byte load / store path
     ("wide_rows_ragged_gated_h0", "fwdbwd_b4_l2048_d2048", dict(batch=2, seqlen=301, dim=96, random_h0=True)),
     ("wide_rows_ungated", "fwdbwd_b4_l2048_d2048", dict(batch=3, seqlen=64, dim=64, gated=False)),
+    ("wide_rows_bf16", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=150, dim=64, random_h0=True, with_dy=True)),
     ("bf16_gated_h0", "fwd_bf16_b4_l4096_d4096", dict(batch=2, seqlen=300, dim=130, random_h0=True, with_dy=True)),
     ("bf16_ragged_n7_ungated", "fwd_bf16_b4_l4096_d4096",
      dict(batch=3, seqlen=77, dim=65, dstate=7, gated=False, with_dy=True)),
@@ -109,33 +110,40 @@ def test_bwd_full_size_workload():
     check(g, oracle_bwd(inp))
 
 
-def test_bwd_16_byte_and_4_byte_paths_agree_bit_for_bit():
-    """With 16 states and whole channel groups the fused backward moves 16-byte pieces;
-    an input that is not 16-byte aligned sends the same call down the 4-byte path.  The
-    arithmetic and every sum order are the same, so all gradients must be bit-identical."""
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_bwd_wide_and_narrow_paths_agree_bit_for_bit(io):
+    """With 16 states and whole channel groups the fused backward moves 4 elements per
+    access (16 bytes of fp32, 8 of bf16); an input that is not 16-byte aligned sends the
+    same call down the one-element path.  The arithmetic and every sum order are the same,
+    so all gradients must be bit-identical."""
+    import dataclasses
     from selective_state_space_03_amd import ops
-    inp = W.make_inputs(W.WORKLOADS["fwdbwd_b4_l2048_d2048"], batch=2, seqlen=203, dim=64, random_h0=True)
-    say("bwd 16-byte vs 4-byte path B=2 L=203 D=64")
+    w = W.WORKLOADS["fwdbwd_b4_l2048_d2048"]
+    if io == "bf16":
+        w = dataclasses.replace(w, io="bf16")
+    inp = W.make_inputs(w, batch=2, seqlen=203, dim=64, random_h0=True)
+    say("bwd wide vs narrow path %s B=2 L=203 D=64" % io)
 
     def run(shift):
         def dev(a):
+            t = to_dev(a, io)
             if shift == 0:
-                return to_dev(a, "fp32")
-            buf = torch.zeros(a.size + shift, dtype=torch.float32, device="cuda")
-            v = buf[shift:].view(a.shape)  # contiguous, 4 bytes past a 16-byte boundary
-            v.copy_(torch.from_numpy(np.ascontiguousarray(a, np.float32)))
+                return t
+            buf = torch.zeros(t.numel() + shift, dtype=t.dtype, device="cuda")
+            v = buf[shift:].view(t.shape)  # contiguous, one element past a 16-byte boundary
+            v.copy_(t)
             return v
-        g = ops.ssm_scan_bwd(dev(inp["x"]), to_dev(inp["delta_raw"], "fp32"), to_dev(inp["B"], "fp32"),
-                             to_dev(inp["C"], "fp32"), to_dev32(inp["A_log"]), to_dev(inp["dy"], "fp32"),
+        g = ops.ssm_scan_bwd(dev(inp["x"]), to_dev(inp["delta_raw"], io), to_dev(inp["B"], io),
+                             to_dev(inp["C"], io), to_dev32(inp["A_log"]), to_dev(inp["dy"], io),
                              D_skip=to_dev32(inp["D"]), dt_bias=to_dev32(inp["dt_bias"]),
-                             z=to_dev(inp["z"], "fp32"), h0=to_dev32(inp["h0"]))
+                             z=to_dev(inp["z"], io), h0=to_dev32(inp["h0"]))
         torch.cuda.synchronize()
         return {k: host(v) for k, v in g.items() if v is not None}
 
-    a16, a4 = run(0), run(1)
+    wide, narrow = run(0), run(1)
     for k in GRADS:
-        assert np.array_equal(a16[k], a4[k]), k
-    check(a16, oracle_bwd(inp))
+        assert np.array_equal(wide[k], narrow[k]), k
+    check(wide, oracle_bwd(inp), tol(io))
 
 
 def test_bwd_is_bit_identical_across_runs():
