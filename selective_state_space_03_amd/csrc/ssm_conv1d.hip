@@ -151,85 +151,123 @@ conv_step_kernel(T* __restrict__ state, const T* __restrict__ x, const float* __
 // backward of one (b, time segment, channel group): each wave walks its time tiles of
 // the segment in ascending order, writes dx, and accumulates the tile's
 // dw[k] = sum_t dp[t] x[t-K+1+k] and dbias = sum_t dp[t]; the waves' sums are then
-// added in wave order through LDS and stored as the segment's partial, [b][seg][k][d]
-template <int K, bool SILU>
+// added in wave order through LDS and stored as the segment's partial, [b][seg][k][d].
+// V = 2: two neighbouring channels per lane in 8-byte accesses (d_inner even, rows
+// aligned), 128 channels per workgroup; the per-channel arithmetic and sum order are
+// those of V = 1.
+template <int K, bool SILU, int V>
 __global__ void __launch_bounds__(64 * kWaves)
 conv_bwd_kernel(const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
                 const float* __restrict__ dout, float* __restrict__ dx, float* __restrict__ pdw,
                 float* __restrict__ pdb, int64_t L, int64_t Dm, int64_t ngroups, int64_t ntg, int64_t tgs,
                 int64_t nseg) {
   constexpr int TL = kBwdTile;
-  __shared__ float red[kWaves][K + 1][64];
+  __shared__ float red[kWaves][K + 1][64 * V];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t grp = blockIdx.x % ngroups;
   const int64_t r = blockIdx.x / ngroups;
   const int64_t seg = r % nseg, b = r / nseg;
-  const int64_t d = grp * 64 + lane;
-  const bool dvalid = d < Dm;
-  float wk[K];
+  const int64_t d = grp * 64 * V + lane * V;  // first channel of the lane
+  const bool dvalid = d < Dm;                 // V = 2: Dm is even, so d + 1 < Dm too
+  float wk[K][V], bs[V];
 #pragma unroll
-  for (int k = 0; k < K; ++k) wk[k] = dvalid ? w[d * K + k] : 0.f;
-  const float bs = (dvalid && bias) ? bias[d] : 0.f;
-  float sw[K], sb = 0.f;
+  for (int v = 0; v < V; ++v) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) sw[k] = 0.f;
+    for (int k = 0; k < K; ++k) wk[k][v] = dvalid ? w[(d + v) * K + k] : 0.f;
+    bs[v] = (dvalid && bias) ? bias[d + v] : 0.f;
+  }
+  float sw[K][V], sb[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    sb[v] = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) sw[k][v] = 0.f;
+  }
+  auto ld = [&](const float* p, int64_t i, float (&o)[V]) __attribute__((always_inline)) {
+    if (V == 2) {
+      const float2 q = *reinterpret_cast<const float2*>(p + i);
+      o[0] = q.x; o[V - 1] = q.y;
+    } else {
+      o[0] = p[i];
+    }
+  };
   const int64_t tg_end = (seg + 1) * tgs < ntg ? (seg + 1) * tgs : ntg;
   for (int64_t tg = seg * tgs; tg < tg_end; ++tg) {
     const int64_t t0 = (tg * kWaves + wave) * TL;
     if (!dvalid || t0 >= L) continue;  // uniform per wave; the barrier below is outside the loop
     // x[t0-K+1 .. t0+TL+K-2] and dout[t0 .. t0+TL+K-2], zero outside the sequence
     constexpr int NX = TL + 2 * (K - 1), NG = TL + K - 1;
-    float xr[NX], gr[NG];
+    float xr[NX][V], gr[NG][V];
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int64_t t = t0 - (K - 1) + i;
-      xr[i] = (t >= 0 && t < L) ? x[(b * L + t) * Dm + d] : 0.f;
+      if (t >= 0 && t < L) ld(x, (b * L + t) * Dm + d, xr[i]);
+      else
+#pragma unroll
+        for (int v = 0; v < V; ++v) xr[i][v] = 0.f;
     }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int64_t t = t0 + i;
-      gr[i] = t < L ? dout[(b * L + t) * Dm + d] : 0.f;
+      if (t < L) ld(dout, (b * L + t) * Dm + d, gr[i]);
+      else
+#pragma unroll
+        for (int v = 0; v < V; ++v) gr[i][v] = 0.f;
     }
     // dp[t0 + i] for i < TL + K - 1 (dp = 0 past the end since dout = 0 there)
-    float dp[NG];
+    float dp[NG][V];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if (SILU) {
-        float p = bs;
+    for (int i = 0; i < NG; ++i)
 #pragma unroll
-        for (int k = 0; k < K; ++k) p = fmaf(wk[k], xr[i + k], p);
-        const float sg = sigmoid_f(p);
-        dp[i] = gr[i] * sg * fmaf(p, 1.f - sg, 1.f);
-      } else {
-        dp[i] = gr[i];
+      for (int v = 0; v < V; ++v) {
+        if (SILU) {
+          float p = bs[v];
+#pragma unroll
+          for (int k = 0; k < K; ++k) p = fmaf(wk[k][v], xr[i + k][v], p);
+          const float sg = sigmoid_f(p);
+          dp[i][v] = gr[i][v] * sg * fmaf(p, 1.f - sg, 1.f);
+        } else {
+          dp[i][v] = gr[i][v];
+        }
       }
-    }
 #pragma unroll
     for (int i = 0; i < TL; ++i) {
-      float g = 0.f;
+      float g[V];
 #pragma unroll
-      for (int k = 0; k < K; ++k) g = fmaf(wk[k], dp[i + K - 1 - k], g);
-      if (t0 + i < L) dx[(b * L + t0 + i) * Dm + d] = g;
-      // the tile's own steps only (dp of the halo belongs to the next tile)
+      for (int v = 0; v < V; ++v) {
+        g[v] = 0.f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) sw[k] = fmaf(dp[i], xr[i + k], sw[k]);
-      sb += dp[i];
+        for (int k = 0; k < K; ++k) g[v] = fmaf(wk[k][v], dp[i + K - 1 - k][v], g[v]);
+        // the tile's own steps only (dp of the halo belongs to the next tile)
+#pragma unroll
+        for (int k = 0; k < K; ++k) sw[k][v] = fmaf(dp[i][v], xr[i + k][v], sw[k][v]);
+        sb[v] += dp[i][v];
+      }
+      if (t0 + i < L) {
+        if (V == 2) *reinterpret_cast<float2*>(dx + (b * L + t0 + i) * Dm + d) = make_float2(g[0], g[V - 1]);
+        else dx[(b * L + t0 + i) * Dm + d] = g[0];
+      }
     }
   }
   // the waves' sums, added in wave order
 #pragma unroll
-  for (int k = 0; k < K; ++k) red[wave][k][lane] = sw[k];
-  red[wave][K][lane] = sb;
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[wave][k][lane * V + v] = sw[k][v];
+    red[wave][K][lane * V + v] = sb[v];
+  }
   __syncthreads();
   if (wave == 0 && dvalid) {
     const int64_t o = (b * nseg + seg) * K;
 #pragma unroll
-    for (int k = 0; k <= K; ++k) {
-      float s = red[0][k][lane];
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-      for (int v = 1; v < kWaves; ++v) s += red[v][k][lane];
-      if (k < K) pdw[(o + k) * Dm + d] = s; else pdb[(b * nseg + seg) * Dm + d] = s;
-    }
+      for (int k = 0; k <= K; ++k) {
+        float s = red[0][k][lane * V + v];
+#pragma unroll
+        for (int u = 1; u < kWaves; ++u) s += red[u][k][lane * V + v];
+        if (k < K) pdw[(o + k) * Dm + d + v] = s; else pdb[(b * nseg + seg) * Dm + d + v] = s;
+      }
   }
 }
 
@@ -297,16 +335,15 @@ hipError_t bwd_k(const ConvArgs& a, void* ws, hipStream_t stream) {
   const ConvBwdLayout l = conv_bwd_layout(a.batch, a.seqlen, a.dim, a.width);
   float* pdw = (float*)((char*)ws + l.off_dw);
   float* pdb = (float*)((char*)ws + l.off_db);
-  const int64_t ngroups = (a.dim + 63) / 64;
+  // two channels per lane when d_inner is even and x, dout, dx allow 8-byte accesses
+  const bool v2 = a.dim % 2 == 0 && ((uintptr_t)a.x & 7) == 0 && ((uintptr_t)a.dout & 7) == 0 &&
+                  ((uintptr_t)a.dx & 7) == 0;
+  const int64_t ngroups = v2 ? (a.dim + 127) / 128 : (a.dim + 63) / 64;
   const dim3 grid((unsigned)(ngroups * l.nseg * a.batch));
-  if (a.silu)
-    hipLaunchKernelGGL((conv_bwd_kernel<K, true>), grid, dim3(64 * kWaves), 0, stream, (const float*)a.x, a.w,
-                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg,
-                       l.tgs, l.nseg);
-  else
-    hipLaunchKernelGGL((conv_bwd_kernel<K, false>), grid, dim3(64 * kWaves), 0, stream, (const float*)a.x, a.w,
-                       a.bias, (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg,
-                       l.tgs, l.nseg);
+  auto kern = a.silu ? (v2 ? conv_bwd_kernel<K, true, 2> : conv_bwd_kernel<K, true, 1>)
+                     : (v2 ? conv_bwd_kernel<K, false, 2> : conv_bwd_kernel<K, false, 1>);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kWaves), 0, stream, (const float*)a.x, a.w, a.bias,
+                     (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg, l.tgs, l.nseg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = K * a.dim;
