@@ -157,3 +157,26 @@ def test_conv_bwd_optional_outputs_and_determinism():
     g = gpu_bwd(inp, want_params=False)
     assert g["dweight"] is None and g["dbias"] is None
     assert np.array_equal(g["dx"], runs[0]["dx"])
+
+
+def test_conv_bwd_two_and_one_channel_paths_agree_bit_for_bit():
+    """With an even d_inner the backward gives each lane two neighbouring channels in
+    8-byte accesses; an x that is not 8-byte aligned sends the same call down the
+    one-channel path.  Per channel the arithmetic and the sum order are the same, so dx,
+    dweight and dbias must be bit-identical."""
+    inp = W.make_conv_inputs(W.CONV_WORKLOADS["conv_b8_l2048_d1536_k4"], batch=2, seqlen=301, dim=200)
+    say("conv bwd two-channel vs one-channel path")
+    x = to_dev32(inp["x"])
+    buf = torch.zeros(x.numel() + 1, dtype=torch.float32, device="cuda")
+    x_odd = buf[1:].view(x.shape)  # contiguous, 4 bytes past an 8-byte boundary
+    x_odd.copy_(x)
+    w, dout, bias = to_dev32(inp["weight"]), to_dev32(inp["dout"]), to_dev32(inp["bias"])
+    runs = []
+    for xx in (x, x_odd):
+        g = ops().conv1d_bwd(xx, w, dout, bias, silu=True)
+        torch.cuda.synchronize()
+        runs.append({k: host(v) for k, v in g.items() if v is not None})
+    for k in ("dx", "dweight", "dbias"):
+        assert np.array_equal(runs[0][k], runs[1][k]), k
+    r = oracle.conv_bwd(inp["x"], inp["weight"], inp["dout"], inp["bias"], silu=True)
+    assert rel_err(runs[0]["dx"], r["dx"]) <= 1e-4
