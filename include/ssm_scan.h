@@ -60,7 +60,7 @@ typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,        /* a required pointer is NULL                          */
   SSM_ERR_DIM = 2,         /* a size is out of range                              */
-  SSM_ERR_UNSUPPORTED = 3, /* valid request this build does not handle            */
+  SSM_ERR_UNSUPPORTED = 3, /* valid request this library does not handle          */
   SSM_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size        */
   SSM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input                         */

@@ -115,7 +115,7 @@ const char* ssm_status_string(int status) {
     case SSM_OK: return "SSM_OK";
     case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
     case SSM_ERR_DIM: return "SSM_ERR_DIM: a size is out of range";
-    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: request not handled by this build";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: request not handled by this library";
     case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: a pointer is not aligned to its element size";
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
