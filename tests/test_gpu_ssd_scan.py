@@ -109,6 +109,34 @@ def test_repeat_runs_are_bit_identical():
         assert y.tobytes() == runs[0][0].tobytes() and hf.tobytes() == runs[0][1].tobytes()
 
 
+@pytest.mark.parametrize("dstate", [128, 64])
+def test_wide_and_narrow_chunk_loads_agree_bit_for_bit(dstate):
+    """With x, B and C 16-byte aligned the scan loads each chunk as 16-byte pieces; an x
+    that is not 16-byte aligned sends the same call down the one-value path.  The staged
+    tiles and every product are the same, so y, the final state and the saved block
+    states must be bit-identical."""
+    from selective_state_space_03_amd import ops
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=2, seqlen=300, heads=3, dstate=dstate, h0=True)
+    say("ssd scan wide vs narrow chunk loads, d_state %d" % dstate)
+    cs, dto = ops.ssd_chunk_cumsum_fwd(to_dev32(inp["dt"]), to_dev32(inp["A"]), inp["chunk"],
+                                       dt_bias=to_dev32(inp["dt_bias"]))
+    x = to_dev32(inp["x"])
+    buf = torch.zeros(x.numel() + 1, dtype=torch.float32, device="cuda")
+    x_odd = buf[1:].view(x.shape)  # contiguous, 4 bytes past a 16-byte boundary
+    x_odd.copy_(x)
+    b, l, h, p = inp["x"].shape
+    outs = []
+    for xx in (x, x_odd):
+        bs = torch.empty(ops.ssd_block_states_shape(b, l, h, p, dstate), dtype=torch.float32, device="cuda")
+        y, hf = ops.ssd_chunk_scan_fwd(xx, dto, cs, to_dev32(inp["B"]), to_dev32(inp["C"]), D=to_dev32(inp["D"]),
+                                       h0=to_dev32(inp["h0"]), block_states=bs)
+        torch.cuda.synchronize()
+        outs.append((host(y), host(hf), host(bs)))
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert np.array_equal(a_, b_)
+
+
 def test_unsupported_sizes_are_refused():
     from selective_state_space_03_amd import ops
     dev = "cuda"
