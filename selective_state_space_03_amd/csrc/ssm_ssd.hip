@@ -782,15 +782,15 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
     if (tid < W) rcs = dA_cs[(bh * nc + c) * W + tid];
   };
   load_chunk(nc - 1);
-  // fragment order: ((wave TPW + j) 4 + r) 64 + lane, P N floats per (batch, head, chunk)
-  float* const gfrag = Gbuf + (int64_t)wave * TPW * 256 + lane;
+  // fragment order: ((wave TPW + j) 64 + lane) 4 + r, P N floats per (batch, head, chunk):
+  // a lane's 4 values of a tile are one 16-byte store here and one 16-byte load in the
+  // chunk kernel
+  float* const gfrag = Gbuf + (int64_t)wave * TPW * 256 + 4 * lane;
 
   for (int64_t c = nc - 1; c >= 0; --c) {
     float* const gc = gfrag + (bh * nc + c) * (int64_t)(P * N);
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gc[(j * 4 + r) * 64] = G[j][r];
+    for (int j = 0; j < TPW; ++j) *(f32x4*)(gc + j * 256) = G[j];
 #pragma unroll
     for (int k = 0; k < 8; k += 4)
       *(f32x4*)&YT[lane * SW + 8 * wave + k] = f32x4{ry[k], ry[k + 1], ry[k + 2], ry[k + 3]};
@@ -833,8 +833,12 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
 }
 
 // the chunk kernel: dx, ddA_cumsum, ddt_out of its heads, dB and dC of its chunk summed
-// over its heads (at dBo / dCo + grp * gstride), dD of each head and chunk into dDp
-template <int N>
+// over its heads (at dBo / dCo + grp * gstride), dD of each head and chunk into dDp.
+// VEC: x, dy, B, C and the block states are 16-byte aligned, and each thread loads them as
+// 16-byte pieces (x, dy: 4 channels of one step; B, C, states: 4 consecutive values of the
+// block), staged with 16-byte writes.  Either way a thread takes the entering state in
+// the same pieces, so the <G, S> sums agree bit for bit.
+template <int N, bool VEC>
 __global__ void __launch_bounds__(kScanThreads)
 ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
                      const float* __restrict__ dA_cs, const float* __restrict__ Bm,
@@ -851,7 +855,9 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   constexpr int NH = NT / 2;   // ... per half
   constexpr int TPW = NT / 2;  // G fragment tiles per wave
   constexpr int XL = W * P / T, BL = W * N / T, SL = P * N / T;  // staged elements per thread
+  constexpr int XV = XL / 4, BV = BL / 4, SV = SL / 4;            // ... 16-byte pieces
   static_assert(W == 64, "one lane per step of a chunk in the last phase");
+  static_assert(XV * 4 == XL && BV * 4 == BL && SV * 4 == SL, "whole pieces per thread");
   __shared__ __attribute__((aligned(16))) float Xs[W * SX];
   __shared__ __attribute__((aligned(16))) float Ys[W * SX];
   __shared__ __attribute__((aligned(16))) float Bs[W * SB];
@@ -886,7 +892,19 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
 
   // ---- B and C rows of the chunk (shared by every head), then C_i.B_s of this wave's
   // causal blocks into Ms below the diagonal and cbd on it
-  {
+  if constexpr (VEC) {
+    // piece i: values 4 i .. 4 i + 3 of the chunk's block
+    const float* const bp = Bm + (b * L + t0) * N;
+    const float* const cp = Cm + (b * L + t0) * N;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < BV; ++k) {
+      const int e = 4 * (tid + T * k);
+      const bool v = e / N < nv;
+      *(f32x4*)&Bs[(e / N) * SB + e % N] = v ? *(const f32x4*)(bp + e) : zero;
+      *(f32x4*)&Cs[(e / N) * SB + e % N] = v ? *(const f32x4*)(cp + e) : zero;
+    }
+  } else {
     const float* const bp = Bm + (b * L + t0) * N + tid;
     const float* const cp = Cm + (b * L + t0) * N + tid;
 #pragma unroll 4
@@ -928,19 +946,35 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   const int64_t xrow0 = ((b * L + t0) * H) * P + (int64_t)(tid / P) * H * P + tid % P;
 
   // the next head's x and dy rows, G fragment and step values, loaded one head ahead
-  float px[XL], py[XL], pc0 = 0.f, pcl = 0.f, pdt = 0.f;
+  // (VEC: x and dy piece k of a thread is step (tid + T k) / 16, channels 4 (tid % 16) ..)
+  float px[VEC ? 1 : XL], py[VEC ? 1 : XL], pc0 = 0.f, pcl = 0.f, pdt = 0.f;
+  f32x4 px4[VEC ? XV : 1], py4[VEC ? XV : 1];
   f32x4 pG[TPW];
   auto load_head = [&](int hn) __attribute__((always_inline)) {
     const int64_t bhn = b * H + hn;
-    const float* const xc = x + xrow0 + (int64_t)hn * P;
-    const float* const yc = dy + xrow0 + (int64_t)hn * P;
-    if (nv >= W) {  // a whole chunk (uniform): no per-element checks
+    if constexpr (VEC) {
+      const float* const xb = x + ((b * L + t0) * H + hn) * P;
+      const float* const yb = dy + ((b * L + t0) * H + hn) * P;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < XV; ++k) {
+        const int i = tid + T * k, st = i / (P / 4);
+        const int64_t o = (int64_t)st * H * P + 4 * (i % (P / 4));
+        const bool v = st < nv;
+        px4[k] = v ? *(const f32x4*)(xb + o) : zero;
+        py4[k] = v ? *(const f32x4*)(yb + o) : zero;
+      }
+    } else if (nv >= W) {  // a whole chunk (uniform): no per-element checks
+      const float* const xc = x + xrow0 + (int64_t)hn * P;
+      const float* const yc = dy + xrow0 + (int64_t)hn * P;
 #pragma unroll
       for (int k = 0; k < XL; ++k) {
         px[k] = xc[k * xstep];
         py[k] = yc[k * xstep];
       }
     } else {
+      const float* const xc = x + xrow0 + (int64_t)hn * P;
+      const float* const yc = dy + xrow0 + (int64_t)hn * P;
 #pragma unroll
       for (int k = 0; k < XL; ++k) {
         const bool v = tid / P + (T / P) * k < nv;
@@ -948,11 +982,9 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
         py[k] = v ? yc[k * xstep] : 0.f;
       }
     }
-    const float* const gc = Gbuf + (bhn * nc + c) * (int64_t)(P * N) + (int64_t)wave * TPW * 256 + lane;
+    const float* const gc = Gbuf + (bhn * nc + c) * (int64_t)(P * N) + (int64_t)wave * TPW * 256 + 4 * lane;
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pG[j][r] = gc[(j * 4 + r) * 64];
+    for (int j = 0; j < TPW; ++j) pG[j] = *(const f32x4*)(gc + j * 256);
     if (tid < W) {
       const int64_t o = (bhn * nc + c) * W;
       pc0 = dA_cs[o + tid];
@@ -1000,11 +1032,20 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
       ev[par][tid] = exp2_hw(pc0 * kLog2e);
       wv[par][tid] = exp2_hw((pcl - pc0) * kLog2e) * pdt;
     }
+    if constexpr (VEC) {
 #pragma unroll
-    for (int k = 0; k < XL; ++k) {
-      const int i = tid + T * k;
-      Xs[(i / P) * SX + i % P] = px[k];
-      Ys[(i / P) * SX + i % P] = py[k];
+      for (int k = 0; k < XV; ++k) {
+        const int i = tid + T * k, o = (i / (P / 4)) * SX + 4 * (i % (P / 4));
+        *(f32x4*)&Xs[o] = px4[k];
+        *(f32x4*)&Ys[o] = py4[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < XL; ++k) {
+        const int i = tid + T * k;
+        Xs[(i / P) * SX + i % P] = px[k];
+        Ys[(i / P) * SX + i % P] = py[k];
+      }
     }
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
@@ -1013,12 +1054,21 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     __syncthreads();
     if (wave == 0 && h > hlo) finish_head(h - 1, par ^ 1);  // the previous head's
 
-    // the entering state, loaded now and staged after the G products
-    float rs[SL];
+    // the entering state, loaded now and staged after the G products: piece k of a thread
+    // is values 4 (tid + T k) .. of the block
+    f32x4 rs[SV];
     {
-      const float* const sc = bstates + (bh * nc + c) * (int64_t)(P * N) + tid;
+      const float* const sc = bstates + (bh * nc + c) * (int64_t)(P * N);
 #pragma unroll
-      for (int k = 0; k < SL; ++k) rs[k] = sc[T * k];
+      for (int k = 0; k < SV; ++k) {
+        const int e = 4 * (tid + T * k);
+        if constexpr (VEC) {
+          rs[k] = *(const f32x4*)(sc + e);
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) rs[k][m] = sc[e + m];
+        }
+      }
     }
 
     // ---- (b) with G: B G^T (columns of half ph) and diag(w) X G (column tiles of half ph)
@@ -1058,10 +1108,12 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
     {
       float gs = 0.f;
 #pragma unroll
-      for (int k = 0; k < SL; ++k) {
-        const int i = tid + T * k;
-        float* const pst = &ST[(i / N) * SB + i % N];
-        gs = fmaf(*pst, rs[k], gs);
+      for (int k = 0; k < SV; ++k) {
+        const int e = 4 * (tid + T * k);
+        f32x4* const pst = (f32x4*)&ST[(e / N) * SB + e % N];
+        const f32x4 gv = *pst;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) gs = fmaf(gv[m], rs[k][m], gs);
         *pst = rs[k];
       }
       gs = wave_sum64(gs);
@@ -1510,7 +1562,9 @@ extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const
   hipLaunchKernelGGL(carry, dim3((unsigned)(batch * heads)), dim3(kScanThreads), 0, stream, dA_cumsum, C, dy,
                      dh_final, Gbuf, dh0, seqlen, (int)heads, nc);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
-  auto chunk_k = dstate == 128 ? ssd_bwd_chunk_kernel<128> : ssd_bwd_chunk_kernel<64>;
+  const bool vec = aligned16(x) && aligned16(dy) && aligned16(B) && aligned16(C) && aligned16(block_states);
+  auto chunk_k = dstate == 128 ? (vec ? ssd_bwd_chunk_kernel<128, true> : ssd_bwd_chunk_kernel<128, false>)
+                               : (vec ? ssd_bwd_chunk_kernel<64, true> : ssd_bwd_chunk_kernel<64, false>);
   hipLaunchKernelGGL(chunk_k, dim3((unsigned)(batch * nc * sp.ngrp)), dim3(kScanThreads), 0, stream, x, dt_out,
                      dA_cumsum, B, C, D, dy, block_states, Gbuf, dx, ddA_cumsum, ddt_out, dBp, dCp, dDp, seqlen,
                      (int)heads, nc, sp.hpg, sp.ngrp, gstride);

@@ -236,6 +236,38 @@ def test_scan_backward_is_bit_identical_across_runs():
                 assert v.tobytes() == runs[0][k].tobytes(), k
 
 
+
+@pytest.mark.parametrize("dstate", [128, 64])
+def test_backward_wide_and_narrow_loads_agree_bit_for_bit(dstate):
+    """With x, dy, B, C and the block states 16-byte aligned the backward's chunk kernel
+    loads them as 16-byte pieces; a dy that is not 16-byte aligned sends the same call
+    down the one-value path.  The staged tiles are the same and both paths take the
+    entering state in the same pieces, so every output must be bit-identical."""
+    from selective_state_space_03_amd import ops
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=2, seqlen=300, heads=5, dstate=dstate, h0=True)
+    say("ssd scan bwd wide vs narrow loads, d_state %d" % dstate)
+    cs, dto = ops.ssd_chunk_cumsum_fwd(to_dev32(inp["dt"]), to_dev32(inp["A"]), inp["chunk"],
+                                       dt_bias=to_dev32(inp["dt_bias"]))
+    b, l, h, p = inp["x"].shape
+    x, Bm, Cm, D = to_dev32(inp["x"]), to_dev32(inp["B"]), to_dev32(inp["C"]), to_dev32(inp["D"])
+    bs = torch.empty(ops.ssd_block_states_shape(b, l, h, p, dstate), dtype=torch.float32, device="cuda")
+    ops.ssd_chunk_scan_fwd(x, dto, cs, Bm, Cm, D=D, h0=to_dev32(inp["h0"]), block_states=bs)
+    rng = np.random.default_rng(w.seed + 17)
+    dy = to_dev32(rng.standard_normal(inp["x"].shape))
+    dhf = to_dev32(rng.standard_normal((b, h, p, dstate)))
+    buf = torch.zeros(dy.numel() + 1, dtype=torch.float32, device="cuda")
+    dy_odd = buf[1:].view(dy.shape)  # contiguous, 4 bytes past a 16-byte boundary
+    dy_odd.copy_(dy)
+    outs = []
+    for d in (dy, dy_odd):
+        g = ops.ssd_chunk_scan_bwd(x, dto, cs, Bm, Cm, d, bs, D=D, dh_final=dhf, return_dh0=True)
+        torch.cuda.synchronize()
+        outs.append({k: host(v) for k, v in g.items() if v is not None})
+    assert outs[0].keys() == outs[1].keys()
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+
 def test_scan_backward_full_workload_sampled_sequences():
     w = W.SSD_SCAN_WORKLOADS["ssd_scan_b8_l2048_h64_p64_n128"]
     inp = W.make_ssd_scan_inputs(w)
