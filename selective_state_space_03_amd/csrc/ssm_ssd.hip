@@ -416,9 +416,16 @@ ssd_cb_kernel(const float* __restrict__ Bm, const float* __restrict__ Cm, float*
   }
 }
 
-// VEC: x, B and C are 16-byte aligned, and each thread loads the next chunk as 16-byte
-// pieces (x: 4 channels of one step; B, C: 4 consecutive values of the block), 10 loads
-// per thread instead of 40 single values; B and C are then staged with 16-byte writes.
+// 16 bytes through a buffer resource (0 outside its range)
+__device__ __forceinline__ f32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// VEC: x, B and C are 16-byte aligned (and a chunk's x rows span under 2 GB), and each
+// thread loads the next chunk as 16-byte pieces (x: 4 channels of one step; B, C: 4
+// consecutive values of the block) through buffer resources, 10 loads per thread instead
+// of 40 single values and no per-load address arithmetic; B and C are then staged with
+// 16-byte writes.
 template <int N, bool SAVE, bool VEC>
 __global__ void __launch_bounds__(kScanThreads)
 ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
@@ -474,27 +481,30 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   const float* const bt = Bm + b * L * N + tid;
   const float* const ct = Cm + b * L * N + tid;
   const int64_t xstep = (int64_t)(T / P) * H * P;
+  // x piece k of a thread: step (tid + T k) / 16, channels 4 ((tid + T k) % 16) ..; B/C piece
+  // k: values 4 (tid + T k) .. of the chunk's block.  Byte offsets within the chunk are the
+  // same for every chunk; a chunk's descriptors end after its last valid step, so pieces
+  // of later steps (and every piece past the last chunk) read 0.
+  uint32_t xo4[VEC ? XV : 1];
+#pragma unroll
+  for (int k = 0; k < (VEC ? XV : 1); ++k) {
+    const int i = tid + T * k;
+    xo4[k] = (uint32_t)((i / (P / 4)) * H * P + 4 * (i % (P / 4))) * 4u;
+  }
   auto load_chunk_v = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W;
     const int64_t nv = c < nc ? L - t0 : 0;  // valid steps of the chunk (may exceed W)
-    {
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      // x piece i: step i / 16, channels 4 (i % 16) ..; B/C piece i: values 4 i .. of the block
-      const float* const xb = x + ((b * L + t0) * H + h) * P;
-      const float* const bb = Bm + (b * L + t0) * N;
-      const float* const cb = Cm + (b * L + t0) * N;
+    const int nvw = nv < W ? (int)nv : W;
+    const auto rxs = tile_rsrc(x + ((b * L + t0) * H + h) * P, nvw > 0 ? ((int64_t)(nvw - 1) * H * P + P) * 4 : 0);
+    const auto rbs = tile_rsrc(Bm + (b * L + t0) * N, (int64_t)nvw * N * 4);
+    const auto rcs = tile_rsrc(Cm + (b * L + t0) * N, (int64_t)nvw * N * 4);
 #pragma unroll
-      for (int k = 0; k < XV; ++k) {
-        const int i = tid + T * k, st = i / (P / 4);
-        rx4[k] = st < nv ? *(const f32x4*)(xb + (int64_t)st * H * P + 4 * (i % (P / 4))) : zero;
-      }
+    for (int k = 0; k < XV; ++k) rx4[k] = ld16(rxs, xo4[k]);
 #pragma unroll
-      for (int k = 0; k < BV; ++k) {
-        const int i = tid + T * k;
-        const bool v = (4 * i) / N < nv;
-        rb4[k] = v ? *(const f32x4*)(bb + 4 * i) : zero;
-        rc4[k] = v ? *(const f32x4*)(cb + 4 * i) : zero;
-      }
+    for (int k = 0; k < BV; ++k) {
+      const uint32_t o = (uint32_t)(tid + T * k) * 16u;
+      rb4[k] = ld16(rbs, o);
+      rc4[k] = ld16(rcs, o);
     }
   };
   auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
@@ -578,6 +588,21 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
           block_states[((bh * nc + c) * P + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
       }
     __syncthreads();
+    // C_i.B_s of this wave's causal blocks (step blocks ph, ph + 2 that are <= rb) from
+    // the shared table, in flight during C S^T
+    const bool one = ph <= rb, two = ph + 2 <= rb;  // wave-uniform
+    f32x4 G0 = {0.f, 0.f, 0.f, 0.f}, G1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const float* const cbt = CBw + ((b * nc + c) * W + 16 * rb + 4 * lq) * W + lr;
+      if (one) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G0[r] = cbt[r * W + ph * 16];
+      }
+      if (two) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G1[r] = cbt[r * W + (ph + 2) * 16];
+      }
+    }
     load_chunk(c + 1);  // in flight during the products below (zeros past the end)
 
     // ---- outputs of rows 16 rb .., columns 32 ph ..: inter-chunk part
@@ -600,18 +625,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int r = 0; r < 4; ++r) Y[q][r] *= ecs[r];
     // ---- masked C B^T for step blocks sb = ph, ph + 2 (those <= rb), two accumulators
     {
-      const bool two = ph + 2 <= rb;  // wave-uniform
-      if (ph <= rb) {
-        // C_i.B_s of this block from the shared table (the same for every head)
+      if (one) {
         const int s0 = ph * 16, s1 = (ph + 2) * 16;
-        const float* const cbt = CBw + ((b * nc + c) * W + i0 + 4 * lq) * W + lr;
-        f32x4 G0, G1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) G0[r] = cbt[r * W + s0];
-        if (two) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) G1[r] = cbt[r * W + s1];
-        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           if (u == 1 && !two) break;
@@ -1497,7 +1512,8 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
   const dim3 grid((unsigned)(batch * heads));
   // (saving the block states is a separate instantiation: the plain forward stays as lean)
-  const bool vec = ((uintptr_t)x & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & 15) == 0;
+  const bool vec = ((uintptr_t)x & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & 15) == 0 &&
+                   (double)chunk * heads * headdim * 4 < (double)((int64_t)1 << 31);
   auto kern = dstate == 128
                   ? (block_states ? (vec ? ssd_chunk_scan_fwd_kernel<128, true, true> : ssd_chunk_scan_fwd_kernel<128, true, false>)
                                   : (vec ? ssd_chunk_scan_fwd_kernel<128, false, true> : ssd_chunk_scan_fwd_kernel<128, false, false>))
