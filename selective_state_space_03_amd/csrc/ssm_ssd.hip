@@ -421,7 +421,7 @@ __device__ __forceinline__ f32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// VEC: x, B and C are 16-byte aligned (and a chunk's x rows span under 2 GB), and each
+// VEC: x, B and C are 16-byte aligned (and a block's x rows span under 2 GB), and each
 // thread loads the next chunk as 16-byte pieces (x: 4 channels of one step; B, C: 4
 // consecutive values of the block) through buffer resources, 10 loads per thread instead
 // of 40 single values and no per-load address arithmetic; B and C are then staged with
@@ -485,11 +485,13 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   // k: values 4 (tid + T k) .. of the chunk's block.  Byte offsets within the chunk are the
   // same for every chunk; a chunk's descriptors end after its last valid step, so pieces
   // of later steps (and every piece past the last chunk) read 0.
-  uint32_t xo4[VEC ? XV : 1];
+  uint32_t xo4[VEC ? XV : 1] = {};
+  if constexpr (VEC) {
 #pragma unroll
-  for (int k = 0; k < (VEC ? XV : 1); ++k) {
-    const int i = tid + T * k;
-    xo4[k] = (uint32_t)((i / (P / 4)) * H * P + 4 * (i % (P / 4))) * 4u;
+    for (int k = 0; k < XV; ++k) {
+      const int i = tid + T * k;
+      xo4[k] = (uint32_t)(((int64_t)(i / (P / 4)) * H * P + 4 * (i % (P / 4))) * 4);
+    }
   }
   auto load_chunk_v = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W;
@@ -1513,7 +1515,7 @@ extern "C" int ssm_ssd_chunk_scan_fwd(const float* x, const float* dt_out, const
   const dim3 grid((unsigned)(batch * heads));
   // (saving the block states is a separate instantiation: the plain forward stays as lean)
   const bool vec = ((uintptr_t)x & 15) == 0 && ((uintptr_t)B & 15) == 0 && ((uintptr_t)C & 15) == 0 &&
-                   (double)chunk * heads * headdim * 4 < (double)((int64_t)1 << 31);
+                   (double)kScanW * heads * headdim * 4 < (double)((int64_t)1 << 31);
   auto kern = dstate == 128
                   ? (block_states ? (vec ? ssd_chunk_scan_fwd_kernel<128, true, true> : ssd_chunk_scan_fwd_kernel<128, true, false>)
                                   : (vec ? ssd_chunk_scan_fwd_kernel<128, false, true> : ssd_chunk_scan_fwd_kernel<128, false, false>))

@@ -8,7 +8,9 @@ and an initial state.  The scan is
 checked both as a pipeline (the GPU chunk cumsum feeding it) and alone (fed the
 oracle's dt_out and dA_cumsum rounded to fp32).  On the full workload (8 x 2048, 64
 heads of 64, d_state 128) sampled (batch, head) sequences are compared with the oracle
-run on that sequence alone (sequences are independent).  Repeated runs are
+run on that sequence alone (sequences are independent).  Around the head count at which a
+block's x rows reach 2 GB (131071 and 131072 heads of 64), where the scan switches from
+16-byte to one-value loads, sampled heads are compared the same way.  Repeated runs are
 bit-identical, and unsupported sizes are refused.
 """
 import numpy as np
@@ -100,6 +102,27 @@ def test_full_workload_sampled_sequences():
         assert rel_err(y[b, :, h], ref["y"][0, :, 0]) <= RTOL_F32
         assert rel_err(hf[b, h], ref["h_final"][0, 0]) <= RTOL_F32
 
+
+
+@pytest.mark.parametrize("heads", [131071, 131072])
+def test_heads_at_the_wide_load_offset_bound(heads):
+    """A 64-step block's x rows span 64 x heads x headdim x 4 bytes.  The 16-byte chunk
+    loads address them with 32-bit offsets, so from 2 GB on the scan takes the one-value
+    path instead.  131072 heads of 64 are exactly 2 GB and 131071 just below it: sampled
+    heads of a two-step sequence against the oracle, on both sides of the bound."""
+    from selective_state_space_03_amd import ops
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=1, seqlen=2, heads=heads, dstate=64, seed=w.seed + heads)
+    say("ssd scan, %d heads of 64, two steps" % heads)
+    cs, dto = ops.ssd_chunk_cumsum_fwd(to_dev32(inp["dt"]), to_dev32(inp["A"]), inp["chunk"],
+                                       dt_bias=to_dev32(inp["dt_bias"]))
+    y, _ = ops.ssd_chunk_scan_fwd(to_dev32(inp["x"]), dto, cs, to_dev32(inp["B"]), to_dev32(inp["C"]),
+                                  D=to_dev32(inp["D"]), h_final=None)
+    torch.cuda.synchronize()
+    y = host(y)
+    for h in (0, 77777, heads - 1):
+        ref = oracle_run(inp, 0, h)
+        assert rel_err(y[0, :, h], ref["y"][0, :, 0]) <= RTOL_F32, h
 
 def test_repeat_runs_are_bit_identical():
     w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
