@@ -778,20 +778,22 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
   // Thread (wave w, lane l) moves steps 8 w .. 8 w + 7 of channel l of dy and of states
   // l, l + 64 of C: each of its loads is one contiguous 256-byte row across the wave, and
   // its 8 steps go to the transposed tiles as two 16-byte writes (no bank conflicts).
-  // Loads go through buffer resources with uniform bases and 32-bit lane offsets; a
-  // chunk's range ends after its last valid step, so rows past the end read 0.
-  static_assert(W == 8 * (T / 64) && YL == 8 && CL == 8 * (N / 64), "8 steps per thread");
-  const unsigned yoff = (unsigned)((8 * wave) * H * P + lane) * 4u;
-  const unsigned ystep4 = (unsigned)(H * P) * 4u;
+  // Loads go through buffer resources with uniform bases and 32-bit lane offsets: one per
+  // dy row (rows are H P values apart, too far for 32-bit offsets at many heads), one
+  // per chunk of C; rows past the chunk's last valid step read 0.
+  static_assert(W == 8 * (T / 64) && YL == 8 && CL == 8 * (N / 64) && P == 64, "8 steps per thread");
   const unsigned coff = (unsigned)((8 * wave) * N + lane) * 4u;
   float ry[YL], rc[CL], rcs = 0.f;
   auto load_chunk = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * W, nv = L - t0;  // valid steps (at least 1, may exceed W)
     const int nvw = nv < W ? (int)nv : W;
-    const auto rdy = tile_rsrc(dy + ((b * L + t0) * H + h) * P, ((int64_t)(nvw - 1) * H * P + P) * 4);
+    const float* const yw = dy + ((b * L + t0 + 8 * wave) * H + h) * P;  // this wave's first row
     const auto rcm = tile_rsrc(Cm + (b * L + t0) * N, (int64_t)nvw * N * 4);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ry[k] = buf_ld<float>(rdy, yoff + k * ystep4);
+    for (int k = 0; k < 8; ++k) {
+      const auto rdy = tile_rsrc(yw + (int64_t)k * H * P, 8 * wave + k < nvw ? P * 4 : 0);
+      ry[k] = buf_ld<float>(rdy, (unsigned)lane * 4u);
+    }
 #pragma unroll
     for (int q = 0; q < N / 64; ++q)
 #pragma unroll

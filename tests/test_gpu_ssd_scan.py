@@ -10,7 +10,9 @@ oracle's dt_out and dA_cumsum rounded to fp32).  On the full workload (8 x 2048,
 heads of 64, d_state 128) sampled (batch, head) sequences are compared with the oracle
 run on that sequence alone (sequences are independent).  Around the head count at which a
 block's x rows reach 2 GB (131071 and 131072 heads of 64), where the scan switches from
-16-byte to one-value loads, sampled heads are compared the same way.  Repeated runs are
+16-byte to one-value loads, sampled heads are compared the same way.  The backward is
+checked the same way at 266400 heads of 64, where one chunk's dy rows span more than
+4 GB.  Repeated runs are
 bit-identical, and unsupported sizes are refused.
 """
 import numpy as np
@@ -306,6 +308,43 @@ def test_scan_backward_full_workload_sampled_sequences():
         assert rel_err(g["dh0"][b, h], r["dh0"][0, 0]) <= RTOL_F32
         assert rel_err(g["ddt_raw"][b, :, h], r["ddt_raw"][0, :, 0]) <= RTOL_F32
 
+
+
+def test_scan_backward_rows_more_than_4gb_apart_in_a_chunk():
+    """dy rows of one chunk are heads x headdim x 4 bytes apart.  At 266400 heads of 64 a
+    full chunk's 64 rows span more than 4 GB, past any 32-bit offset from the chunk's
+    first row.  One full chunk; x and dy (1.1 G values each) are drawn on the device from
+    a seeded generator, the rest on the host.  Sampled heads are compared with the oracle
+    run on that head alone."""
+    from selective_state_space_03_amd import ops
+    b, l, h, p, n, chunk = 1, 64, 266400, 64, 64, 64
+    assert 63 * h * p * 4 >= 1 << 32
+    rng = np.random.default_rng(4242)
+    dt = rng.standard_normal((b, l, h)).astype(np.float32)
+    dt_bias = np.log(np.expm1(rng.uniform(1e-3, 1e-1, h))).astype(np.float32)
+    A = (-rng.uniform(1.0, 16.0, h)).astype(np.float32)
+    Bm = rng.standard_normal((b, l, n)).astype(np.float32)
+    Cm = rng.standard_normal((b, l, n)).astype(np.float32)
+    D = np.ones(h, np.float32)
+    gen = torch.Generator(device="cuda").manual_seed(4243)
+    x = torch.randn((b, l, h, p), generator=gen, device="cuda")
+    dy = torch.randn((b, l, h, p), generator=gen, device="cuda")
+    say("ssd scan bwd, %d heads of 64, one chunk" % h)
+    cs, dto = ops.ssd_chunk_cumsum_fwd(to_dev32(dt), to_dev32(A), chunk, dt_bias=to_dev32(dt_bias))
+    Bd, Cd, Dd = to_dev32(Bm), to_dev32(Cm), to_dev32(D)
+    bs = torch.empty(ops.ssd_block_states_shape(b, l, h, p, n), dtype=torch.float32, device="cuda")
+    ops.ssd_chunk_scan_fwd(x, dto, cs, Bd, Cd, D=Dd, h_final=None, block_states=bs)
+    g = ops.ssd_chunk_scan_bwd(x, dto, cs, Bd, Cd, dy, bs, D=Dd, return_dh0=True)
+    gc = ops.ssd_chunk_cumsum_bwd(g["ddA_cumsum"], g["ddt_out"], to_dev32(dt), to_dev32(A), dt_bias=to_dev32(dt_bias))
+    torch.cuda.synchronize()
+    for hh in (0, 123457, h - 1):
+        one = {"seqlen": l, "chunk": chunk, "dt": dt[:, :, hh:hh + 1], "A": A[hh:hh + 1],
+               "dt_bias": dt_bias[hh:hh + 1], "x": host(x[:, :, hh:hh + 1]), "B": Bm, "C": Cm,
+               "D": D[hh:hh + 1], "h0": None}
+        r = oracle_bwd(one, host(dy[:, :, hh:hh + 1]), None)
+        assert rel_err(host(g["dx"][:, :, hh]), r["dx"][:, :, 0]) <= RTOL_F32, hh
+        assert rel_err(host(g["dh0"][:, hh]), r["dh0"][:, 0]) <= RTOL_F32, hh
+        assert rel_err(host(gc["ddt"][:, :, hh]), r["ddt_raw"][:, :, 0]) <= RTOL_F32, hh
 
 def test_scan_backward_full_length_all_heads_one_batch_element():
     """Every output of the backward at the workload's per-sequence size (L = 2048,
