@@ -271,24 +271,39 @@ conv_bwd_kernel(const float* __restrict__ x, const float* __restrict__ w, const 
   }
 }
 
-// dw[d,k] and dbias[d]: sums of the partials over (b, segment) in lexical order
+// dw[d,k] and dbias[d]: sums of the partials over (b, segment) in a fixed order.  A
+// workgroup takes 32 outputs (output j < K Dm is dw's (k, d) = (j / Dm, j % Dm), the
+// next Dm are dbias); each of 8 threads per output adds a contiguous eighth of the
+// parts in lexical order, and the 8 sums are then added in part order.
+constexpr int kRedOut = 32, kRedGroups = 8;
 template <int K>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRedOut * kRedGroups)
 conv_reduce_kernel(const float* __restrict__ pdw, const float* __restrict__ pdb, float* __restrict__ dw,
                    float* __restrict__ dbias, int64_t nparts, int64_t Dm) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (k, d), d fastest
-  if (i < K * Dm && dw) {
-    const int64_t k = i / Dm, d = i % Dm;
-    float s = 0.f;
+  __shared__ float sums[kRedGroups][kRedOut];
+  const int o = threadIdx.x % kRedOut, g = threadIdx.x / kRedOut;
+  const int64_t j = (int64_t)blockIdx.x * kRedOut + o;
+  const bool isw = j < K * Dm;
+  const bool live = isw ? dw != nullptr : (j < (K + 1) * Dm && dbias != nullptr);
+  const int64_t per = (nparts + kRedGroups - 1) / kRedGroups;
+  const int64_t p0 = g * per, p1 = p0 + per < nparts ? p0 + per : nparts;
+  float s = 0.f;
+  if (live) {
+    const float* const src = isw ? pdw + j : pdb + (j - K * Dm);
+    const int64_t stride = isw ? K * Dm : Dm;
 #pragma unroll 8
-    for (int64_t p = 0; p < nparts; ++p) s += pdw[p * K * Dm + i];
-    dw[d * K + k] = s;
+    for (int64_t p = p0; p < p1; ++p) s += src[p * stride];
   }
-  if (i < Dm && dbias) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int64_t p = 0; p < nparts; ++p) s += pdb[p * Dm + i];
-    dbias[i] = s;
+  sums[g][o] = s;
+  __syncthreads();
+  if (g == 0 && live) {
+    float t = sums[0][o];
+#pragma unroll
+    for (int q = 1; q < kRedGroups; ++q) t += sums[q][o];
+    if (isw)
+      dw[(j % Dm) * K + j / Dm] = t;
+    else
+      dbias[j - K * Dm] = t;
   }
 }
 
@@ -346,9 +361,9 @@ hipError_t bwd_k(const ConvArgs& a, void* ws, hipStream_t stream) {
                      (const float*)a.dout, (float*)a.dx, pdw, pdb, a.seqlen, a.dim, ngroups, l.ntg, l.tgs, l.nseg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = K * a.dim;
-  hipLaunchKernelGGL((conv_reduce_kernel<K>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, pdw, pdb,
-                     a.dw, a.dbias, a.batch * l.nseg, a.dim);
+  const int64_t n = (K + 1) * a.dim;
+  hipLaunchKernelGGL((conv_reduce_kernel<K>), dim3((unsigned)((n + kRedOut - 1) / kRedOut)),
+                     dim3(kRedOut * kRedGroups), 0, stream, pdw, pdb, a.dw, a.dbias, a.batch * l.nseg, a.dim);
   return hipGetLastError();
 }
 
