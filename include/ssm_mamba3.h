@@ -40,8 +40,9 @@
  *   (epsilon < 0 or not finite, dt_min < 0, dt_min > dt_max, a NaN bound or floor),
  *   SSM_ERR_ALIGN, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE, SSM_ERR_HIP.  d_dt_bias may be
  *   NULL (not written).
- * d_dt_bias is summed in two fixed-order passes (64-row chunks in ascending row order,
- * then the chunk sums in ascending order) through a caller workspace of
+ * d_dt_bias is summed in fixed-order passes (64-row chunks in ascending row order; the
+ * chunk sums in eight contiguous runs, each in ascending order; then the eight run sums
+ * in ascending order) through a caller workspace of
  * ssm_mamba3_preprocess_bwd_workspace_bytes(rows, heads) bytes, 256-byte aligned,
  * required when d_dt_bias is given; its contents on entry are ignored.
  */

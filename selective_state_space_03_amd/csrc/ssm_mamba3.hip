@@ -129,15 +129,30 @@ m3_dt_bias_chunk_kernel(const float* __restrict__ partial, float* __restrict__ c
   chunk_sums[blockIdx.x * heads + h] = acc;
 }
 
-__global__ void __launch_bounds__(64)
+// the chunk sums of 64 heads: 8 threads per head each add a contiguous eighth of the
+// chunks in ascending order, then the 8 sums are added in ascending order
+constexpr int kFinalGroups = 8;
+__global__ void __launch_bounds__(64 * kFinalGroups)
 m3_dt_bias_final_kernel(const float* __restrict__ chunk_sums, float* __restrict__ d_dt_bias, int64_t nchunks,
                         int64_t heads) {
-  const int64_t h = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (h >= heads) return;
+  __shared__ float sums[kFinalGroups][64];
+  const int o = threadIdx.x % 64, g = threadIdx.x / 64;
+  const int64_t h = (int64_t)blockIdx.x * 64 + o;
+  const int64_t per = (nchunks + kFinalGroups - 1) / kFinalGroups;
+  const int64_t c0 = g * per, c1 = c0 + per < nchunks ? c0 + per : nchunks;
   float acc = 0.f;
-#pragma unroll 16
-  for (int64_t c = 0; c < nchunks; ++c) acc += chunk_sums[c * heads + h];
-  d_dt_bias[h] = acc;
+  if (h < heads) {
+#pragma unroll 8
+    for (int64_t c = c0; c < c1; ++c) acc += chunk_sums[c * heads + h];
+  }
+  sums[g][o] = acc;
+  __syncthreads();
+  if (g == 0 && h < heads) {
+    float t = sums[0][o];
+#pragma unroll
+    for (int q = 1; q < kFinalGroups; ++q) t += sums[q][o];
+    d_dt_bias[h] = t;
+  }
 }
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
@@ -224,8 +239,8 @@ extern "C" int ssm_mamba3_preprocess_bwd(const float* projected, const float* dt
     hipLaunchKernelGGL(m3_dt_bias_chunk_kernel, dim3((unsigned)nchunks, hgroups), dim3(64), 0, stream,
                        dt_bias_partial, chunk_sums, rows, heads);
     if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
-    hipLaunchKernelGGL(m3_dt_bias_final_kernel, dim3(hgroups), dim3(64), 0, stream, chunk_sums, d_dt_bias,
-                       nchunks, heads);
+    hipLaunchKernelGGL(m3_dt_bias_final_kernel, dim3(hgroups), dim3(64 * kFinalGroups), 0, stream, chunk_sums,
+                       d_dt_bias, nchunks, heads);
     if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
   }
   return SSM_OK;
