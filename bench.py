@@ -1,7 +1,7 @@
 """Benchmark of the gfx950 selective-scan hot path on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                  [--only fwd|bf16|long|step|fwd5|bwd|bwd_bf16|train|mamba3|ssd|conv|conv_bf16|conv_step|conv_bwd|copy]
+                  [--only fwd|bf16|long|step|decode|fwd5|bwd|bwd_bf16|train|mamba3|ssd|conv|conv_bf16|conv_step|conv_bwd|copy]
 
 Timed step: one forward scan of the workload B=8, L=2048, d_inner=1536, N=16, fp32
 I/O, SiLU gate (x, delta_raw, z, B, C, A_log, D_skip, dt_bias in HBM; y and the
@@ -14,7 +14,7 @@ Printed: ONE JSON line on stdout (everything else goes to stderr) with the
 headline forward GB/s, its roofline (algorithmic bytes per launch / average launch
 time from HIP events on the launch stream, against 8 TB/s), the fp64 CPU oracle
 timed on the host cores, and secondary lines for the bf16 forward, the decode
-step, the backward, the conv1d, the Mamba-3 preprocess adjoint and the Mamba-2 SSD
+step (alone, and fused with the conv1d step), the backward, the conv1d, the Mamba-3 preprocess adjoint and the Mamba-2 SSD
 chunk cumsum and scan (the scan also in TFLOP/s against the fp32 matrix-core
 peak).  `traffic` comes from the committed rocprofv3 counter
 summary for the forward kernel when that summary matches the current kernel
@@ -124,6 +124,12 @@ def conv_bytes(b, l, d, k, es):
 def conv_step_bytes(b, d, k, es):
     """one decode step: state read and written, x read, out written, weight and bias read"""
     return 2 * b * d * (k - 1) * es + 2 * b * d * es + d * k * 4 + d * 4
+
+
+def decode_bytes(b, d, n, k, es, gated):
+    """the fused decode step: the scan step's and the conv1d step's bytes, less the
+    convolution's output, which neither writes nor reads (x enters the convolution)"""
+    return step_bytes(b, d, n, es, gated) + conv_step_bytes(b, d, k, es) - 2 * b * d * es
 
 
 def conv_bwd_bytes(b, l, d, k):
@@ -268,7 +274,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    choices=["all", "fwd", "bf16", "long", "step", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
+                    choices=["all", "fwd", "bf16", "long", "step", "decode", "fwd5", "bwd", "bwd_bf16", "train", "mamba3", "conv", "conv_bf16", "conv_step", "conv_bwd",
                              "ssd", "copy"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -371,6 +377,51 @@ def main():
         log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d" %
             (name, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets))
         return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs)
+
+    def decode_case(name="step_b256_d5120", conv="conv_step_b256_d5120_k4"):
+        # the fused decode step (conv1d step, then the scan step, one launch), and the
+        # same token through the two separate launches for comparison
+        w, cw = W.WORKLOADS[name], W.CONV_WORKLOADS[conv]
+        inp, cin = W.make_inputs(w), W.make_conv_inputs(cw, batch=w.batch, dim=w.dim)
+        nb = decode_bytes(w.batch, w.dim, w.dstate, cw.width, 4, w.gated)
+        nsets = max(2, int(np.ceil(1.2e9 / nb)))
+        base = dict(st=t32(inp["state"]), cs=t32(cin["state"]), x=t32(cin["x"]), dr=t32(inp["delta_raw"]),
+                    z=t32(inp["z"]), B=t32(inp["B"]), C=t32(inp["C"]))
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+        A_log, Dsk, dtb = t32(inp["A_log"]), t32(inp["D"]), t32(inp["dt_bias"])
+        wt, cb = t32(cin["weight"]), t32(cin["bias"])
+        ys = [torch.empty_like(base["x"]) for _ in range(nsets)]
+        us = [torch.empty_like(base["x"]) for _ in range(nsets)]
+        act = ops.SSM_ACT_SILU if cw.silu else ops.SSM_ACT_NONE
+        fused, pair = [], []
+        for i, s in enumerate(sets):
+            ops.decode_step(s["cs"], s["x"], wt, s["st"], s["dr"], s["B"], s["C"], A_log, conv_bias=cb, silu=cw.silu,
+                            D_skip=Dsk, dt_bias=dtb, z=s["z"], y=ys[i])
+            fused.append(direct("ssm_decode_step", s["cs"], s["x"], wt, cb, cw.width, act, s["st"], s["dr"], s["z"],
+                                s["B"], s["C"], A_log, Dsk, dtb, None, ys[i], w.batch, w.dim, w.dstate, ops.SSM_F32,
+                                None, ops._stream()))
+            c1 = direct("ssm_conv1d_step", s["cs"], s["x"], wt, cb, us[i], w.batch, w.dim, cw.width, act,
+                        ops.SSM_F32, ops._stream())
+            c2 = direct("ssm_scan_step", s["st"], us[i], s["dr"], s["z"], s["B"], s["C"], A_log, Dsk, dtb, ys[i],
+                        w.batch, w.dim, w.dstate, ops.SSM_F32, ops._stream())
+            pair.append((c1, c2))
+
+        def fn(i):
+            fused[i]()
+
+        def fn_pair(i):
+            pair[i][0]()
+            pair[i][1]()
+
+        wall_ms, ev_ms, ev_min = timer.run(fn, K, Wm, nsets)
+        gbs = nb / (ev_ms * 1e-3) / 1e9
+        pw, pe, pm = timer.run(fn_pair, K, Wm, nsets)
+        label = "decode_b%d_d%d_k%d" % (w.batch, w.dim, cw.width)
+        log("%-26s %8.1f us/launch (min %.1f, wall %.1f)  %7.1f GB/s  %.1f%% of 8 TB/s  sets=%d  "
+            "(conv1d step + scan step as two launches: %.1f us)" %
+            (label, ev_ms * 1e3, ev_min * 1e3, wall_ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, nsets, pe * 1e3))
+        return dict(workload=w, bytes=nb, wall_ms=wall_ms, ev_ms=ev_ms, ev_min_ms=ev_min, gbs=gbs,
+                    pair_us=pe * 1e3)
 
     def bwd_case(name="fwdbwd_b4_l2048_d2048", io="fp32", saved=False):
         # io = "bf16": the same workload with its activations, B, C and dy rounded to bf16
@@ -634,6 +685,8 @@ def main():
         results["fwd_long_b1_l65536_d1536"] = fwd_case("fwd_long_b1_l65536_d1536")
     if args.only in ("all", "step"):
         results["step_b256_d5120"] = step_case()
+    if args.only in ("all", "decode"):
+        results["decode_b256_d5120_k4"] = decode_case()
     if args.only in ("all", "bwd"):
         results["bwd_b4_l2048_d2048"] = bwd_case()
     if args.only in ("all", "bwd_bf16"):
@@ -686,6 +739,8 @@ def main():
             secondary[k]["flops"] = v["flops"]
         if v["workload"].kind in ("fwd", "fwdbwd"):
             secondary[k]["state_updates_per_s"] = round(v["workload"].state_updates / (v["ev_ms"] * 1e-3), 1)
+        if "pair_us" in v:
+            secondary[k]["two_launches_us"] = round(v["pair_us"], 1)
 
     out = {
         "metric": "selective-scan fwd achieved HBM GB/s and % of peak at 1 MI355X; step/bwd GB/s",

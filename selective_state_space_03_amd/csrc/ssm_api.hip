@@ -7,6 +7,7 @@
 #include <new>
 
 #include "../../include/ssm_conv1d.h"
+#include "../../include/ssm_decode.h"
 #include "../../include/ssm_scan.h"
 #include "ssm_internal.h"
 
@@ -246,6 +247,51 @@ int ssm_scan_step_ex(float* state, const void* x, const void* delta_raw, const v
   a.D_skip = D_skip; a.dt_bias = dt_bias; a.y = y;
   a.batch = batch; a.dim = d_inner; a.dstate = (int)d_state; a.bf16 = io_dtype == SSM_BF16;
   a.dt_lo = dt_lo; a.dt_hi = dt_hi;
+  return ssm::launch_step(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_decode_step(void* conv_state, const void* x, const float* conv_weight, const float* conv_bias,
+                    int64_t width, int activation, float* state, const void* delta_raw, const void* z,
+                    const void* B, const void* C, const float* A_log, const float* D_skip,
+                    const float* dt_bias, void* u, void* y, int64_t batch, int64_t d_inner, int64_t d_state,
+                    int io_dtype, const ssm_scan_options* options, hipStream_t stream) {
+  if (!state || !x || !conv_weight || !delta_raw || !B || !C || !A_log || !y || (width > 1 && !conv_state))
+    return SSM_ERR_NULL;
+  float dt_lo, dt_hi;
+  if (!options_ok(options, false, &dt_lo, &dt_hi, true)) return SSM_ERR_ARG;
+  if (io_dtype != SSM_F32 && io_dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (activation != SSM_ACT_NONE && activation != SSM_ACT_SILU) return SSM_ERR_UNSUPPORTED;
+  if (!dims_ok(batch, 1, d_inner, d_state) || !conv_dims_ok(batch, 1, d_inner, width)) return SSM_ERR_DIM;
+  if (batch * d_inner * 4 >= ((int64_t)1 << 31) * 256) return SSM_ERR_DIM;  // grid limit
+  const size_t es = esize(io_dtype);
+  const void* io_ptrs[] = {x, delta_raw, z, B, C, y, u, conv_state};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {state, A_log, D_skip, dt_bias, conv_weight, conv_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const size_t E = (size_t)batch * d_inner, S = (size_t)batch * d_state, H = E * d_state;
+  const Range ins[] = {rng(x, E * es), rng(delta_raw, E * es), rng(z, z ? E * es : 0), rng(B, S * es),
+                       rng(C, S * es), rng(A_log, (size_t)d_inner * d_state * 4),
+                       rng(D_skip, D_skip ? d_inner * 4 : 0), rng(dt_bias, dt_bias ? d_inner * 4 : 0),
+                       rng(conv_weight, (size_t)d_inner * width * 4), rng(conv_bias, conv_bias ? d_inner * 4 : 0)};
+  const Range outs[] = {rng(state, H * 4), rng(y, E * es), rng(u, u ? E * es : 0),
+                        rng(conv_state, width > 1 ? E * (width - 1) * es : 0)};
+  const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSM_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+  }
+
+  ssm::StepArgs a;
+  a.state = state; a.x = x; a.delta_raw = delta_raw; a.z = z; a.B = B; a.C = C; a.A_log = A_log;
+  a.D_skip = D_skip; a.dt_bias = dt_bias; a.y = y;
+  a.batch = batch; a.dim = d_inner; a.dstate = (int)d_state; a.bf16 = io_dtype == SSM_BF16;
+  a.dt_lo = dt_lo; a.dt_hi = dt_hi;
+  a.conv_state = width > 1 ? conv_state : nullptr; a.conv_w = conv_weight; a.conv_b = conv_bias; a.u = u;
+  a.width = (int)width; a.silu = activation == SSM_ACT_SILU;
   return ssm::launch_step(a, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -41,7 +41,7 @@ FwdSplit fwd_split(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
 
 struct StepArgs {
   float* state;
-  const void* x;
+  const void* x;  // with a conv1d step first: the token before the convolution
   const void* delta_raw;
   const void* z;  // nullable
   const void* B;
@@ -54,6 +54,15 @@ struct StepArgs {
   int dstate;
   int bf16;
   float dt_lo = 0.f, dt_hi = __builtin_inff();  // clamp of Delta (none by default)
+  // decode: the token first goes through the depthwise conv1d step (width > 0):
+  // conv_state [B, D, width - 1] io dtype, read and shifted in place; conv_w [D, width];
+  // conv_b [D] nullable; u [B, D] io dtype, nullable (the convolution's output)
+  void* conv_state = nullptr;
+  const float* conv_w = nullptr;
+  const float* conv_b = nullptr;
+  void* u = nullptr;
+  int width = 0;
+  bool silu = false;
 };
 
 struct BwdArgs {

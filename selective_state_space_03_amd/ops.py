@@ -17,9 +17,9 @@ Functions mirror the C entry points:
    with the state entering every 16-step chunk, which ssm_scan_bwd then reuses)
 The step-size clamp (dt_min, dt_max) and the state gradients go through the _ex entry
 points and their ssm_scan_options struct; without them the calls are the plain ones.
-Also bound (include/ssm_conv1d.h, ssm_mamba3.h, ssm_ssd.h): conv1d_fwd / conv1d_step /
-conv1d_bwd, mamba3_preprocess_bwd, ssd_chunk_cumsum_fwd / ssd_chunk_cumsum_bwd and
-ssd_chunk_scan_fwd.
+Also bound (include/ssm_conv1d.h, ssm_decode.h, ssm_mamba3.h, ssm_ssd.h): conv1d_fwd /
+conv1d_step / conv1d_bwd, decode_step (the conv1d step and the scan step in one launch),
+mamba3_preprocess_bwd, ssd_chunk_cumsum_fwd / ssd_chunk_cumsum_bwd and ssd_chunk_scan_fwd.
 """
 from __future__ import annotations
 
@@ -42,7 +42,7 @@ EXPORTS = ("ssm_status_string", "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", 
            "ssm_conv1d_bwd", "ssm_conv1d_bwd_noalloc", "ssm_mamba3_preprocess_bwd_workspace_bytes", "ssm_mamba3_preprocess_bwd",
            "ssm_ssd_chunk_cumsum_fwd", "ssm_ssd_chunk_cumsum_bwd_workspace_bytes", "ssm_ssd_chunk_cumsum_bwd",
            "ssm_ssd_chunk_scan_fwd_workspace_bytes", "ssm_ssd_chunk_scan_fwd",
-           "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd")
+           "ssm_ssd_chunk_scan_bwd_workspace_bytes", "ssm_ssd_chunk_scan_bwd", "ssm_decode_step")
 
 
 class ScanOptions(ctypes.Structure):
@@ -97,6 +97,8 @@ def lib():
         L.ssm_conv1d_fwd.restype = I
         L.ssm_conv1d_step.argtypes = [P] * 5 + [I64] * 3 + [I, I, P]
         L.ssm_conv1d_step.restype = I
+        L.ssm_decode_step.argtypes = [P] * 4 + [I64, I] + [P] * 10 + [I64] * 3 + [I, OP, P]
+        L.ssm_decode_step.restype = I
         L.ssm_conv1d_bwd_workspace_bytes.argtypes = [I64] * 4 + [I]
         L.ssm_conv1d_bwd_workspace_bytes.restype = SZ
         L.ssm_conv1d_bwd.argtypes = [P] * 7 + [P, SZ] + [I64] * 4 + [I, I, P]
@@ -326,6 +328,38 @@ def conv1d_step(conv_state, x, weight, bias=None, silu=True, out=None):
                                                     _ptr(bias), _ptr(out), b, d, k,
                                                     SSM_ACT_SILU if silu else SSM_ACT_NONE, io, _stream()))
     return out
+
+
+def decode_step(conv_state, x, conv_weight, state, delta_raw, B, C, A_log, conv_bias=None, silu=True,
+                D_skip=None, dt_bias=None, z=None, u=None, y=None, dt_min=None, dt_max=None):
+    """One decode token (include/ssm_decode.h): the conv1d step on x (conv_state [batch, dim,
+    K-1] shifted in place), then the scan step on its output (state [batch, dim, d_state]
+    updated in place).  u (optional) receives the convolution's output.  Returns y."""
+    b, d, n = state.shape
+    k = conv_weight.shape[1]
+    dev, dt = x.device, x.dtype
+    io = _io_dtype(x)
+    f32 = torch.float32
+    _req(state, "state", (b, d, n), f32, dev)
+    for name, t, shp in (("x", x, (b, d)), ("delta_raw", delta_raw, (b, d)), ("z", z, (b, d)),
+                         ("B", B, (b, n)), ("C", C, (b, n)), ("u", u, (b, d))):
+        _req(t, name, shp, dt, dev)
+    _req(conv_weight, "conv_weight", (d, k), f32, dev)
+    _req(conv_bias, "conv_bias", (d,), f32, dev)
+    if k > 1:
+        _req(conv_state, "conv_state", (b, d, k - 1), dt, dev)
+    _req(A_log, "A_log", (d, n), f32, dev)
+    _req(D_skip, "D_skip", (d,), f32, dev)
+    _req(dt_bias, "dt_bias", (d,), f32, dev)
+    if y is None:
+        y = torch.empty((b, d), dtype=dt, device=dev)
+    _req(y, "y", (b, d), dt, dev)
+    _check("ssm_decode_step", lib().ssm_decode_step(
+        _ptr(conv_state) if k > 1 else None, _ptr(x), _ptr(conv_weight), _ptr(conv_bias), k,
+        SSM_ACT_SILU if silu else SSM_ACT_NONE, _ptr(state), _ptr(delta_raw), _ptr(z), _ptr(B), _ptr(C),
+        _ptr(A_log), _ptr(D_skip), _ptr(dt_bias), _ptr(u), _ptr(y), b, d, n, io, _options(dt_min, dt_max),
+        _stream()))
+    return y
 
 
 def conv1d_bwd_workspace_bytes(batch, seqlen, dim, width, io_dtype=SSM_F32):

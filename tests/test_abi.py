@@ -167,6 +167,37 @@ def test_bwd_validation():
     assert bwd_call(dA_log=addr(14, 2)) == ALIGN
 
 
+
+def decode_call(**over):
+    a = dict(cs=addr(10), x=addr(1), w=addr(11), cb=addr(12), k=4, act=1, state=addr(0), delta_raw=addr(2),
+             z=addr(3), B=addr(4), C=addr(5), A_log=addr(6), D=addr(7), dt_bias=addr(8), u=addr(13), y=addr(9),
+             b=4, d=64, n=16, io=ops.SSM_F32, opts=None, stream=None)
+    a.update(over)
+    return ops.lib().ssm_decode_step(a["cs"], a["x"], a["w"], a["cb"], a["k"], a["act"], a["state"],
+                                     a["delta_raw"], a["z"], a["B"], a["C"], a["A_log"], a["D"], a["dt_bias"],
+                                     a["u"], a["y"], a["b"], a["d"], a["n"], a["io"], a["opts"], a["stream"])
+
+
+@no_gpu_only
+def test_decode_step_validation():
+    assert decode_call(state=None) == NULL
+    assert decode_call(w=None) == NULL
+    assert decode_call(cs=None) == NULL              # width 4 needs the conv state
+    assert decode_call(n=0) == DIM
+    assert decode_call(k=0) == DIM
+    assert decode_call(k=9) == DIM
+    assert decode_call(io=2) == UNSUP
+    assert decode_call(act=5) == UNSUP
+    assert decode_call(cs=addr(10, 2)) == ALIGN       # fp32 conv state needs 4 B
+    assert decode_call(io=ops.SSM_BF16, u=addr(13, 1)) == ALIGN
+    assert decode_call(w=addr(11, 2)) == ALIGN
+    assert decode_call(y=addr(1)) == ALIAS           # y == x
+    assert decode_call(u=addr(9)) == ALIAS           # u == y
+    assert decode_call(cs=addr(11)) == ALIAS         # conv state == weight
+    assert decode_call(cs=addr(0, 64)) == ALIAS      # conv state inside the scan state
+    o = ops.ScanOptions(dt_min=0.5, dt_max=0.1)
+    assert decode_call(opts=ctypes.pointer(o)) == 8  # SSM_ERR_ARG: dt_min > dt_max
+
 # ---------------------------------------------------------------- conv1d
 
 def conv_call(x=addr(0), w=addr(5), bias=addr(6), out=addr(9), b=2, l=64, d=32, k=4, act=1, io=0):
