@@ -9,6 +9,7 @@ bit with the same calls made eagerly:
 
   * a decode step: the depthwise conv1d step (its window state updated in place), then
     the selective-scan step on the conv output (its state updated in place);
+  * the same decode step as one fused call (ssm_decode_step);
   * the SSD forward pair: the chunk cumsum, then the chunked scan.
 
 No entry point records a memset into the graph (every workspace the kernels read is
@@ -92,6 +93,50 @@ def test_decode_step_graph_replays_match_eager():
         torch.cuda.synchronize()
     assert np.isfinite(host(y_g)).all()
 
+
+
+def test_fused_decode_step_graph_replays_match_eager():
+    from selective_state_space_03_amd import ops
+    from selective_state_space_03_amd import workloads as W
+    b, d = 16, 640
+    sc = W.make_inputs(W.WORKLOADS["step_b256_d5120"], batch=b, dim=d)
+    cv = W.make_conv_inputs(W.CONV_WORKLOADS["conv_step_b256_d5120_k4"], batch=b, dim=d)
+    rng = np.random.default_rng(78)
+    toks = [{k: rng.standard_normal(shp).astype(np.float32) for k, shp in
+             (("x", (b, d)), ("dr", (b, d)), ("B", (b, sc["dstate"])), ("C", (b, sc["dstate"])), ("z", (b, d)))}
+            for _ in range(4)]
+    w, cb = t32(cv["weight"]), t32(cv["bias"])
+    A, Dv, dtb = t32(sc["A_log"]), t32(sc["D"]), t32(sc["dt_bias"])
+
+    def step(conv_state, ssm_state, st, y_out):
+        ops.decode_step(conv_state, st["x"], w, ssm_state, st["dr"], st["B"], st["C"], A, conv_bias=cb, silu=True,
+                        D_skip=Dv, dt_bias=dtb, z=st["z"], y=y_out)
+
+    st = {k: t32(v) for k, v in toks[0].items()}
+    conv_g, ssm_g = t32(cv["state"]), t32(sc["state"])
+    conv_e, ssm_e = conv_g.clone(), ssm_g.clone()
+    y_g, y_e = torch.empty((b, d), device="cuda"), torch.empty((b, d), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(conv_g, ssm_g, st, y_g)
+    torch.cuda.current_stream().wait_stream(s)
+    step(conv_e, ssm_e, st, y_e)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(conv_g, ssm_g, st, y_g)
+    for i, tk in enumerate(toks):
+        say("fused decode graph replay %d" % i)
+        for k in st:
+            st[k].copy_(t32(tk[k]))
+        g.replay()
+        step(conv_e, ssm_e, st, y_e)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), i
+        assert torch.equal(conv_g, conv_e) and torch.equal(ssm_g, ssm_e), i
+        ssm_g.mul_(1.0)  # eager work on the graph's own buffers between replays
+        torch.cuda.synchronize()
 
 def test_ssd_forward_graph_replays_match_eager():
     from selective_state_space_03_amd import ops
