@@ -435,8 +435,7 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
                           float* __restrict__ block_states, const float* __restrict__ CBw, int64_t L, int H,
                           int64_t nc, int64_t cw, int64_t nct) {
   constexpr int P = kScanP, W = kScanW, T = kScanThreads;
-  constexpr int SX = P + 4;  // row strides (floats) of the LDS tiles
-  constexpr int SB = N + 4;
+  constexpr int SB = N + 4;  // row strides (floats) of the LDS tiles
   constexpr int SM = W + 4;
   constexpr int NT = N / 16;   // 16-column state tiles
   constexpr int TPW = NT / 2;  // state tiles per wave (32 or 16 tiles over 8 waves)
