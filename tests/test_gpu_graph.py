@@ -94,7 +94,6 @@ def test_decode_step_graph_replays_match_eager():
     assert np.isfinite(host(y_g)).all()
 
 
-
 def test_fused_decode_step_graph_replays_match_eager():
     from selective_state_space_03_amd import ops
     from selective_state_space_03_amd import workloads as W
@@ -137,6 +136,7 @@ def test_fused_decode_step_graph_replays_match_eager():
         assert torch.equal(conv_g, conv_e) and torch.equal(ssm_g, ssm_e), i
         ssm_g.mul_(1.0)  # eager work on the graph's own buffers between replays
         torch.cuda.synchronize()
+
 
 def test_ssd_forward_graph_replays_match_eager():
     from selective_state_space_03_amd import ops
