@@ -292,7 +292,9 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
 //        waves of a row block), M = G exp(cs_i - cs_s) dt_s where s <= i, else 0, to LDS
 //   Y += M X over the step blocks s <= its rows, y = Y + D x, stored;
 // then every wave updates its state tiles: S = exp(cs_last) S + (X exp(cs_last - cs_s)
-// dt_s)^T B (K = W).  The next chunk's x, B and C are loaded into registers while the
+// dt_s)^T B (K = W), computed as its transpose, so that a lane holds 4 consecutive states
+// of one channel: the state is staged as 16-byte rows of [channel][state] (the layout
+// that C S^T reads) and stored as 16-byte pieces.  The next chunk's x, B and C are loaded into registers while the
 // matrix products run.  Sums over s and n have a fixed order: results are
 // deterministic.  LDS rows are padded so that a wavefront's operand reads fall in
 // distinct banks.
@@ -457,15 +459,21 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
   // the causal work of the two phases between barriers
   const int ph = wave >> 2, rb = ph ? 3 - (wave & 3) : (wave & 3);
   const float Dh = Dv ? Dv[h] : 0.f;
-  // state tiles of this wave: rows (pb0 + j) * 16 .., columns nbw * 16 ..
+  // state tiles of this wave, held transposed: tile j covers channels (pb0 + j) * 16 ..
+  // and states nbw * 16 ..; lane l holds channel (pb0 + j) * 16 + l % 16 and the four
+  // states nbw * 16 + 4 (l / 16) + r, r = 0..3
   const int nbw = wave % NT, pb0 = (wave / NT) * TPW;
+  auto st_index = [&](int j) __attribute__((always_inline)) {
+    return ((pb0 + j) * 16 + lr) * N + nbw * 16 + 4 * lq;
+  };
+  // block_states and h_final take 16-byte stores when 16-byte aligned (uniform)
+  const bool bs16 = ((uintptr_t)block_states & 15) == 0, hf16 = ((uintptr_t)h_final & 15) == 0;
 
   f32x4 S[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[j][r] = h0 ? h0[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] : 0.f;
+    for (int r = 0; r < 4; ++r) S[j][r] = h0 ? h0[bh * P * N + st_index(j) + r] : 0.f;
 
   // registers of the next chunk's x, B, C (element tid + T * k of each tile; VEC: piece
   // tid + T * k of 4 values)
@@ -580,14 +588,19 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       wd[tid] = exp2_hw((cl - ci) * kLog2e) * dv;
     }
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+    for (int j = 0; j < TPW; ++j) {
+      *(f32x4*)&Ss[((pb0 + j) * 16 + lr) * SB + nbw * 16 + 4 * lq] = S[j];
+      // the state entering block c, [batch * heads, blocks, P, N]
+      if (SAVE) {
+        float* const bsp = block_states + (bh * nc + c) * P * N + st_index(j);
+        if (bs16) {
+          *(f32x4*)bsp = S[j];
+        } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Ss[((pb0 + j) * 16 + 4 * lq + r) * SB + nbw * 16 + lr] = S[j][r];
-        // the state entering block c, [batch * heads, blocks, P, N]
-        if (SAVE)
-          block_states[((bh * nc + c) * P + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
+          for (int r = 0; r < 4; ++r) bsp[r] = S[j][r];
+        }
       }
+    }
     __syncthreads();
     // C_i.B_s of this wave's causal blocks (step blocks ph, ph + 2 that are <= rb) from
     // the shared table, in flight during C S^T
@@ -669,8 +682,8 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
           yrow[r * ystep + q * 16] = fmaf(Dh, XT[((2 * ph + q) * 16 + lr) * SM + i], Y[q][r]);
       }
     }
-    // ---- state: S = exp(cs_last) S + X^T (wd B)  (the step weight scales the B operand,
-    // which all of the wave's tiles share)
+    // ---- state: S^T = exp(cs_last) S^T + (wd B)^T X  (the step weight scales the A
+    // operand, which all of the wave's tiles share)
     const float el = exp2_hw(cs[W - 1] * kLog2e);
 #pragma unroll
     for (int j = 0; j < TPW; ++j) S[j] *= el;
@@ -688,17 +701,22 @@ ssd_chunk_scan_fwd_kernel(const float* __restrict__ x, const float* __restrict__
       for (int m = 0; m < 4; ++m) {
         const float bo = bv[m] * w4[m];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) S[j] = mfma4(xa[j][m], bo, S[j]);
+        for (int j = 0; j < TPW; ++j) S[j] = mfma4(bo, xa[j][m], S[j]);
       }
     }
     __syncthreads();  // the next chunk's staging overwrites every tile
   }
   if (h_final) {
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+    for (int j = 0; j < TPW; ++j) {
+      float* const hp = h_final + bh * P * N + st_index(j);
+      if (hf16) {
+        *(f32x4*)hp = S[j];
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        h_final[((bh * P) + (pb0 + j) * 16 + 4 * lq + r) * N + nbw * 16 + lr] = S[j][r];
+        for (int r = 0; r < 4; ++r) hp[r] = S[j][r];
+      }
+    }
   }
 }
 
