@@ -870,10 +870,13 @@ ssd_bwd_carry_kernel(const float* __restrict__ dA_cs, const float* __restrict__ 
 
 // the chunk kernel: dx, ddA_cumsum, ddt_out of its heads, dB and dC of its chunk summed
 // over its heads (at dBo / dCo + grp * gstride), dD of each head and chunk into dDp.
-// VEC: x, dy, B, C and the block states are 16-byte aligned, and each thread loads them as
-// 16-byte pieces (x, dy: 4 channels of one step; B, C, states: 4 consecutive values of the
-// block), staged with 16-byte writes.  Either way a thread takes the entering state in
-// the same pieces, so the <G, S> sums agree bit for bit.
+// VEC: x, dy, B, C and the block states are 16-byte aligned (and a chunk's x rows span
+// under 2 GB), and each thread loads them as 16-byte pieces (x, dy: 4 channels of one
+// step; B, C, states: 4 consecutive values of the block), staged with 16-byte writes.  x
+// and dy come through buffer resources over the head's rows of the chunk, ending after
+// its last valid step, at byte offsets that are the same for every head and chunk.
+// Either way a thread takes the entering state in the same pieces, so the <G, S> sums
+// agree bit for bit.
 template <int N, bool VEC>
 __global__ void __launch_bounds__(kScanThreads)
 ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_out,
@@ -986,19 +989,26 @@ ssd_bwd_chunk_kernel(const float* __restrict__ x, const float* __restrict__ dt_o
   float px[VEC ? 1 : XL], py[VEC ? 1 : XL], pc0 = 0.f, pcl = 0.f, pdt = 0.f;
   f32x4 px4[VEC ? XV : 1], py4[VEC ? XV : 1];
   f32x4 pG[TPW];
+  uint32_t xo4[VEC ? XV : 1] = {};  // byte offset of x / dy piece k within a head's rows
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < XV; ++k) {
+      const int i = tid + T * k;
+      xo4[k] = (uint32_t)(((int64_t)(i / (P / 4)) * H * P + 4 * (i % (P / 4))) * 4);
+    }
+  }
+  // bytes from a head's first row of the chunk to the end of its last valid row
+  const int64_t xspan = ((int64_t)(nvw - 1) * H * P + P) * 4;
   auto load_head = [&](int hn) __attribute__((always_inline)) {
     const int64_t bhn = b * H + hn;
     if constexpr (VEC) {
-      const float* const xb = x + ((b * L + t0) * H + hn) * P;
-      const float* const yb = dy + ((b * L + t0) * H + hn) * P;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      // pieces of steps past the end of the sequence read 0
+      const auto rxs = tile_rsrc(x + ((b * L + t0) * H + hn) * P, xspan);
+      const auto rys = tile_rsrc(dy + ((b * L + t0) * H + hn) * P, xspan);
 #pragma unroll
       for (int k = 0; k < XV; ++k) {
-        const int i = tid + T * k, st = i / (P / 4);
-        const int64_t o = (int64_t)st * H * P + 4 * (i % (P / 4));
-        const bool v = st < nv;
-        px4[k] = v ? *(const f32x4*)(xb + o) : zero;
-        py4[k] = v ? *(const f32x4*)(yb + o) : zero;
+        px4[k] = ld16(rxs, xo4[k]);
+        py4[k] = ld16(rys, xo4[k]);
       }
     } else if (nv >= W) {  // a whole chunk (uniform): no per-element checks
       const float* const xc = x + xrow0 + (int64_t)hn * P;
@@ -1599,7 +1609,9 @@ extern "C" int ssm_ssd_chunk_scan_bwd(const float* x, const float* dt_out, const
   hipLaunchKernelGGL(carry, dim3((unsigned)(batch * heads)), dim3(kScanThreads), 0, stream, dA_cumsum, C, dy,
                      dh_final, Gbuf, dh0, seqlen, (int)heads, nc);
   if (hipGetLastError() != hipSuccess) return SSM_ERR_HIP;
-  const bool vec = aligned16(x) && aligned16(dy) && aligned16(B) && aligned16(C) && aligned16(block_states);
+  // (the wide path addresses a chunk's x and dy rows with 32-bit byte offsets)
+  const bool vec = aligned16(x) && aligned16(dy) && aligned16(B) && aligned16(C) && aligned16(block_states) &&
+                   (double)kScanW * heads * headdim * 4 < (double)((int64_t)1 << 31);
   auto chunk_k = dstate == 128 ? (vec ? ssd_bwd_chunk_kernel<128, true> : ssd_bwd_chunk_kernel<128, false>)
                                : (vec ? ssd_bwd_chunk_kernel<64, true> : ssd_bwd_chunk_kernel<64, false>);
   hipLaunchKernelGGL(chunk_k, dim3((unsigned)(batch * nc * sp.ngrp)), dim3(kScanThreads), 0, stream, x, dt_out,

@@ -11,8 +11,9 @@ heads of 64, d_state 128) sampled (batch, head) sequences are compared with the 
 run on that sequence alone (sequences are independent).  Around the head count at which a
 block's x rows reach 2 GB (131071 and 131072 heads of 64), where the scan switches from
 16-byte to one-value loads, sampled heads are compared the same way.  The backward is
-checked the same way at 266400 heads of 64, where one chunk's dy rows span more than
-4 GB.  Repeated runs are
+checked the same way at 131071 and 131072 heads of 64 (its chunk kernel's 16-byte x and
+dy loads switch to one-value loads at 2 GB of a chunk's rows) and at 266400 heads of 64,
+where one chunk's dy rows span more than 4 GB.  Repeated runs are
 bit-identical, and unsupported sizes are refused.
 """
 import numpy as np
@@ -308,6 +309,37 @@ def test_scan_backward_full_workload_sampled_sequences():
         assert rel_err(g["dh0"][b, h], r["dh0"][0, 0]) <= RTOL_F32
         assert rel_err(g["ddt_raw"][b, :, h], r["ddt_raw"][0, :, 0]) <= RTOL_F32
 
+
+
+@pytest.mark.parametrize("heads", [131071, 131072])
+def test_scan_backward_heads_at_the_wide_load_offset_bound(heads):
+    """The chunk kernel's 16-byte x and dy loads address a chunk's rows with 32-bit byte
+    offsets from the head's first row, so from 2 GB of rows (131072 heads of 64) on, the
+    backward takes the one-value path.  Both sides of the bound, a two-step sequence:
+    dx, dh0 and the raw step gradient of sampled heads against the oracle."""
+    from selective_state_space_03_amd import ops
+    w = W.SSD_SCAN_WORKLOADS["ssd_scan_small"]
+    inp = W.make_ssd_scan_inputs(w, batch=1, seqlen=2, heads=heads, dstate=64, seed=w.seed + heads)
+    b, l, h, p = inp["x"].shape
+    n = inp["B"].shape[-1]
+    dy = np.random.default_rng(heads).standard_normal(inp["x"].shape).astype(np.float32)
+    say("ssd scan bwd, %d heads of 64, two steps" % heads)
+    dt, A, dtb = to_dev32(inp["dt"]), to_dev32(inp["A"]), to_dev32(inp["dt_bias"])
+    cs, dto = ops.ssd_chunk_cumsum_fwd(dt, A, inp["chunk"], dt_bias=dtb)
+    x, Bd, Cd, Dd = to_dev32(inp["x"]), to_dev32(inp["B"]), to_dev32(inp["C"]), to_dev32(inp["D"])
+    bs = torch.empty(ops.ssd_block_states_shape(b, l, h, p, n), dtype=torch.float32, device="cuda")
+    ops.ssd_chunk_scan_fwd(x, dto, cs, Bd, Cd, D=Dd, h_final=None, block_states=bs)
+    g = ops.ssd_chunk_scan_bwd(x, dto, cs, Bd, Cd, to_dev32(dy), bs, D=Dd, return_dh0=True)
+    gc = ops.ssd_chunk_cumsum_bwd(g["ddA_cumsum"], g["ddt_out"], dt, A, dt_bias=dtb)
+    torch.cuda.synchronize()
+    for hh in (0, 77777, h - 1):
+        one = {"seqlen": l, "chunk": inp["chunk"], "dt": inp["dt"][:, :, hh:hh + 1], "A": inp["A"][hh:hh + 1],
+               "dt_bias": inp["dt_bias"][hh:hh + 1], "x": inp["x"][:, :, hh:hh + 1], "B": inp["B"], "C": inp["C"],
+               "D": inp["D"][hh:hh + 1], "h0": None}
+        r = oracle_bwd(one, dy[:, :, hh:hh + 1], None)
+        assert rel_err(host(g["dx"][:, :, hh]), r["dx"][:, :, 0]) <= RTOL_F32, hh
+        assert rel_err(host(g["dh0"][:, hh]), r["dh0"][:, 0]) <= RTOL_F32, hh
+        assert rel_err(host(gc["ddt"][:, :, hh]), r["ddt_raw"][:, :, 0]) <= RTOL_F32, hh
 
 
 def test_scan_backward_rows_more_than_4gb_apart_in_a_chunk():
