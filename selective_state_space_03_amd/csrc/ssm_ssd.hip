@@ -118,6 +118,13 @@ ssd_cumsum_fwd_kernel(const float* __restrict__ dt, const float* __restrict__ A,
   const int h0 = blockIdx.y * kHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float carry[kHPW] = {};
+  // A of the wave's heads, loaded with the first staging loads rather than after its barrier
+  float av[kHPW];
+#pragma unroll
+  for (int k = 0; k < kHPW; ++k) {
+    const int h = h0 + wave * kHPW + k;
+    av[k] = h < m.H ? A[h] : 0.f;
+  }
   for (int64_t l0 = 0; l0 < m.W; l0 += kSub) {
     const int n = (int)(m.W - l0 < kSub ? m.W - l0 : kSub);
     // stage dt_out of [n steps x 16 heads], read in 64-byte head rows; all of a
@@ -134,7 +141,7 @@ ssd_cumsum_fwd_kernel(const float* __restrict__ dt, const float* __restrict__ A,
     for (int k = 0; k < kHPW; ++k) {
       const int hh = wave * kHPW + k, h = h0 + hh;
       if (h >= m.H) break;  // wave-uniform
-      const float a = A[h];
+      const float a = av[k];
       const float4 q = *reinterpret_cast<const float4*>(&tile[hh][4 * lane]);
       float p[4];
       p[0] = q.x * a;
@@ -170,22 +177,19 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
   const int h0 = blockIdx.y * kHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float carry[kHPW] = {}, pa[kHPW] = {}, pb[kHPW] = {};
+  // A of the wave's heads, loaded with the first staging loads rather than after its barrier
+  float av[kHPW];
+#pragma unroll
+  for (int k = 0; k < kHPW; ++k) {
+    const int h = h0 + wave * kHPW + k;
+    av[k] = h < m.H ? A[h] : 0.f;
+  }
   const int64_t nsub = (m.W + kSub - 1) / kSub;
   for (int64_t s_i = nsub - 1; s_i >= 0; --s_i) {  // sub-tiles from the end of the chunk
     const int64_t l0 = s_i * kSub;
     const int n = (int)(m.W - l0 < kSub ? m.W - l0 : kSub);
-    // stage raw = dt + dt_bias of [n steps x 16 heads]
-    {
-      float raw[kStage];
-      stage_load(dt, dt_bias, b, c * m.W + l0, n, h0, tid, m, raw);
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) {
-        const int i = tid + 256 * j;
-        tile[i % kHeads][i / kHeads] = raw[j];
-      }
-    }
-    __syncthreads();
-    // the ddA and ddt_out rows of the wave's 4 heads, all loads issued first
+    // the ddA and ddt_out rows of the wave's heads, issued before the dt loads of the
+    // staging below, so that both sets are in flight together (one round trip)
     const int nl = n - 4 * lane;
     float dA4s[kHPW][4], dO4s[kHPW][4];
 #pragma unroll
@@ -199,11 +203,22 @@ ssd_cumsum_bwd_kernel(const float* __restrict__ ddA, const float* __restrict__ d
         ld4<VEC>(ddt_out + row, nl, dO4s[k]);
       }
     }
+    // stage raw = dt + dt_bias of [n steps x kHeads heads]
+    {
+      float raw[kStage];
+      stage_load(dt, dt_bias, b, c * m.W + l0, n, h0, tid, m, raw);
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) {
+        const int i = tid + 256 * j;
+        tile[i % kHeads][i / kHeads] = raw[j];
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kHPW; ++k) {
       const int hh = wave * kHPW + k, h = h0 + hh;
       if (h >= m.H) break;  // wave-uniform
-      const float a = A[h];
+      const float a = av[k];
       const float(&dA4)[4] = dA4s[k];
       const float(&dO4)[4] = dO4s[k];
       // reverse running sums: inside the lane, across lanes, then the later sub-tiles
