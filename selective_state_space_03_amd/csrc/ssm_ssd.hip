@@ -309,10 +309,10 @@ ssd_param_reduce_kernel(const float* __restrict__ part_a, const float* __restric
 // then every wave updates its state tiles: S = exp(cs_last) S + (X exp(cs_last - cs_s)
 // dt_s)^T B (K = W), computed as its transpose, so that a lane holds 4 consecutive states
 // of one channel: the state is staged as 16-byte rows of [channel][state] (the layout
-// that C S^T reads) and stored as 16-byte pieces.  The next chunk's x, B and C are loaded into registers while the
-// matrix products run.  Sums over s and n have a fixed order: results are
-// deterministic.  LDS rows are padded so that a wavefront's operand reads fall in
-// distinct banks.
+// that C S^T reads) and stored as 16-byte pieces.  The next chunk's x, B and C are
+// loaded into registers while the matrix products run.  Sums over s and n have a fixed
+// order: results are deterministic.  LDS rows are padded so that a wavefront's operand
+// reads fall in distinct banks.
 constexpr int kScanP = 64;  // headdim
 constexpr int kScanW = 64;  // steps per block (the chunk width is a multiple of it)
 constexpr int kScanThreads = 512;
